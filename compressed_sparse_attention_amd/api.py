@@ -1,0 +1,243 @@
+"""Python binding of libcsa (ctypes).  Argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; it passes their device pointers,
+sizes and strides, plus the current torch stream, to the library.  All
+computation happens in the library's HIP kernels.  If ``libcsa.so`` is not
+built, the first call raises ``CSAError``: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "csa.h")
+
+CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(5)
+CSA_F32, CSA_BF16 = 0, 1
+_STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
+           4: "CSA_ERR_HIP"}
+
+
+class CSAError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "csa_abi_version": (ctypes.c_int, []),
+    "csa_last_error": (ctypes.c_char_p, []),
+    "csa_project": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
+                                   _i64, _vp]),
+    "csa_compress": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                    _i64, _vp]),
+    "csa_index_topk_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "csa_index_topk": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "csa_sparse_mqa_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "csa_sparse_mqa": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _sz, _vp]),
+    "csa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "csa_timing_reset": (ctypes.c_int, []),
+    "csa_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(_i64)]),
+}
+
+
+def header_functions():
+    """Names of the functions declared in include/csa.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:csa_status|int|const char\*)\s+(csa_\w+)\s*\(", text, re.M)))
+
+
+def lib():
+    """Load libcsa.so (once).  Raises CSAError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CSAError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m compressed_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != CSA_OK:
+        msg = lib().csa_last_error().decode(errors="replace")
+        raise CSAError(f"{what} failed with {_STATUS.get(status, status)}: {msg}", status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise CSAError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CSAError("tensor must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _rowmajor(t: torch.Tensor, name: str) -> int:
+    """Leading dimension of a 2-D row-major view (unit column stride)."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise CSAError(f"{name} must be a 2-D view with unit column stride")
+    return t.stride(0)
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise CSAError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+
+def csa_abi_version() -> int:
+    return lib().csa_abi_version()
+
+
+def csa_project(X: torch.Tensor, Wt: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+    """Y = X . Wt^T  (X [M,K], Wt [N,K] = W transposed, Y [M,N]; views allowed)."""
+    M, K = X.shape
+    N = Wt.shape[0]
+    if Wt.shape[1] != K or tuple(Y.shape) != (M, N):
+        raise CSAError("csa_project: shape mismatch")
+    if X.dtype != Wt.dtype:
+        raise CSAError("csa_project: X and Wt dtypes differ")
+    _check(lib().csa_project(_dt(X), _dt(Y), M, N, K, _ptr(X), _rowmajor(X, "X"), _ptr(Wt),
+                             _rowmajor(Wt, "Wt"), _ptr(Y), _rowmajor(Y, "Y"), _stream(X.device)),
+           "csa_project")
+    return Y
+
+
+def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, Ccomp: torch.Tensor) -> torch.Tensor:
+    """Eqs 3-4.  Ca/Cb/Za/Zb: [n, c] views sharing one leading dimension; Ba/Bb [m, c]."""
+    n, c = Ca.shape
+    ld = _rowmajor(Ca, "Ca")
+    for t, nm in ((Cb, "Cb"), (Za, "Za"), (Zb, "Zb")):
+        if tuple(t.shape) != (n, c) or _rowmajor(t, nm) != ld or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress: Ca, Cb, Za, Zb must share shape, dtype and leading dimension")
+    for t, nm in ((Ba, "Ba"), (Bb, "Bb")):
+        _contig(t, nm)
+        if tuple(t.shape) != (m, c):
+            raise CSAError(f"csa_compress: {nm} must be [m, c]")
+    if tuple(Ccomp.shape) != (n // m, c):
+        raise CSAError("csa_compress: Ccomp must be [n // m, c]")
+    _check(lib().csa_compress(_dt(Ca), n, m, c, _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _ptr(Ba),
+                              _ptr(Bb), _ptr(Ccomp), _rowmajor(Ccomp, "Ccomp"), _stream(Ca.device)),
+           "csa_compress")
+    return Ccomp
+
+
+def csa_index_topk_workspace(n_queries: int, max_cand: int, n_hI: int, k: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_index_topk_workspace(n_queries, max_cand, n_hI, k, ctypes.byref(b)),
+           "csa_index_topk_workspace")
+    return b.value
+
+
+def csa_index_topk(qI, wI, KIcomp, m: int, k: int, max_cand: int, idx_out, score_out=None,
+                   q_seq=None, q_pos=None, kv_offset=None, workspace=None):
+    """Eqs 8-9.  qI [nq, n_hI, cI], wI [nq, n_hI] fp32, KIcomp [rows, cI] -> idx_out [nq, k]."""
+    nq, nhI, cI = qI.shape
+    for t, nm in ((qI, "qI"), (wI, "wI"), (KIcomp, "KIcomp"), (idx_out, "idx_out")):
+        _contig(t, nm)
+    if wI.dtype != torch.float32 or tuple(wI.shape) != (nq, nhI):
+        raise CSAError("csa_index_topk: wI must be fp32 [n_queries, n_hI]")
+    if idx_out.dtype != torch.int32 or tuple(idx_out.shape) != (nq, k):
+        raise CSAError("csa_index_topk: idx_out must be int32 [n_queries, k]")
+    if score_out is not None:
+        _contig(score_out, "score_out")
+        if score_out.dtype != torch.float32 or tuple(score_out.shape) != (nq, k):
+            raise CSAError("csa_index_topk: score_out must be fp32 [n_queries, k]")
+    if q_seq is not None and (q_seq.dtype != torch.int32 or q_seq.numel() != nq):
+        raise CSAError("csa_index_topk: q_seq must be int32 [n_queries]")
+    if q_pos is not None and (q_pos.dtype != torch.int64 or q_pos.numel() != nq):
+        raise CSAError("csa_index_topk: q_pos must be int64 [n_queries]")
+    if kv_offset is not None and kv_offset.dtype != torch.int64:
+        raise CSAError("csa_index_topk: kv_offset must be int64")
+    need = csa_index_topk_workspace(nq, max_cand, nhI, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qI.device)
+    _check(lib().csa_index_topk(_dt(qI), nq, nhI, cI, m, k, _ptr(qI), _ptr(wI), _ptr(KIcomp), _ptr(q_seq),
+                                _ptr(q_pos), _ptr(kv_offset), max_cand, _ptr(idx_out), _ptr(score_out),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(qI.device)),
+           "csa_index_topk")
+    return idx_out
+
+
+def csa_sparse_mqa_workspace(n_queries: int, n_h: int, c: int, k: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_sparse_mqa_workspace(n_queries, n_h, c, k, ctypes.byref(b)), "csa_sparse_mqa_workspace")
+    return b.value
+
+
+def csa_sparse_mqa(q, Ccomp, idx, scale: float, o, lse=None, q_seq=None, kv_offset=None, workspace=None):
+    """Eq 11.  q [nq, n_h, c], Ccomp [rows, c], idx [nq, k] int32 -> o [nq, n_h, c] (+ lse [nq, n_h])."""
+    nq, nh, c = q.shape
+    k = idx.shape[1]
+    for t, nm in ((q, "q"), (Ccomp, "Ccomp"), (idx, "idx"), (o, "o")):
+        _contig(t, nm)
+    if idx.dtype != torch.int32 or idx.shape[0] != nq:
+        raise CSAError("csa_sparse_mqa: idx must be int32 [n_queries, k]")
+    if o.dtype != q.dtype or tuple(o.shape) != (nq, nh, c) or Ccomp.dtype != q.dtype:
+        raise CSAError("csa_sparse_mqa: o/Ccomp must match q's dtype and o q's shape")
+    if lse is not None:
+        _contig(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (nq, nh):
+            raise CSAError("csa_sparse_mqa: lse must be fp32 [n_queries, n_h]")
+    if q_seq is not None and (q_seq.dtype != torch.int32 or q_seq.numel() != nq):
+        raise CSAError("csa_sparse_mqa: q_seq must be int32 [n_queries]")
+    if kv_offset is not None and kv_offset.dtype != torch.int64:
+        raise CSAError("csa_sparse_mqa: kv_offset must be int64")
+    need = csa_sparse_mqa_workspace(nq, nh, c, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().csa_sparse_mqa(_dt(q), nq, nh, c, k, float(scale), _ptr(q), _ptr(Ccomp), _ptr(q_seq),
+                                _ptr(kv_offset), _ptr(idx), _ptr(o), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(q.device)),
+           "csa_sparse_mqa")
+    return o
+
+
+def csa_timing_enable(on: bool = True):
+    _check(lib().csa_timing_enable(1 if on else 0), "csa_timing_enable")
+
+
+def csa_timing_reset():
+    _check(lib().csa_timing_reset(), "csa_timing_reset")
+
+
+def csa_timing_read(name: str):
+    ms = ctypes.c_double(0)
+    n = _i64(0)
+    _check(lib().csa_timing_read(name.encode(), ctypes.byref(ms), ctypes.byref(n)), "csa_timing_read")
+    return ms.value, n.value

@@ -1,0 +1,288 @@
+// C-ABI layer of libcsa: argument validation, device check, workspace layout,
+// dispatch to the kernels and the optional kernel-timing instrumentation.
+// Host code only.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+csa_status fail(csa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+csa_status hip_fail(hipError_t e, const char* what) {
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// device check (once per device)
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];  // 1 = gfx950, 0 = other, -1 = query failed
+char g_dev_arch[kMaxDevices][64];
+
+csa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+      g_dev_ok[dev] = -1;
+      return;
+    }
+    snprintf(g_dev_arch[dev], sizeof(g_dev_arch[dev]), "%s", p.gcnArchName);
+    g_dev_ok[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  if (g_dev_ok[dev] == -1) return fail(CSA_ERR_HIP, "hipGetDeviceProperties failed for device %d", dev);
+  if (g_dev_ok[dev] == 0)
+    return fail(CSA_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 (MI355X) only", dev,
+                g_dev_arch[dev]);
+  return CSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int vec_elems(csa_dtype dt) { return dt == CSA_BF16 ? 8 : 4; }
+bool dtype_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+#define CSA_REQUIRE(cond, ...)                                   \
+  do {                                                           \
+    if (!(cond)) return fail(CSA_ERR_INVALID_ARG, __VA_ARGS__);  \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// kernel timing
+// ---------------------------------------------------------------------------
+std::atomic<bool> g_timing{false};
+std::mutex g_timing_mu;
+struct Family {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  double ms = 0.0;
+  int64_t launches = 0;
+};
+std::map<std::string, Family> g_families;
+
+long scores_ld(long max_cand) { return (max_cand + 3) & ~3L; }
+
+}  // namespace
+
+namespace csa {
+
+TimedScope::TimedScope(const char* family, hipStream_t s) : family_(family), stream_(s) {
+  if (!g_timing.load(std::memory_order_relaxed)) return;
+  if (hipEventCreate(&start_) != hipSuccess) {
+    start_ = nullptr;
+    return;
+  }
+  (void)hipEventRecord(start_, stream_);
+}
+
+TimedScope::~TimedScope() {
+  if (!start_) return;
+  hipEvent_t stop = nullptr;
+  if (hipEventCreate(&stop) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    return;
+  }
+  (void)hipEventRecord(stop, stream_);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_families[family_].pending.emplace_back(start_, stop);
+}
+
+}  // namespace csa
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_last_error(void) { return g_error.c_str(); }
+
+csa_status csa_timing_enable(int on) {
+  g_timing.store(on != 0);
+  return CSA_OK;
+}
+
+csa_status csa_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& kv : g_families) {
+    for (auto& pr : kv.second.pending) {
+      (void)hipEventSynchronize(pr.second);
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
+  }
+  g_families.clear();
+  return CSA_OK;
+}
+
+csa_status csa_timing_read(const char* name, double* total_ms, int64_t* launches) {
+  CSA_REQUIRE(name && total_ms && launches, "csa_timing_read: null argument");
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  auto it = g_families.find(name);
+  if (it == g_families.end()) {
+    *total_ms = 0.0;
+    *launches = 0;
+    return CSA_OK;
+  }
+  Family& f = it->second;
+  for (auto& pr : f.pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+    if (e != hipSuccess) {
+      f.pending.clear();
+      return hip_fail(e, "csa_timing_read");
+    }
+    f.ms += ms;
+    f.launches += 1;
+  }
+  f.pending.clear();
+  *total_ms = f.ms;
+  *launches = f.launches;
+  return CSA_OK;
+}
+
+csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                       const void* X, int64_t ldx, const void* Wt, int64_t ldw, void* Y,
+                       int64_t ldy, void* stream) {
+  CSA_REQUIRE(dtype_ok(in_dt) && dtype_ok(out_dt), "csa_project: unknown dtype");
+  CSA_REQUIRE(!(in_dt == CSA_F32 && out_dt == CSA_BF16),
+              "csa_project: fp32 input with bf16 output is not supported");
+  CSA_REQUIRE(M > 0 && N > 0 && K > 0, "csa_project: M, N, K must be positive (got %lld, %lld, %lld)",
+              (long long)M, (long long)N, (long long)K);
+  CSA_REQUIRE(M <= 0x7FFFFFFF && N <= 0x7FFFFFFF && K <= 0x7FFFFFFF, "csa_project: size exceeds 2^31-1");
+  CSA_REQUIRE(K % 8 == 0, "csa_project: K must be a multiple of 8 (got %lld)", (long long)K);
+  CSA_REQUIRE(X && Wt && Y, "csa_project: null pointer");
+  CSA_REQUIRE(aligned16(X) && aligned16(Wt) && aligned16(Y), "csa_project: pointers must be 16-byte aligned");
+  const int v = vec_elems(in_dt);
+  CSA_REQUIRE(ldx >= K && ldw >= K && ldy >= N, "csa_project: leading dimension smaller than row length");
+  CSA_REQUIRE(ldx % v == 0 && ldw % v == 0, "csa_project: ldx/ldw must keep rows 16-byte aligned");
+  CSA_REQUIRE(ldy % vec_elems(out_dt) == 0, "csa_project: ldy must keep rows 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_gemm(in_dt, out_dt, M, N, K, X, ldx, Wt, ldw, Y, ldy, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_project launch");
+}
+
+csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const void* Ca,
+                        const void* Cb, const void* Za, const void* Zb, int64_t ld_in,
+                        const void* Ba, const void* Bb, void* Ccomp, int64_t ld_out,
+                        void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress: unknown dtype");
+  CSA_REQUIRE(n >= 0, "csa_compress: n must be >= 0");
+  CSA_REQUIRE(m >= 1 && m <= 64, "csa_compress: m must be in [1, 64] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress: c must be a positive multiple of 4 (got %d)", c);
+  if (n / m == 0) return CSA_OK;
+  CSA_REQUIRE(Ca && Cb && Za && Zb && Ba && Bb && Ccomp, "csa_compress: null pointer");
+  CSA_REQUIRE(aligned16(Ca) && aligned16(Cb) && aligned16(Za) && aligned16(Zb) && aligned16(Ba) &&
+                  aligned16(Bb) && aligned16(Ccomp),
+              "csa_compress: pointers must be 16-byte aligned");
+  const int v = vec_elems(dt);
+  CSA_REQUIRE(ld_in >= c && ld_out >= c, "csa_compress: leading dimension smaller than c");
+  CSA_REQUIRE(ld_in % v == 0 && ld_out % v == 0, "csa_compress: leading dimensions must keep rows 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_compress(dt, n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, Ccomp, ld_out,
+                                      (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress launch");
+}
+
+csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t k,
+                                    size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_index_topk_workspace: null bytes");
+  CSA_REQUIRE(n_queries >= 0 && max_cand >= 0, "csa_index_topk_workspace: negative size");
+  CSA_REQUIRE(n_hI >= 1 && k >= 1, "csa_index_topk_workspace: n_hI and k must be >= 1");
+  *bytes = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float));
+  return CSA_OK;
+}
+
+csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m,
+                          int32_t k, const void* qI, const float* wI, const void* KIcomp,
+                          const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
+                          int64_t max_cand, int32_t* idx_out, float* score_out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_index_topk: unknown dtype");
+  CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_index_topk: bad n_queries");
+  CSA_REQUIRE(n_hI >= 1 && n_hI <= 64, "csa_index_topk: n_hI must be in [1, 64] (got %d)", n_hI);
+  CSA_REQUIRE(cI == 32 || cI == 64 || cI == 128 || cI == 256,
+              "csa_index_topk: cI must be 32, 64, 128 or 256 (got %d)", cI);
+  CSA_REQUIRE(m >= 1, "csa_index_topk: m must be >= 1");
+  CSA_REQUIRE(k >= 1 && k <= (1 << 24), "csa_index_topk: k must be in [1, 2^24]");
+  CSA_REQUIRE(max_cand >= 0 && max_cand <= 0x7FFFFFFF, "csa_index_topk: bad max_cand");
+  if (n_queries == 0) return CSA_OK;
+  CSA_REQUIRE(qI && wI && KIcomp && idx_out, "csa_index_topk: null pointer");
+  CSA_REQUIRE(aligned16(qI) && aligned16(wI) && aligned16(KIcomp) && aligned16(idx_out),
+              "csa_index_topk: pointers must be 16-byte aligned");
+  size_t need = 0;
+  csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &need);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "csa_index_topk: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  CSA_REQUIRE(workspace == nullptr || aligned16(workspace), "csa_index_topk: workspace must be 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* scores = (float*)workspace;
+  const long ld = scores_ld(max_cand);
+  hipError_t e = csa::launch_indexer(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, q_seq, q_pos, kv_offset,
+                                     max_cand, scores, ld, s);
+  if (e != hipSuccess) return hip_fail(e, "csa_index_topk indexer launch");
+  e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, idx_out, score_out, s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk top-k launch");
+}
+
+csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_sparse_mqa_workspace: null bytes");
+  CSA_REQUIRE(n_queries >= 0 && n_h >= 1 && c >= 1 && k >= 1, "csa_sparse_mqa_workspace: bad size");
+  *bytes = csa::mqa_workspace_bytes(n_queries, n_h, c, k);
+  return CSA_OK;
+}
+
+csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
+                          float scale, const void* q, const void* Ccomp, const int32_t* q_seq,
+                          const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_sparse_mqa: unknown dtype");
+  CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_sparse_mqa: bad n_queries");
+  CSA_REQUIRE(n_h >= 1 && n_h <= 256, "csa_sparse_mqa: n_h must be in [1, 256] (got %d)", n_h);
+  CSA_REQUIRE(csa::mqa_supported_c(c), "csa_sparse_mqa: c must be 64, 128, 256, 512 or 1024 (got %d)", c);
+  CSA_REQUIRE(k >= 1 && k <= (1 << 24), "csa_sparse_mqa: k must be in [1, 2^24]");
+  CSA_REQUIRE(scale == scale && scale > 0.f && scale < 1e30f, "csa_sparse_mqa: scale must be positive and finite");
+  if (n_queries == 0) return CSA_OK;
+  CSA_REQUIRE(q && Ccomp && idx && o, "csa_sparse_mqa: null pointer");
+  CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(idx) && aligned16(o),
+              "csa_sparse_mqa: pointers must be 16-byte aligned");
+  const size_t need = csa::mqa_workspace_bytes(n_queries, n_h, c, k);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  CSA_REQUIRE(aligned16(workspace), "csa_sparse_mqa: workspace must be 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx, o, lse,
+                                 workspace, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_sparse_mqa launch");
+}
+
+}  // extern "C"

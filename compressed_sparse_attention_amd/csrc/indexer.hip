@@ -1,0 +1,286 @@
+// Lightning indexer, eq 8 of "Compressed Sparse Attention" (section "Lightning
+// Indexer for Sparse Selection"):
+//
+//   I[t, s] = sum_h w[t, h] * ReLU(q^I[t, h] . K^IComp[s]),  s < n_cand(t).
+//
+// The head dot products are one contraction [heads x cI] . [cI x keys]; it
+// runs on MFMA with heads as the 16-row M side and keys as the 16-column N
+// side.  The accumulator then holds, per lane, 4 heads of one key, so ReLU,
+// the head weight and the head sum are an in-register fused epilogue plus
+// two cross-lane adds.
+//
+// Contraction slots are mapped so that a lane reads ONE contiguous run of a
+// key row: in step kk, lane group g's slot j is dimension g*8*KK + 8*kk + j
+// (KK = cI/32 steps).  The query fragments use the same map.
+//
+// Two kernels:
+//  * indexer_sweep -- any query/sequence layout (decode, ragged batches).
+//    A workgroup takes one query and a chunk of its candidates; every wave
+//    streams 16-key groups straight from HBM into MFMA operands (no LDS),
+//    with the next group's loads in flight while the current one computes.
+//  * indexer_prefill -- one sequence, query t at position t.  A workgroup
+//    owns 16 consecutive tokens (2 per wave, q^I held in registers) and walks
+//    the causal key prefix once in 64-key tiles staged through LDS, so each
+//    key tile is fetched once per 16 tokens.  Heaviest token blocks first.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+namespace {
+
+constexpr int kSweepKeysPerWG = 512;
+
+template <typename T, int KK, int NHT>
+__global__ __launch_bounds__(256) void indexer_sweep_kernel(
+    int nhI, int m, const T* __restrict__ qI, const float* __restrict__ wI,
+    const T* __restrict__ K, const int32_t* __restrict__ q_seq, const int64_t* __restrict__ q_pos,
+    const int64_t* __restrict__ kv_off, long max_cand, float* __restrict__ scores, long ld_sc,
+    int chunks) {
+  constexpr int CI = 32 * KK;
+  const int r = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - r * chunks;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const long pos = q_pos ? q_pos[r] : (long)r;
+  const int seq = q_seq ? q_seq[r] : 0;
+  const long off = kv_off ? kv_off[seq] : 0;
+  long ncand = pos > 0 ? pos / m : 0;
+  ncand = ncand < max_cand ? ncand : max_cand;
+  const long chunk0 = (long)chunk * kSweepKeysPerWG;
+  if (chunk0 >= ncand) return;
+  const long chunk_end = min(chunk0 + (long)kSweepKeysPerWG, ncand);
+
+  Frag<T> qa[NHT][KK];
+  float wv[NHT][4];
+#pragma unroll
+  for (int mt = 0; mt < NHT; ++mt) {
+    const int head = 16 * mt + c16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (head < nhI)
+        qa[mt][kk].load(qI + ((long)r * nhI + head) * CI + g * 8 * KK + 8 * kk);
+      else
+        qa[mt][kk].zero();
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = 16 * mt + 4 * g + rr;
+      wv[mt][rr] = h < nhI ? wI[(long)r * nhI + h] : 0.f;
+    }
+  }
+
+  const T* Kb = K + off * CI + g * 8 * KK;
+  auto fetch = [&](long s0, Frag<T>* kb) {
+    const long s = s0 + c16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (s < chunk_end)
+        kb[kk].load(Kb + s * CI + 8 * kk);
+      else
+        kb[kk].zero();
+    }
+  };
+
+  Frag<T> cur[KK], nxt[KK];
+  long s0 = chunk0 + 16 * wave;
+  if (s0 < chunk_end) fetch(s0, cur);
+  for (; s0 < chunk_end; s0 += 64) {
+    if (s0 + 64 < chunk_end) fetch(s0 + 64, nxt);
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NHT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) mma(acc, qa[mt][kk], cur[kk]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[mt][rr], fmaxf(acc[rr], 0.f), part);
+    }
+    part = wave_sum_xor_16_32(part);
+    const long s = s0 + c16;
+    if (g == 0 && s < chunk_end) scores[(long)r * ld_sc + s] = part;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) cur[kk] = nxt[kk];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill: tokens t0 .. t0+15 per workgroup (8 waves x 2 tokens)
+// ---------------------------------------------------------------------------
+constexpr int kPfWaves = 8;
+constexpr int kPfTokPerWave = 2;
+constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
+constexpr int kPfTile = 64;  // keys per LDS tile
+
+template <typename T, int KK, int NHT>
+__global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, int m,
+                                                              const T* __restrict__ qI,
+                                                              const float* __restrict__ wI,
+                                                              const T* __restrict__ K,
+                                                              const int64_t* __restrict__ kv_off,
+                                                              long max_cand,
+                                                              float* __restrict__ scores,
+                                                              long ld_sc) {
+  constexpr int CI = 32 * KK;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PITCH = CI + VEC;  // padded LDS row (elements)
+  constexpr int CHUNKS = CI / VEC;
+  constexpr int TILE_VECS = kPfTile * CHUNKS;
+  __shared__ __attribute__((aligned(16))) T Ks[2][kPfTile * PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nblocks = (n + kPfTokens - 1) / kPfTokens;
+  const long t0 = (long)(nblocks - 1 - (int)blockIdx.x) * kPfTokens;  // heaviest first
+
+  // candidate count of the last token of this block bounds the key range
+  const long t_last = min(t0 + kPfTokens - 1, (long)n - 1);
+  long kend = t_last / m;
+  kend = kend < max_cand ? kend : max_cand;
+  if (kend <= 0) return;
+
+  Frag<T> qa[kPfTokPerWave][NHT][KK];
+  float wv[kPfTokPerWave][NHT][4];
+  long tok[kPfTokPerWave], nc[kPfTokPerWave];
+#pragma unroll
+  for (int tt = 0; tt < kPfTokPerWave; ++tt) {
+    const long t = t0 + wave * kPfTokPerWave + tt;
+    tok[tt] = t;
+    long c = t < n ? t / m : 0;
+    nc[tt] = c < max_cand ? c : max_cand;
+    const bool live = t < n;
+#pragma unroll
+    for (int mt = 0; mt < NHT; ++mt) {
+      const int head = 16 * mt + c16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (live && head < nhI)
+          qa[tt][mt][kk].load(qI + (t * nhI + head) * CI + g * 8 * KK + 8 * kk);
+        else
+          qa[tt][mt][kk].zero();
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int h = 16 * mt + 4 * g + rr;
+        wv[tt][mt][rr] = (live && h < nhI) ? wI[t * nhI + h] : 0.f;
+      }
+    }
+  }
+
+  if (kv_off) K += kv_off[0] * CI;
+  const int ntiles = (int)((kend + kPfTile - 1) / kPfTile);
+  constexpr int LOADS = (TILE_VECS + 511) / 512;
+  u32x4 stage[LOADS];
+  auto fetch = [&](int tile) {
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int v = tid + p * 512;
+      const long key = (long)tile * kPfTile + v / CHUNKS;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      stage[p] = (v < TILE_VECS && key < kend)
+                     ? *reinterpret_cast<const u32x4*>(K + key * CI + (v % CHUNKS) * VEC)
+                     : z;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < LOADS; ++p) {
+      const int v = tid + p * 512;
+      if (v < TILE_VECS)
+        *reinterpret_cast<u32x4*>(&Ks[buf][(v / CHUNKS) * PITCH + (v % CHUNKS) * VEC]) = stage[p];
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int cur = tile & 1;
+    if (tile + 1 < ntiles) fetch(tile + 1);
+#pragma unroll
+    for (int grp = 0; grp < kPfTile / 16; ++grp) {
+      const long s = (long)tile * kPfTile + grp * 16 + c16;
+      Frag<T> kb[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kb[kk].load(&Ks[cur][(grp * 16 + c16) * PITCH + g * 8 * KK + 8 * kk]);
+#pragma unroll
+      for (int tt = 0; tt < kPfTokPerWave; ++tt) {
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < NHT; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) mma(acc, qa[tt][mt][kk], kb[kk]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[tt][mt][rr], fmaxf(acc[rr], 0.f), part);
+        }
+        part = wave_sum_xor_16_32(part);
+        if (g == 0 && s < nc[tt]) scores[tok[tt] * ld_sc + s] = part;
+      }
+    }
+    if (tile + 1 < ntiles) stash(cur ^ 1);
+    __syncthreads();
+  }
+}
+
+template <typename T, int KK, int NHT>
+hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const void* K,
+               const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off, long max_cand,
+               float* scores, long ld_sc, hipStream_t s) {
+  if (q_seq == nullptr && q_pos == nullptr) {
+    const int nblocks = (int)((nq + kPfTokens - 1) / kPfTokens);
+    TimedScope t("indexer_prefill", s);
+    hipLaunchKernelGGL((indexer_prefill_kernel<T, KK, NHT>), dim3(nblocks), dim3(512), 0, s,
+                       (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores,
+                       ld_sc);
+  } else {
+    const unsigned chunks = (unsigned)((max_cand + kSweepKeysPerWG - 1) / kSweepKeysPerWG);
+    TimedScope t("indexer_sweep", s);
+    hipLaunchKernelGGL((indexer_sweep_kernel<T, KK, NHT>), dim3(chunks * (unsigned)nq), dim3(256),
+                       0, s, nhI, m, (const T*)qI, wI, (const T*)K, q_seq, q_pos, kv_off,
+                       max_cand, scores, ld_sc, (int)chunks);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int KK>
+hipError_t pick_nht(long nq, int nhI, int m, const void* qI, const float* wI, const void* K,
+                    const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off,
+                    long max_cand, float* scores, long ld_sc, hipStream_t s) {
+  switch ((nhI + 15) / 16) {
+    case 1: return run<T, KK, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 2: return run<T, KK, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 3: return run<T, KK, 3>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    default: return run<T, KK, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+  }
+}
+
+template <typename T>
+hipError_t pick_kk(long nq, int nhI, int cI, int m, const void* qI, const float* wI, const void* K,
+                   const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off,
+                   long max_cand, float* scores, long ld_sc, hipStream_t s) {
+  switch (cI / 32) {
+    case 1: return pick_nht<T, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 2: return pick_nht<T, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 4: return pick_nht<T, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 8: return pick_nht<T, 8>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, const void* qI,
+                          const float* wI, const void* K, const int32_t* q_seq,
+                          const int64_t* q_pos, const int64_t* kv_offset, long max_cand,
+                          float* scores, long ld_sc, hipStream_t s) {
+  if (n_queries == 0 || max_cand == 0) return hipSuccess;
+  if (dt == CSA_F32)
+    return pick_kk<float>(n_queries, nhI, cI, m, qI, wI, K, q_seq, q_pos, kv_offset, max_cand,
+                          scores, ld_sc, s);
+  return pick_kk<bf16_t>(n_queries, nhI, cI, m, qI, wI, K, q_seq, q_pos, kv_offset, max_cand,
+                         scores, ld_sc, s);
+}
+
+}  // namespace csa

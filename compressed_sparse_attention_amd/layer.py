@@ -1,0 +1,131 @@
+"""CSA layer composites on top of the C ABI: ``prefill`` and ``decode``.
+
+Only device-memory plumbing happens here (allocating outputs and taking
+views); each step runs in libcsa's kernels through ``api``.
+
+Parameter layout (done once by ``pack_prefill_params``):
+  * every weight is stored transposed ([out, in], the way a linear layer
+    keeps it), which is the operand layout of ``csa_project``;
+  * the nine projections of the hidden states -- W^aKV, W^bKV, W^aZ, W^bZ
+    (eqs 1-2), their indexer-key counterparts, and W^DQ (eq 5) -- are
+    stacked into one [4c + 4c^I + d_c, d] matrix, so a single GEMM reads H
+    once and writes all of them side by side into one [n, 4c + 4c^I + d_c]
+    buffer; compression then reads column slices of that buffer;
+  * W^w (eq 7) is its own small GEMM with an fp32 output (head weights are
+    fp32), W^UQ of eq 6 and of eq 10 are two GEMMs on c^Q.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import api
+from .synth import bf16_to_f32
+
+_H_SIDE = ("W_aKV", "W_bKV", "W_aZ", "W_bZ", "W_aKV_I", "W_bKV_I", "W_aZ_I", "W_bZ_I", "W_DQ")
+
+
+def to_device(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Stored array (fp32, or bf16 bits as uint16) -> torch tensor on `device`."""
+    if dtype == "bf16" and x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    if x.dtype == np.uint16:
+        x = bf16_to_f32(x)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def pack_prefill_params(P: Dict[str, np.ndarray], dtype: str, device) -> Dict[str, torch.Tensor]:
+    """Device copies of the parameters in the layout the prefill path uses."""
+    t = {}
+    WH = np.concatenate([np.asarray(P[name]) for name in _H_SIDE], axis=1)  # [d, 4c+4cI+dc]
+    t["W_H_t"] = to_device(np.ascontiguousarray(WH.T), dtype, device)
+    t["W_w_t"] = to_device(np.ascontiguousarray(np.asarray(P["W_w"]).T), dtype, device)
+    t["W_UQI_t"] = to_device(np.ascontiguousarray(np.asarray(P["W_UQI"]).T), dtype, device)
+    t["W_UQ_t"] = to_device(np.ascontiguousarray(np.asarray(P["W_UQ"]).T), dtype, device)
+    for name in ("B_a", "B_b", "B_aI", "B_bI"):
+        t[name] = to_device(np.asarray(P[name]), dtype, device)
+    t["c"] = int(np.asarray(P["B_a"]).shape[1])
+    t["cI"] = int(np.asarray(P["B_aI"]).shape[1])
+    t["dc"] = int(np.asarray(P["W_DQ"]).shape[1])
+    return t
+
+
+class PrefillBuffers:
+    """Intermediate and output buffers of one prefill shape (reused across calls)."""
+
+    def __init__(self, n: int, m: int, k: int, nh: int, nhI: int, c: int, cI: int, dc: int, dtype, device):
+        width = 4 * c + 4 * cI + dc
+        N = n // m
+        self.Y_H = torch.empty(n, width, dtype=dtype, device=device)
+        self.wI = torch.empty(n, nhI, dtype=torch.float32, device=device)
+        self.qI = torch.empty(n, nhI * cI, dtype=dtype, device=device)
+        self.q = torch.empty(n, nh * c, dtype=dtype, device=device)
+        self.Ccomp = torch.empty(N, c, dtype=dtype, device=device)
+        self.KIcomp = torch.empty(N, cI, dtype=dtype, device=device)
+        self.idx = torch.empty(n, k, dtype=torch.int32, device=device)
+        self.o = torch.empty(n, nh, c, dtype=dtype, device=device)
+        self.lse = torch.empty(n, nh, dtype=torch.float32, device=device)
+        ws_i = api.csa_index_topk_workspace(n, N, nhI, k)
+        ws_m = api.csa_sparse_mqa_workspace(n, nh, c, k)
+        self.ws_index = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=device)
+        self.ws_mqa = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=device)
+
+
+def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int, nhI: int,
+            scale: Optional[float] = None, buf: Optional[PrefillBuffers] = None) -> PrefillBuffers:
+    """Eqs 1-11 for one sequence H [n, d]: every token is a query (causal)."""
+    n = H.shape[0]
+    c, cI, dc = W["c"], W["cI"], W["dc"]
+    if buf is None:
+        buf = PrefillBuffers(n, m, k, nh, nhI, c, cI, dc, H.dtype, H.device)
+    Y = buf.Y_H
+    api.csa_project(H, W["W_H_t"], Y)  # eqs 1, 2 (+ indexer copies), 5
+    api.csa_project(H, W["W_w_t"], buf.wI)  # eq 7
+    cQ = Y[:, 4 * c + 4 * cI:]
+    api.csa_project(cQ, W["W_UQI_t"], buf.qI)  # eq 6
+    api.csa_project(cQ, W["W_UQ_t"], buf.q)  # eq 10
+    api.csa_compress(Y[:, 0:c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:4 * c], W["B_a"], W["B_b"], m,
+                     buf.Ccomp)  # eqs 3-4
+    o = 4 * c
+    api.csa_compress(Y[:, o:o + cI], Y[:, o + cI:o + 2 * cI], Y[:, o + 2 * cI:o + 3 * cI],
+                     Y[:, o + 3 * cI:o + 4 * cI], W["B_aI"], W["B_bI"], m, buf.KIcomp)
+    api.csa_index_topk(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, n // m, buf.idx,
+                       workspace=buf.ws_index)  # eqs 8-9
+    sc = 1.0 / math.sqrt(c) if scale is None else scale
+    api.csa_sparse_mqa(buf.q.view(n, nh, c), buf.Ccomp, buf.idx, sc, buf.o, buf.lse,
+                       workspace=buf.ws_mqa)  # eq 11
+    return buf
+
+
+class DecodeBuffers:
+    def __init__(self, B: int, k: int, nh: int, c: int, nhI: int, max_cand: int, dtype, device):
+        self.idx = torch.empty(B, k, dtype=torch.int32, device=device)
+        self.scores = torch.empty(B, k, dtype=torch.float32, device=device)
+        self.o = torch.empty(B, nh, c, dtype=dtype, device=device)
+        self.lse = torch.empty(B, nh, dtype=torch.float32, device=device)
+        self.q_seq = torch.arange(B, dtype=torch.int32, device=device)
+        ws_i = api.csa_index_topk_workspace(B, max_cand, nhI, k)
+        ws_m = api.csa_sparse_mqa_workspace(B, nh, c, k)
+        self.ws_index = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=device)
+        self.ws_mqa = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=device)
+
+
+def decode(q, qI, wI, Ccomp, KIcomp, seq_len, kv_offset, m: int, k: int, max_cand: int,
+           scale: Optional[float] = None, buf: Optional[DecodeBuffers] = None) -> DecodeBuffers:
+    """One decode step: query b is appended after seq_len[b] tokens of sequence b.
+
+    seq_len, kv_offset: int64 device tensors [B]; max_cand >= max_b floor(seq_len[b]/m).
+    """
+    B, nh, c = q.shape
+    nhI = qI.shape[1]
+    if buf is None:
+        buf = DecodeBuffers(B, k, nh, c, nhI, max_cand, q.dtype, q.device)
+    api.csa_index_topk(qI, wI, KIcomp, m, k, max_cand, buf.idx, score_out=buf.scores, q_seq=buf.q_seq,
+                       q_pos=seq_len, kv_offset=kv_offset, workspace=buf.ws_index)
+    sc = 1.0 / math.sqrt(c) if scale is None else scale
+    api.csa_sparse_mqa(q, Ccomp, buf.idx, sc, buf.o, buf.lse, q_seq=buf.q_seq, kv_offset=kv_offset,
+                       workspace=buf.ws_mqa)
+    return buf

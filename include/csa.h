@@ -1,0 +1,199 @@
+/*
+ * csa.h -- C ABI of the Compressed Sparse Attention (CSA) hot path on one
+ * AMD Instinct MI355X (gfx950) GPU.
+ *
+ * The operations are those of the web page "Compressed Sparse Attention
+ * (压缩稀疏注意力)" (cnblogs): the linear projections of eqs 1, 2, 5, 6, 7 and
+ * 10; the softmax-gated overlapping compression of eqs 3-4 (section
+ * "Compressed Key-Value Entries"); the lightning indexer of eq 8 with the
+ * top-k selector of eq 9 (section "Lightning Indexer for Sparse Selection");
+ * and the shared-key-value multi-query attention of eq 11 (section "Shared
+ * Key-Value MQA").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer into memory the caller owns.
+ *   Sizes, strides, scalars and the `bytes` out-parameters are host values.
+ *   The library never allocates, frees or keeps device memory; scratch
+ *   space is the caller-provided `workspace` sized by the *_workspace query.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL means
+ *   the null stream) and returns without synchronising.  Outputs are valid
+ *   once the stream has reached that point.
+ * - Arrays are row-major.  A "leading dimension" (ld*) is the distance, in
+ *   elements, between consecutive rows; it must be >= the row length.
+ * - Device pointers must be 16-byte aligned and every leading dimension must
+ *   keep rows 16-byte aligned (a multiple of 8 for bf16, 4 for fp32).
+ * - Errors: argument validation happens before any launch.  A failing call
+ *   returns a nonzero csa_status, enqueues nothing, leaves every output
+ *   untouched and sets a thread-local message readable by csa_last_error().
+ *   A failed launch returns CSA_ERR_HIP.  Faults inside kernels surface, as
+ *   usual in HIP, at the caller's next synchronisation.  No C++ exception
+ *   crosses this interface.
+ * - The library is thread-safe: its only global state is a per-device
+ *   property cache filled once and the thread-local error text.  Calls that
+ *   share a workspace or output buffer on the same device race unless they
+ *   are ordered on one stream.
+ * - Inputs must be finite (no NaN/Inf); behaviour on non-finite input is
+ *   unspecified.
+ * - The first call on a device checks that it is a gfx950 GPU and returns
+ *   CSA_ERR_UNSUPPORTED otherwise.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad dtype */
+  CSA_ERR_UNSUPPORTED = 2, /* device is not gfx950, or a shape the kernels do not cover */
+  CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query returned */
+  CSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0, /* IEEE binary32 */
+  CSA_BF16 = 1 /* bfloat16 (upper half of binary32), round-to-nearest-even on store */
+} csa_dtype;
+
+/* Version of this interface (CSA_ABI_VERSION of the built library). */
+int csa_abi_version(void);
+
+/* Message describing the last failure on the calling thread ("" if none).
+ * The pointer stays valid until the thread's next failing call. */
+const char* csa_last_error(void);
+
+/*
+ * csa_project -- Y = X . W   (eqs 1, 2, 5, 6, 7 and 10 are all of this form:
+ * C^a = H W^aKV, C^b = H W^bKV, Z^a = H W^aZ, Z^b = H W^bZ, c^Q = H W^DQ,
+ * q^I = c^Q W^UQ(indexer), w^I = H W^w, q = c^Q W^UQ(attention)).
+ *
+ *   X   [M, K]  row-major, leading dimension ldx, dtype in_dt
+ *   Wt  [N, K]  W stored TRANSPOSED (row n holds column n of W, the way a
+ *               linear layer keeps its weight), leading dimension ldw, in_dt
+ *   Y   [M, N]  row-major, leading dimension ldy, dtype out_dt
+ *
+ * Products accumulate in fp32.  Supported (in_dt, out_dt): (F32, F32),
+ * (BF16, BF16), (BF16, F32).  Several projections that share X are one call
+ * with their weights stacked along N; a column slice of a wider Y is written
+ * by passing Y + col0 with the wide ldy.  K must be a multiple of 8.
+ * M, N, K > 0.
+ */
+csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, int64_t K,
+                       const void* X, int64_t ldx, const void* Wt, int64_t ldw, void* Y,
+                       int64_t ldy, void* stream);
+
+/*
+ * csa_compress -- eqs 3-4: for every block i = 0 .. floor(n/m)-1 and channel j,
+ * softmax over the 2m logits Z^a[m*i+r, j] + B^a[r, j] and
+ * Z^b[m*(i-1)+r, j] + B^b[r, j] (r < m), then
+ * Ccomp[i, j] = sum_r S^a_r C^a[m*i+r, j] + sum_r S^b_r C^b[m*(i-1)+r, j].
+ * Block 0 has no b-terms (the page pads them with -inf logits and zero values).
+ * Trailing rows n mod m form no block.  The same call produces the indexer
+ * keys K^IComp from the indexer's own projections and biases.
+ *
+ *   Ca, Cb, Za, Zb  [n, c]  leading dimension ld_in (they may be column slices
+ *                           of one [n, >= 4c] projection output)
+ *   Ba, Bb          [m, c]  contiguous
+ *   Ccomp           [floor(n/m), c]  leading dimension ld_out
+ *   dt              dtype of every array (arithmetic is fp32)
+ *
+ * n >= 0 (n < m writes nothing), 1 <= m <= 64, c > 0 and a multiple of 4.
+ */
+csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const void* Ca,
+                        const void* Cb, const void* Za, const void* Zb, int64_t ld_in,
+                        const void* Ba, const void* Bb, void* Ccomp, int64_t ld_out,
+                        void* stream);
+
+/*
+ * csa_index_topk -- eq 8 scores and the eq 9 selection for a batch of queries.
+ *
+ * Query r belongs to sequence seq = q_seq[r] (q_seq NULL: 0) and sits at token
+ * position pos = q_pos[r] (q_pos NULL: pos = r).  Its candidates are the
+ * n_cand = min(floor(pos/m), max_cand) compressed blocks s < n_cand of that
+ * sequence, whose keys are rows kv_offset[seq] + s of KIcomp (kv_offset
+ * NULL: 0).  For a decode query appended after L context tokens, pass
+ * pos = L: every one of the floor(L/m) cached blocks is a candidate.
+ *
+ *   score I[r, s] = sum_h wI[r, h] * max(0, qI[r, h, :] . KIcomp[kv_offset[seq] + s, :])
+ *
+ * idx_out[r, :] receives the min(k, n_cand) candidates with the largest
+ * scores; equal scores are ordered by lower block index, and -0.0 equals
+ * +0.0.  The order of indices within a row is unspecified (treat each row
+ * as a set).  Slots beyond min(k, n_cand) hold -1.  If score_out is not NULL,
+ * score_out[r, j] holds the fp32 score of idx_out[r, j] (-inf for -1 slots).
+ *
+ *   qI       [n_queries, n_hI, cI]  dtype dt, contiguous
+ *   wI       [n_queries, n_hI]      fp32, contiguous
+ *   KIcomp   [rows, cI]             dtype dt, contiguous
+ *   q_seq    [n_queries] int32 or NULL;  q_pos [n_queries] int64 or NULL
+ *   kv_offset[n_seqs] int64 or NULL
+ *   idx_out  [n_queries, k] int32;  score_out [n_queries, k] fp32 or NULL
+ *
+ * Scores are fp32 (products of dt values, fp32 accumulation).  With q_seq and
+ * q_pos both NULL (one sequence, query r at position r: a prefill) a tiled
+ * kernel shares key tiles between neighbouring queries; otherwise each
+ * query sweeps its own keys.  Supported: 1 <= n_hI <= 64, cI a multiple of
+ * 32 up to 256, k >= 1, m >= 1, max_cand >= 0.
+ */
+csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t k,
+                                    size_t* bytes);
+csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m,
+                          int32_t k, const void* qI, const float* wI, const void* KIcomp,
+                          const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
+                          int64_t max_cand, int32_t* idx_out, float* score_out, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * csa_sparse_mqa -- eq 11: shared key-value multi-query attention over the
+ * selected compressed entries.  For query r of sequence seq (q_seq NULL: 0)
+ * and head h, with the selected rows C_s = Ccomp[kv_offset[seq] + idx[r, j]]
+ * (slots holding -1 are skipped):
+ *
+ *   o[r, h, :] = sum_s softmax_s(scale * q[r, h, :] . C_s) C_s
+ *   lse[r, h]  = log sum_s exp(scale * q[r, h, :] . C_s)
+ *
+ * Each selected entry is both key and value.  A row with no valid slot gives
+ * o = 0 and lse = -inf.  The page leaves the attention scale open; pass
+ * 1/sqrt(c) for the usual choice.
+ *
+ *   q      [n_queries, n_h, c]  dtype dt, contiguous
+ *   Ccomp  [rows, c]            dtype dt, contiguous
+ *   idx    [n_queries, k] int32, entries in [-1, number of blocks of seq)
+ *   o      [n_queries, n_h, c]  dtype dt;  lse [n_queries, n_h] fp32 or NULL
+ *
+ * Softmax and accumulation are fp32.  Supported: c a multiple of 64 up to
+ * 1024, 1 <= n_h <= 256, k >= 1.
+ */
+csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
+                                    size_t* bytes);
+csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
+                          float scale, const void* q, const void* Ccomp, const int32_t* q_seq,
+                          const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing (instrumentation, off by default).  While enabled, every
+ * kernel the library launches is bracketed by a pair of HIP events recorded
+ * on the launch stream.  csa_timing_read synchronises on the recorded events
+ * and returns, for the kernel family `name` ("gemm", "compress",
+ * "indexer_sweep", "indexer_prefill", "topk", "mqa_split", "mqa_combine"),
+ * the summed duration in milliseconds and the number of launches since the
+ * last reset.  Unknown names give 0 launches.
+ */
+csa_status csa_timing_enable(int on);
+csa_status csa_timing_reset(void);
+csa_status csa_timing_read(const char* name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

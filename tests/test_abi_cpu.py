@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and rejects bad arguments before touching any device (no compute calls)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from compressed_sparse_attention_amd import api
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(api.LIB_PATH):
+        pytest.fail("libcsa.so is not built (run __graft_entry__.build())")
+    return api.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = api.header_functions()
+    assert {"csa_project", "csa_compress", "csa_index_topk", "csa_sparse_mqa"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(csa_\w+)$", out, re.M))
+    missing = set(declared) - exported
+    assert not missing, f"declared but not exported: {sorted(missing)}"
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_abi_version(L):
+    assert api.csa_abi_version() == 1
+
+
+def _err():
+    return api.lib().csa_last_error().decode()
+
+
+def test_project_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+    assert L.csa_project(1, 1, 0, 8, 8, p, 8, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert "positive" in _err()
+    assert L.csa_project(1, 1, 8, 8, 12, p, 16, p, 16, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert "multiple of 8" in _err()
+    assert L.csa_project(1, 1, 8, 8, 8, None, 8, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_project(1, 1, 8, 8, 8, ctypes.c_void_p(18), 8, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert L.csa_project(0, 1, 8, 8, 8, p, 8, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_project(7, 1, 8, 8, 8, p, 8, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_project(1, 1, 8, 8, 8, p, 4, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
+
+
+def test_compress_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+    assert L.csa_compress(1, 64, 0, 64, p, p, p, p, 256, p, p, p, 64, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_compress(1, 64, 4, 6, p, p, p, p, 256, p, p, p, 64, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_compress(1, 64, 4, 64, p, None, p, p, 256, p, p, p, 64, None) == api.CSA_ERR_INVALID_ARG
+    assert L.csa_compress(1, 64, 4, 64, p, p, p, p, 60, p, p, p, 64, None) == api.CSA_ERR_INVALID_ARG
+    # fewer rows than one block: nothing to do, succeeds without touching pointers or the device
+    assert L.csa_compress(1, 3, 4, 64, None, None, None, None, 64, None, None, None, 64, None) == api.CSA_OK
+
+
+def test_index_topk_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+    args = dict(dt=1, nq=4, nhI=64, cI=128, m=4, k=16, qI=p, wI=p, K=p, seq=None, pos=None, off=None,
+                maxc=100, idx=p, sc=None, ws=p, wsb=1 << 20)
+
+    def call(**over):
+        a = dict(args, **over)
+        return L.csa_index_topk(a["dt"], a["nq"], a["nhI"], a["cI"], a["m"], a["k"], a["qI"], a["wI"], a["K"],
+                                a["seq"], a["pos"], a["off"], a["maxc"], a["idx"], a["sc"], a["ws"], a["wsb"],
+                                None)
+    assert call(nhI=65) == api.CSA_ERR_INVALID_ARG
+    assert call(cI=96) == api.CSA_ERR_INVALID_ARG
+    assert call(k=0) == api.CSA_ERR_INVALID_ARG
+    assert call(m=0) == api.CSA_ERR_INVALID_ARG
+    assert call(qI=None) == api.CSA_ERR_INVALID_ARG
+    assert call(wsb=10) == api.CSA_ERR_WORKSPACE
+    assert "workspace" in _err()
+    assert call(ws=None) == api.CSA_ERR_WORKSPACE
+    assert call(nq=0, qI=None) == api.CSA_OK  # empty batch: nothing enqueued
+
+
+def test_sparse_mqa_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def call(dt=1, nq=2, nh=64, c=512, k=32, scale=0.04, q=p, C=p, idx=p, o=p, ws=p, wsb=1 << 30):
+        return L.csa_sparse_mqa(dt, nq, nh, c, k, scale, q, C, None, None, idx, o, None, ws, wsb, None)
+    assert call(c=96) == api.CSA_ERR_INVALID_ARG
+    assert call(nh=0) == api.CSA_ERR_INVALID_ARG
+    assert call(scale=-1.0) == api.CSA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == api.CSA_ERR_INVALID_ARG
+    assert call(o=None) == api.CSA_ERR_INVALID_ARG
+    assert call(wsb=64) == api.CSA_ERR_WORKSPACE
+
+
+def test_workspace_queries(L):
+    assert api.csa_index_topk_workspace(8, 32768, 64, 1024) >= 8 * 32768 * 4
+    b1 = api.csa_sparse_mqa_workspace(8, 64, 512, 1024)
+    b2 = api.csa_sparse_mqa_workspace(16, 64, 512, 1024)
+    assert 0 < b1 < b2
+    with pytest.raises(api.CSAError):
+        api.csa_index_topk_workspace(-1, 10, 4, 4)
+
+
+def test_timing_interface(L):
+    api.csa_timing_reset()
+    assert api.csa_timing_read("gemm") == (0.0, 0)
+    api.csa_timing_enable(False)

@@ -1,0 +1,245 @@
+"""GPU parity: each C-ABI entry point against the oracle on the same seeded inputs.
+
+Inputs are drawn by ``synth`` (never by the HIP side); the oracle widens the
+stored values exactly to float64.  Sizes span several tiles and a ragged
+tail; edge cases cover empty and short inputs.  Tolerances: see parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_amd import api, synth
+from compressed_sparse_attention_amd.layer import to_device
+from oracle import csa_oracle as O
+from parity import assert_rows_close, check_topk, exact_sets_equal, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def draw(rng, shape, std, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    return synth.f32_to_bf16(x) if dtype == "bf16" else x
+
+
+def f64(x, dtype):
+    return synth.to_f64(x, dtype)
+
+
+# ---------------------------------------------------------------------------
+# projections (eqs 1, 2, 5, 6, 7, 10)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("din,dout,M,N,K", [
+    ("f32", "f32", 512, 512, 256),
+    ("f32", "f32", 77, 40, 24),
+    ("bf16", "bf16", 300, 200, 136),
+    ("bf16", "f32", 130, 64, 4096),
+    ("bf16", "bf16", 1000, 1536, 4096),
+])
+def test_project(din, dout, M, N, K):
+    rng = synth.rng_for(M * 7 + N)
+    X = draw(rng, (M, K), 1.0, din)
+    W = draw(rng, (K, N), 1.0 / math.sqrt(K), din)
+    Xd = to_device(X, din, DEV)
+    Wt = to_device(np.ascontiguousarray(W.T), din, DEV)
+    Y = torch.empty(M, N, dtype=TD[dout], device=DEV)
+    api.csa_project(Xd, Wt, Y)
+    torch.cuda.synchronize()
+    assert_rows_close(to_np64(Y), O.project(f64(X, din), f64(W, din)), what="project")
+
+
+def test_project_strided_views():
+    """Input column slice (ldx > K) and output column slice of a wider buffer (ldy > N)."""
+    rng = synth.rng_for(99)
+    M, K, N = 257, 128, 96
+    X = draw(rng, (M, 3 * K), 1.0, "bf16")
+    W = draw(rng, (K, N), 0.1, "bf16")
+    Xd = to_device(X, "bf16", DEV)
+    Wt = to_device(np.ascontiguousarray(W.T), "bf16", DEV)
+    Ybig = torch.full((M, 4 * N), 7.0, dtype=torch.bfloat16, device=DEV)
+    api.csa_project(Xd[:, K:2 * K], Wt, Ybig[:, N:2 * N])
+    torch.cuda.synchronize()
+    ref = O.project(f64(X, "bf16")[:, K:2 * K], f64(W, "bf16"))
+    assert_rows_close(to_np64(Ybig[:, N:2 * N]), ref, what="project slice")
+    untouched = torch.cat([Ybig[:, :N], Ybig[:, 2 * N:]], 1)
+    assert torch.all(untouched == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# compression (eqs 3-4)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,n,m,c", [
+    ("f32", 512, 4, 64), ("f32", 514, 4, 32), ("bf16", 1000, 4, 512), ("bf16", 999, 8, 128),
+    ("bf16", 64, 1, 512), ("bf16", 37, 2, 12), ("bf16", 3, 4, 64),
+])
+def test_compress(dtype, n, m, c):
+    rng = synth.rng_for(n + m + c)
+    P = draw(rng, (n, 4 * c), 1.0, dtype)
+    Pz = draw(rng, (n, 4 * c), 2.0, dtype)  # logits with spread so the softmax is not flat
+    P = np.where((np.arange(4 * c) // c)[None, :] >= 2, Pz, P)
+    Ba = draw(rng, (m, c), 0.5, dtype)
+    Bb = draw(rng, (m, c), 0.5, dtype)
+    Pd = to_device(P, dtype, DEV)
+    out = torch.full((n // m, c), 3.0, dtype=TD[dtype], device=DEV)
+    api.csa_compress(Pd[:, 0:c], Pd[:, c:2 * c], Pd[:, 2 * c:3 * c], Pd[:, 3 * c:], to_device(Ba, dtype, DEV),
+                     to_device(Bb, dtype, DEV), m, out)
+    torch.cuda.synchronize()
+    P64 = f64(P, dtype)
+    ref = O.compress(P64[:, :c], P64[:, c:2 * c], P64[:, 2 * c:3 * c], P64[:, 3 * c:], f64(Ba, dtype),
+                     f64(Bb, dtype), m)
+    if n // m:
+        assert_rows_close(to_np64(out), ref, what="compress")
+
+
+def test_compress_mean_pool_exact():
+    """Equal logits and B = 0: mean pooling; integer values and m = 4 make fp32 exact."""
+    rng = synth.rng_for(5)
+    n, m, c = 256, 4, 64
+    C = rng.integers(-50, 50, size=(n, 2 * c)).astype(np.float32)
+    Z = np.full((n, 2 * c), 0.75, dtype=np.float32)
+    P = np.concatenate([C, Z], 1)
+    B = np.zeros((m, c), np.float32)
+    Pd = to_device(P, "f32", DEV)
+    out = torch.empty(n // m, c, dtype=torch.float32, device=DEV)
+    Bd = to_device(B, "f32", DEV)
+    api.csa_compress(Pd[:, 0:c], Pd[:, c:2 * c], Pd[:, 2 * c:3 * c], Pd[:, 3 * c:], Bd, Bd, m, out)
+    torch.cuda.synchronize()
+    ref = O.compress(P[:, :c], P[:, c:2 * c], P[:, 2 * c:3 * c], P[:, 3 * c:], B, B, m)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
+
+
+# ---------------------------------------------------------------------------
+# indexer + top-k (eqs 8-9)
+# ---------------------------------------------------------------------------
+def _run_index_topk(qI, wI, K, m, k, lens, kv_offset, dtype, prefill_mode=False):
+    B = qI.shape[0]
+    idx = torch.full((B, k), 123456, dtype=torch.int32, device=DEV)
+    sc = torch.empty(B, k, dtype=torch.float32, device=DEV)
+    if prefill_mode:
+        max_cand = B // m
+        api.csa_index_topk(to_device(qI, dtype, DEV), to_device(wI, "f32", DEV), to_device(K, dtype, DEV), m, k,
+                           max_cand, idx, score_out=sc)
+    else:
+        max_cand = int(max(lens) // m) if len(lens) else 0
+        api.csa_index_topk(to_device(qI, dtype, DEV), to_device(wI, "f32", DEV), to_device(K, dtype, DEV), m, k,
+                           max_cand, idx, score_out=sc,
+                           q_seq=torch.arange(B, dtype=torch.int32, device=DEV),
+                           q_pos=torch.tensor(lens, dtype=torch.int64, device=DEV),
+                           kv_offset=torch.tensor(kv_offset, dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+
+
+def _decode_case(rng, lens, m, nhI, cI, dtype):
+    lens = np.asarray(lens, np.int64)
+    nblk = lens // m
+    off = np.zeros_like(nblk)
+    off[1:] = np.cumsum(nblk)[:-1]
+    rows = max(int(nblk.sum()), 1)
+    K = draw(rng, (rows, cI), 1.0, dtype)
+    qI = draw(rng, (len(lens), nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((len(lens), nhI), dtype=np.float32)
+    return lens, off, K, qI, wI
+
+
+def _oracle_rows(qI, wI, K, lens, off, m, dtype):
+    K64 = f64(K, dtype)
+    rows = []
+    for b in range(len(lens)):
+        nc = int(lens[b] // m)
+        rows.append(O.index_scores_row(f64(qI[b], dtype), wI[b].astype(np.float64), K64[off[b]:off[b] + nc], nc))
+    return rows
+
+
+@pytest.mark.parametrize("dtype,lens,m,nhI,cI,k", [
+    ("bf16", [0, 7, 100, 2051, 8195, 4096], 4, 64, 128, 64),
+    ("bf16", [9000, 1024, 30000], 8, 32, 128, 256),
+    ("f32", [512, 3, 64, 200], 4, 4, 32, 16),
+    ("bf16", [2048 * 4, 2048 * 4], 4, 64, 128, 512),
+    ("bf16", [777, 5000], 4, 20, 64, 33),
+])
+def test_index_topk_decode(dtype, lens, m, nhI, cI, k):
+    rng = synth.rng_for(sum(lens) + k)
+    lens, off, K, qI, wI = _decode_case(rng, lens, m, nhI, cI, dtype)
+    idx, sc = _run_index_topk(qI, wI, K, m, k, lens, off, dtype)
+    rows = _oracle_rows(qI, wI, K, lens, off, m, dtype)
+    check_topk(idx, rows, k)
+    for b, s in enumerate(rows):  # returned scores are the selected candidates' scores
+        sel = idx[b][idx[b] >= 0]
+        got = sc[b][idx[b] >= 0]
+        assert np.allclose(got, s[sel], rtol=1e-3, atol=1e-4 * (np.abs(s).max() + 1e-30))
+        assert np.all(np.isneginf(sc[b][idx[b] < 0]))
+
+
+@pytest.mark.parametrize("nhI,wset", [(1, (1.0,)), (8, (-1.0, 0.5, 2.0)), (64, (-2.0, -0.5, 0.0, 1.0, 3.0))])
+def test_index_topk_exact_ties(nhI, wset):
+    """Small-integer inputs make every fp32 score exact: sets must equal the oracle's exactly,
+    including the lower-index tie-break and -0.0 == +0.0."""
+    rng = synth.rng_for(nhI)
+    cI, m, k = 64, 4, 40
+    lens = np.array([4 * 600, 4 * 41, 4 * 1000], np.int64)
+    nblk = lens // m
+    off = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    K = synth.f32_to_bf16(rng.integers(-2, 3, size=(int(nblk.sum()), cI)).astype(np.float32))
+    qI = synth.f32_to_bf16(rng.integers(-1, 2, size=(3, nhI, cI)).astype(np.float32))
+    wI = rng.choice(np.array(wset, np.float32), size=(3, nhI))
+    idx, _ = _run_index_topk(qI, wI, K, m, k, lens, off, "bf16")
+    rows = _oracle_rows(qI, wI, K, lens, off, m, "bf16")
+    exact_sets_equal(idx, O.topk_rows(rows, k))
+
+
+@pytest.mark.parametrize("dtype,n,m,nhI,cI,k", [
+    ("f32", 512, 4, 4, 32, 16), ("bf16", 1000, 4, 64, 128, 64), ("bf16", 333, 2, 16, 64, 8),
+])
+def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
+    rng = synth.rng_for(n + nhI)
+    K = draw(rng, (n // m, cI), 1.0, dtype)
+    qI = draw(rng, (n, nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((n, nhI), dtype=np.float32)
+    idx, _ = _run_index_topk(qI, wI, K, m, k, None, None, dtype, prefill_mode=True)
+    K64 = f64(K, dtype)
+    rows = [O.index_scores_row(f64(qI[t], dtype), wI[t].astype(np.float64), K64, t // m) for t in range(n)]
+    check_topk(idx, rows, k)
+
+
+# ---------------------------------------------------------------------------
+# sparse MQA (eq 11)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,B,nh,c,k,nblk,qmult", [
+    ("bf16", 4, 64, 512, 512, 3000, 1.0),
+    ("bf16", 3, 64, 512, 100, 700, 8.0),
+    ("bf16", 2, 128, 512, 256, 400, 32.0),
+    ("f32", 5, 8, 64, 16, 128, 1.0),
+    ("bf16", 3, 20, 128, 70, 90, 4.0),
+])
+def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
+    rng = synth.rng_for(B * nh + k)
+    C = draw(rng, (B * nblk, c), 1.0, dtype)
+    q = draw(rng, (B, nh, c), qmult / math.sqrt(c), dtype)
+    ncand = np.full(B, nblk)
+    ncand[-1] = 0  # one query with nothing selected
+    if B > 2:
+        ncand[1] = min(nblk, k // 2 + 1)  # a short selection padded with -1
+    idx = synth.random_selection(rng, ncand, k)
+    off = np.arange(B, dtype=np.int64) * nblk
+    o = torch.full((B, nh, c), 5.0, dtype=TD[dtype], device=DEV)
+    lse = torch.empty(B, nh, dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(c)
+    api.csa_sparse_mqa(to_device(q, dtype, DEV), to_device(C, dtype, DEV),
+                       torch.from_numpy(idx).to(DEV), scale, o, lse,
+                       q_seq=torch.arange(B, dtype=torch.int32, device=DEV),
+                       kv_offset=torch.from_numpy(off).to(DEV))
+    torch.cuda.synchronize()
+    C64, q64 = f64(C, dtype), f64(q, dtype)
+    for b in range(B):
+        sel = idx[b][idx[b] >= 0]
+        ro, rl = O.mqa(q64[b], C64[off[b] + sel], scale)
+        assert_rows_close(to_np64(o[b]), ro, what=f"mqa o[{b}]")
+        got = lse[b].cpu().numpy().astype(np.float64)
+        if sel.size == 0:
+            assert np.all(np.isneginf(got))
+        else:
+            assert np.allclose(got, rl, rtol=1e-3, atol=1e-3)
