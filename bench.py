@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA hot path on one MI355X (gfx950).
+
+Headline: decode queries/s on a batch of 8 sequences with 131072-token
+contexts (m = 4 -> 32768 compressed entries each, c = 512, c^I = 128,
+64 indexer heads, 64 attention heads, top-1024).  One step = the whole decode
+path for one batch: the lightning-indexer sweep over every compressed key,
+the top-k selection, and the shared-KV sparse MQA with its split merge.
+
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+A decode step streams ~73 MiB, which would otherwise sit in the 256 MB
+Infinity Cache between steps; the timed steps therefore rotate through
+--replicas device copies of the inputs (8 by default: > 512 MiB of key
+sweeps), the way a server alternates between batches.  The warm-cache rate
+(one copy) is reported beside it.
+
+Also reported on the same line: the per-kernel durations measured with HIP
+events recorded on the launch stream around every library kernel of the
+timed steps (a second pass over the same steps), the roofline of the
+dominant kernel, the prefill of one 32768-token sequence (tokens/s), and the
+CPU oracle on a bounded sample of the decode workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def _kernel_stats(api, names):
+    out = {}
+    for n in names:
+        ms, cnt = api.csa_timing_read(n)
+        if cnt:
+            out[n] = {"launches": cnt, "avg_us": 1000.0 * ms / cnt, "total_ms": ms}
+    return out
+
+
+def _traffic(kernel: str, src: str, per_launch_units: float):
+    """HBM bytes per launch from committed counter runs, if the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec:
+        return None
+    with open(os.path.join(ROOT, "compressed_sparse_attention_amd", "csrc", src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_decode(args, torch, api, synth, layer):
+    w = synth.WORKLOADS[4]
+    dev = "cuda:0"
+    D = synth.make_decode(w)
+    B = int(D["seq_len"].shape[0])
+    max_cand = int(D["n_blocks"].max())
+    base = {
+        "q": layer.to_device(D["q"], w.dtype, dev),
+        "qI": layer.to_device(D["qI"], w.dtype, dev),
+        "wI": layer.to_device(D["wI"], "f32", dev),
+        "C": layer.to_device(D["Ccomp"], w.dtype, dev),
+        "K": layer.to_device(D["KIcomp"], w.dtype, dev),
+    }
+    reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.replicas - 1)]
+    seq_len = torch.from_numpy(D["seq_len"]).to(dev)
+    off = torch.from_numpy(D["kv_offset"]).to(dev)
+    buf = layer.DecodeBuffers(B, w.k, w.nh, w.c, w.nhI, max_cand, base["q"].dtype, dev)
+
+    def step(i, pool):
+        r = pool[i % len(pool)]
+        layer.decode(r["q"], r["qI"], r["wI"], r["C"], r["K"], seq_len, off, w.m, w.k, max_cand, buf=buf)
+
+    def timed(run_one, n_pool, steps, warmup):
+        for i in range(warmup):
+            run_one(i % n_pool)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            run_one(i % n_pool)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    # eager reference output of copy 0, then one HIP graph per input copy
+    step(0, reps)
+    torch.cuda.synchronize()
+    ref_idx, ref_o = buf.idx.clone(), buf.o.clone()
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0, reps)
+    torch.cuda.current_stream().wait_stream(side)
+    for i in range(len(reps)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i, reps)
+        graphs.append(g)
+    for _ in range(3):  # replays, with eager work in between, must reproduce the eager result
+        buf.idx.fill_(-7)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(buf.idx, ref_idx) and torch.equal(buf.o, ref_o)):
+            raise RuntimeError("graph replay differs from the eager decode step")
+        step(1, reps)
+        torch.cuda.synchronize()
+
+    ms_eager = timed(lambda i: step(i, reps), len(reps), args.steps, args.warmup)
+    ms = timed(lambda i: graphs[i].replay(), len(reps), args.steps, args.warmup)
+    print(f"[bench] decode: {ms * 1000:.2f} us/step over {args.steps} graph replays "
+          f"({len(reps)} input copies); eager launches {ms_eager * 1000:.2f} us/step", flush=True)
+    ms_warm = timed(lambda i: graphs[0].replay(), 1, args.steps, args.warmup)
+    print(f"[bench] decode warm cache: {ms_warm * 1000:.2f} us/step", flush=True)
+
+    # second pass over the same steps with per-kernel HIP events on the launch stream
+    api.csa_timing_reset()
+    api.csa_timing_enable(True)
+    timed(lambda i: step(i, reps), len(reps), args.steps, 0)
+    api.csa_timing_enable(False)
+    kern = _kernel_stats(api, ["indexer_sweep", "topk", "mqa", "mqa_combine"])
+    api.csa_timing_reset()
+    for n, s in kern.items():
+        print(f"[bench]   {n:14s} {s['avg_us']:8.2f} us/launch", flush=True)
+
+    # algorithmic bytes of the indexer sweep per query: every candidate key of the
+    # sequence (N_b * cI bf16), the query's indexer heads and head weights
+    N = max_cand
+    sweep_bytes = B * (2 * N * w.cI + 2 * w.nhI * w.cI + 4 * w.nhI)
+    # whole decode step per query: key sweep + gathered entries + q + o + selected indices
+    step_bytes = B * (2 * N * w.cI + 2 * min(w.k, N) * w.c + 2 * (w.nh * w.c + w.nhI * w.cI) + 4 * w.nhI
+                      + 2 * w.nh * w.c + 4 * w.k)
+    sw = kern.get("indexer_sweep")
+    roof = None
+    if sw:
+        achieved = sweep_bytes / (sw["avg_us"] * 1e-6) / 1e9
+        roof = {"kernel": "indexer_sweep", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": _traffic("indexer_sweep", "indexer.hip", B),
+                "algorithmic_bytes_per_launch": sweep_bytes}
+    return {
+        "workload": w, "B": B, "ms": ms, "ms_warm": ms_warm, "ms_eager": ms_eager, "kernels": kern, "roofline": roof,
+        "step_bytes": step_bytes, "max_cand": max_cand, "D": D,
+    }
+
+
+def bench_prefill(args, torch, api, synth, layer):
+    w = synth.WORKLOADS[3]
+    dev = "cuda:0"
+    P = synth.make_prefill(w)
+    W = layer.pack_prefill_params(P, w.dtype, dev)
+    H = layer.to_device(P["H"], w.dtype, dev)
+    del P
+    buf = layer.PrefillBuffers(w.n, w.m, w.k, w.nh, w.nhI, w.c, w.cI, w.dc, H.dtype, dev)
+
+    def run(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            layer.prefill(H, W, w.m, w.k, w.nh, w.nhI, buf=buf)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    run(max(1, args.prefill_warmup))
+    ms = run(args.prefill_steps)
+    api.csa_timing_reset()
+    api.csa_timing_enable(True)
+    run(args.prefill_steps)
+    api.csa_timing_enable(False)
+    kern = _kernel_stats(api, ["gemm", "compress", "indexer_prefill", "topk", "mqa", "mqa_combine"])
+    api.csa_timing_reset()
+    print(f"[bench] prefill: {ms:.2f} ms per {w.n}-token sequence", flush=True)
+    for n, s in kern.items():
+        print(f"[bench]   {n:16s} {s['total_ms'] / args.prefill_steps:9.3f} ms/step "
+              f"({s['launches'] // args.prefill_steps} launches)", flush=True)
+    n_pairs = sum(t // w.m for t in range(w.n))
+    idx_flops = 2.0 * n_pairs * w.nhI * w.cI
+    ip = kern.get("indexer_prefill")
+    roof = None
+    if ip:
+        ach = idx_flops / (ip["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": "indexer_prefill", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": idx_flops}
+    return {"workload": w.name, "tokens": w.n, "ms": ms, "tokens_per_s": w.n / (ms * 1e-3),
+            "kernels_ms_per_step": {n: round(s["total_ms"] / args.prefill_steps, 4) for n, s in kern.items()},
+            "indexer_roofline": roof}
+
+
+def cpu_baseline(dec, seconds):
+    """The float64 oracle, as it stands, on whole queries of the same decode batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from compressed_sparse_attention_amd import synth
+    from oracle import csa_oracle as O
+
+    D, w = dec["D"], dec["workload"]
+    scale = 1.0 / math.sqrt(w.c)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        b = done % dec["B"]
+        nc = int(D["seq_len"][b] // w.m)
+        off = int(D["kv_offset"][b])
+        K = synth.bf16_to_f64(D["KIcomp"][off:off + nc])
+        s = O.index_scores_row(synth.bf16_to_f64(D["qI"][b]), D["wI"][b].astype(np.float64), K, nc)
+        sel = O.topk(s, w.k)
+        O.mqa(synth.bf16_to_f64(D["q"][b]), synth.bf16_to_f64(D["Ccomp"][off + sel]), scale)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(done / el, 3), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole decode queries of the 8 x 131072-token batch (32768-key sweep, "
+                      f"top-{w.k}, {w.nh}-head MQA each), float64 NumPy, {el:.1f} s"}
+
+
+def calib_copy(torch):
+    """A plain device copy of known size (for scaling memory counters)."""
+    n = 1 << 28  # 2^28 fp32 = 1 GiB each way
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_each_way": 4 * n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--prefill-warmup", type=int, default=1)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the CSA path here is single-GPU "
+              "(no sharding, no collectives); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calib_copy:
+        calib_copy(torch)
+        return
+    from compressed_sparse_attention_amd import api, layer, synth
+    api.lib()
+
+    dec = bench_decode(args, torch, api, synth, layer)
+    pre = None if args.no_prefill else bench_prefill(args, torch, api, synth, layer)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
+
+    w = dec["workload"]
+    qps = dec["B"] / (dec["ms"] * 1e-3)
+    line = {
+        "metric": "CSA decode queries/s at 128K ctx; prefill tokens/s; % HBM / MFMA roofline",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; caches N(0,1), queries std dim^-1/2, head weights N(0,1))",
+        "config": {"workload": w.name, "batch": dec["B"], "context": w.L, "m": w.m, "c": w.c, "cI": w.cI,
+                   "nhI": w.nhI, "nh": w.nh, "k": w.k, "input_copies": args.replicas},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_step_hbm_fraction": round(dec["step_bytes"] / (dec["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "warm_cache_queries_per_s": round(dec["B"] / (dec["ms_warm"] * 1e-3), 1),
+        "eager_queries_per_s": round(dec["B"] / (dec["ms_eager"] * 1e-3), 1),
+        "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
+        "prefill": pre,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -275,7 +275,7 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(idx) && aligned16(o),
               "csa_sparse_mqa: pointers must be 16-byte aligned");
   const size_t need = csa::mqa_workspace_bytes(n_queries, n_h, c, k);
-  if (workspace == nullptr || ws_bytes < need)
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   CSA_REQUIRE(aligned16(workspace), "csa_sparse_mqa: workspace must be 16-byte aligned");
   csa_status st = check_device();

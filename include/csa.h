@@ -169,8 +169,11 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
  *   idx    [n_queries, k] int32, entries in [-1, number of blocks of seq)
  *   o      [n_queries, n_h, c]  dtype dt;  lse [n_queries, n_h] fp32 or NULL
  *
- * Softmax and accumulation are fp32.  Supported: c a multiple of 64 up to
- * 1024, 1 <= n_h <= 256, k >= 1.
+ * Softmax and accumulation are fp32.  Supported: c in {64, 128, 256, 512,
+ * 1024}, 1 <= n_h <= 256, 1 <= k <= 2^24.  Small batches split each query's
+ * slots across workgroups and merge the partial results through the
+ * workspace; when the workspace query returns 0 bytes (large batches),
+ * `workspace` may be NULL.
  */
 csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
                                     size_t* bytes);
@@ -184,7 +187,7 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
  * kernel the library launches is bracketed by a pair of HIP events recorded
  * on the launch stream.  csa_timing_read synchronises on the recorded events
  * and returns, for the kernel family `name` ("gemm", "compress",
- * "indexer_sweep", "indexer_prefill", "topk", "mqa_split", "mqa_combine"),
+ * "indexer_sweep", "indexer_prefill", "topk", "mqa", "mqa_combine"),
  * the summed duration in milliseconds and the number of launches since the
  * last reset.  Unknown names give 0 launches.
  */

@@ -87,7 +87,7 @@ def test_index_topk_rejects_bad_args(L):
 def test_sparse_mqa_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
 
-    def call(dt=1, nq=2, nh=64, c=512, k=32, scale=0.04, q=p, C=p, idx=p, o=p, ws=p, wsb=1 << 30):
+    def call(dt=1, nq=2, nh=64, c=512, k=1024, scale=0.04, q=p, C=p, idx=p, o=p, ws=p, wsb=1 << 30):
         return L.csa_sparse_mqa(dt, nq, nh, c, k, scale, q, C, None, None, idx, o, None, ws, wsb, None)
     assert call(c=96) == api.CSA_ERR_INVALID_ARG
     assert call(nh=0) == api.CSA_ERR_INVALID_ARG
@@ -95,6 +95,8 @@ def test_sparse_mqa_rejects_bad_args(L):
     assert call(scale=float("nan")) == api.CSA_ERR_INVALID_ARG
     assert call(o=None) == api.CSA_ERR_INVALID_ARG
     assert call(wsb=64) == api.CSA_ERR_WORKSPACE
+    # large batches need no workspace: the size query says 0 bytes
+    assert api.csa_sparse_mqa_workspace(32768, 64, 512, 512) == 0
 
 
 def test_workspace_queries(L):

@@ -76,20 +76,22 @@ def test_project_strided_views():
     ("bf16", 64, 1, 512), ("bf16", 37, 2, 12), ("bf16", 3, 4, 64),
 ])
 def test_compress(dtype, n, m, c):
+    """Ca, Cb, Za, Zb are column slices of one projection buffer (slices start on 16-byte boundaries)."""
     rng = synth.rng_for(n + m + c)
-    P = draw(rng, (n, 4 * c), 1.0, dtype)
-    Pz = draw(rng, (n, 4 * c), 2.0, dtype)  # logits with spread so the softmax is not flat
-    P = np.where((np.arange(4 * c) // c)[None, :] >= 2, Pz, P)
+    cp = (c + 7) // 8 * 8  # slice spacing keeps every slice 16-byte aligned
+    P = draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = draw(rng, (n, 4 * cp), 2.0, dtype)  # logits with spread so the softmax is not flat
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
     Ba = draw(rng, (m, c), 0.5, dtype)
     Bb = draw(rng, (m, c), 0.5, dtype)
     Pd = to_device(P, dtype, DEV)
-    out = torch.full((n // m, c), 3.0, dtype=TD[dtype], device=DEV)
-    api.csa_compress(Pd[:, 0:c], Pd[:, c:2 * c], Pd[:, 2 * c:3 * c], Pd[:, 3 * c:], to_device(Ba, dtype, DEV),
-                     to_device(Bb, dtype, DEV), m, out)
+    out = torch.full((n // m, cp), 3.0, dtype=TD[dtype], device=DEV)[:, :c]  # rows padded to 16 bytes
+    sl = [Pd[:, i * cp:i * cp + c] for i in range(4)]
+    api.csa_compress(*sl, to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV), m, out)
     torch.cuda.synchronize()
     P64 = f64(P, dtype)
-    ref = O.compress(P64[:, :c], P64[:, c:2 * c], P64[:, 2 * c:3 * c], P64[:, 3 * c:], f64(Ba, dtype),
-                     f64(Bb, dtype), m)
+    parts = [P64[:, i * cp:i * cp + c] for i in range(4)]
+    ref = O.compress(*parts, f64(Ba, dtype), f64(Bb, dtype), m)
     if n // m:
         assert_rows_close(to_np64(out), ref, what="compress")
 
@@ -168,6 +170,9 @@ def test_index_topk_decode(dtype, lens, m, nhI, cI, k):
     rows = _oracle_rows(qI, wI, K, lens, off, m, dtype)
     check_topk(idx, rows, k)
     for b, s in enumerate(rows):  # returned scores are the selected candidates' scores
+        if s.size == 0:
+            assert np.all(idx[b] == -1) and np.all(np.isneginf(sc[b]))
+            continue
         sel = idx[b][idx[b] >= 0]
         got = sc[b][idx[b] >= 0]
         assert np.allclose(got, s[sel], rtol=1e-3, atol=1e-4 * (np.abs(s).max() + 1e-30))
@@ -214,6 +219,8 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
     ("bf16", 2, 128, 512, 256, 400, 32.0),
     ("f32", 5, 8, 64, 16, 128, 1.0),
     ("bf16", 3, 20, 128, 70, 90, 4.0),
+    ("bf16", 600, 64, 512, 200, 300, 4.0),
+    ("f32", 530, 8, 64, 70, 40, 2.0),
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
     rng = synth.rng_for(B * nh + k)
