@@ -85,29 +85,21 @@ std::map<std::string, Family> g_families;
 
 long scores_ld(long max_cand) { return (max_cand + 3) & ~3L; }
 
+// Long rows get the top-k's first radix level from the indexer sweep.
+bool use_hist(long max_cand) { return max_cand > 8192; }
+size_t hist_bytes(long n_queries, long max_cand) {
+  return use_hist(max_cand) ? align256((size_t)n_queries * (1u << csa::kTopkL1Bits) * sizeof(uint32_t)) : 0;
+}
+
 }  // namespace
 
 namespace csa {
 
-TimedScope::TimedScope(const char* family, hipStream_t s) : family_(family), stream_(s) {
-  if (!g_timing.load(std::memory_order_relaxed)) return;
-  if (hipEventCreate(&start_) != hipSuccess) {
-    start_ = nullptr;
-    return;
-  }
-  (void)hipEventRecord(start_, stream_);
-}
+bool timing_enabled() { return g_timing.load(std::memory_order_relaxed); }
 
-TimedScope::~TimedScope() {
-  if (!start_) return;
-  hipEvent_t stop = nullptr;
-  if (hipEventCreate(&stop) != hipSuccess) {
-    (void)hipEventDestroy(start_);
-    return;
-  }
-  (void)hipEventRecord(stop, stream_);
+void timing_record(const char* family, hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
-  g_families[family_].pending.emplace_back(start_, stop);
+  g_families[family].pending.emplace_back(start, stop);
 }
 
 }  // namespace csa
@@ -215,7 +207,7 @@ csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t
   CSA_REQUIRE(bytes, "csa_index_topk_workspace: null bytes");
   CSA_REQUIRE(n_queries >= 0 && max_cand >= 0, "csa_index_topk_workspace: negative size");
   CSA_REQUIRE(n_hI >= 1 && k >= 1, "csa_index_topk_workspace: n_hI and k must be >= 1");
-  *bytes = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float));
+  *bytes = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float)) + hist_bytes(n_queries, max_cand);
   return CSA_OK;
 }
 
@@ -246,17 +238,27 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
   hipStream_t s = (hipStream_t)stream;
   float* scores = (float*)workspace;
   const long ld = scores_ld(max_cand);
+  // the per-query sweep (q_seq or q_pos given) builds the level-1 histogram
+  uint32_t* hist = nullptr;
+  if (use_hist(max_cand) && (q_seq || q_pos)) {
+    hist = (uint32_t*)((char*)workspace + align256((size_t)n_queries * ld * sizeof(float)));
+    hipError_t e0 = csa::launch_hist_clear(hist, n_queries * (1L << csa::kTopkL1Bits), s);
+    if (e0 != hipSuccess) return hip_fail(e0, "csa_index_topk histogram clear");
+  }
   hipError_t e = csa::launch_indexer(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, q_seq, q_pos, kv_offset,
-                                     max_cand, scores, ld, s);
+                                     max_cand, scores, ld, hist, s);
   if (e != hipSuccess) return hip_fail(e, "csa_index_topk indexer launch");
-  e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, idx_out, score_out, s);
+  e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, idx_out, score_out, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk top-k launch");
 }
 
 csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, size_t* bytes) {
   CSA_REQUIRE(bytes, "csa_sparse_mqa_workspace: null bytes");
   CSA_REQUIRE(n_queries >= 0 && n_h >= 1 && c >= 1 && k >= 1, "csa_sparse_mqa_workspace: bad size");
-  *bytes = csa::mqa_workspace_bytes(n_queries, n_h, c, k);
+  // the query has no dtype: cover both kernels' plans
+  const size_t a = csa::mqa_workspace_bytes(n_queries, n_h, c, k, true);
+  const size_t b = csa::mqa_workspace_bytes(n_queries, n_h, c, k, false);
+  *bytes = a > b ? a : b;
   return CSA_OK;
 }
 
@@ -274,7 +276,7 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   CSA_REQUIRE(q && Ccomp && idx && o, "csa_sparse_mqa: null pointer");
   CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(idx) && aligned16(o),
               "csa_sparse_mqa: pointers must be 16-byte aligned");
-  const size_t need = csa::mqa_workspace_bytes(n_queries, n_h, c, k);
+  const size_t need = csa::mqa_workspace_bytes(n_queries, n_h, c, k, dt == CSA_BF16);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   CSA_REQUIRE(aligned16(workspace), "csa_sparse_mqa: workspace must be 16-byte aligned");

@@ -33,6 +33,28 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return
 // 2^x on the hardware exp unit.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x, 0) as one v_med3_f32 (median of x, 0 and a finite bound far above any
+// score; an infinite bound would be folded back into a NaN-quieting max pair).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
+
+// Keeps the instruction scheduler from moving anything across this point.
+// Placed right after a batch of load issues so the compiler cannot sink part
+// of the batch below the first use of its data (which would make the wave pay
+// two memory latencies instead of one).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Guarded 16-byte load without control flow: loads from p, or from
+// `fallback` (any readable address holding finite input values) when !pred.
+// The value loaded for !pred is NOT zeroed: every caller discards or masks
+// those lanes' results (zero head weight, -inf logit, unwritten output).
+// Neither a branch around the load (the compiler then waits for all loads in
+// flight where the branches merge) nor a select on the loaded value (it ties
+// each load to the next through the shared condition register) is used, so
+// a batch of these loads stays in flight together.
+__device__ __forceinline__ u32x4 load16_clamped(const void* p, bool pred, const void* fallback) {
+  return *reinterpret_cast<const u32x4*>(pred ? p : fallback);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragments.
 //
@@ -53,6 +75,10 @@ template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // see load16_clamped
+  __device__ __forceinline__ void load_clamped(const bf16_t* p, bool pred, const void* fallback) {
+    v = __builtin_bit_cast(bf16x8, load16_clamped(p, pred, fallback));
+  }
   __device__ __forceinline__ void zero() {
     u32x4 z = {0u, 0u, 0u, 0u};
     v = __builtin_bit_cast(bf16x8, z);
@@ -70,6 +96,10 @@ template <> struct Frag<float> {
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int j = 0; j < 8; ++j) f[j] = 0.f;
+  }
+  // see load16_clamped (fallback must hold at least 8 readable floats)
+  __device__ __forceinline__ void load_clamped(const float* p, bool pred, const void* fallback) {
+    load(pred ? p : reinterpret_cast<const float*>(fallback));
   }
 };
 

@@ -119,10 +119,8 @@ hipError_t run(long nblk, int m, int c, const void* Ca, const void* Cb, const vo
                hipStream_t s) {
   const long threads = nblk * (c / V);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
-  hipLaunchKernelGGL((compress_kernel<T, V>), dim3(blocks), dim3(256), 0, s, nblk, m, c,
-                     (const T*)Ca, (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba,
-                     (const T*)Bb, (T*)out, ldo);
-  return hipGetLastError();
+  return launch("compress", compress_kernel<T, V>, dim3(blocks), dim3(256), 0, s, nblk, m, c, (const T*)Ca,
+                (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba, (const T*)Bb, (T*)out, ldo);
 }
 
 }  // namespace
@@ -132,7 +130,6 @@ hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, c
                            const void* Bb, void* out, long ld_out, hipStream_t s) {
   const long nblk = n / m;
   if (nblk == 0) return hipSuccess;
-  TimedScope t("compress", s);
   if (dt == CSA_F32) return run<float, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
   if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
     return run<bf16_t, 8>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);

@@ -45,15 +45,23 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
   const int lcol = (tid % CHUNKS) * VEC;
 
   u32x4 ra[PASSES], rb[PASSES];
+  const int KT = (K + BK - 1) / BK;
   auto fetch = [&](int kt) {
     const long k = (long)kt * BK + lcol;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const long row = m0 + lrow + p * ROWS_PER_PASS;
       const long col = n0 + lrow + p * ROWS_PER_PASS;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      ra[p] = (row < M && k < K) ? *reinterpret_cast<const u32x4*>(X + row * ldx + k) : z;
-      rb[p] = (col < N && k < K) ? *reinterpret_cast<const u32x4*>(W + col * ldw + k) : z;
+      // out-of-range rows/columns load filler that only reaches unwritten outputs
+      ra[p] = load16_clamped(X + row * ldx + k, row < M && k < K, X);
+      rb[p] = load16_clamped(W + col * ldw + k, col < N && k < K, W);
+    }
+    if (kt == KT - 1 && (K % BK) != 0) {  // the K tail must contribute zeros (uniform branch)
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        if (k >= K) rb[p] = z;
+      }
     }
   };
   auto stash = [&](int buf) {
@@ -71,7 +79,6 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = (K + BK - 1) / BK;
   fetch(0);
   stash(0);
   __syncthreads();
@@ -114,18 +121,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s) {
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
-  TimedScope t("gemm", s);
-  if (in_dt == CSA_F32) {
-    hipLaunchKernelGGL((gemm_nt_kernel<float, float>), grid, dim3(256), 0, s, (int)M, (int)N, (int)K,
-                       (const float*)X, ldx, (const float*)W, ldw, (float*)Y, ldy);
-  } else if (out_dt == CSA_BF16) {
-    hipLaunchKernelGGL((gemm_nt_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, (int)M, (int)N,
-                       (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
-  } else {
-    hipLaunchKernelGGL((gemm_nt_kernel<bf16_t, float>), grid, dim3(256), 0, s, (int)M, (int)N,
-                       (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
-  }
-  return hipGetLastError();
+  if (in_dt == CSA_F32)
+    return launch("gemm", gemm_nt_kernel<float, float>, grid, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                  (const float*)X, ldx, (const float*)W, ldw, (float*)Y, ldy);
+  if (out_dt == CSA_BF16)
+    return launch("gemm", gemm_nt_kernel<bf16_t, bf16_t>, grid, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                  (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
+  return launch("gemm", gemm_nt_kernel<bf16_t, float>, grid, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
 }
 
 }  // namespace csa

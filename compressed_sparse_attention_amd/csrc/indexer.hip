@@ -15,9 +15,10 @@
 //
 // Two kernels:
 //  * indexer_sweep -- any query/sequence layout (decode, ragged batches).
-//    A workgroup takes one query and a chunk of its candidates; every wave
-//    streams 16-key groups straight from HBM into MFMA operands (no LDS),
-//    with the next group's loads in flight while the current one computes.
+//    A workgroup of eight waves takes one query and a chunk of 1024 of its
+//    candidates; the query's heads and weights are staged once in LDS, and
+//    every wave loads its run of 16-key groups straight from HBM into MFMA
+//    operands, issuing up to eight groups' loads before the first is used.
 //  * indexer_prefill -- one sequence, query t at position t.  A workgroup
 //    owns 16 consecutive tokens (2 per wave, q^I held in registers) and walks
 //    the causal key prefix once in 64-key tiles staged through LDS, so each
@@ -28,78 +29,115 @@
 namespace csa {
 namespace {
 
-constexpr int kSweepKeysPerWG = 512;
+constexpr int kSweepWaves = 8;
+constexpr int kSweepKeysPerWG = 1024;  // 128 keys (eight 16-key groups) per wave
 
 template <typename T, int KK, int NHT>
-__global__ __launch_bounds__(256) void indexer_sweep_kernel(
+__global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
     int nhI, int m, const T* __restrict__ qI, const float* __restrict__ wI,
     const T* __restrict__ K, const int32_t* __restrict__ q_seq, const int64_t* __restrict__ q_pos,
     const int64_t* __restrict__ kv_off, long max_cand, float* __restrict__ scores, long ld_sc,
-    int chunks) {
+    int chunks, uint32_t* __restrict__ hist) {
   constexpr int CI = 32 * KK;
+  constexpr int NB = 1 << kTopkL1Bits;
+  constexpr int NTH = 64 * kSweepWaves;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int QPITCH = CI + VEC;  // padded LDS row: the 16 lanes reading one k-slice hit distinct banks
+  constexpr int QCH = CI / VEC;     // 16-byte pieces per query row
+  __shared__ uint32_t s_hist[NB];
+  __shared__ __attribute__((aligned(16))) T s_q[16 * NHT * QPITCH];
+  __shared__ float s_w[16 * NHT];
+
   const int r = blockIdx.x / chunks;
   const int chunk = blockIdx.x - r * chunks;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
+
+  // Stage the query's heads (zero rows for padded heads) and head weights in
+  // LDS once per workgroup; every wave then reads its fragments from there.
+  for (int v = tid; v < 16 * NHT * QCH; v += NTH) {
+    const int head = v / QCH, pc = (v - head * QCH) * VEC;
+    u32x4 val = load16_clamped(qI + ((long)r * nhI + head) * CI + pc, head < nhI, qI);
+    if (head >= nhI) val = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&s_q[head * QPITCH + pc]) = val;
+  }
+  for (int h = tid; h < 16 * NHT; h += NTH) s_w[h] = h < nhI ? wI[(long)r * nhI + h] : 0.f;
   const long pos = q_pos ? q_pos[r] : (long)r;
   const int seq = q_seq ? q_seq[r] : 0;
-  const long off = kv_off ? kv_off[seq] : 0;
   long ncand = pos > 0 ? pos / m : 0;
   ncand = ncand < max_cand ? ncand : max_cand;
   const long chunk0 = (long)chunk * kSweepKeysPerWG;
   if (chunk0 >= ncand) return;
+  const long off = kv_off ? kv_off[seq] : 0;
   const long chunk_end = min(chunk0 + (long)kSweepKeysPerWG, ncand);
+  if (hist)
+    for (int b = tid; b < NB; b += NTH) s_hist[b] = 0u;
 
+  // Each wave owns GPW consecutive 16-key groups of the chunk and issues the
+  // loads of G groups at once (G x KK fragments staged in registers), so a
+  // wave keeps up to 32 KiB of keys in flight.  Lanes past the end of the
+  // chunk read the chunk's first key instead; their scores are never stored.
+  constexpr int GPW = kSweepKeysPerWG / (16 * kSweepWaves);
+  constexpr int VPF = sizeof(T) == 2 ? 4 : 8;  // VGPRs per fragment
+  constexpr int GB = 128 / (KK * VPF);
+  constexpr int G = GB < 1 ? 1 : (GB > GPW ? GPW : GB);
+  const T* Kb = K + off * CI + g * 8 * KK;
+  const long wbase = chunk0 + (long)wave * GPW * 16;
+  Frag<T> kb[G][KK];
+  auto issue = [&](int g0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      const long s = wbase + (g0 + gi) * 16 + c16;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kb[gi][kk].load_clamped(Kb + s * CI + 8 * kk, s < chunk_end, Kb + 8 * kk);
+    }
+    issue_fence();
+  };
+  issue(0);  // the first batch is in flight while the query is staged
+
+  __syncthreads();
   Frag<T> qa[NHT][KK];
   float wv[NHT][4];
 #pragma unroll
   for (int mt = 0; mt < NHT; ++mt) {
-    const int head = 16 * mt + c16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (head < nhI)
-        qa[mt][kk].load(qI + ((long)r * nhI + head) * CI + g * 8 * KK + 8 * kk);
-      else
-        qa[mt][kk].zero();
-    }
+    for (int kk = 0; kk < KK; ++kk) qa[mt][kk].load(&s_q[(16 * mt + c16) * QPITCH + g * 8 * KK + 8 * kk]);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int h = 16 * mt + 4 * g + rr;
-      wv[mt][rr] = h < nhI ? wI[(long)r * nhI + h] : 0.f;
-    }
+    for (int rr = 0; rr < 4; ++rr) wv[mt][rr] = s_w[16 * mt + 4 * g + rr];
   }
 
-  const T* Kb = K + off * CI + g * 8 * KK;
-  auto fetch = [&](long s0, Frag<T>* kb) {
-    const long s = s0 + c16;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (s < chunk_end)
-        kb[kk].load(Kb + s * CI + 8 * kk);
-      else
-        kb[kk].zero();
+  for (int g0 = 0; g0 < GPW; g0 += G) {
+    if (g0 > 0) {
+      if (wbase + g0 * 16 >= chunk_end) break;
+      issue(g0);
     }
-  };
-
-  Frag<T> cur[KK], nxt[KK];
-  long s0 = chunk0 + 16 * wave;
-  if (s0 < chunk_end) fetch(s0, cur);
-  for (; s0 < chunk_end; s0 += 64) {
-    if (s0 + 64 < chunk_end) fetch(s0 + 64, nxt);
-    float part = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < NHT; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < G; ++gi) {
+      float part = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) mma(acc, qa[mt][kk], cur[kk]);
+      for (int mt = 0; mt < NHT; ++mt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[mt][rr], fmaxf(acc[rr], 0.f), part);
+        for (int kk = 0; kk < KK; ++kk) mma(acc, qa[mt][kk], kb[gi][kk]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[mt][rr], relu(acc[rr]), part);
+      }
+      part = wave_sum_xor_16_32(part);
+      const long s = wbase + (g0 + gi) * 16 + c16;
+      if (g == 0 && s < chunk_end) {
+        scores[(long)r * ld_sc + s] = part;
+        if (hist) atomicAdd(&s_hist[score_key(part) >> (32 - kTopkL1Bits)], 1u);
+      }
     }
-    part = wave_sum_xor_16_32(part);
-    const long s = s0 + c16;
-    if (g == 0 && s < chunk_end) scores[(long)r * ld_sc + s] = part;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) cur[kk] = nxt[kk];
+  }
+  if (hist) {
+    __syncthreads();
+    uint32_t* hrow = hist + (long)r * NB;
+    for (int b = tid; b < NB; b += NTH) {
+      const uint32_t v = s_hist[b];
+      if (v) atomicAdd(&hrow[b], v);
+    }
   }
 }
 
@@ -153,12 +191,8 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
     for (int mt = 0; mt < NHT; ++mt) {
       const int head = 16 * mt + c16;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        if (live && head < nhI)
-          qa[tt][mt][kk].load(qI + (t * nhI + head) * CI + g * 8 * KK + 8 * kk);
-        else
-          qa[tt][mt][kk].zero();
-      }
+      for (int kk = 0; kk < KK; ++kk)
+        qa[tt][mt][kk].load_clamped(qI + (t * nhI + head) * CI + g * 8 * KK + 8 * kk, live && head < nhI, qI);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int h = 16 * mt + 4 * g + rr;
@@ -176,10 +210,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
     for (int p = 0; p < LOADS; ++p) {
       const int v = tid + p * 512;
       const long key = (long)tile * kPfTile + v / CHUNKS;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      stage[p] = (v < TILE_VECS && key < kend)
-                     ? *reinterpret_cast<const u32x4*>(K + key * CI + (v % CHUNKS) * VEC)
-                     : z;
+      stage[p] = load16_clamped(K + key * CI + (v % CHUNKS) * VEC, v < TILE_VECS && key < kend, K);
     }
   };
   auto stash = [&](int buf) {
@@ -213,7 +244,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) mma(acc, qa[tt][mt][kk], kb[kk]);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[tt][mt][rr], fmaxf(acc[rr], 0.f), part);
+          for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[tt][mt][rr], relu(acc[rr]), part);
         }
         part = wave_sum_xor_16_32(part);
         if (g == 0 && s < nc[tt]) scores[tok[tt] * ld_sc + s] = part;
@@ -227,44 +258,41 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
 template <typename T, int KK, int NHT>
 hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const void* K,
                const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off, long max_cand,
-               float* scores, long ld_sc, hipStream_t s) {
+               float* scores, long ld_sc, uint32_t* hist, hipStream_t s) {
   if (q_seq == nullptr && q_pos == nullptr) {
     const int nblocks = (int)((nq + kPfTokens - 1) / kPfTokens);
-    TimedScope t("indexer_prefill", s);
-    hipLaunchKernelGGL((indexer_prefill_kernel<T, KK, NHT>), dim3(nblocks), dim3(512), 0, s,
-                       (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores,
-                       ld_sc);
+    return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3(nblocks), dim3(512), 0, s,
+                  (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc);
   } else {
     const unsigned chunks = (unsigned)((max_cand + kSweepKeysPerWG - 1) / kSweepKeysPerWG);
-    TimedScope t("indexer_sweep", s);
-    hipLaunchKernelGGL((indexer_sweep_kernel<T, KK, NHT>), dim3(chunks * (unsigned)nq), dim3(256),
-                       0, s, nhI, m, (const T*)qI, wI, (const T*)K, q_seq, q_pos, kv_off,
-                       max_cand, scores, ld_sc, (int)chunks);
+    return launch("indexer_sweep", indexer_sweep_kernel<T, KK, NHT>, dim3(chunks * (unsigned)nq),
+                  dim3(64 * kSweepWaves), 0,
+                  s, nhI, m, (const T*)qI, wI, (const T*)K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc,
+                  (int)chunks, hist);
   }
-  return hipGetLastError();
 }
 
 template <typename T, int KK>
 hipError_t pick_nht(long nq, int nhI, int m, const void* qI, const float* wI, const void* K,
                     const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off,
-                    long max_cand, float* scores, long ld_sc, hipStream_t s) {
+                    long max_cand, float* scores, long ld_sc, uint32_t* hist, hipStream_t s) {
   switch ((nhI + 15) / 16) {
-    case 1: return run<T, KK, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    case 2: return run<T, KK, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    case 3: return run<T, KK, 3>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    default: return run<T, KK, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 1: return run<T, KK, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    case 2: return run<T, KK, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    case 3: return run<T, KK, 3>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    default: return run<T, KK, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
   }
 }
 
 template <typename T>
 hipError_t pick_kk(long nq, int nhI, int cI, int m, const void* qI, const float* wI, const void* K,
                    const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off,
-                   long max_cand, float* scores, long ld_sc, hipStream_t s) {
+                   long max_cand, float* scores, long ld_sc, uint32_t* hist, hipStream_t s) {
   switch (cI / 32) {
-    case 1: return pick_nht<T, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    case 2: return pick_nht<T, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    case 4: return pick_nht<T, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
-    case 8: return pick_nht<T, 8>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, s);
+    case 1: return pick_nht<T, 1>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    case 2: return pick_nht<T, 2>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    case 4: return pick_nht<T, 4>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
+    case 8: return pick_nht<T, 8>(nq, nhI, m, qI, wI, K, q_seq, q_pos, kv_off, max_cand, scores, ld_sc, hist, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -274,13 +302,13 @@ hipError_t pick_kk(long nq, int nhI, int cI, int m, const void* qI, const float*
 hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, const void* qI,
                           const float* wI, const void* K, const int32_t* q_seq,
                           const int64_t* q_pos, const int64_t* kv_offset, long max_cand,
-                          float* scores, long ld_sc, hipStream_t s) {
+                          float* scores, long ld_sc, uint32_t* hist, hipStream_t s) {
   if (n_queries == 0 || max_cand == 0) return hipSuccess;
   if (dt == CSA_F32)
     return pick_kk<float>(n_queries, nhI, cI, m, qI, wI, K, q_seq, q_pos, kv_offset, max_cand,
-                          scores, ld_sc, s);
+                          scores, ld_sc, hist, s);
   return pick_kk<bf16_t>(n_queries, nhI, cI, m, qI, wI, K, q_seq, q_pos, kv_offset, max_cand,
-                         scores, ld_sc, s);
+                         scores, ld_sc, hist, s);
 }
 
 }  // namespace csa

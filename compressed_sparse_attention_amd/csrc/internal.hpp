@@ -1,6 +1,7 @@
 // Internal launcher interface between the C-ABI layer (api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -8,20 +9,30 @@
 
 namespace csa {
 
-// Records a HIP event pair around the enclosed launches when kernel timing is
-// enabled (csa_timing_enable); a no-op otherwise.
-class TimedScope {
- public:
-  TimedScope(const char* family, hipStream_t s);
-  ~TimedScope();
-  TimedScope(const TimedScope&) = delete;
-  TimedScope& operator=(const TimedScope&) = delete;
+// Kernel timing (csa_timing_*): when enabled, launches carry a start/stop
+// event pair in their own dispatch packet, so the elapsed time is the
+// kernel's execution time, without the queueing before it.
+bool timing_enabled();
+void timing_record(const char* family, hipEvent_t start, hipEvent_t stop);
 
- private:
-  const char* family_;
-  hipStream_t stream_;
-  hipEvent_t start_ = nullptr;
-};
+// Every kernel of the library is launched through here.
+template <typename F, typename... Args>
+hipError_t launch(const char* family, F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                  Args... args) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (timing_enabled()) {
+    if (hipEventCreate(&a) != hipSuccess) a = nullptr;
+    if (a && hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      a = nullptr;
+      b = nullptr;
+    }
+  }
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, a, b, 0, args...);
+  const hipError_t e = hipGetLastError();
+  if (a) timing_record(family, a, b);
+  return e;
+}
 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s);
@@ -30,19 +41,29 @@ hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, c
                            const void* Za, const void* Zb, long ld_in, const void* Ba,
                            const void* Bb, void* out, long ld_out, hipStream_t s);
 
+// The top-k selector's first radix level: a histogram of the top kTopkL1Bits
+// bits of each row's score keys (see score_key).
+constexpr int kTopkL1Bits = 12;
+
 // Scores of eq 8 for every query and candidate into `scores` [n_queries, ld_sc].
+// When `hist` is not null (per-query sweep only) the kernel also adds each
+// row's level-1 key histogram into hist [n_queries, 2^kTopkL1Bits], which must
+// be zero on entry.
 hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, const void* qI,
                           const float* wI, const void* K, const int32_t* q_seq,
                           const int64_t* q_pos, const int64_t* kv_offset, long max_cand,
-                          float* scores, long ld_sc, hipStream_t s);
+                          float* scores, long ld_sc, uint32_t* hist, hipStream_t s);
 
-// Eq 9 selection per row of `scores`.
+hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s);
+
+// Eq 9 selection per row of `scores`; `hist` (nullable) is the level-1
+// histogram produced by the indexer.
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
-                       const int64_t* q_pos, long max_cand, int k, int32_t* idx_out,
-                       float* score_out, hipStream_t s);
+                       const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
+                       int32_t* idx_out, float* score_out, hipStream_t s);
 
 bool mqa_supported_c(int c);
-size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k);
+size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16);
 hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float scale,
                       const void* q, const void* C, const int32_t* q_seq,
                       const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,

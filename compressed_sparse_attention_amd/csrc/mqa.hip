@@ -39,6 +39,61 @@ template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int 
   f.f[j] = v;
 }
 
+// Copies ROWS rows of C (row ids in lanes 0..ROWS-1 of `myid`) into LDS rows
+// row0 .. row0+ROWS-1 of Cs (pitch CPITCH elements), using one wave.  A slot
+// with id -1 receives finite filler from `fallback`; its logit is masked to
+// -inf, so it carries zero weight.  Every lane moves 16-byte pieces; up to 16 pieces per lane are loaded
+// before the first is stored, so the whole gather is one or two memory
+// round trips.  For c = 512 bf16 one wave instruction moves one 1 KiB row.
+template <typename T, int CD, int ROWS, int CPITCH>
+__device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, T* Cs, int row0, int lane,
+                                            const void* fallback) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int LPR = CD / VEC;  // 16-byte pieces per row
+  if constexpr (LPR <= 64) {
+    constexpr int RPI = 64 / LPR;  // rows per instruction
+    constexpr int N = (ROWS + RPI - 1) / RPI;
+    constexpr int B = N < 16 ? N : 16;
+    const int sub = lane / LPR, pc = (lane % LPR) * VEC;
+    for (int q0 = 0; q0 < N; q0 += B) {
+      u32x4 buf[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int rl = (q0 + q) * RPI + sub;
+        const int id = __shfl(myid, rl < ROWS ? rl : 0);
+        buf[q] = load16_clamped(Cb + (long)id * CD + pc, rl < ROWS && id >= 0, fallback);
+      }
+      issue_fence();
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int rl = (q0 + q) * RPI + sub;
+        if (rl < ROWS) *reinterpret_cast<u32x4*>(&Cs[(row0 + rl) * CPITCH + pc]) = buf[q];
+      }
+    }
+  } else {
+    constexpr int IPR = LPR / 64;  // instructions per row
+    constexpr int N = ROWS * IPR;
+    constexpr int B = N < 16 ? N : 16;
+    for (int q0 = 0; q0 < N; q0 += B) {
+      u32x4 buf[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int rl = (q0 + q) / IPR;
+        const int pc = (((q0 + q) % IPR) * 64 + lane) * VEC;
+        const int id = __shfl(myid, rl);
+        buf[q] = load16_clamped(Cb + (long)id * CD + pc, id >= 0, fallback);
+      }
+      issue_fence();
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int rl = (q0 + q) / IPR;
+        const int pc = (((q0 + q) % IPR) * 64 + lane) * VEC;
+        *reinterpret_cast<u32x4*>(&Cs[(row0 + rl) * CPITCH + pc]) = buf[q];
+      }
+    }
+  }
+}
+
 template <typename T> __device__ __forceinline__ void store4(T* p, const float* v);
 template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -63,7 +118,6 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CPITCH = CD + VEC;
   constexpr int PPITCH = kKS + VEC;
-  constexpr int CHUNKS = CD / VEC;
   __shared__ __attribute__((aligned(16))) T Cs[kKS * CPITCH];
   __shared__ __attribute__((aligned(16))) T Ps[kHG * PPITCH];
   __shared__ int32_t s_rows[kKS];
@@ -97,18 +151,13 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   for (int ch = 0; ch < cps; ++ch) {
     const int slot0 = (j * cps + ch) * kKS;
     if (slot0 >= k) break;  // uniform across the workgroup
-    if (tid < kKS) {
-      const int slot = slot0 + tid;
-      s_rows[tid] = slot < k ? idx[r * k + slot] : -1;
-    }
-    __syncthreads();
-    for (int v = tid; v < kKS * CHUNKS; v += 256) {
-      const int key = v / CHUNKS;
-      const int cc = (v - key * CHUNKS) * VEC;
-      const int id = s_rows[key];
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (id >= 0) val = *reinterpret_cast<const u32x4*>(C + (off + id) * CD + cc);
-      *reinterpret_cast<u32x4*>(&Cs[key * CPITCH + cc]) = val;
+    {
+      constexpr int RPW = kKS / 4;  // rows gathered by each wave
+      const int slot = slot0 + RPW * wave + lane;
+      const int raw = idx[r * k + (slot < k ? slot : k - 1)];  // always in bounds
+      const int myid = (lane < RPW && slot < k) ? raw : -1;
+      if (lane < RPW) s_rows[RPW * wave + lane] = myid;
+      wave_gather<T, CD, RPW, CPITCH>(C + off * CD, myid, Cs, RPW * wave, lane, q);
     }
     __syncthreads();
 
@@ -120,10 +169,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
 #pragma unroll 4
       for (int kk = 0; kk < CD / 32; ++kk) {
         Frag<T> bq;
-        if (qhead < nh)
-          bq.load(qrow + 32 * kk);
-        else
-          bq.zero();
+        bq.load_clamped(qrow + 32 * kk, qhead < nh, q);
 #pragma unroll
         for (int mt = 0; mt < kKS / 16; ++mt) {
           Frag<T> ac;
@@ -232,11 +278,184 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short batches (decode): one workgroup per (query, 16-head tile, split).
+// The split's slots are walked in chunks of kTileRows gathered rows; the four
+// waves share the chunk's keys for S^T (32 keys each, the per-head max and sum
+// exchanged through LDS) and the output dims for O^T.  Block b maps to
+// (unit, tile) so that the head tiles of one unit have the same b mod 8 and
+// therefore run on the same XCD, where the gathered rows are reused from L2.
+// Partial outputs are 16 heads x c fp32 per split.
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 128;
+
+template <int DTW>
+__global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, int nht, int nsplit, int cps,
+                                                       float scale_log2, const bf16_t* __restrict__ q,
+                                                       const bf16_t* __restrict__ C,
+                                                       const int32_t* __restrict__ q_seq,
+                                                       const int64_t* __restrict__ kv_off,
+                                                       const int32_t* __restrict__ idx,
+                                                       bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                       float* __restrict__ part_o,
+                                                       float* __restrict__ part_ml) {
+  constexpr int CD = 64 * DTW;
+  constexpr int CPITCH = CD + 8;
+  constexpr int PPITCH = kTileRows + 8;
+  constexpr int KSTEPS = CD / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Cs[kTileRows * CPITCH];
+  __shared__ __attribute__((aligned(16))) bf16_t Ps[16 * PPITCH];
+  __shared__ int32_t s_rows[kTileRows];
+  __shared__ float s_red[2][4][16];
+  __shared__ __attribute__((aligned(16))) bf16_t s_q[16 * CPITCH];  // the tile's 16 query heads
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int b = blockIdx.x;
+  const int grp = b / (8 * nht);
+  const int rem = b - grp * 8 * nht;
+  const int ht = rem >> 3;
+  const long u = (long)grp * 8 + (rem & 7);
+  if (u >= (long)nq * nsplit) return;
+  const long r = u / nsplit;
+  const int j = (int)(u - r * nsplit);
+  const int head = 16 * ht + c16;  // this lane's head (B-operand column, output column)
+  const bool hlive = head < nh;
+  const int seq = q_seq ? q_seq[r] : 0;
+  const long off = kv_off ? kv_off[seq] : 0;
+
+  // the first chunk's row ids are loaded before the query fragments: the
+  // gather depends on them, the fragments are needed only after it
+  const int slot_first = (j * cps) * kTileRows + (kTileRows / 4) * wave + lane;
+  int raw_first = idx[r * k + (slot_first < k ? slot_first : k - 1)];
+  // the tile's 16 query heads: each wave stages 4 of them in LDS (16-byte pieces)
+  {
+    constexpr int QCH = CD / 8;
+#pragma unroll
+    for (int v = lane; v < 4 * QCH; v += 64) {
+      const int hl = 4 * wave + v / QCH, pc = (v % QCH) * 8;
+      const int hh = 16 * ht + hl;
+      *reinterpret_cast<u32x4*>(&s_q[hl * CPITCH + pc]) = load16_clamped(q + (r * nh + hh) * CD + pc, hh < nh, q);
+    }
+  }
+  Frag<bf16_t> qf[KSTEPS];
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[DTW];
+#pragma unroll
+  for (int dt = 0; dt < DTW; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ch = 0; ch < cps; ++ch) {
+    const int slot0 = (j * cps + ch) * kTileRows;
+    if (slot0 >= k) break;  // uniform
+    {
+      constexpr int RPW = kTileRows / 4;  // rows gathered by each wave
+      const int slot = slot0 + RPW * wave + lane;
+      const int raw = ch == 0 ? raw_first : idx[r * k + (slot < k ? slot : k - 1)];  // always in bounds
+      const int myid = (lane < RPW && slot < k) ? raw : -1;
+      if (lane < RPW) s_rows[RPW * wave + lane] = myid;
+      wave_gather<bf16_t, CD, RPW, CPITCH>(C + off * CD, myid, Cs, RPW * wave, lane, q);
+    }
+    __syncthreads();
+
+    if (ch == 0) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) qf[kk].load(&s_q[c16 * CPITCH + 32 * kk + 8 * g]);
+    }
+    // S^T for keys 32*wave .. 32*wave+31 (two 16-key M tiles), this tile's 16 heads
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        Frag<bf16_t> ac;
+        ac.load(&Cs[(32 * wave + 16 * t + c16) * CPITCH + 32 * kk + 8 * g]);
+        mma(acc[t], ac, qf[kk]);
+      }
+    }
+    float x[2][4];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = 32 * wave + 16 * t + 4 * g + rr;
+        x[t][rr] = s_rows[key] >= 0 ? acc[t][rr] * scale_log2 : -INFINITY;
+        cm = fmaxf(cm, x[t][rr]);
+      }
+    cm = wave_max_xor_16_32(cm);
+    if (g == 0) s_red[0][wave][c16] = cm;
+    __syncthreads();
+    cm = fmaxf(fmaxf(s_red[0][0][c16], s_red[0][1][c16]), fmaxf(s_red[0][2][c16], s_red[0][3][c16]));
+    const float m_new = fmaxf(m_run, cm);
+    const bool none = (m_new == -INFINITY);
+    const float alpha = none ? 1.f : exp2_fast(m_run - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float p = none ? 0.f : exp2_fast(x[t][rr] - m_new);
+        ps += p;
+        Ps[c16 * PPITCH + 32 * wave + 16 * t + 4 * g + rr] = f2bf(p);
+      }
+    ps = wave_sum_xor_16_32(ps);
+    if (g == 0) s_red[1][wave][c16] = ps;
+    __syncthreads();
+    l_run = l_run * alpha + (s_red[1][0][c16] + s_red[1][1][c16]) + (s_red[1][2][c16] + s_red[1][3][c16]);
+    m_run = m_new;
+
+    // O^T for dims tiles wave*DTW .. : C_sel^T (2-byte LDS reads) x P^T
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) acc_o[dt] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < kTileRows / 32; ++kk) {
+      Frag<bf16_t> bp;
+      bp.load(&Ps[c16 * PPITCH + 32 * kk + 8 * g]);
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt) {
+        Frag<bf16_t> ac;
+        const int dim = (wave * DTW + dt) * 16 + c16;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) frag_set<bf16_t>(ac, jj, Cs[(32 * kk + 8 * g + jj) * CPITCH + dim]);
+        mma(acc_o[dt], ac, bp);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!hlive) return;
+  if (nsplit == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) v[rr] = acc_o[dt][rr] * inv;
+      store4<bf16_t>(o + (r * nh + head) * CD + (wave * DTW + dt) * 16 + 4 * g, v);
+    }
+    if (wave == 0 && g == 0 && lse)
+      lse[r * nh + head] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+  } else {
+    const long pb = u * nh + head;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt)
+      *reinterpret_cast<float4*>(part_o + pb * CD + (wave * DTW + dt) * 16 + 4 * g) =
+          make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (wave == 0 && g == 0) {
+      part_ml[pb * 2] = m_run;
+      part_ml[pb * 2 + 1] = l_run;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, int c, int nsplit,
                                                           const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           T* __restrict__ o, float* __restrict__ lse) {
+  constexpr int U = 8;  // splits whose loads are in flight together
   const int groups = c / 4;
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long rh = gid / groups;
@@ -244,46 +463,79 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
   const int d4 = (int)(gid - rh * groups) * 4;
   const long r = rh / nh;
   const int h = (int)(rh - r * nh);
+  const long b0 = r * nsplit * (long)nh + h;  // split j at b0 + j*nh
   float M = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) M = fmaxf(M, part_ml[((r * nsplit + j) * nh + h) * 2]);
+  for (int j0 = 0; j0 < nsplit; j0 += U) {
+    float mj[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mj[u] = j0 + u < nsplit ? part_ml[(b0 + (long)(j0 + u) * nh) * 2] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mj[u]);
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int j = 0; j < nsplit; ++j) {
-      const long b = (r * nsplit + j) * nh + h;
-      const float mj = part_ml[b * 2];
-      if (mj == -INFINITY) continue;
-      const float wgt = exp2_fast(mj - M);
-      L = fmaf(part_ml[b * 2 + 1], wgt, L);
-      const float4 po = *reinterpret_cast<const float4*>(part_o + b * c + d4);
-      acc[0] = fmaf(wgt, po.x, acc[0]);
-      acc[1] = fmaf(wgt, po.y, acc[1]);
-      acc[2] = fmaf(wgt, po.z, acc[2]);
-      acc[3] = fmaf(wgt, po.w, acc[3]);
+    for (int j0 = 0; j0 < nsplit; j0 += U) {
+      float2 ml[U];
+      float4 po[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const long b = b0 + (long)(j0 + u) * nh;
+        if (j0 + u < nsplit) {
+          ml[u] = *reinterpret_cast<const float2*>(part_ml + b * 2);
+          po[u] = *reinterpret_cast<const float4*>(part_o + b * c + d4);
+        } else {
+          ml[u] = make_float2(-INFINITY, 0.f);
+          po[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wgt = ml[u].x == -INFINITY ? 0.f : exp2_fast(ml[u].x - M);
+        L = fmaf(ml[u].y, wgt, L);
+        acc[0] = fmaf(wgt, po[u].x, acc[0]);
+        acc[1] = fmaf(wgt, po[u].y, acc[1]);
+        acc[2] = fmaf(wgt, po[u].z, acc[2]);
+        acc[3] = fmaf(wgt, po[u].w, acc[3]);
+      }
     }
   }
   const float inv = (M == -INFINITY) ? 0.f : 1.f / L;
-  T* dst = o + rh * c + d4;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dst[q] = from_f32<T>(acc[q] * inv);
+  float v[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  store4<T>(o + rh * c + d4, v);
   if (d4 == 0 && lse) lse[rh] = (M == -INFINITY) ? -INFINITY : (M + log2f(L)) * 0.6931471805599453f;
 }
 
 struct Plan {
+  bool tile;  // short-batch kernel (16-head tiles) instead of the 64-head-group kernel
   int nhg, nchunks, nsplit, cps;
 };
 
-// Splits of the selection per (query, head group): enough workgroups to cover
-// the GPU twice over when the batch alone does not.
-Plan plan(long nq, int nh, int k) {
+constexpr long kTargetWGs = 512;  // two workgroups per CU
+
+// Large batches: one workgroup per (query, 64-head group), no split.  Short
+// bf16 batches (decode) use the 16-head tile kernel and split each query's
+// slots into as many 128-row chunks per workgroup as keeps about kTargetWGs
+// workgroups busy.  Other short batches split the 64-head-group kernel.
+Plan plan(long nq, int nh, int c, int k, bool bf16) {
   Plan p;
-  p.nhg = (nh + kHG - 1) / kHG;
-  p.nchunks = (k + kKS - 1) / kKS;
-  const long base = nq * p.nhg;
-  const long target = 512;
-  long ns = base >= target ? 1 : (target + base - 1) / base;
-  if (ns > p.nchunks) ns = p.nchunks;
-  p.cps = (int)((p.nchunks + ns - 1) / ns);
+  const long base = nq * ((nh + kHG - 1) / kHG);
+  p.tile = bf16 && c <= 512 && base < kTargetWGs;
+  if (p.tile) {
+    p.nhg = (nh + 15) / 16;
+    p.nchunks = (k + kTileRows - 1) / kTileRows;
+    const long units = nq * p.nhg;
+    long ns = (kTargetWGs + units - 1) / units;
+    if (ns > p.nchunks) ns = p.nchunks;
+    if (ns < 1) ns = 1;
+    p.cps = (int)((p.nchunks + ns - 1) / ns);
+  } else {
+    p.nhg = (nh + kHG - 1) / kHG;
+    p.nchunks = (k + kKS - 1) / kKS;
+    long ns = base >= kTargetWGs ? 1 : (kTargetWGs + base - 1) / base;
+    if (ns > p.nchunks) ns = p.nchunks;
+    p.cps = (int)((p.nchunks + ns - 1) / ns);
+  }
   p.nsplit = (p.nchunks + p.cps - 1) / p.cps;
   return p;
 }
@@ -292,22 +544,27 @@ template <typename T, int DTW>
 hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C,
                const int32_t* q_seq, const int64_t* kv_off, const int32_t* idx, void* o,
                float* lse, float* part_o, float* part_ml, hipStream_t s) {
-  const Plan p = plan(nq, nh, k);
-  {
-    TimedScope t("mqa", s);
-    hipLaunchKernelGGL((mqa_kernel<T, DTW>), dim3((unsigned)(nq * p.nhg * p.nsplit)), dim3(256), 0, s,
-                       nh, k, p.nhg, p.nsplit, p.cps, scale * kLog2e, (const T*)q, (const T*)C, q_seq,
-                       kv_off, idx, (T*)o, lse, part_o, part_ml);
+  const Plan p = plan(nq, nh, 64 * DTW, k, sizeof(T) == 2);
+  hipError_t e = hipSuccess;
+  bool done = false;
+  if constexpr (sizeof(T) == 2 && DTW <= 8) {
+    if (p.tile) {
+      const long units = nq * p.nsplit;
+      const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * p.nhg);
+      e = launch("mqa", mqa_tile_kernel<DTW>, dim3(blocks), dim3(256), 0, s, (int)nq, nh, k, p.nhg, p.nsplit,
+                 p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx, (bf16_t*)o,
+                 lse, part_o, part_ml);
+      done = true;
+    }
   }
-  hipError_t e = hipGetLastError();
+  if (!done)
+    e = launch("mqa", mqa_kernel<T, DTW>, dim3((unsigned)(nq * p.nhg * p.nsplit)), dim3(256), 0, s, nh, k,
+               p.nhg, p.nsplit, p.cps, scale * kLog2e, (const T*)q, (const T*)C, q_seq, kv_off, idx, (T*)o,
+               lse, part_o, part_ml);
   if (e != hipSuccess || p.nsplit == 1) return e;
   const long threads = nq * nh * (64 * DTW / 4);
-  {
-    TimedScope t("mqa_combine", s);
-    hipLaunchKernelGGL((mqa_combine_kernel<T>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       s, nq, nh, 64 * DTW, p.nsplit, part_o, part_ml, (T*)o, lse);
-  }
-  return hipGetLastError();
+  return launch("mqa_combine", mqa_combine_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                nq, nh, 64 * DTW, p.nsplit, (const float*)part_o, (const float*)part_ml, (T*)o, lse);
 }
 
 template <typename T>
@@ -330,8 +587,8 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 bool mqa_supported_c(int c) { return c == 64 || c == 128 || c == 256 || c == 512 || c == 1024; }
 
-size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k) {
-  const Plan p = plan(n_queries, nh, k);
+size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
+  const Plan p = plan(n_queries, nh, c, k, bf16);
   if (p.nsplit == 1) return 0;
   return align256((size_t)n_queries * p.nsplit * nh * c * sizeof(float)) +
          align256((size_t)n_queries * p.nsplit * nh * 2 * sizeof(float));
@@ -342,7 +599,7 @@ hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float 
                       const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
                       void* workspace, hipStream_t s) {
   if (n_queries == 0) return hipSuccess;
-  const Plan p = plan(n_queries, nh, k);
+  const Plan p = plan(n_queries, nh, c, k, dt == CSA_BF16);
   float* part_o = (float*)workspace;
   float* part_ml =
       p.nsplit == 1 ? nullptr

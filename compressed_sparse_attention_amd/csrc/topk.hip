@@ -3,20 +3,46 @@
 // to the lower block index; -0.0 equals +0.0.
 //
 // One workgroup per query row.  Scores are mapped to order-preserving uint32
-// keys and the k-th largest key T is found by a 4-pass MSB-first radix select
-// (8-bit digits, 256-bin LDS histogram, the bin that crosses the remaining
-// count found by one wave's prefix sum).  After it, exactly k - e keys are
-// > T and e of the keys == T must be taken; the output pass walks the row in
-// index order, one workgroup-wide round at a time, and a block-wide
-// exclusive scan of packed (greater, equal) flags gives every kept index a
-// deterministic slot: keys > T fill slots [0, k-e), the first e ties in
-// index order fill [k-e, k).  The pass stops once both quotas are filled.
+// keys (larger score -> larger key) and the k-th largest key T is found by an
+// MSB-first radix select:
+//   level 1: a 4096-bin histogram of the top 12 key bits -- built by the
+//            indexer while it produced the scores (long rows), or here;
+//   one ordered pass then selects every key whose 12-bit digit lies above the
+//            threshold bin and compacts the keys inside it, in index order,
+//            into a small candidate list;
+//   levels 2-4: 8+8+4-bit histograms over the candidates only, then one
+//            ordered pass over the candidates.
+// The row is staged in LDS in segments of 32 x TPB keys (coalesced loads; one
+// padding word per 32 keys, so the 64 lanes of a wave reading "their" 32
+// consecutive keys hit 64 different banks).  Thread t owns keys [32t, 32t+32)
+// of a segment, so thread order is index order: an ordered pass is one burst
+// read and classification per thread, one workgroup-wide exclusive scan, and
+// an emit of the (few) selected keys.  Keys > T fill the
+// first slots; among keys == T the lowest indices fill the rest, which is
+// the tie-break.  The result, slot order included, is deterministic.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace csa {
 namespace {
 
+constexpr int kL1Bins = 1 << kTopkL1Bits;
+constexpr int kL1Shift = 32 - kTopkL1Bits;
+constexpr int kCandCap = kL1Bins / 2;  // the candidate list (index, key) reuses the level-1 histogram's LDS
+constexpr int kEPT = 32;           // keys per thread per segment
+
+__global__ void hist_clear_kernel(uint32_t* __restrict__ h, long n) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) h[i] = 0u;
+}
+
+// Inverse of score_key (a -0.0 score comes back as +0.0).
+__device__ __forceinline__ float key_score(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+  return __uint_as_float(u);
+}
+
+// Exclusive scan over the workgroup; also returns the total.  Contains barriers.
 template <int TPB>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -40,20 +66,91 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave
   return before + x - v;
 }
 
+// Scanning bins from the highest digit down, finds the bin where the running
+// count reaches `need`; writes the bin and the count strictly above it.
+template <int TPB>
+__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* s_wave,
+                         uint32_t* s_out) {
+  const int per = (nbins + TPB - 1) / TPB;
+  const int tid = threadIdx.x;
+  uint32_t local = 0;
+  for (int q = 0; q < per; ++q) {
+    const int b = nbins - 1 - (tid * per + q);
+    if (b >= 0) local += hist[b];
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan<TPB>(local, s_wave, total);
+  if (excl < need && excl + local >= need) {
+    uint32_t cum = excl;
+    for (int q = 0; q < per; ++q) {
+      const int b = nbins - 1 - (tid * per + q);
+      const uint32_t h = hist[b];
+      if (cum + h >= need) {
+        s_out[0] = (uint32_t)b;
+        s_out[1] = cum;
+        break;
+      }
+      cum += h;
+    }
+  }
+  __syncthreads();
+}
+
+// One wave finds the bin of a small histogram (nbins <= 256) where the count
+// from the top reaches `need`; the caller follows with a barrier.
+__device__ void find_bin_wave(const uint32_t* hist, int nbins, uint32_t need, uint32_t* s_out) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins / 64 > 0 ? nbins / 64 : 1;  // 4 for 256 bins, 1 for 16
+  uint32_t h[4] = {0u, 0u, 0u, 0u};
+  uint32_t local = 0;
+  for (int q = 0; q < per; ++q) {
+    const int b = nbins - 1 - (lane * per + q);
+    h[q] = b >= 0 ? hist[b] : 0u;
+    local += h[q];
+  }
+  uint32_t incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  const uint32_t excl = incl - local;
+  if (excl < need && incl >= need) {
+    uint32_t cum = excl;
+    for (int q = 0; q < per; ++q) {
+      if (cum + h[q] >= need) {
+        s_out[0] = (uint32_t)(nbins - 1 - (lane * per + q));
+        s_out[1] = cum;
+        break;
+      }
+      cum += h[q];
+    }
+  }
+}
+
 template <int TPB>
 __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restrict__ scores, long ld,
                                                    const int64_t* __restrict__ q_pos, long max_cand,
-                                                   int k, int32_t* __restrict__ idx_out,
+                                                   int k, const uint32_t* __restrict__ hist_g,
+                                                   int32_t* __restrict__ idx_out,
                                                    float* __restrict__ score_out) {
-  __shared__ uint32_t hist[256];
+  constexpr int SEG = TPB * kEPT;     // keys per staged segment
+  constexpr int VPT = SEG / 4 / TPB;  // float4 loads per thread per segment
+  __shared__ uint32_t s_keys[SEG + SEG / 32];
+  // level-1 histogram; afterwards the candidate list: indices in [0, kCandCap),
+  // their keys in [kCandCap, 2 kCandCap)
+  __shared__ uint32_t s_hist[kL1Bins];
+  __shared__ uint32_t s_h2[3][256];  // levels 2-4
   __shared__ uint32_t s_wave[TPB / 64];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t s_res[4];
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   const long r = blockIdx.x;
   const long pos = q_pos ? q_pos[r] : r;
-  long nc = pos > 0 ? pos / m : 0;
-  nc = nc < max_cand ? nc : max_cand;
+  long ncl = pos > 0 ? pos / m : 0;
+  ncl = ncl < max_cand ? ncl : max_cand;
+  const int nc = (int)ncl;
   const float* row = scores + r * ld;
   int32_t* out = idx_out + r * k;
   float* sout = score_out ? score_out + r * k : nullptr;
@@ -66,95 +163,243 @@ __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restric
     }
     return;
   }
+  for (int b = tid; b < 3 * 256; b += TPB) (&s_h2[0][0])[b] = 0u;
 
-  uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += TPB) hist[i] = 0;
+  const int nseg = (nc + SEG - 1) / SEG;
+  const int first = tid * kEPT;  // this thread's keys: [first, first + 32) of a segment
+  const uint32_t* mykeys = s_keys + first + (first >> 5);
+  // Stage segment sg: coalesced 16-byte loads (all issued first) into padded
+  // LDS.  Rows live in a workspace whose leading dimension is a multiple of 4
+  // and >= nc, so a load clamped to [0, ld-4] stays in bounds; keys past nc
+  // are staged but never used.
+  auto stage = [&](int sg) {
     __syncthreads();
-    for (long s = tid; s < nc; s += TPB) {
-      const uint32_t key = score_key(row[s]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    const long base = (long)sg * SEG;
+    float4 buf[VPT];
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const long a = base + 4L * (tid + j * TPB);
+      buf[j] = *reinterpret_cast<const float4*>(row + (a < ld - 4 ? a : ld - 4));
+    }
+    issue_fence();
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int i = 4 * (tid + j * TPB);
+      const int a = i + (i >> 5);
+      s_keys[a] = score_key(buf[j].x);
+      s_keys[a + 1] = score_key(buf[j].y);
+      s_keys[a + 2] = score_key(buf[j].z);
+      s_keys[a + 3] = score_key(buf[j].w);
     }
     __syncthreads();
-    if (tid < 64) {
-      uint32_t h[4], sum4 = 0;
+  };
+  auto nvalid = [&](int sg) { return max(0, min(kEPT, nc - sg * SEG - first)); };
+  auto put = [&](uint32_t slot, int i, uint32_t kv) {
+    if (slot < (uint32_t)k) {  // always true when the counts are exact; keeps writes in the row
+      out[slot] = i;
+      if (sout) sout[slot] = key_score(kv);
+    }
+  };
+  // Ordered pass over the whole row: cls(key) in {0, 1, 2}.  Each thread reads
+  // its 32 keys in one burst and records the classes as two bit masks; after
+  // the workgroup scan it visits only the set bits.  Classes 1 and 2 are
+  // numbered separately in index order and handed to emit1 / emit2.
+  auto ordered_row = [&](auto&& cls, auto&& emit1, auto&& emit2, uint32_t& tot1, uint32_t& tot2) {
+    tot1 = 0;
+    tot2 = 0;
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (nseg > 1) stage(sg);
+      const int nv = nvalid(sg);
+      uint32_t m1 = 0, m2 = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        h[q] = hist[255 - 4 * tid - q];
-        sum4 += h[q];
+      for (int e = 0; e < kEPT; ++e) {
+        const int c = cls(mykeys[e]);
+        m1 |= (uint32_t)(c == 1 && e < nv) << e;
+        m2 |= (uint32_t)(c == 2 && e < nv) << e;
       }
-      uint32_t incl = sum4;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(incl, d);
-        if (tid >= d) incl += y;
+      uint32_t tot;
+      const uint32_t ex = block_excl_scan<TPB>(__popc(m1) | (__popc(m2) << 16), s_wave, tot);
+      uint32_t p1 = tot1 + (ex & 0xFFFFu), p2 = tot2 + (ex >> 16);
+      for (uint32_t mm = m1 | m2; mm; mm &= mm - 1) {
+        const int e = __ffs(mm) - 1;
+        const uint32_t kv = mykeys[e];
+        if ((m1 >> e) & 1u)
+          emit1(sg * SEG + first + e, kv, p1++);
+        else
+          emit2(sg * SEG + first + e, kv, p2++);
       }
-      const uint32_t excl = incl - sum4;
-      if (excl < need && incl >= need) {
-        uint32_t cum = excl;
+      tot1 += tot & 0xFFFFu;
+      tot2 += tot >> 16;
+    }
+  };
+
+  // the indexer's histogram is fetched together with the row
+  constexpr int HPT = kL1Bins / TPB;  // bins per thread
+  uint32_t hreg[HPT];
+  if (hist_g) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (cum + h[q] >= need) {
-            s_digit = 255u - 4u * tid - q;
-            s_above = cum;
-            break;
-          }
-          cum += h[q];
+    for (int q = 0; q < HPT; ++q) hreg[q] = hist_g[r * kL1Bins + q * TPB + tid];
+  }
+  if (nseg == 1) stage(0);
+
+  // ---- level 1: 12-bit digit ----------------------------------------------
+  if (hist_g) {
+#pragma unroll
+    for (int q = 0; q < HPT; ++q) s_hist[q * TPB + tid] = hreg[q];
+    __syncthreads();
+  } else {
+    for (int b = tid; b < kL1Bins; b += TPB) s_hist[b] = 0u;
+    __syncthreads();
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (nseg > 1) stage(sg);
+      const int nv = nvalid(sg);
+#pragma unroll
+      for (int e = 0; e < kEPT; ++e)
+        if (e < nv) atomicAdd(&s_hist[mykeys[e] >> kL1Shift], 1u);
+    }
+    __syncthreads();
+  }
+  find_bin<TPB>(s_hist, kL1Bins, (uint32_t)k, s_wave, s_res);
+  const uint32_t b1 = s_res[0];
+  const uint32_t g1 = s_res[1];  // keys with a higher digit: all selected
+  const uint32_t need1 = (uint32_t)k - g1;
+
+  // Digit > b1: selected.  Digit == b1: candidate list, in index order.
+  uint32_t* c_idx = s_hist;
+  uint32_t* c_key = s_hist + kCandCap;
+  uint32_t n_gt1, n_cand;
+  ordered_row([&](uint32_t kv) -> int {
+        const uint32_t d = kv >> kL1Shift;
+        return d > b1 ? 1 : (d == b1 ? 2 : 0);
+      },
+      [&](int i, uint32_t kv, uint32_t p) { put(p, i, kv); },
+      [&](int i, uint32_t kv, uint32_t p) {
+        if (p < (uint32_t)kCandCap) {
+          c_idx[p] = (uint32_t)i;
+          c_key[p] = kv;
         }
+      },
+      n_gt1, n_cand);
+  __syncthreads();
+  const bool listed = n_cand <= (uint32_t)kCandCap;
+
+  // ---- levels 2-4: 8 + 8 + 4 bits ---------------------------------------------
+  const int shifts[3] = {12, 4, 0};
+  const int widths[3] = {8, 8, 4};
+  if (listed) {
+    // The candidates fit in the list: one wave finishes the row, with wave-level
+    // scans only (no workgroup barriers).
+    if (wave != 0) return;
+    const int lane = tid & 63;
+    uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift, need = need1;
+    for (int lv = 0; lv < 3; ++lv) {
+      const int sh = shifts[lv];
+      const uint32_t dm = (1u << widths[lv]) - 1u;
+      uint32_t* h2 = s_h2[lv];
+      for (int j = lane; j < (int)n_cand; j += 64) {
+        const uint32_t kv = c_key[j];
+        if ((kv & pmask) == prefix) atomicAdd(&h2[(kv >> sh) & dm], 1u);
+      }
+      __builtin_amdgcn_wave_barrier();
+      find_bin_wave(h2, 1 << widths[lv], need, s_res);
+      __builtin_amdgcn_wave_barrier();
+      prefix |= s_res[0] << sh;
+      pmask |= dm << sh;
+      need -= s_res[1];
+    }
+    const uint32_t T = prefix;      // the k-th largest key
+    const uint32_t take_eq = need;  // ties at T to take, lowest indices first
+    const uint32_t gt2 = need1 - take_eq;
+    // list positions [cpt*lane, cpt*lane + cpt); list order is index order
+    const int cpt = ((int)n_cand + 63) / 64;
+    const int f = lane * cpt;
+    const int lim = max(0, min(cpt, (int)n_cand - f));
+    uint32_t c1 = 0, c2 = 0;
+    for (int e = 0; e < lim; ++e) {
+      const uint32_t kv = c_key[f + e];
+      c1 += kv > T;
+      c2 += kv == T;
+    }
+    const uint32_t packed = c1 | (c2 << 16);
+    uint32_t incl = packed;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const uint32_t ex = incl - packed;
+    uint32_t p1 = ex & 0xFFFFu, p2 = ex >> 16;
+    for (int e = 0; e < lim; ++e) {
+      const uint32_t kv = c_key[f + e];
+      const int i = (int)c_idx[f + e];
+      if (kv > T) put(g1 + p1++, i, kv);
+      if (kv == T) {
+        if (p2 < take_eq) put(g1 + gt2 + p2, i, kv);
+        ++p2;
       }
     }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= 255u << shift;
-    need -= s_above;
+    return;
   }
 
+  // More candidates than the list holds: finish over the whole row.
+  uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift, need = need1;
+  for (int lv = 0; lv < 3; ++lv) {
+    const int sh = shifts[lv];
+    const uint32_t dm = (1u << widths[lv]) - 1u;
+    uint32_t* h2 = s_h2[lv];
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (nseg > 1) stage(sg);
+      const int nv = nvalid(sg);
+#pragma unroll
+      for (int e = 0; e < kEPT; ++e) {
+        const uint32_t kv = mykeys[e];
+        if (e < nv && (kv & pmask) == prefix) atomicAdd(&h2[(kv >> sh) & dm], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) find_bin_wave(h2, 1 << widths[lv], need, s_res);
+    __syncthreads();
+    prefix |= s_res[0] << sh;
+    pmask |= dm << sh;
+    need -= s_res[1];
+  }
   const uint32_t T = prefix;
   const uint32_t take_eq = need;
-  const uint32_t gt_total = (uint32_t)k - need;
-  uint32_t base_gt = 0, base_eq = 0;
-  for (long s0 = 0; s0 < nc; s0 += TPB) {
-    const long s = s0 + tid;
-    const bool live = s < nc;
-    const float v = live ? row[s] : 0.f;
-    const uint32_t key = score_key(v);
-    const bool gt = live && key > T;
-    const bool eq = live && key == T;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<TPB>((gt ? 1u : 0u) | (eq ? 0x10000u : 0u), s_wave, tot);
-    if (gt) {
-      const uint32_t p = base_gt + (ex & 0xFFFFu);
-      if (p < gt_total) {  // always true when the select is exact; keeps writes inside the row
-        out[p] = (int32_t)s;
-        if (sout) sout[p] = v;
-      }
-    } else if (eq) {
-      const uint32_t rank = base_eq + (ex >> 16);
-      if (rank < take_eq) {
-        out[gt_total + rank] = (int32_t)s;
-        if (sout) sout[gt_total + rank] = v;
-      }
-    }
-    base_gt += tot & 0xFFFFu;
-    base_eq += tot >> 16;
-    if (base_gt >= gt_total && base_eq >= take_eq) break;
-  }
+  const uint32_t gt2 = need1 - take_eq;
+  uint32_t t1, t2;
+  ordered_row([&](uint32_t kv) -> int {
+        if ((kv >> kL1Shift) != b1) return 0;
+        return kv > T ? 1 : (kv == T ? 2 : 0);
+      },
+      [&](int i, uint32_t kv, uint32_t p) { put(g1 + p, i, kv); },
+      [&](int i, uint32_t kv, uint32_t p) {
+        if (p < take_eq) put(g1 + gt2 + p, i, kv);
+      },
+      t1, t2);
+}
+
+template <int TPB>
+void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const int64_t* q_pos, long max_cand,
+            int k, const uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
+  (void)csa::launch("topk", topk_kernel<TPB>, dim3((unsigned)n_queries), dim3(TPB), 0, s, m, scores, ld_sc, q_pos,
+               max_cand, k, hist, idx_out, score_out);
 }
 
 }  // namespace
 
+hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return launch("hist_clear", hist_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, hist, n);
+}
+
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
-                       const int64_t* q_pos, long max_cand, int k, int32_t* idx_out,
-                       float* score_out, hipStream_t s) {
+                       const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
+                       int32_t* idx_out, float* score_out, hipStream_t s) {
   if (n_queries == 0) return hipSuccess;
-  TimedScope t("topk", s);
-  if (max_cand >= 16384)
-    hipLaunchKernelGGL((topk_kernel<1024>), dim3((unsigned)n_queries), dim3(1024), 0, s, m, scores,
-                       ld_sc, q_pos, max_cand, k, idx_out, score_out);
+  if (max_cand <= 8192)
+    launch_rows<256>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
   else
-    hipLaunchKernelGGL((topk_kernel<256>), dim3((unsigned)n_queries), dim3(256), 0, s, m, scores,
-                       ld_sc, q_pos, max_cand, k, idx_out, score_out);
+    launch_rows<1024>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
   return hipGetLastError();
 }
 

@@ -162,6 +162,8 @@ def _oracle_rows(qI, wI, K, lens, off, m, dtype):
     ("f32", [512, 3, 64, 200], 4, 4, 32, 16),
     ("bf16", [2048 * 4, 2048 * 4], 4, 64, 128, 512),
     ("bf16", [777, 5000], 4, 20, 64, 33),
+    ("bf16", [4 * 20000, 4 * 9000, 4 * 12345, 4 * 32768], 4, 64, 128, 1000),  # indexer-built histogram
+    ("bf16", [4 * 40000, 4 * 70000], 4, 64, 128, 2048),  # rows longer than the LDS row cache
 ])
 def test_index_topk_decode(dtype, lens, m, nhI, cI, k):
     rng = synth.rng_for(sum(lens) + k)
@@ -196,6 +198,27 @@ def test_index_topk_exact_ties(nhI, wset):
     exact_sets_equal(idx, O.topk_rows(rows, k))
 
 
+@pytest.mark.parametrize("lens,k", [
+    ([4 * 20000, 4 * 30000], 15000),  # k-th score is 0: > 4096 candidates share the threshold bin
+    ([4 * 40000], 22000),  # same, on a row longer than the LDS row cache
+    ([4 * 3000, 4 * 7000], 2500),  # short rows: histogram built by the selector itself
+])
+def test_index_topk_many_ties_long_rows(lens, k):
+    """One head with w = 1 and integer dots: about half the scores are exactly 0, so the
+    threshold bin is huge and the lower-index tie-break decides thousands of slots."""
+    rng = synth.rng_for(len(lens) * 1000 + k)
+    cI, m = 32, 4
+    lens = np.array(lens, np.int64)
+    nblk = lens // m
+    off = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    K = synth.f32_to_bf16(rng.integers(-2, 3, size=(int(nblk.sum()), cI)).astype(np.float32))
+    qI = synth.f32_to_bf16(rng.integers(-1, 2, size=(len(lens), 1, cI)).astype(np.float32))
+    wI = np.ones((len(lens), 1), np.float32)
+    idx, _ = _run_index_topk(qI, wI, K, m, k, lens, off, "bf16")
+    rows = _oracle_rows(qI, wI, K, lens, off, m, "bf16")
+    exact_sets_equal(idx, O.topk_rows(rows, k))
+
+
 @pytest.mark.parametrize("dtype,n,m,nhI,cI,k", [
     ("f32", 512, 4, 4, 32, 16), ("bf16", 1000, 4, 64, 128, 64), ("bf16", 333, 2, 16, 64, 8),
 ])
@@ -221,6 +244,7 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
     ("bf16", 3, 20, 128, 70, 90, 4.0),
     ("bf16", 600, 64, 512, 200, 300, 4.0),
     ("f32", 530, 8, 64, 70, 40, 2.0),
+    ("bf16", 64, 64, 512, 1024, 1500, 8.0),  # several 128-row chunks per split
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
     rng = synth.rng_for(B * nh + k)
