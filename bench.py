@@ -274,7 +274,11 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     w = dec["workload"]
-    qps = dec["B"] / (dec["ms"] * 1e-3)
+    # the step is timed both as HIP-graph replays and as eager launches; the
+    # faster of the two is the reported rate (the other is on the line too)
+    launch = "graph" if dec["ms"] <= dec["ms_eager"] else "eager"
+    ms_step = min(dec["ms"], dec["ms_eager"])
+    qps = dec["B"] / (ms_step * 1e-3)
     line = {
         "metric": "CSA decode queries/s at 128K ctx; prefill tokens/s; % HBM / MFMA roofline",
         "value": round(qps, 1),
@@ -282,19 +286,20 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["ms"], 5),
+        "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; caches N(0,1), queries std dim^-1/2, head weights N(0,1))",
         "config": {"workload": w.name, "batch": dec["B"], "context": w.L, "m": w.m, "c": w.c, "cI": w.cI,
-                   "nhI": w.nhI, "nh": w.nh, "k": w.k, "input_copies": args.replicas},
+                   "nhI": w.nhI, "nh": w.nh, "k": w.k, "input_copies": args.replicas, "launch": launch},
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
-        "decode_step_hbm_fraction": round(dec["step_bytes"] / (dec["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_step_hbm_fraction": round(dec["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "warm_cache_queries_per_s": round(dec["B"] / (dec["ms_warm"] * 1e-3), 1),
         "eager_queries_per_s": round(dec["B"] / (dec["ms_eager"] * 1e-3), 1),
+        "graph_queries_per_s": round(dec["B"] / (dec["ms"] * 1e-3), 1),
         "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
         "prefill": pre,
     }

@@ -5,8 +5,9 @@
 //   o[r, h] = sum_s softmax_s(scale * q[r, h] . C_s) C_s.
 //
 // A workgroup owns one query, one group of up to 64 heads and a contiguous
-// range of its selection slots, which it walks in chunks of kKS slots with an
-// online softmax.  Per chunk it gathers the kKS selected rows of C^Comp ONCE
+// range of its selection slots, which it walks in chunks of 64 slots (32 for
+// rows over 1 KiB) with an online softmax.  Per chunk it gathers the selected
+// rows of C^Comp ONCE
 // into LDS and serves every head of the group from there (one read of a
 // selected entry for all heads: the point of a shared key-value MQA):
 //   * S^T = C_sel . q^T on MFMA, keys as M (rows read from LDS with 16-byte
@@ -16,8 +17,8 @@
 //   * P = exp2(S*scale*log2e - running max) goes to LDS as [head][key], with
 //     each head's rescale factor for the running output;
 //   * O^T = C_sel^T . P^T on MFMA, output dims as M split across the 4 waves,
-//     heads as N.  The C^T operand is read from the same LDS rows with 2-byte
-//     reads (8 per fragment); P^T is one 16-byte read.
+//     heads as N.  The C^T operand comes from the same LDS rows through two
+//     transposing LDS reads per fragment; P^T is one 16-byte read.
 // With one split per query the workgroup normalises and writes o and lse
 // itself.  Short batches (decode) split the slots across workgroups to fill
 // the GPU; each split then writes its unnormalised output and (max, sum) per
@@ -28,7 +29,6 @@
 namespace csa {
 namespace {
 
-constexpr int kKS = 32;  // selection slots per split
 constexpr int kHG = 64;  // heads per pass (4 waves x 16)
 
 template <typename T> __device__ __forceinline__ void frag_set(Frag<T>& f, int j, T v);
@@ -94,6 +94,31 @@ __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, 
   }
 }
 
+// A-operand fragment of C_sel^T for the output product: rows = output dims
+// dim0 .. dim0+15, contraction slots = keys key0 + 8g .. key0 + 8g + 7, taken
+// from row-major LDS rows of C_sel (pitch `pitch` elements).  bf16 uses two
+// transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane
+// s points at 4 consecutive columns dim0 + 4(s%4) of row key0 + 8g + s/4 (+4),
+// and lane j receives column dim0 + j of those four rows.  fp32 reads the 8
+// values one by one.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_ct(const T* Cs, int pitch, int key0, int dim0, int lane) {
+  Frag<T> f;
+  const int g = lane >> 4, s = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((address_space(3))) bf16x4 lds4;
+    const T* p0 = Cs + (key0 + 8 * g + (s >> 2)) * pitch + dim0 + 4 * (s & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)p0);
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(p0 + 4 * pitch));
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) frag_set<T>(f, jj, Cs[(key0 + 8 * g + jj) * pitch + dim0 + (lane & 15)]);
+  }
+  return f;
+}
+
 template <typename T> __device__ __forceinline__ void store4(T* p, const float* v);
 template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -103,6 +128,13 @@ template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const floa
   u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
   u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
   *reinterpret_cast<uint2*>(p) = u;
+}
+
+// Selection slots per chunk of the 64-head-group kernel: 64 while a gathered
+// row is at most 1 KiB, else 32 (keeps the chunk within ~70 KiB of LDS).
+template <typename T, int DTW>
+constexpr int group_chunk() {
+  return 64 * DTW * (int)sizeof(T) <= 1024 ? 64 : 32;
 }
 
 template <typename T, int DTW>
@@ -115,12 +147,16 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
                                                   float* __restrict__ lse, float* __restrict__ part_o,
                                                   float* __restrict__ part_ml) {
   constexpr int CD = 64 * DTW;  // head dim c
+  constexpr int KS = group_chunk<T, DTW>();
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CPITCH = CD + VEC;
-  constexpr int PPITCH = kKS + VEC;
-  __shared__ __attribute__((aligned(16))) T Cs[kKS * CPITCH];
+  constexpr int PPITCH = KS + VEC;
+  constexpr int KSTEPS = CD / 32;
+  constexpr int VPF = sizeof(T) == 2 ? 4 : 8;          // VGPRs per fragment
+  constexpr bool QREG = KSTEPS * VPF <= 64;             // keep the query fragments in registers
+  __shared__ __attribute__((aligned(16))) T Cs[KS * CPITCH];
   __shared__ __attribute__((aligned(16))) T Ps[kHG * PPITCH];
-  __shared__ int32_t s_rows[kKS];
+  __shared__ int32_t s_rows[KS];
   __shared__ float s_alpha[kHG];
   __shared__ float s_l[kHG];
 
@@ -141,6 +177,13 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   const int qhead = h0 + 16 * wave + c16;
   const bool qwave = wave < NT;
   float m_run = -INFINITY, l_run = 0.f;
+  const T* qrow = q + (r * nh + qhead) * CD + 8 * g;
+
+  Frag<T> qf[QREG ? KSTEPS : 1];
+  if constexpr (QREG) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk].load_clamped(qrow + 32 * kk, qwave && qhead < nh, q);
+  }
 
   f32x4 acc_o[DTW][4];
 #pragma unroll
@@ -149,10 +192,10 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
     for (int nt = 0; nt < 4; ++nt) acc_o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int ch = 0; ch < cps; ++ch) {
-    const int slot0 = (j * cps + ch) * kKS;
+    const int slot0 = (j * cps + ch) * KS;
     if (slot0 >= k) break;  // uniform across the workgroup
     {
-      constexpr int RPW = kKS / 4;  // rows gathered by each wave
+      constexpr int RPW = KS / 4;  // rows gathered by each wave
       const int slot = slot0 + RPW * wave + lane;
       const int raw = idx[r * k + (slot < k ? slot : k - 1)];  // always in bounds
       const int myid = (lane < RPW && slot < k) ? raw : -1;
@@ -162,25 +205,27 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
     __syncthreads();
 
     if (qwave) {
-      f32x4 acc[kKS / 16];
+      f32x4 acc[KS / 16];
 #pragma unroll
-      for (int mt = 0; mt < kKS / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const T* qrow = q + (r * nh + qhead) * CD + 8 * g;
+      for (int mt = 0; mt < KS / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int kk = 0; kk < CD / 32; ++kk) {
+      for (int kk = 0; kk < KSTEPS; ++kk) {
         Frag<T> bq;
-        bq.load_clamped(qrow + 32 * kk, qhead < nh, q);
+        if constexpr (QREG)
+          bq = qf[kk];
+        else
+          bq.load_clamped(qrow + 32 * kk, qhead < nh, q);
 #pragma unroll
-        for (int mt = 0; mt < kKS / 16; ++mt) {
+        for (int mt = 0; mt < KS / 16; ++mt) {
           Frag<T> ac;
           ac.load(&Cs[(16 * mt + c16) * CPITCH + 32 * kk + 8 * g]);
           mma(acc[mt], ac, bq);
         }
       }
-      float x[kKS / 16][4];
+      float x[KS / 16][4];
       float cm = -INFINITY;
 #pragma unroll
-      for (int mt = 0; mt < kKS / 16; ++mt)
+      for (int mt = 0; mt < KS / 16; ++mt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int key = 16 * mt + 4 * g + rr;
@@ -193,7 +238,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
       const float alpha = none ? 1.f : exp2_fast(m_run - m_new);
       float sum = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < kKS / 16; ++mt)
+      for (int mt = 0; mt < KS / 16; ++mt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float p = none ? 0.f : exp2_fast(x[mt][rr] - m_new);
@@ -216,17 +261,14 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < kKS / 32; ++kk) {
+    for (int kk = 0; kk < KS / 32; ++kk) {
       Frag<T> bp[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         if (nt < NT) bp[nt].load(&Ps[(16 * nt + c16) * PPITCH + 32 * kk + 8 * g]);
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) {
-        Frag<T> ac;
-        const int dim = (wave * DTW + dt) * 16 + c16;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) frag_set<T>(ac, jj, Cs[(32 * kk + 8 * g + jj) * CPITCH + dim]);
+        const Frag<T> ac = frag_ct<T>(Cs, CPITCH, 32 * kk, (wave * DTW + dt) * 16, lane);
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
           if (nt < NT) mma(acc_o[dt][nt], ac, bp[nt]);
@@ -273,6 +315,236 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
           *reinterpret_cast<float4*>(dst) =
               make_float4(acc_o[dt][nt][0], acc_o[dt][nt][1], acc_o[dt][nt][2], acc_o[dt][nt][3]);
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Long bf16 batches with 128 <= c <= 512 (prefill): eight waves per
+// (query, 64-head group), 64-slot chunks, double buffered.  While chunk i is
+// scored and accumulated from one LDS buffer, the rows of chunk i+1 are in
+// flight into registers (and the ids of chunk i+2 are being read), and are
+// stored into the other buffer after the output update.  S^T is split over
+// (16-head tile, 32-key half) with the per-head max and sum exchanged through
+// LDS; O^T is split over the output dims (c/8 per wave).
+// ---------------------------------------------------------------------------
+constexpr int kG8Chunk = 64;
+
+template <int DTW>
+__global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg, int nsplit, int cps,
+                                                         float scale_log2, const bf16_t* __restrict__ q,
+                                                         const bf16_t* __restrict__ C,
+                                                         const int32_t* __restrict__ q_seq,
+                                                         const int64_t* __restrict__ kv_off,
+                                                         const int32_t* __restrict__ idx,
+                                                         bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                         float* __restrict__ part_o,
+                                                         float* __restrict__ part_ml) {
+  constexpr int CD = 64 * DTW;
+  constexpr int KS = kG8Chunk;
+  constexpr int CPITCH = CD + 8;
+  constexpr int PPITCH = KS + 8;
+  constexpr int KSTEPS = CD / 32;
+  constexpr int DTPW = CD / 16 / 8;  // output 16-dim tiles per wave
+  constexpr int RPW = KS / 8;        // rows gathered per wave per chunk
+  constexpr int LPR = CD / 8;        // 16-byte pieces per row
+  constexpr int RPI = 64 / LPR;      // rows per wave instruction
+  constexpr int NLD = RPW / RPI;     // row loads per lane per chunk
+  __shared__ __attribute__((aligned(16))) bf16_t Cs[2][KS * CPITCH];
+  __shared__ __attribute__((aligned(16))) bf16_t Ps[kHG * PPITCH];
+  __shared__ int32_t s_rows[2][KS];
+  __shared__ float s_red[2][2][kHG];
+  __shared__ float s_alpha[kHG];
+  __shared__ float s_l[kHG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const long bid = blockIdx.x;
+  const int j = (int)(bid % nsplit);
+  const long rest = bid / nsplit;
+  const int hg = (int)(rest % nhg);
+  const long r = rest / nhg;
+  const int h0 = hg * kHG;
+  const int NT = min(4, (nh - h0 + 15) / 16);
+  const int seq = q_seq ? q_seq[r] : 0;
+  const long off = kv_off ? kv_off[seq] : 0;
+  const bf16_t* Cb = C + off * CD;
+  const int nch = min(cps, (k - j * cps * KS + KS - 1) / KS);  // chunks of this split (>= 1)
+
+  const int ht = wave & 3, kh = wave >> 2;  // S^T work: head tile, key half
+  const int qhead = h0 + 16 * ht + c16;
+  const bool qlive = ht < NT;
+
+  // row ids of chunk c for this wave's RPW rows (lane < RPW), -1 past k
+  auto load_ids = [&](int c) -> int {
+    const int slot = (j * cps + c) * KS + RPW * wave + lane;
+    const int raw = idx[r * k + (slot < k ? slot : k - 1)];
+    return (lane < RPW && slot < k) ? raw : -1;
+  };
+  u32x4 stg[NLD];
+  auto issue_rows = [&](int ids) {
+    const int sub = lane / LPR, pc = (lane % LPR) * 8;
+#pragma unroll
+    for (int qd = 0; qd < NLD; ++qd) {
+      const int id = __shfl(ids, qd * RPI + sub);
+      stg[qd] = load16_clamped(Cb + (long)id * CD + pc, id >= 0, q);
+    }
+    issue_fence();
+  };
+  auto store_rows = [&](int buf, int ids) {
+    const int sub = lane / LPR, pc = (lane % LPR) * 8;
+#pragma unroll
+    for (int qd = 0; qd < NLD; ++qd)
+      *reinterpret_cast<u32x4*>(&Cs[buf][(RPW * wave + qd * RPI + sub) * CPITCH + pc]) = stg[qd];
+    if (lane < RPW) s_rows[buf][RPW * wave + lane] = ids;
+  };
+
+  // prologue: chunk 0 into buffer 0, chunk 1 in flight, ids of chunk 2 requested
+  int ids_cur = load_ids(0);
+  int ids_nxt = nch > 1 ? load_ids(1) : -1;
+  issue_rows(ids_cur);
+  Frag<bf16_t> qf[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) qf[kk].load_clamped(q + (r * nh + qhead) * CD + 32 * kk + 8 * g, qlive && qhead < nh, q);
+  store_rows(0, ids_cur);
+  if (nch > 1) issue_rows(ids_nxt);
+  int ids_nn = nch > 2 ? load_ids(2) : -1;
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 acc_o[DTPW][4];
+#pragma unroll
+  for (int dt = 0; dt < DTPW; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc_o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int ch = 0; ch < nch; ++ch) {
+    const int cur = ch & 1;
+    const bf16_t* Cc = Cs[cur];
+    // ---- S^T for keys 32*kh .. +31 of this chunk, head tile ht
+    float x[2][4];
+    float cm = -INFINITY;
+    if (qlive) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          Frag<bf16_t> ac;
+          ac.load(&Cc[(32 * kh + 16 * t + c16) * CPITCH + 32 * kk + 8 * g]);
+          mma(acc[t], ac, qf[kk]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = 32 * kh + 16 * t + 4 * g + rr;
+          x[t][rr] = s_rows[cur][key] >= 0 ? acc[t][rr] * scale_log2 : -INFINITY;
+          cm = fmaxf(cm, x[t][rr]);
+        }
+      cm = wave_max_xor_16_32(cm);
+      if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
+    }
+    __syncthreads();
+    float alpha = 1.f;
+    if (qlive) {
+      const int hl = 16 * ht + c16;
+      const float m_new = fmaxf(m_run, fmaxf(s_red[0][0][hl], s_red[0][1][hl]));
+      const bool none = (m_new == -INFINITY);
+      alpha = none ? 1.f : exp2_fast(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float p = none ? 0.f : exp2_fast(x[t][rr] - m_new);
+          ps += p;
+          Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g + rr] = f2bf(p);
+        }
+      ps = wave_sum_xor_16_32(ps);
+      if (g == 0) {
+        s_red[1][kh][hl] = ps;
+        if (kh == 0) s_alpha[hl] = alpha;
+      }
+      m_run = m_new;
+    }
+    __syncthreads();
+    if (qlive) {
+      const int hl = 16 * ht + c16;
+      l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
+    }
+    // ---- O^T for dims tiles DTPW*wave .. : C_sel^T x P^T
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt < NT) {
+        const float a = s_alpha[16 * nt + c16];
+#pragma unroll
+        for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KS / 32; ++kk) {
+      Frag<bf16_t> bp[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        if (nt < NT) bp[nt].load(&Ps[(16 * nt + c16) * PPITCH + 32 * kk + 8 * g]);
+#pragma unroll
+      for (int dt = 0; dt < DTPW; ++dt) {
+        const Frag<bf16_t> ac = frag_ct<bf16_t>(Cc, CPITCH, 32 * kk, (wave * DTPW + dt) * 16, lane);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) mma(acc_o[dt][nt], ac, bp[nt]);
+      }
+    }
+    // ---- rows of chunk ch+1 land in the other buffer; chunk ch+2 goes in flight
+    if (ch + 1 < nch) store_rows(cur ^ 1, ids_nxt);
+    __syncthreads();
+    if (ch + 2 < nch) {
+      issue_rows(ids_nn);
+      ids_nxt = ids_nn;
+      ids_nn = ch + 3 < nch ? load_ids(ch + 3) : -1;
+    }
+  }
+
+  if (nsplit == 1) {
+    if (qlive && kh == 0 && g == 0) {
+      s_l[16 * ht + c16] = l_run;
+      if (lse && qhead < nh)
+        lse[r * nh + qhead] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int head = h0 + 16 * nt + c16;
+      if (nt < NT && head < nh) {
+        const float l = s_l[16 * nt + c16];
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DTPW; ++dt) {
+          float v[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] = acc_o[dt][nt][rr] * inv;
+          store4<bf16_t>(o + (r * nh + head) * CD + (wave * DTPW + dt) * 16 + 4 * g, v);
+        }
+      }
+    }
+  } else {
+    const long pbase = (r * nsplit + j) * (long)nh;
+    if (qlive && kh == 0 && g == 0 && qhead < nh) {
+      part_ml[(pbase + qhead) * 2] = m_run;
+      part_ml[(pbase + qhead) * 2 + 1] = l_run;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int head = h0 + 16 * nt + c16;
+      if (nt < NT && head < nh) {
+#pragma unroll
+        for (int dt = 0; dt < DTPW; ++dt)
+          *reinterpret_cast<float4*>(part_o + (pbase + head) * CD + (wave * DTPW + dt) * 16 + 4 * g) =
+              make_float4(acc_o[dt][nt][0], acc_o[dt][nt][1], acc_o[dt][nt][2], acc_o[dt][nt][3]);
       }
     }
   }
@@ -415,10 +687,7 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
       bp.load(&Ps[c16 * PPITCH + 32 * kk + 8 * g]);
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) {
-        Frag<bf16_t> ac;
-        const int dim = (wave * DTW + dt) * 16 + c16;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) frag_set<bf16_t>(ac, jj, Cs[(32 * kk + 8 * g + jj) * CPITCH + dim]);
+        const Frag<bf16_t> ac = frag_ct<bf16_t>(Cs, CPITCH, 32 * kk, (wave * DTW + dt) * 16, lane);
         mma(acc_o[dt], ac, bp);
       }
     }
@@ -507,7 +776,8 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
 }
 
 struct Plan {
-  bool tile;  // short-batch kernel (16-head tiles) instead of the 64-head-group kernel
+  bool tile;    // short-batch kernel (16-head tiles) instead of the 64-head-group kernels
+  bool group8;  // eight-wave double-buffered 64-head-group kernel (bf16, 128 <= c <= 512)
   int nhg, nchunks, nsplit, cps;
 };
 
@@ -521,6 +791,7 @@ Plan plan(long nq, int nh, int c, int k, bool bf16) {
   Plan p;
   const long base = nq * ((nh + kHG - 1) / kHG);
   p.tile = bf16 && c <= 512 && base < kTargetWGs;
+  p.group8 = !p.tile && bf16 && c >= 128 && c <= 512;
   if (p.tile) {
     p.nhg = (nh + 15) / 16;
     p.nchunks = (k + kTileRows - 1) / kTileRows;
@@ -531,7 +802,8 @@ Plan plan(long nq, int nh, int c, int k, bool bf16) {
     p.cps = (int)((p.nchunks + ns - 1) / ns);
   } else {
     p.nhg = (nh + kHG - 1) / kHG;
-    p.nchunks = (k + kKS - 1) / kKS;
+    const int ks = p.group8 ? kG8Chunk : ((long)c * (bf16 ? 2 : 4) <= 1024 ? 64 : 32);  // group_chunk<T, c/64>()
+    p.nchunks = (k + ks - 1) / ks;
     long ns = base >= kTargetWGs ? 1 : (kTargetWGs + base - 1) / base;
     if (ns > p.nchunks) ns = p.nchunks;
     p.cps = (int)((p.nchunks + ns - 1) / ns);
@@ -554,6 +826,14 @@ hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C
       e = launch("mqa", mqa_tile_kernel<DTW>, dim3(blocks), dim3(256), 0, s, (int)nq, nh, k, p.nhg, p.nsplit,
                  p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx, (bf16_t*)o,
                  lse, part_o, part_ml);
+      done = true;
+    }
+  }
+  if constexpr (sizeof(T) == 2 && DTW >= 2 && DTW <= 8) {
+    if (!done && p.group8) {
+      e = launch("mqa", mqa_group8_kernel<DTW>, dim3((unsigned)(nq * p.nhg * p.nsplit)), dim3(512), 0, s, nh, k,
+                 p.nhg, p.nsplit, p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx,
+                 (bf16_t*)o, lse, part_o, part_ml);
       done = true;
     }
   }

@@ -245,6 +245,8 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
     ("bf16", 600, 64, 512, 200, 300, 4.0),
     ("f32", 530, 8, 64, 70, 40, 2.0),
     ("bf16", 64, 64, 512, 1024, 1500, 8.0),  # several 128-row chunks per split
+    ("bf16", 520, 128, 256, 130, 500, 2.0),  # long batch, two 64-head groups, c = 256
+    ("bf16", 512, 20, 128, 200, 260, 1.0),  # long batch, partial head tile, c = 128
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
     rng = synth.rng_for(B * nh + k)
