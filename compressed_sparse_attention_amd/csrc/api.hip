@@ -87,8 +87,44 @@ long scores_ld(long max_cand) { return (max_cand + 3) & ~3L; }
 
 // Long rows get the top-k's first radix level from the indexer sweep.
 bool use_hist(long max_cand) { return max_cand > 8192; }
-size_t hist_bytes(long n_queries, long max_cand) {
-  return use_hist(max_cand) ? align256((size_t)n_queries * (1u << csa::kTopkL1Bits) * sizeof(uint32_t)) : 0;
+// ... and, for few rows, a selector that spreads each row over workgroups.
+int topk_chunks(long max_cand) { return (int)((max_cand + csa::kMChunk - 1) / csa::kMChunk); }
+bool use_lists(long n_queries, long max_cand) {
+  const long P = topk_chunks(max_cand);
+  return use_hist(max_cand) && P <= csa::kMMaxChunks && n_queries * P <= csa::kMMaxWorkgroups;
+}
+
+// Workspace layout of csa_index_topk (each area 256-byte aligned):
+//   scores [n_queries, scores_ld]            fp32
+//   hist   [n_queries, 2^kTopkL1Bits]        uint32   (use_hist)
+//   arrive [n_queries]                       uint32   (use_lists; right after hist)
+//   counts [n_queries, P, 2]                 uint32   (use_lists)
+//   gt     [n_queries, P, min(kMChunk, k)]   uint64   (use_lists)
+//   eq     [n_queries, P, kMChunk]           uint64   (use_lists)
+struct IndexWs {
+  size_t scores = 0, hist = 0, arrive = 0, counts = 0, gt = 0, eq = 0, total = 0;
+};
+IndexWs index_ws(long n_queries, long max_cand, int k) {
+  IndexWs w;
+  size_t at = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float));
+  if (use_hist(max_cand)) {
+    w.hist = at;
+    at += (size_t)n_queries * (1u << csa::kTopkL1Bits) * sizeof(uint32_t);
+    w.arrive = at;  // contiguous with hist: one clear covers both
+    at = align256(at + (use_lists(n_queries, max_cand) ? (size_t)n_queries * sizeof(uint32_t) : 0));
+  }
+  if (use_lists(n_queries, max_cand)) {
+    const size_t P = (size_t)topk_chunks(max_cand);
+    const size_t gtc = (size_t)(k < csa::kMChunk ? k : csa::kMChunk);
+    w.counts = at;
+    at = align256(at + (size_t)n_queries * P * 2 * sizeof(uint32_t));
+    w.gt = at;
+    at = align256(at + (size_t)n_queries * P * gtc * sizeof(uint64_t));
+    w.eq = at;
+    at = align256(at + (size_t)n_queries * P * csa::kMChunk * sizeof(uint64_t));
+  }
+  w.total = at;
+  return w;
 }
 
 }  // namespace
@@ -207,7 +243,7 @@ csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t
   CSA_REQUIRE(bytes, "csa_index_topk_workspace: null bytes");
   CSA_REQUIRE(n_queries >= 0 && max_cand >= 0, "csa_index_topk_workspace: negative size");
   CSA_REQUIRE(n_hI >= 1 && k >= 1, "csa_index_topk_workspace: n_hI and k must be >= 1");
-  *bytes = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float)) + hist_bytes(n_queries, max_cand);
+  *bytes = index_ws(n_queries, max_cand, k).total;
   return CSA_OK;
 }
 
@@ -239,16 +275,31 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
   float* scores = (float*)workspace;
   const long ld = scores_ld(max_cand);
   // the per-query sweep (q_seq or q_pos given) builds the level-1 histogram
+  const IndexWs w = index_ws(n_queries, max_cand, k);
+  char* ws = (char*)workspace;
   uint32_t* hist = nullptr;
-  if (use_hist(max_cand) && (q_seq || q_pos)) {
-    hist = (uint32_t*)((char*)workspace + align256((size_t)n_queries * ld * sizeof(float)));
-    hipError_t e0 = csa::launch_hist_clear(hist, n_queries * (1L << csa::kTopkL1Bits), s);
+  csa::TopkLists lists{};
+  const bool sweep = q_seq || q_pos;
+  const bool multi = sweep && use_lists(n_queries, max_cand);
+  if (use_hist(max_cand) && sweep) {
+    hist = (uint32_t*)(ws + w.hist);
+    const long words = n_queries * (1L << csa::kTopkL1Bits) + (multi ? n_queries : 0);
+    hipError_t e0 = csa::launch_hist_clear(hist, words, s);
     if (e0 != hipSuccess) return hip_fail(e0, "csa_index_topk histogram clear");
+  }
+  if (multi) {
+    lists.arrive = (uint32_t*)(ws + w.arrive);
+    lists.counts = (uint32_t*)(ws + w.counts);
+    lists.gt = (uint64_t*)(ws + w.gt);
+    lists.eq = (uint64_t*)(ws + w.eq);
+    lists.P = topk_chunks(max_cand);
+    lists.gtc = k < csa::kMChunk ? k : csa::kMChunk;
   }
   hipError_t e = csa::launch_indexer(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, q_seq, q_pos, kv_offset,
                                      max_cand, scores, ld, hist, s);
   if (e != hipSuccess) return hip_fail(e, "csa_index_topk indexer launch");
-  e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, idx_out, score_out, s);
+  e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, multi ? &lists : nullptr, idx_out,
+                       score_out, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk top-k launch");
 }
 

@@ -43,6 +43,24 @@ __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(
 // two memory latencies instead of one).
 __device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Cross-workgroup hand-off without cache maintenance.  Data that one
+// workgroup publishes for another one of the same launch is written with
+// st_agent (write-through to the device-coherent level) and read with
+// ld_agent (which bypasses possibly stale cache lines), so no cache-wide
+// write-back or invalidate is needed.  Before a workgroup announces its data
+// (an atomic), every thread waits for its own stores with wait_stores()
+// and the workgroup meets at a barrier.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): this thread's loads and stores have completed.
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Guarded 16-byte load without control flow: loads from p, or from
 // `fallback` (any readable address holding finite input values) when !pred.
 // The value loaded for !pred is NOT zeroed: every caller discards or masks
@@ -119,6 +137,24 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), built
+// from DPP moves: shifts by 1, 2, 4, 8 inside each 16-lane row, then the
+// last lane of row 0 is added to row 1 (and of row 2 to row 3), then the last
+// lane of row 1 to rows 2 and 3.  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)v;
+}
+
+// Value of lane 63 (a uniform result).
+__device__ __forceinline__ uint32_t wave_last(uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 63); }
 
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {
   v += __shfl_xor(v, 16);

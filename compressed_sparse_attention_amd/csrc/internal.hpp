@@ -56,11 +56,31 @@ hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, 
 
 hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s);
 
+// Long rows (with the indexer's histogram) can be selected by many
+// workgroups per row: chunks of kMChunk keys, at most kMMaxChunks per row.
+constexpr int kMChunk = 2048;
+constexpr int kMMaxChunks = 64;
+constexpr long kMMaxWorkgroups = 4096;  // bounds the list workspace
+
+// Workspace areas of the multi-workgroup selector.  `arrive` [n_queries]
+// must be zero on entry (it is cleared together with the histogram); the
+// lists need no initialisation.  List entries hold the candidate index in
+// the low 32 bits and the fp32 score bits (gt) or the score key (eq) above.
+struct TopkLists {
+  uint32_t* arrive;  // [n_queries]
+  uint32_t* counts;  // [n_queries, P, 2]
+  uint64_t* gt;      // [n_queries, P, gtc]
+  uint64_t* eq;      // [n_queries, P, kMChunk]
+  int P;             // chunks per row: ceil(max_cand / kMChunk)
+  int gtc;           // min(kMChunk, k)
+};
+
 // Eq 9 selection per row of `scores`; `hist` (nullable) is the level-1
-// histogram produced by the indexer.
+// histogram produced by the indexer; `lists` (nullable, needs `hist`) selects
+// the multi-workgroup path.
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
                        const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
-                       int32_t* idx_out, float* score_out, hipStream_t s);
+                       const TopkLists* lists, int32_t* idx_out, float* score_out, hipStream_t s);
 
 bool mqa_supported_c(int c);
 size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16);

@@ -46,12 +46,7 @@ __device__ __forceinline__ float key_score(uint32_t key) {
 template <int TPB>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -98,30 +93,27 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_
 
 // One wave finds the bin of a small histogram (nbins <= 256) where the count
 // from the top reaches `need`; the caller follows with a barrier.
+// nbins is 256 or 16.
 __device__ void find_bin_wave(const uint32_t* hist, int nbins, uint32_t need, uint32_t* s_out) {
   const int lane = threadIdx.x & 63;
-  const int per = nbins / 64 > 0 ? nbins / 64 : 1;  // 4 for 256 bins, 1 for 16
-  uint32_t h[4] = {0u, 0u, 0u, 0u};
-  uint32_t local = 0;
-  for (int q = 0; q < per; ++q) {
-    const int b = nbins - 1 - (lane * per + q);
-    h[q] = b >= 0 ? hist[b] : 0u;
-    local += h[q];
-  }
-  uint32_t incl = local;
+  // lane l holds bins nbins-1-4l .. nbins-4-4l (highest first); lanes past the
+  // histogram hold zeros
+  uint32_t h[4];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
+  for (int q = 0; q < 4; ++q) {
+    const int b = nbins - 1 - (4 * lane + q);
+    h[q] = b >= 0 ? hist[b] : 0u;
   }
+  const uint32_t local = h[0] + h[1] + h[2] + h[3];
+  const uint32_t incl = wave_incl_scan(local);
   const uint32_t excl = incl - local;
   if (excl < need && incl >= need) {
     uint32_t cum = excl;
-    for (int q = 0; q < per; ++q) {
-      if (cum + h[q] >= need) {
-        s_out[0] = (uint32_t)(nbins - 1 - (lane * per + q));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum < need && cum + h[q] >= need) {
+        s_out[0] = (uint32_t)(nbins - 1 - (4 * lane + q));
         s_out[1] = cum;
-        break;
       }
       cum += h[q];
     }
@@ -321,13 +313,7 @@ __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restric
       c2 += kv == T;
     }
     const uint32_t packed = c1 | (c2 << 16);
-    uint32_t incl = packed;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    const uint32_t ex = incl - packed;
+    const uint32_t ex = wave_incl_scan(packed) - packed;
     uint32_t p1 = ex & 0xFFFFu, p2 = ex >> 16;
     for (int e = 0; e < lim; ++e) {
       const uint32_t kv = c_key[f + e];
@@ -378,6 +364,300 @@ __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restric
       t1, t2);
 }
 
+// ---------------------------------------------------------------------------
+// Long rows with the indexer's level-1 histogram: many workgroups per row.
+//
+// A row of n_cand scores is cut into chunks of kMChunk keys, one 256-thread
+// workgroup each (8 keys per thread), so the row is read by many CUs at once.
+// Every chunk workgroup fetches the row's histogram, finds the threshold bin
+// b1 itself, classifies its keys (digit > b1: selected; digit == b1:
+// candidate) and appends both kinds, in index order, to per-chunk lists in
+// the workspace.  The last chunk workgroup of a row to finish (a per-row
+// arrival counter) then:
+//   * copies the selected lists, chunk by chunk, to the first g1 slots;
+//   * stages the candidate lists (all chunks, index order) in LDS, runs
+//     levels 2-4 on them and emits the rest exactly as the one-workgroup
+//     selector does.
+// The output, slot order included, is the same as that selector's.
+// ---------------------------------------------------------------------------
+constexpr int kMTPB = 256;
+constexpr int kMEPT = 8;
+constexpr int kMSeg = 4096;   // candidates staged in LDS at once
+constexpr int kMUnroll = 8;   // list entries fetched per thread per batch
+
+// chunk holding list position e, given the exclusive prefix pre[0..P] of the
+// per-chunk counts (pre[P] = total); P <= kMMaxChunks
+__device__ __forceinline__ int chunk_of(const uint32_t* pre, int P, uint32_t e) {
+  int lo = 0, hi = P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= e) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
+    int m, const float* __restrict__ scores, long ld, const int64_t* __restrict__ q_pos, long max_cand, int k,
+    const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
+    uint64_t* __restrict__ gt_list, uint64_t* __restrict__ eq_list, int P, int gtc, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  __shared__ uint32_t s_ckey[kMSeg];
+  __shared__ uint32_t s_cidx[kMSeg];
+  __shared__ uint32_t s_h2[3][256];
+  __shared__ uint32_t s_pg[kMMaxChunks + 1], s_pe[kMMaxChunks + 1];
+  __shared__ uint32_t s_wave[kMTPB / 64];
+  __shared__ uint32_t s_res[4];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const long r = blockIdx.x / P;
+  const int j = (int)(blockIdx.x - r * P);
+  const long pos = q_pos ? q_pos[r] : r;
+  long ncl = pos > 0 ? pos / m : 0;
+  ncl = ncl < max_cand ? ncl : max_cand;
+  const int nc = (int)ncl;
+  const float* row = scores + r * ld;
+  int32_t* out = idx_out + r * k;
+  float* sout = score_out ? score_out + r * k : nullptr;
+
+  if (nc <= k) {  // every candidate is kept
+    if (j == 0)
+      for (int e = tid; e < k; e += kMTPB) {
+        const bool live = e < nc;
+        out[e] = live ? e : -1;
+        if (sout) sout[e] = live ? row[e] : -INFINITY;
+      }
+    return;
+  }
+  const int Pr = (nc + kMChunk - 1) / kMChunk;
+  if (j >= Pr) return;
+
+  // ---- chunk phase ------------------------------------------------------------
+  // this thread's keys: a .. a+7 (loads clamped into the row; keys past nc unused)
+  const long a = (long)j * kMChunk + kMEPT * tid;
+  const float4 v0 = *reinterpret_cast<const float4*>(row + (a < ld - 4 ? a : ld - 4));
+  const float4 v1 = *reinterpret_cast<const float4*>(row + (a + 4 < ld - 4 ? a + 4 : ld - 4));
+  constexpr int HPT = kL1Bins / kMTPB;  // 16 bins per thread: [HPT*tid, HPT*tid + HPT)
+  const uint32_t* hrow = hist_g + r * kL1Bins;
+  u32x4 hv[HPT / 4];
+#pragma unroll
+  for (int q = 0; q < HPT / 4; ++q) hv[q] = *reinterpret_cast<const u32x4*>(hrow + HPT * tid + 4 * q);
+  issue_fence();
+  if (tid == 0) {
+    s_res[0] = 0u;
+    s_res[1] = 0u;
+  }
+  uint32_t hb[HPT];
+#pragma unroll
+  for (int q = 0; q < HPT / 4; ++q) {
+    hb[4 * q] = hv[q].x;
+    hb[4 * q + 1] = hv[q].y;
+    hb[4 * q + 2] = hv[q].z;
+    hb[4 * q + 3] = hv[q].w;
+  }
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < HPT; ++q) local += hb[q];
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan<kMTPB>(local, s_wave, tot);
+  const uint32_t above = tot - excl - local;  // keys in bins above this thread's bins
+  if (above < (uint32_t)k && above + local >= (uint32_t)k) {
+    uint32_t cum = above;
+#pragma unroll
+    for (int q = HPT - 1; q >= 0; --q) {
+      if (cum < (uint32_t)k && cum + hb[q] >= (uint32_t)k) {
+        s_res[0] = (uint32_t)(HPT * tid + q);
+        s_res[1] = cum;
+      }
+      cum += hb[q];
+    }
+  }
+  __syncthreads();
+  const uint32_t b1 = s_res[0];
+  const uint32_t g1 = s_res[1];
+
+  const float sv[kMEPT] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t kv[kMEPT];
+  uint32_t mg = 0, me = 0;
+#pragma unroll
+  for (int e = 0; e < kMEPT; ++e) {
+    kv[e] = score_key(sv[e]);
+    const bool valid = a + e < nc;
+    const uint32_t d = kv[e] >> kL1Shift;
+    mg |= (uint32_t)(valid && d > b1) << e;
+    me |= (uint32_t)(valid && d == b1) << e;
+  }
+  uint32_t tot2;
+  const uint32_t ex2 = block_excl_scan<kMTPB>(__popc(mg) | (__popc(me) << 16), s_wave, tot2);
+  uint32_t pg = ex2 & 0xFFFFu, pe = ex2 >> 16;
+  // list entries: index in the low word, score bits (gt) or key (eq) in the high word
+  uint64_t* gl = gt_list + (r * P + j) * (long)gtc;
+  uint64_t* el = eq_list + (r * P + j) * (long)kMChunk;
+#pragma unroll
+  for (int e = 0; e < kMEPT; ++e) {
+    const uint64_t i = (uint64_t)(a + e);
+    if ((mg >> e) & 1u) {
+      if (pg < (uint32_t)gtc) st_agent(gl + pg, i | ((uint64_t)__float_as_uint(sv[e]) << 32));
+      ++pg;
+    }
+    if ((me >> e) & 1u) st_agent(el + pe++, i | ((uint64_t)kv[e] << 32));
+  }
+  if (tid == 0) {
+    const uint32_t ng = tot2 & 0xFFFFu;
+    st_agent(counts + (r * P + j) * 2, ng < (uint32_t)gtc ? ng : (uint32_t)gtc);
+    st_agent(counts + (r * P + j) * 2 + 1, tot2 >> 16);
+  }
+  // publish the lists, then count this chunk in; the last one finishes the row
+  wait_stores();
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(arrive + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(Pr - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- finishing phase (last chunk workgroup of the row) ----------------------
+  for (int b = tid; b < 3 * 256; b += kMTPB) (&s_h2[0][0])[b] = 0u;
+  if (wave == 0) {
+    const uint32_t cg = lane < Pr ? ld_agent(counts + (r * P + lane) * 2) : 0u;
+    const uint32_t ce = lane < Pr ? ld_agent(counts + (r * P + lane) * 2 + 1) : 0u;
+    const uint32_t ig = wave_incl_scan(cg), ie = wave_incl_scan(ce);
+    s_pg[lane] = ig - cg;
+    s_pe[lane] = ie - ce;
+    if (lane == 63) {
+      s_pg[kMMaxChunks] = ig;
+      s_pe[kMMaxChunks] = ie;
+    }
+  }
+  __syncthreads();
+  const uint32_t n_cand = s_pe[kMMaxChunks];
+  const int nseg = (int)((n_cand + kMSeg - 1) / kMSeg);
+
+  auto put = [&](uint32_t slot, uint32_t i, uint32_t key) {
+    if (slot < (uint32_t)k) {
+      out[slot] = (int32_t)i;
+      if (sout) sout[slot] = key_score(key);
+    }
+  };
+  // Both lists in one pass: a group of TPC threads serves each chunk, so list
+  // positions need no search.  Selected entries go straight to their slots
+  // (chunk order = index order); candidates go to LDS when they all fit.
+  {
+    int p2 = 1;
+    while (p2 < Pr) p2 <<= 1;
+    const int tpc = kMTPB / p2;  // >= 4
+    const int c = tid / tpc, sub = tid - c * tpc;
+    if (c < Pr) {
+      const uint32_t g0 = s_pg[c], ng = s_pg[c + 1] - g0;
+      const uint32_t e0c = s_pe[c], ne = s_pe[c + 1] - e0c;
+      const uint32_t nmax = nseg == 1 ? max(ng, ne) : ng;
+      const uint64_t* gsrc = gt_list + (r * P + c) * (long)gtc;
+      const uint64_t* esrc = eq_list + (r * P + c) * (long)kMChunk;
+      for (uint32_t base = sub; base < nmax; base += tpc * kMUnroll) {
+        uint64_t eg[kMUnroll], ee[kMUnroll];
+#pragma unroll
+        for (int u = 0; u < kMUnroll; ++u) {
+          const uint32_t e = base + u * tpc;
+          eg[u] = ld_agent(gsrc + (e < ng ? e : 0u));
+          ee[u] = ld_agent(esrc + (e < ne ? e : 0u));
+        }
+        issue_fence();
+#pragma unroll
+        for (int u = 0; u < kMUnroll; ++u) {
+          const uint32_t e = base + u * tpc;
+          if (e < ng && g0 + e < (uint32_t)k) {
+            out[g0 + e] = (int32_t)(uint32_t)eg[u];
+            if (sout) sout[g0 + e] = __uint_as_float((uint32_t)(eg[u] >> 32));
+          }
+          if (nseg == 1 && e < ne) {
+            s_cidx[e0c + e] = (uint32_t)ee[u];
+            s_ckey[e0c + e] = (uint32_t)(ee[u] >> 32);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // More candidates than LDS holds: stage them kMSeg at a time from the lists.
+  auto stage = [&](int sg) {
+    __syncthreads();
+    const uint32_t base = (uint32_t)sg * kMSeg;
+    const uint32_t cnt = min((uint32_t)kMSeg, n_cand - base);
+    for (uint32_t el_ = tid; el_ < cnt; el_ += kMTPB) {
+      const uint32_t e = base + el_;
+      const int c = chunk_of(s_pe, Pr, e);
+      const uint64_t ent = ld_agent(eq_list + (r * P + c) * (long)kMChunk + (e - s_pe[c]));
+      s_cidx[el_] = (uint32_t)ent;
+      s_ckey[el_] = (uint32_t)(ent >> 32);
+    }
+    __syncthreads();
+  };
+  auto seg_count = [&](int sg) { return (int)min((uint32_t)kMSeg, n_cand - (uint32_t)sg * kMSeg); };
+
+  const int shifts[3] = {12, 4, 0};
+  const int widths[3] = {8, 8, 4};
+  uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift;
+  uint32_t need = (uint32_t)k - g1;
+  for (int lv = 0; lv < 3; ++lv) {
+    const int sh = shifts[lv];
+    const uint32_t dm = (1u << widths[lv]) - 1u;
+    uint32_t* h2 = s_h2[lv];
+    for (int sg = 0; sg < nseg; ++sg) {
+      if (nseg > 1) stage(sg);
+      const int cnt = seg_count(sg);
+      for (int e = tid; e < cnt; e += kMTPB) {
+        const uint32_t key = s_ckey[e];
+        if ((key & pmask) == prefix) atomicAdd(&h2[(key >> sh) & dm], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      if (lane == 0) {
+        s_res[0] = 0u;
+        s_res[1] = 0u;
+      }
+      find_bin_wave(h2, 1 << widths[lv], need, s_res);
+    }
+    __syncthreads();
+    prefix |= s_res[0] << sh;
+    pmask |= dm << sh;
+    need -= s_res[1];
+  }
+  const uint32_t T = prefix;      // the k-th largest key
+  const uint32_t take_eq = need;  // ties at T to take, lowest indices first
+  const uint32_t gt2 = (uint32_t)k - g1 - take_eq;
+
+  uint32_t run1 = 0, run2 = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    if (nseg > 1) stage(sg);
+    const int cnt = seg_count(sg);
+    const int cpt = (cnt + kMTPB - 1) / kMTPB;
+    const int f = tid * cpt;
+    const int lim = max(0, min(cpt, cnt - f));
+    uint32_t c1 = 0, c2 = 0;
+    for (int e = 0; e < lim; ++e) {
+      const uint32_t key = s_ckey[f + e];
+      c1 += key > T;
+      c2 += key == T;
+    }
+    uint32_t tot3;
+    const uint32_t ex3 = block_excl_scan<kMTPB>(c1 | (c2 << 16), s_wave, tot3);
+    uint32_t p1 = run1 + (ex3 & 0xFFFFu), p2 = run2 + (ex3 >> 16);
+    for (int e = 0; e < lim; ++e) {
+      const uint32_t key = s_ckey[f + e];
+      const uint32_t i = s_cidx[f + e];
+      if (key > T) put(g1 + p1++, i, key);
+      if (key == T) {
+        if (p2 < take_eq) put(g1 + gt2 + p2, i, key);
+        ++p2;
+      }
+    }
+    run1 += tot3 & 0xFFFFu;
+    run2 += tot3 >> 16;
+  }
+}
+
 template <int TPB>
 void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const int64_t* q_pos, long max_cand,
             int k, const uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
@@ -394,8 +674,14 @@ hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s) {
 
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
                        const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
-                       int32_t* idx_out, float* score_out, hipStream_t s) {
+                       const TopkLists* lists, int32_t* idx_out, float* score_out, hipStream_t s) {
   if (n_queries == 0) return hipSuccess;
+  if (hist && lists) {
+    (void)csa::launch("topk", topk_multi_kernel, dim3((unsigned)(n_queries * lists->P)), dim3(kMTPB), 0, s, m,
+                      scores, ld_sc, q_pos, max_cand, k, hist, lists->arrive, lists->counts, lists->gt, lists->eq,
+                      lists->P, lists->gtc, idx_out, score_out);
+    return hipGetLastError();
+  }
   if (max_cand <= 8192)
     launch_rows<256>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
   else

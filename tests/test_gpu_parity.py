@@ -164,6 +164,7 @@ def _oracle_rows(qI, wI, K, lens, off, m, dtype):
     ("bf16", [777, 5000], 4, 20, 64, 33),
     ("bf16", [4 * 20000, 4 * 9000, 4 * 12345, 4 * 32768], 4, 64, 128, 1000),  # indexer-built histogram
     ("bf16", [4 * 40000, 4 * 70000], 4, 64, 128, 2048),  # rows longer than the LDS row cache
+    ("bf16", [0, 100, 4 * 9000, 4 * 33000, 4 * 1500], 4, 64, 128, 1024),  # rows of 0..17 chunks
 ])
 def test_index_topk_decode(dtype, lens, m, nhI, cI, k):
     rng = synth.rng_for(sum(lens) + k)
@@ -179,6 +180,31 @@ def test_index_topk_decode(dtype, lens, m, nhI, cI, k):
         got = sc[b][idx[b] >= 0]
         assert np.allclose(got, s[sel], rtol=1e-3, atol=1e-4 * (np.abs(s).max() + 1e-30))
         assert np.all(np.isneginf(sc[b][idx[b] < 0]))
+
+
+def test_index_topk_many_long_rows_shared_sequence():
+    """520 queries at different positions of one 16384-block sequence: too many rows for the
+    per-chunk selector's lists, so each row is selected by one workgroup from the sweep's histogram.
+    The same workspace is used twice in a row."""
+    rng = synth.rng_for(520)
+    cI, nhI, m, k, nb = 32, 2, 4, 300, 16384
+    K = draw(rng, (nb, cI), 1.0, "bf16")
+    B = 520
+    pos = rng.integers(4 * 8200, 4 * nb + 1, size=B).astype(np.int64)
+    qI = draw(rng, (B, nhI, cI), 1.0 / math.sqrt(cI), "bf16")
+    wI = rng.standard_normal((B, nhI), dtype=np.float32)
+    ws = torch.zeros(api.csa_index_topk_workspace(B, nb, nhI, k), dtype=torch.uint8, device=DEV)
+    args = dict(q_seq=torch.zeros(B, dtype=torch.int32, device=DEV), q_pos=torch.tensor(pos, device=DEV),
+                kv_offset=torch.zeros(1, dtype=torch.int64, device=DEV), workspace=ws)
+    qd, wd, Kd = to_device(qI, "bf16", DEV), to_device(wI, "f32", DEV), to_device(K, "bf16", DEV)
+    K64 = f64(K, "bf16")
+    rows = [O.index_scores_row(f64(qI[b], "bf16"), wI[b].astype(np.float64), K64[:pos[b] // m], int(pos[b] // m))
+            for b in range(B)]
+    for _ in range(2):
+        idx = torch.full((B, k), 123456, dtype=torch.int32, device=DEV)
+        api.csa_index_topk(qd, wd, Kd, m, k, nb, idx, **args)
+        torch.cuda.synchronize()
+        check_topk(idx.cpu().numpy(), rows, k)
 
 
 @pytest.mark.parametrize("nhI,wset", [(1, (1.0,)), (8, (-1.0, 0.5, 2.0)), (64, (-2.0, -0.5, 0.0, 1.0, 3.0))])
