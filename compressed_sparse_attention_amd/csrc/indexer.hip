@@ -15,10 +15,10 @@
 //
 // Two kernels:
 //  * indexer_sweep -- any query/sequence layout (decode, ragged batches).
-//    A workgroup of eight waves takes one query and a chunk of 1024 of its
+//    A workgroup of four waves takes one query and a chunk of 512 of its
 //    candidates; the query's heads and weights are staged once in LDS, and
-//    every wave loads its run of 16-key groups straight from HBM into MFMA
-//    operands, issuing up to eight groups' loads before the first is used.
+//    every wave streams its run of 16-key groups straight from HBM into MFMA
+//    operands with a rolling window of groups in flight.
 //  * indexer_prefill -- one sequence, query t at position t.  A workgroup
 //    owns 16 consecutive tokens (2 per wave, q^I held in registers) and walks
 //    the causal key prefix once in 64-key tiles staged through LDS, so each
@@ -29,8 +29,8 @@
 namespace csa {
 namespace {
 
-constexpr int kSweepWaves = 8;
-constexpr int kSweepKeysPerWG = 1024;  // 128 keys (eight 16-key groups) per wave
+constexpr int kSweepWaves = 4;
+constexpr int kSweepKeysPerWG = 512;  // 128 keys (eight 16-key groups) per wave
 
 template <typename T, int KK, int NHT>
 __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
@@ -54,15 +54,23 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
 
-  // Stage the query's heads (zero rows for padded heads) and head weights in
-  // LDS once per workgroup; every wave then reads its fragments from there.
-  for (int v = tid; v < 16 * NHT * QCH; v += NTH) {
+  // The query's heads and head weights are fetched first, by every wave,
+  // before any wave issues key loads (a barrier orders the issue): a CU
+  // serves its waves' requests roughly in issue order, so a query load queued
+  // behind other waves' keys would hold the LDS staging (and with it every
+  // MFMA) until most of the chunk had arrived.  Staging the query in LDS
+  // (zero rows for padded heads; every wave then reads its fragments from
+  // there) then waits only for these loads.
+  constexpr int QPIECES = 16 * NHT * QCH;
+  constexpr int QV = (QPIECES + NTH - 1) / NTH;
+  u32x4 qv[QV];
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    const int v = tid + i * NTH;
     const int head = v / QCH, pc = (v - head * QCH) * VEC;
-    u32x4 val = load16_clamped(qI + ((long)r * nhI + head) * CI + pc, head < nhI, qI);
-    if (head >= nhI) val = u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(&s_q[head * QPITCH + pc]) = val;
+    qv[i] = load16_clamped(qI + ((long)r * nhI + head) * CI + pc, v < QPIECES && head < nhI, qI);
   }
-  for (int h = tid; h < 16 * NHT; h += NTH) s_w[h] = h < nhI ? wI[(long)r * nhI + h] : 0.f;
+  const float wraw = wI[(long)r * nhI + (tid < nhI ? tid : 0)];
   const long pos = q_pos ? q_pos[r] : (long)r;
   const int seq = q_seq ? q_seq[r] : 0;
   long ncand = pos > 0 ? pos / m : 0;
@@ -71,31 +79,42 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
   if (chunk0 >= ncand) return;
   const long off = kv_off ? kv_off[seq] : 0;
   const long chunk_end = min(chunk0 + (long)kSweepKeysPerWG, ncand);
-  if (hist)
-    for (int b = tid; b < NB; b += NTH) s_hist[b] = 0u;
+  __syncthreads();  // every wave's query loads are issued before any key load
 
-  // Each wave owns GPW consecutive 16-key groups of the chunk and issues the
-  // loads of G groups at once (G x KK fragments staged in registers), so a
-  // wave keeps up to 32 KiB of keys in flight.  Lanes past the end of the
-  // chunk read the chunk's first key instead; their scores are never stored.
+  // Each wave owns GPW consecutive 16-key groups of the chunk and keeps D of
+  // them in flight: group gi is computed once its loads have landed and its
+  // register slot is refilled with group gi + D right away.  A wave whose
+  // loads all went out at once would sit in the issue queue (the memory
+  // system back-pressures it) until most of its data had arrived, and only
+  // then start its MFMAs; the rolling window lets a wave compute while its
+  // later groups are still streaming in.  Lanes past the end of the chunk
+  // read the chunk's first key instead; their scores are never stored.
   constexpr int GPW = kSweepKeysPerWG / (16 * kSweepWaves);
   constexpr int VPF = sizeof(T) == 2 ? 4 : 8;  // VGPRs per fragment
-  constexpr int GB = 128 / (KK * VPF);
-  constexpr int G = GB < 1 ? 1 : (GB > GPW ? GPW : GB);
+  constexpr int DB = 32 / (KK * VPF);  // 32 VGPRs of keys in flight per wave
+  constexpr int D = DB < 1 ? 1 : (DB > GPW ? GPW : DB);
   const T* Kb = K + off * CI + g * 8 * KK;
   const long wbase = chunk0 + (long)wave * GPW * 16;
-  Frag<T> kb[G][KK];
-  auto issue = [&](int g0) {
+  Frag<T> kb[D][KK];
+  auto issue = [&](int gi, int slot) {
+    const long s = wbase + gi * 16 + c16;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      const long s = wbase + (g0 + gi) * 16 + c16;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kb[gi][kk].load_clamped(Kb + s * CI + 8 * kk, s < chunk_end, Kb + 8 * kk);
-    }
-    issue_fence();
+    for (int kk = 0; kk < KK; ++kk) kb[slot][kk].load_clamped(Kb + s * CI + 8 * kk, s < chunk_end, Kb + 8 * kk);
   };
-  issue(0);  // the first batch is in flight while the query is staged
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, d);  // in flight while the query is staged
+  issue_fence();
 
+#pragma unroll
+  for (int i = 0; i < QV; ++i) {
+    const int v = tid + i * NTH;
+    const int head = v / QCH, pc = (v - head * QCH) * VEC;
+    if (v < QPIECES)
+      *reinterpret_cast<u32x4*>(&s_q[head * QPITCH + pc]) = head < nhI ? qv[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < 16 * NHT) s_w[tid] = tid < nhI ? wraw : 0.f;
+  if (hist)
+    for (int b = tid; b < NB; b += NTH) s_hist[b] = 0u;
   __syncthreads();
   Frag<T> qa[NHT][KK];
   float wv[NHT][4];
@@ -107,28 +126,27 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
     for (int rr = 0; rr < 4; ++rr) wv[mt][rr] = s_w[16 * mt + 4 * g + rr];
   }
 
-  for (int g0 = 0; g0 < GPW; g0 += G) {
-    if (g0 > 0) {
-      if (wbase + g0 * 16 >= chunk_end) break;
-      issue(g0);
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int slot = gi % D;
+    float part = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NHT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) mma(acc, qa[mt][kk], kb[slot][kk]);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[mt][rr], relu(acc[rr]), part);
     }
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      float part = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < NHT; ++mt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) mma(acc, qa[mt][kk], kb[gi][kk]);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[mt][rr], relu(acc[rr]), part);
-      }
-      part = wave_sum_xor_16_32(part);
-      const long s = wbase + (g0 + gi) * 16 + c16;
-      if (g == 0 && s < chunk_end) {
-        scores[(long)r * ld_sc + s] = part;
-        if (hist) atomicAdd(&s_hist[score_key(part) >> (32 - kTopkL1Bits)], 1u);
-      }
+    if (gi + D < GPW) {
+      issue(gi + D, slot);
+      issue_fence();
+    }
+    part = wave_sum_xor_16_32(part);
+    const long s = wbase + gi * 16 + c16;
+    if (g == 0 && s < chunk_end) {
+      scores[(long)r * ld_sc + s] = part;
+      if (hist) atomicAdd(&s_hist[score_key(part) >> (32 - kTopkL1Bits)], 1u);
     }
   }
   if (hist) {
