@@ -156,16 +156,23 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 // Value of lane 63 (a uniform result).
 __device__ __forceinline__ uint32_t wave_last(uint32_t x) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 63); }
 
+// Sum (max) over the four lanes l, l^16, l^32, l^48.  v_permlane16_swap /
+// v_permlane32_swap exchange 16-lane rows (32-lane halves) between two
+// registers; with both operands equal, the two results of lane l hold x[l]
+// and x[l ^ 16] (x[l ^ 32]) in some order, so their sum (max) is the pair's.
+// Both lanes of a pair compute the same value (addition is commutative).
 __device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float wave_max_xor_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 }  // namespace csa

@@ -20,9 +20,11 @@
 //    every wave streams its run of 16-key groups straight from HBM into MFMA
 //    operands with a rolling window of groups in flight.
 //  * indexer_prefill -- one sequence, query t at position t.  A workgroup
-//    owns 16 consecutive tokens (2 per wave, q^I held in registers) and walks
-//    the causal key prefix once in 64-key tiles staged through LDS, so each
-//    key tile is fetched once per 16 tokens.  Heaviest token blocks first.
+//    owns 16 consecutive tokens (one per wave, its q^I held in registers; at
+//    most 128 VGPRs, so four waves share each SIMD; 8 tokens when q^I is too
+//    large for that) and walks the causal key prefix once in 64-key tiles
+//    staged through LDS, so each key tile is fetched once per 16 tokens.
+//    Heaviest token blocks first.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -160,15 +162,21 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// prefill: tokens t0 .. t0+15 per workgroup (8 waves x 2 tokens)
+// prefill: tokens t0 .. t0+W-1 per workgroup (W waves x 1 token)
 // ---------------------------------------------------------------------------
-constexpr int kPfWaves = 8;
-constexpr int kPfTokPerWave = 2;
-constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
+constexpr int kPfTokPerWave = 1;
 constexpr int kPfTile = 64;  // keys per LDS tile
 
+// Waves (= tokens) per workgroup, from the VGPRs a token's q^I fragments take:
+// 16 waves (128-VGPR budget each) up to 64, 8 waves (256) up to 96, else 4.
 template <typename T, int KK, int NHT>
-__global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, int m,
+constexpr int pf_waves() {
+  constexpr int v = NHT * KK * (sizeof(T) == 2 ? 4 : 8);
+  return v <= 64 ? 16 : (v <= 96 ? 8 : 4);
+}
+
+template <typename T, int KK, int NHT>
+__global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill_kernel(int n, int nhI, int m,
                                                               const T* __restrict__ qI,
                                                               const float* __restrict__ wI,
                                                               const T* __restrict__ K,
@@ -176,6 +184,8 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
                                                               long max_cand,
                                                               float* __restrict__ scores,
                                                               long ld_sc) {
+  constexpr int kPfWaves = pf_waves<T, KK, NHT>();
+  constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
   constexpr int CI = 32 * KK;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PITCH = CI + VEC;  // padded LDS row (elements)
@@ -221,12 +231,12 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
 
   if (kv_off) K += kv_off[0] * CI;
   const int ntiles = (int)((kend + kPfTile - 1) / kPfTile);
-  constexpr int LOADS = (TILE_VECS + 511) / 512;
+  constexpr int LOADS = (TILE_VECS + 64 * kPfWaves - 1) / (64 * kPfWaves);
   u32x4 stage[LOADS];
   auto fetch = [&](int tile) {
 #pragma unroll
     for (int p = 0; p < LOADS; ++p) {
-      const int v = tid + p * 512;
+      const int v = tid + p * 64 * kPfWaves;
       const long key = (long)tile * kPfTile + v / CHUNKS;
       stage[p] = load16_clamped(K + key * CI + (v % CHUNKS) * VEC, v < TILE_VECS && key < kend, K);
     }
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(int n, int nhI, in
   auto stash = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < LOADS; ++p) {
-      const int v = tid + p * 512;
+      const int v = tid + p * 64 * kPfWaves;
       if (v < TILE_VECS)
         *reinterpret_cast<u32x4*>(&Ks[buf][(v / CHUNKS) * PITCH + (v % CHUNKS) * VEC]) = stage[p];
     }
@@ -278,8 +288,9 @@ hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const v
                const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off, long max_cand,
                float* scores, long ld_sc, uint32_t* hist, hipStream_t s) {
   if (q_seq == nullptr && q_pos == nullptr) {
-    const int nblocks = (int)((nq + kPfTokens - 1) / kPfTokens);
-    return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3(nblocks), dim3(512), 0, s,
+    constexpr int waves = pf_waves<T, KK, NHT>();
+    const int nblocks = (int)((nq + waves * kPfTokPerWave - 1) / (waves * kPfTokPerWave));
+    return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3(nblocks), dim3(64 * waves), 0, s,
                   (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc);
   } else {
     const unsigned chunks = (unsigned)((max_cand + kSweepKeysPerWG - 1) / kSweepKeysPerWG);

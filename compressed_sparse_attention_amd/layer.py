@@ -86,7 +86,6 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
     api.csa_project(H, W["W_w_t"], buf.wI)  # eq 7
     cQ = Y[:, 4 * c + 4 * cI:]
     api.csa_project(cQ, W["W_UQI_t"], buf.qI)  # eq 6
-    api.csa_project(cQ, W["W_UQ_t"], buf.q)  # eq 10
     api.csa_compress(Y[:, 0:c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:4 * c], W["B_a"], W["B_b"], m,
                      buf.Ccomp)  # eqs 3-4
     o = 4 * c
@@ -94,6 +93,9 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
                      Y[:, o + 3 * cI:o + 4 * cI], W["B_aI"], W["B_bI"], m, buf.KIcomp)
     api.csa_index_topk(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, n // m, buf.idx,
                        workspace=buf.ws_index)  # eqs 8-9
+    # the largest projection runs after the indexer, whose MFMA rate suffers
+    # when it follows this GEMM directly
+    api.csa_project(cQ, W["W_UQ_t"], buf.q)  # eq 10
     sc = 1.0 / math.sqrt(c) if scale is None else scale
     api.csa_sparse_mqa(buf.q.view(n, nh, c), buf.Ccomp, buf.idx, sc, buf.o, buf.lse,
                        workspace=buf.ws_mqa)  # eq 11
