@@ -22,7 +22,7 @@
 //  * indexer_prefill -- one sequence, query t at position t.  A workgroup
 //    owns 16 consecutive tokens (one per wave, its q^I held in registers; at
 //    most 128 VGPRs, so four waves share each SIMD; 8 tokens when q^I is too
-//    large for that) and walks the causal key prefix once in 64-key tiles
+//    large for that) and walks the causal key prefix once in key tiles
 //    staged through LDS, so each key tile is fetched once per 16 tokens.
 //    Heaviest token blocks first.
 #include "common.hpp"
@@ -165,7 +165,6 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
 // prefill: tokens t0 .. t0+W-1 per workgroup (W waves x 1 token)
 // ---------------------------------------------------------------------------
 constexpr int kPfTokPerWave = 1;
-constexpr int kPfTile = 64;  // keys per LDS tile
 
 // Waves (= tokens) per workgroup, from the VGPRs a token's q^I fragments take:
 // 16 waves (128-VGPR budget each) up to 64, 8 waves (256) up to 96, else 4.
@@ -186,6 +185,9 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
                                                               long ld_sc) {
   constexpr int kPfWaves = pf_waves<T, KK, NHT>();
   constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
+  // keys per LDS tile: 128 (measured faster than 64) while two tiles of key
+  // rows stay well inside LDS, else 64
+  constexpr int kPfTile = 32 * KK * sizeof(T) <= 512 ? 128 : 64;
   constexpr int CI = 32 * KK;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PITCH = CI + VEC;  // padded LDS row (elements)
