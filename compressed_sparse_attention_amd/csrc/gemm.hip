@@ -4,16 +4,29 @@
 // row-vector projections of this form.  Both operands are K-contiguous, so
 // each 16x16x32 MFMA operand is one 16-byte LDS read per lane.
 //
-// Tiling: 128x128 output tile per 256-thread workgroup (4 waves in 2x2, each
-// 64x64 = 4x4 MFMA tiles), K staged through LDS in 128-byte slabs, double
-// buffered: the next slab is fetched into registers while the current one
-// feeds the MFMAs.  Rows are padded by 16 bytes so the 16 lanes reading one
-// column of fragments hit distinct LDS banks.
+// Two kernels: gemm256 (below) for bf16 operands with M, N >= 256, and the
+// general gemm_nt (fp32 too, any shape): 128x128 output tile per 256-thread
+// workgroup (4 waves in 2x2, each 64x64 = 4x4 MFMA tiles), K staged through
+// LDS in 128-byte slabs, double buffered: the next slab is fetched into
+// registers while the current one feeds the MFMAs.  LDS rows are padded by
+// 16 bytes so the 16 lanes reading one column of fragments hit distinct banks.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace csa {
 namespace {
+
+// Four consecutive outputs (16-byte aligned for fp32, 8-byte for bf16).
+template <typename T> __device__ __forceinline__ void store4(T* p, const float* v);
+template <> __device__ __forceinline__ void store4<float>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
+  uint2 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = u;
+}
 
 constexpr int kBM = 128;
 constexpr int kBN = 128;
@@ -116,10 +129,138 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large bf16 projections: 256x256 output tile per 512-thread workgroup.
+//
+// Eight waves (two per SIMD, so one can issue MFMAs while the other waits on
+// LDS or on its slab loads), each owning a 128x64 strip of 8x4 MFMA tiles:
+// a 32-deep k-step reads 12 fragments from LDS for 32 MFMAs, against 8 for
+// 16 in the 128x128 kernel above (whose 64x64 wave tiles keep LDS at its read
+// bandwidth).  K is staged in 64-element slabs, double buffered through
+// registers.  Workgroups are dealt to the eight XCDs round-robin; each XCD
+// gets a contiguous run of the tile sequence, walked in groups of kG2Group
+// tile rows, so the workgroups resident on one XCD share operand strips in
+// its L2.  Measured alternatives: four waves of 128x128 (one per SIMD, with
+// the next k-step's fragments prefetched) and 32x32x16 MFMAs were slower.
+// ---------------------------------------------------------------------------
+constexpr int kG2M = 256;
+constexpr int kG2N = 256;
+constexpr int kG2K = 64;               // elements per slab row (128 bytes)
+constexpr int kG2Pitch = kG2K + 8;     // padded LDS row (elements)
+constexpr int kG2Group = 4;            // tile rows per group in the walk order
+
+template <typename TO>
+__global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const bf16_t* __restrict__ X, long ldx,
+                                                        const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y,
+                                                        long ldy, int tiles_m, int tiles_n, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kG2M * kG2Pitch];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kG2N * kG2Pitch];
+
+  const int seq = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (seq >= tiles_m * tiles_n) return;
+  const int in_group = kG2Group * tiles_n;
+  const int first_m = (seq / in_group) * kG2Group;
+  const int gsize = min(kG2Group, tiles_m - first_m);
+  const int r = seq % in_group;
+  const long m0 = (long)(first_m + r % gsize) * kG2M;
+  const long n0 = (long)(r / gsize) * kG2N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
+  const int g = lane >> 4, c16 = lane & 15;
+  const int lrow = tid >> 3;          // 0..63
+  const int lcol = (tid & 7) * 8;
+  constexpr int PASSES = kG2M / 64;   // 4 rows per thread per operand
+
+  u32x4 ra[PASSES], rb[PASSES];
+  const int KT = (K + kG2K - 1) / kG2K;
+  auto fetch = [&](int kt) {
+    const long k = (long)kt * kG2K + lcol;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const long row = m0 + lrow + 64 * p;
+      const long col = n0 + lrow + 64 * p;
+      ra[p] = load16_clamped(X + row * ldx + k, row < M && k < K, X);
+      rb[p] = load16_clamped(W + col * ldw + k, col < N && k < K, W);
+    }
+    if (kt == KT - 1 && (K % kG2K) != 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p)
+        if (k >= K) rb[p] = u32x4{0u, 0u, 0u, 0u};
+    }
+    issue_fence();
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 64 * p) * kG2Pitch + lcol]) = ra[p];
+      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 64 * p) * kG2Pitch + lcol]) = rb[p];
+    }
+  };
+
+  // acc[j][i] = (W tile j) x (X tile i)^T: lane (g, c16) holds output row
+  // m = ... + 16 i + c16 and the four consecutive columns n = ... + 16 j + 4 g
+  // .. +3, so the epilogue writes 4 adjacent outputs per store.
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) fetch(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kG2K / 32; ++ks) {
+      Frag<bf16_t> fa[8], fb[4];
+      const bf16_t* Ab = &As[cur][(wm * 128 + c16) * kG2Pitch + 8 * g + 32 * ks];
+      const bf16_t* Bb = &Bs[cur][(wn * 64 + c16) * kG2Pitch + 8 * g + 32 * ks];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j].load(Bb + j * 16 * kG2Pitch);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i].load(Ab + i * 16 * kG2Pitch);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mma(acc[j][i], fb[j], fa[i]);
+    }
+    if (kt + 1 < KT) stash(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const long row = m0 + wm * 128 + i * 16 + c16;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long col = n0 + wn * 64 + j * 16 + 4 * g;
+      if (col < N) {
+        float v[4] = {acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
+        store4<TO>(Y + row * ldy + col, v);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s) {
+  if (in_dt == CSA_BF16 && M >= kG2M && N >= kG2N && N % 4 == 0) {
+    const int tm = (int)((M + kG2M - 1) / kG2M), tn = (int)((N + kG2N - 1) / kG2N);
+    const int per_xcd = (tm * tn + 7) / 8;
+    const dim3 grid2((unsigned)(8 * per_xcd));
+    if (out_dt == CSA_BF16)
+      return launch("gemm", gemm256_kernel<bf16_t>, grid2, dim3(512), 0, s, (int)M, (int)N, (int)K,
+                    (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy, tm, tn, per_xcd);
+    return launch("gemm", gemm256_kernel<float>, grid2, dim3(512), 0, s, (int)M, (int)N, (int)K,
+                  (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy, tm, tn, per_xcd);
+  }
   dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
   if (in_dt == CSA_F32)
     return launch("gemm", gemm_nt_kernel<float, float>, grid, dim3(256), 0, s, (int)M, (int)N, (int)K,

@@ -38,6 +38,8 @@ def f64(x, dtype):
     ("bf16", "bf16", 300, 200, 136),
     ("bf16", "f32", 130, 64, 4096),
     ("bf16", "bf16", 1000, 1536, 4096),
+    ("bf16", "bf16", 520, 296, 200),  # large-tile kernel: ragged M and N edges and a K tail
+    ("bf16", "f32", 260, 264, 1000),
 ])
 def test_project(din, dout, M, N, K):
     rng = synth.rng_for(M * 7 + N)
