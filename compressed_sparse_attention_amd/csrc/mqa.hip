@@ -60,8 +60,15 @@ __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, 
 #pragma unroll
       for (int q = 0; q < B; ++q) {
         const int rl = (q0 + q) * RPI + sub;
-        const int id = __shfl(myid, rl < ROWS ? rl : 0);
-        buf[q] = load16_clamped(Cb + (long)id * CD + pc, rl < ROWS && id >= 0, fallback);
+        if constexpr (RPI == 1) {
+          // one row per instruction: its id is wave-uniform (a scalar base address)
+          const int id = __builtin_amdgcn_readlane(myid, q0 + q);
+          const T* rowp = id >= 0 ? Cb + (long)id * CD : reinterpret_cast<const T*>(fallback);
+          buf[q] = *reinterpret_cast<const u32x4*>(rowp + pc);
+        } else {
+          const int id = __shfl(myid, rl < ROWS ? rl : 0);
+          buf[q] = load16_clamped(Cb + (long)id * CD + pc, rl < ROWS && id >= 0, fallback);
+        }
       }
       issue_fence();
 #pragma unroll
@@ -124,10 +131,7 @@ template <> __device__ __forceinline__ void store4<float>(float* p, const float*
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
-  uint2 u;
-  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  *reinterpret_cast<uint2*>(p) = u;
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // Selection slots per chunk of the 64-head-group kernel: 64 while a gathered
@@ -388,8 +392,14 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
     const int sub = lane / LPR, pc = (lane % LPR) * 8;
 #pragma unroll
     for (int qd = 0; qd < NLD; ++qd) {
-      const int id = __shfl(ids, qd * RPI + sub);
-      stg[qd] = load16_clamped(Cb + (long)id * CD + pc, id >= 0, q);
+      if constexpr (RPI == 1) {  // one row per instruction: a wave-uniform (scalar) row address
+        const int id = __builtin_amdgcn_readlane(ids, qd);
+        const bf16_t* rowp = id >= 0 ? Cb + (long)id * CD : q;
+        stg[qd] = *reinterpret_cast<const u32x4*>(rowp + pc);
+      } else {
+        const int id = __shfl(ids, qd * RPI + sub);
+        stg[qd] = load16_clamped(Cb + (long)id * CD + pc, id >= 0, q);
+      }
     }
     issue_fence();
   };
@@ -449,21 +459,29 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
       if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
     }
     __syncthreads();
+    // Lazy rescaling: the reference maximum m_run moves only when a chunk's
+    // maximum exceeds it by more than 2^8, so the exponentials stay below 256
+    // (exact in the fp32 sums and within bf16's range) and the O^T
+    // accumulators are rescaled in the rare chunks where it moves.
     float alpha = 1.f;
     if (qlive) {
       const int hl = 16 * ht + c16;
-      const float m_new = fmaxf(m_run, fmaxf(s_red[0][0][hl], s_red[0][1][hl]));
+      const float cmax = fmaxf(s_red[0][0][hl], s_red[0][1][hl]);
+      const float m_new = (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
       const bool none = (m_new == -INFINITY);
       alpha = none ? 1.f : exp2_fast(m_run - m_new);
       float ps = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        float p[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float p = none ? 0.f : exp2_fast(x[t][rr] - m_new);
-          ps += p;
-          Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g + rr] = f2bf(p);
+          p[rr] = none ? 0.f : exp2_fast(x[t][rr] - m_new);
+          ps += p[rr];
         }
+        *reinterpret_cast<uint2*>(&Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g]) =
+            make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      }
       ps = wave_sum_xor_16_32(ps);
       if (g == 0) {
         s_red[1][kh][hl] = ps;
@@ -481,8 +499,10 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
     for (int nt = 0; nt < 4; ++nt) {
       if (nt < NT) {
         const float a = s_alpha[16 * nt + c16];
+        if (__builtin_amdgcn_read_exec() & __ballot(a != 1.f)) {  // some head of this tile moved its maximum
 #pragma unroll
-        for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+          for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+        }
       }
     }
 #pragma unroll
@@ -733,41 +753,40 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
   const long r = rh / nh;
   const int h = (int)(rh - r * nh);
   const long b0 = r * nsplit * (long)nh + h;  // split j at b0 + j*nh
+  // Online merge, U splits per batch: every split's (m, l) and partial output
+  // of a batch are loaded together (one memory round trip per batch).
   float M = -INFINITY;
-  for (int j0 = 0; j0 < nsplit; j0 += U) {
-    float mj[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mj[u] = j0 + u < nsplit ? part_ml[(b0 + (long)(j0 + u) * nh) * 2] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mj[u]);
-  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (M != -INFINITY) {
-    for (int j0 = 0; j0 < nsplit; j0 += U) {
-      float2 ml[U];
-      float4 po[U];
+  for (int j0 = 0; j0 < nsplit; j0 += U) {
+    float2 ml[U];
+    float4 po[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const long b = b0 + (long)(j0 + u) * nh;
-        if (j0 + u < nsplit) {
-          ml[u] = *reinterpret_cast<const float2*>(part_ml + b * 2);
-          po[u] = *reinterpret_cast<const float4*>(part_o + b * c + d4);
-        } else {
-          ml[u] = make_float2(-INFINITY, 0.f);
-          po[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wgt = ml[u].x == -INFINITY ? 0.f : exp2_fast(ml[u].x - M);
-        L = fmaf(ml[u].y, wgt, L);
-        acc[0] = fmaf(wgt, po[u].x, acc[0]);
-        acc[1] = fmaf(wgt, po[u].y, acc[1]);
-        acc[2] = fmaf(wgt, po[u].z, acc[2]);
-        acc[3] = fmaf(wgt, po[u].w, acc[3]);
-      }
+    for (int u = 0; u < U; ++u) {
+      const long b = b0 + (long)(j0 + u < nsplit ? j0 + u : 0) * nh;  // always in bounds
+      ml[u] = *reinterpret_cast<const float2*>(part_ml + b * 2);
+      po[u] = *reinterpret_cast<const float4*>(part_o + b * c + d4);
     }
+    issue_fence();
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u < nsplit) mb = fmaxf(mb, ml[u].x);
+    if (mb == -INFINITY) continue;  // nothing valid yet
+    const float a = M == -INFINITY ? 0.f : exp2_fast(M - mb);
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wgt = (j0 + u >= nsplit || ml[u].x == -INFINITY) ? 0.f : exp2_fast(ml[u].x - mb);
+      L = fmaf(ml[u].y, wgt, L);
+      acc[0] = fmaf(wgt, po[u].x, acc[0]);
+      acc[1] = fmaf(wgt, po[u].y, acc[1]);
+      acc[2] = fmaf(wgt, po[u].z, acc[2]);
+      acc[3] = fmaf(wgt, po[u].w, acc[3]);
+    }
+    M = mb;
   }
   const float inv = (M == -INFINITY) ? 0.f : 1.f / L;
   float v[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
