@@ -46,7 +46,9 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
   constexpr int VEC = 16 / sizeof(T);
   constexpr int QPITCH = CI + VEC;  // padded LDS row: the 16 lanes reading one k-slice hit distinct banks
   constexpr int QCH = CI / VEC;     // 16-byte pieces per query row
-  __shared__ uint32_t s_hist[NB];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[NB];
+  __shared__ uint32_t s_touched[kSweepKeysPerWG];  // bins this chunk hit, in first-touch order
+  __shared__ uint32_t s_ntouched;
   __shared__ __attribute__((aligned(16))) T s_q[16 * NHT * QPITCH];
   __shared__ float s_w[16 * NHT];
 
@@ -115,8 +117,10 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
       *reinterpret_cast<u32x4*>(&s_q[head * QPITCH + pc]) = head < nhI ? qv[i] : u32x4{0u, 0u, 0u, 0u};
   }
   if (tid < 16 * NHT) s_w[tid] = tid < nhI ? wraw : 0.f;
-  if (hist)
-    for (int b = tid; b < NB; b += NTH) s_hist[b] = 0u;
+  if (hist) {
+    for (int b = tid; b < NB / 4; b += NTH) reinterpret_cast<u32x4*>(s_hist)[b] = u32x4{0u, 0u, 0u, 0u};
+    if (tid == 0) s_ntouched = 0u;
+  }
   __syncthreads();
   Frag<T> qa[NHT][KK];
   float wv[NHT][4];
@@ -148,15 +152,19 @@ __global__ __launch_bounds__(64 * kSweepWaves) void indexer_sweep_kernel(
     const long s = wbase + gi * 16 + c16;
     if (g == 0 && s < chunk_end) {
       scores[(long)r * ld_sc + s] = part;
-      if (hist) atomicAdd(&s_hist[score_key(part) >> (32 - kTopkL1Bits)], 1u);
+      if (hist) {
+        const uint32_t b = score_key(part) >> (32 - kTopkL1Bits);
+        if (atomicAdd(&s_hist[b], 1u) == 0u) s_touched[atomicAdd(&s_ntouched, 1u)] = b;
+      }
     }
   }
-  if (hist) {
+  if (hist) {  // add the touched bins (at most one per key) into the row's histogram
     __syncthreads();
     uint32_t* hrow = hist + (long)r * NB;
-    for (int b = tid; b < NB; b += NTH) {
-      const uint32_t v = s_hist[b];
-      if (v) atomicAdd(&hrow[b], v);
+    const uint32_t nt = s_ntouched;
+    for (uint32_t e = tid; e < nt; e += NTH) {
+      const uint32_t b = s_touched[e];
+      atomicAdd(&hrow[b], s_hist[b]);
     }
   }
 }
