@@ -40,6 +40,8 @@ _SIGS = {
                                    _i64, _vp]),
     "csa_compress": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                     _i64, _vp]),
+    "csa_compress_append": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _i64, _vp]),
     "csa_index_topk_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_index_topk": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -153,6 +155,29 @@ def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, Ccomp: torch.Tensor) -> torch.T
     _check(lib().csa_compress(_dt(Ca), n, m, c, _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _ptr(Ba),
                               _ptr(Bb), _ptr(Ccomp), _rowmajor(Ccomp, "Ccomp"), _stream(Ca.device)),
            "csa_compress")
+    return Ccomp
+
+
+def csa_compress_append(new_rows, ring, Ba, Bb, m: int, t_new, kv_offset, Ccomp) -> torch.Tensor:
+    """Eqs 3-4 for one new token per sequence.  new_rows [B, >= 4c] (C^a|C^b|Z^a|Z^b), ring [B, 2m, 4c],
+    Ba/Bb [m, c], t_new/kv_offset [B] int64 (device), Ccomp [rows, c] (row kv_offset[b] + t_new[b] // m is
+    written when t_new[b] completes a block)."""
+    B = new_rows.shape[0]
+    c = Ccomp.shape[1]
+    _contig(ring, "ring")
+    if tuple(ring.shape) != (B, 2 * m, 4 * c) or ring.dtype != Ccomp.dtype or new_rows.dtype != Ccomp.dtype:
+        raise CSAError("csa_compress_append: ring must be [B, 2m, 4c] of the cache dtype")
+    for t, nm in ((Ba, "Ba"), (Bb, "Bb")):
+        _contig(t, nm)
+        if tuple(t.shape) != (m, c):
+            raise CSAError(f"csa_compress_append: {nm} must be [m, c]")
+    for t, nm in ((t_new, "t_new"), (kv_offset, "kv_offset")):
+        if t.dtype != torch.int64 or tuple(t.shape) != (B,):
+            raise CSAError(f"csa_compress_append: {nm} must be int64 [B]")
+    _check(lib().csa_compress_append(_dt(Ccomp), B, m, c, _ptr(new_rows), _rowmajor(new_rows, "new_rows"),
+                                     _ptr(ring), _ptr(Ba), _ptr(Bb), _ptr(t_new), _ptr(kv_offset), _ptr(Ccomp),
+                                     _rowmajor(Ccomp, "Ccomp"), _stream(Ccomp.device)),
+           "csa_compress_append")
     return Ccomp
 
 

@@ -238,6 +238,29 @@ csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const voi
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress launch");
 }
 
+csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, const void* new_rows,
+                               int64_t ld_new, void* ring, const void* Ba, const void* Bb,
+                               const int64_t* t_new, const int64_t* kv_offset, void* Ccomp,
+                               int64_t ld_out, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress_append: unknown dtype");
+  CSA_REQUIRE(B >= 0 && B <= 0x7FFFFFFF, "csa_compress_append: bad B");
+  CSA_REQUIRE(m >= 1 && m <= 64, "csa_compress_append: m must be in [1, 64] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_append: c must be a positive multiple of 4 (got %d)", c);
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(new_rows && ring && Ba && Bb && t_new && kv_offset && Ccomp, "csa_compress_append: null pointer");
+  CSA_REQUIRE(aligned16(new_rows) && aligned16(ring) && aligned16(Ba) && aligned16(Bb) && aligned16(Ccomp),
+              "csa_compress_append: pointers must be 16-byte aligned");
+  const int v = vec_elems(dt);
+  CSA_REQUIRE(ld_new >= 4L * c && ld_out >= c, "csa_compress_append: leading dimension too small");
+  CSA_REQUIRE(ld_new % v == 0 && ld_out % v == 0,
+              "csa_compress_append: leading dimensions must keep rows 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_compress_append(dt, B, m, c, new_rows, ld_new, ring, Ba, Bb, t_new, kv_offset, Ccomp,
+                                             ld_out, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_append launch");
+}
+
 csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t k,
                                     size_t* bytes) {
   CSA_REQUIRE(bytes, "csa_index_topk_workspace: null bytes");

@@ -113,6 +113,71 @@ __global__ __launch_bounds__(256) void compress_kernel(long nblk, int m, int c,
   Vec<T, V>::store(out + i * ldo + ch, res);
 }
 
+// ---------------------------------------------------------------------------
+// Decode-time append: one new token per sequence.  Workgroup b stores the new
+// projected row [C^a | C^b | Z^a | Z^b] of sequence b in its 2m-row ring (slot
+// t mod 2m) and, when the token completes block i = floor(t/m), compresses
+// block i from the ring (a-terms: block i's rows, b-terms: block i-1's rows,
+// absent for i = 0) into row kv_offset[b] + i of the compressed cache; each
+// thread owns V channels of it.
+// ---------------------------------------------------------------------------
+template <typename T, int V>
+__global__ __launch_bounds__(256) void compress_append_kernel(int m, int c, const T* __restrict__ rows, long ld_new,
+                                                              T* __restrict__ ring, const T* __restrict__ Ba,
+                                                              const T* __restrict__ Bb,
+                                                              const int64_t* __restrict__ t_new,
+                                                              const int64_t* __restrict__ kv_off,
+                                                              T* __restrict__ out, long ldo) {
+  const long b = blockIdx.x;
+  const long t = t_new[b];
+  const int W4 = 4 * c;  // ring row: C^a | C^b | Z^a | Z^b
+  T* rb = ring + b * (long)(2 * m) * W4;
+  const T* src = rows + b * ld_new;
+  T* dst = rb + (t % (2 * m)) * W4;
+  for (int e = threadIdx.x * V; e < W4; e += blockDim.x * V) {
+    float v[V];
+    Vec<T, V>::load(src + e, v);
+    Vec<T, V>::store(dst + e, v);
+  }
+  if (t % m != m - 1) return;  // the token does not complete a block (uniform)
+  __syncthreads();             // the new row is in the ring for every thread
+  const long i = t / m;
+  for (int ch = threadIdx.x * V; ch < c; ch += blockDim.x * V) {
+    float mx[V], den[V], acc[V];
+    auto absorb = [&](const T* rrow, const T* brow, int zoff, int coff, bool first) {
+      float z[V], v[V], bb[V];
+      Vec<T, V>::load(rrow + zoff + ch, z);
+      Vec<T, V>::load(rrow + coff + ch, v);
+      Vec<T, V>::load(brow, bb);
+#pragma unroll
+      for (int q = 0; q < V; ++q) {
+        const float l = (z[q] + bb[q]) * kLog2e;
+        if (first) {
+          mx[q] = l;
+          den[q] = 1.f;
+          acc[q] = v[q];
+        } else {
+          const float d = l - mx[q];
+          const float e = exp2_fast(-fabsf(d));
+          const bool up = d > 0.f;
+          acc[q] = up ? fmaf(acc[q], e, v[q]) : fmaf(e, v[q], acc[q]);
+          den[q] = up ? fmaf(den[q], e, 1.f) : den[q] + e;
+          mx[q] = up ? l : mx[q];
+        }
+      }
+    };
+    for (int r = 0; r < m; ++r)  // block i: C^a (offset 0), Z^a (offset 2c)
+      absorb(rb + ((i * m + r) % (2 * m)) * W4, Ba + (long)r * c + ch, 2 * c, 0, r == 0);
+    if (i > 0)
+      for (int r = 0; r < m; ++r)  // block i-1: C^b (offset c), Z^b (offset 3c)
+        absorb(rb + (((i - 1) * m + r) % (2 * m)) * W4, Bb + (long)r * c + ch, 3 * c, c, false);
+    float res[V];
+#pragma unroll
+    for (int q = 0; q < V; ++q) res[q] = acc[q] / den[q];
+    Vec<T, V>::store(out + (kv_off[b] + i) * ldo + ch, res);
+  }
+}
+
 template <typename T, int V>
 hipError_t run(long nblk, int m, int c, const void* Ca, const void* Cb, const void* Za,
                const void* Zb, long ld, const void* Ba, const void* Bb, void* out, long ldo,
@@ -134,6 +199,24 @@ hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, c
   if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
     return run<bf16_t, 8>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
   return run<bf16_t, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
+}
+
+hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,
+                                  const void* Ba, const void* Bb, const int64_t* t_new, const int64_t* kv_off,
+                                  void* out, long ld_out, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)B);
+  if (dt == CSA_F32)
+    return launch("compress_append", compress_append_kernel<float, 4>, grid, dim3(256), 0, s, m, c,
+                  (const float*)rows, ld_new, (float*)ring, (const float*)Ba, (const float*)Bb, t_new, kv_off,
+                  (float*)out, ld_out);
+  if (c % 8 == 0 && ld_new % 8 == 0 && ld_out % 8 == 0)
+    return launch("compress_append", compress_append_kernel<bf16_t, 8>, grid, dim3(256), 0, s, m, c,
+                  (const bf16_t*)rows, ld_new, (bf16_t*)ring, (const bf16_t*)Ba, (const bf16_t*)Bb, t_new, kv_off,
+                  (bf16_t*)out, ld_out);
+  return launch("compress_append", compress_append_kernel<bf16_t, 4>, grid, dim3(256), 0, s, m, c,
+                (const bf16_t*)rows, ld_new, (bf16_t*)ring, (const bf16_t*)Ba, (const bf16_t*)Bb, t_new, kv_off,
+                (bf16_t*)out, ld_out);
 }
 
 }  // namespace csa

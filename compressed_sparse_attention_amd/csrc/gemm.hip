@@ -4,8 +4,9 @@
 // row-vector projections of this form.  Both operands are K-contiguous, so
 // each 16x16x32 MFMA operand is one 16-byte LDS read per lane.
 //
-// Two kernels: gemm256 (below) for bf16 operands with M, N >= 256, and the
-// general gemm_nt (fp32 too, any shape): 128x128 output tile per 256-thread
+// Three kernels: gemm_smallm (below) for bf16 with M <= 16, gemm256 (below)
+// for bf16 operands with M, N >= 256, and the general gemm_nt (fp32 too, any
+// shape): 128x128 output tile per 256-thread
 // workgroup (4 waves in 2x2, each 64x64 = 4x4 MFMA tiles), K staged through
 // LDS in 128-byte slabs, double buffered: the next slab is fetched into
 // registers while the current one feeds the MFMAs.  LDS rows are padded by
@@ -247,10 +248,98 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (M <= 16: one decode token per sequence): the weights are the
+// traffic.  A 256-thread workgroup owns 16 output columns over all of K; its
+// four waves split K and stream their share of the 16 weight rows straight
+// from HBM into MFMA operands (the rows of X, read from L2, are the other
+// operand; rows past M produce outputs that are not written), two 128-deep
+// super-steps in flight per wave.  Within a super-step lane group g covers
+// k = 32 g .. 32 g + 31 of both operands, so each lane reads 64 contiguous
+// bytes of its row.  The four partial 16x16 tiles are summed through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kSmN = 16;        // output columns per workgroup
+constexpr int kSmSuper = 128;   // k per super-step
+
+template <typename TO>
+__global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, const bf16_t* __restrict__ X, long ldx,
+                                                          const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y,
+                                                          long ldy) {
+  __shared__ float s_part[3][256];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const long n0 = (long)blockIdx.x * kSmN;
+  const int nsup = (K + kSmSuper - 1) / kSmSuper;
+  const int s0 = (wave * nsup) / 4, s1 = ((wave + 1) * nsup) / 4;  // this wave's super-steps
+  const long wrow = n0 + c16 < N ? n0 + c16 : 0;  // rows past N / M read row 0: their outputs are not written
+  const long xrow = c16 < M ? c16 : 0;
+  const bf16_t* Wr = W + wrow * ldw + 32 * g;
+  const bf16_t* Xr = X + xrow * ldx + 32 * g;
+
+  Frag<bf16_t> wb[2][4], xb[2][4];
+  // Loads of super-step ss into slot; pieces past K, and super-steps past this
+  // wave's range, read filler from the start of the operands (never used).
+  auto issue = [&](int ss, int slot) {
+    const long k = (long)ss * kSmSuper;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bool ok = ss < s1 && k + 32 * g + 8 * kk < K;  // K % 8 == 0: a piece is all in or all out
+      wb[slot][kk].load_clamped(Wr + k + 8 * kk, ok, W);
+      xb[slot][kk].load_clamped(Xr + k + 8 * kk, ok, X);
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int ss, int slot) {
+    if (ss == nsup - 1 && (K % kSmSuper) != 0) {  // the K tail contributes zeros (uniform branch)
+      const long k = (long)ss * kSmSuper;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (k + 32 * g + 8 * kk >= K) xb[slot][kk].zero();
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) mma(acc, xb[slot][kk], wb[slot][kk]);
+  };
+  issue(s0, 0);
+  issue(s0 + 1, 1);
+  issue_fence();
+  for (int ss = s0; ss < s1; ss += 2) {
+    compute(ss, 0);
+    issue(ss + 2, 0);
+    issue_fence();
+    if (ss + 1 < s1) compute(ss + 1, 1);
+    issue(ss + 3, 1);
+    issue_fence();
+  }
+  // acc[r] = partial of Y[4 g + r][n0 + c16]
+  if (wave > 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_part[wave - 1][lane * 4 + r] = acc[r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const long col = n0 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[r] + s_part[0][lane * 4 + r] + s_part[1][lane * 4 + r] + s_part[2][lane * 4 + r];
+      const int row = 4 * g + r;
+      if (row < M && col < N) Y[row * ldy + col] = from_f32<TO>(v);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s) {
+  if (in_dt == CSA_BF16 && M <= 16) {
+    const dim3 grid1((unsigned)((N + kSmN - 1) / kSmN));
+    if (out_dt == CSA_BF16)
+      return launch("gemm", gemm_smallm_kernel<bf16_t>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                    (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
+    return launch("gemm", gemm_smallm_kernel<float>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                  (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
+  }
   if (in_dt == CSA_BF16 && M >= kG2M && N >= kG2N && N % 4 == 0) {
     const int tm = (int)((M + kG2M - 1) / kG2M), tn = (int)((N + kG2N - 1) / kG2N);
     const int per_xcd = (tm * tn + 7) / 8;

@@ -41,6 +41,11 @@ hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, c
                            const void* Za, const void* Zb, long ld_in, const void* Ba,
                            const void* Bb, void* out, long ld_out, hipStream_t s);
 
+// Decode-time append (one new token per sequence); see csa_compress_append.
+hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,
+                                  const void* Ba, const void* Bb, const int64_t* t_new, const int64_t* kv_off,
+                                  void* out, long ld_out, hipStream_t s);
+
 // The top-k selector's first radix level: a histogram of the top kTopkL1Bits
 // bits of each row's score keys (see score_key).
 constexpr int kTopkL1Bits = 12;

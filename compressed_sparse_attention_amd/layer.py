@@ -131,3 +131,66 @@ def decode(q, qI, wI, Ccomp, KIcomp, seq_len, kv_offset, m: int, k: int, max_can
     api.csa_sparse_mqa(q, Ccomp, buf.idx, sc, buf.o, buf.lse, q_seq=buf.q_seq, kv_offset=kv_offset,
                        workspace=buf.ws_mqa)
     return buf
+
+
+class DecodeState:
+    """Per-sequence decode state of B sequences (the cache maintenance of a decode loop).
+
+    * Ccomp / KIcomp: compressed caches with room for ``capacity`` blocks per
+      sequence; sequence b's rows start at kv_offset[b] = b * capacity.
+    * ring / ring_I: the projected rows [C^a|C^b|Z^a|Z^b] of each sequence's last
+      2m tokens (token t in slot t mod 2m), main and indexer widths.
+    * t: position of each sequence's next token (int64, device).
+    """
+
+    def __init__(self, B: int, capacity: int, m: int, c: int, cI: int, dtype, device):
+        self.B, self.capacity, self.m = B, capacity, m
+        self.Ccomp = torch.zeros(B * capacity, c, dtype=dtype, device=device)
+        self.KIcomp = torch.zeros(B * capacity, cI, dtype=dtype, device=device)
+        self.kv_offset = torch.arange(B, dtype=torch.int64, device=device) * capacity
+        self.ring = torch.zeros(B, 2 * m, 4 * c, dtype=dtype, device=device)
+        self.ring_I = torch.zeros(B, 2 * m, 4 * cI, dtype=dtype, device=device)
+        self.t = torch.zeros(B, dtype=torch.int64, device=device)
+
+    def load_prefill(self, b: int, buf: "PrefillBuffers", c: int, cI: int):
+        """Hand sequence b over from a prefill of its first L tokens (copies only)."""
+        L = buf.Y_H.shape[0]
+        nb = L // self.m
+        if nb > self.capacity:
+            raise ValueError("prefill longer than the cache capacity")
+        o = b * self.capacity
+        self.Ccomp[o:o + nb].copy_(buf.Ccomp[:nb])
+        self.KIcomp[o:o + nb].copy_(buf.KIcomp[:nb])
+        for tok in range(max(0, L - 2 * self.m), L):
+            slot = tok % (2 * self.m)
+            self.ring[b, slot].copy_(buf.Y_H[tok, :4 * c])
+            self.ring_I[b, slot].copy_(buf.Y_H[tok, 4 * c:4 * c + 4 * cI])
+        self.t[b] = L
+
+
+def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeState, m: int, k: int, nh: int,
+                nhI: int, scale: Optional[float] = None, buf: Optional[DecodeBuffers] = None) -> DecodeBuffers:
+    """One decode step with cache maintenance: every sequence b appends token state.t[b] with hidden
+    state H_new[b].  Eqs 1, 2, 5, 6, 7, 10 for the new tokens (few-row GEMMs), eqs 3-4 appended to the
+    compressed caches when a block completes, then eqs 8, 9, 11 for the new tokens; positions advance."""
+    B = H_new.shape[0]
+    c, cI = W["c"], W["cI"]
+    width = 4 * c + 4 * cI + W["dc"]
+    Y = torch.empty(B, width, dtype=H_new.dtype, device=H_new.device)
+    wI = torch.empty(B, nhI, dtype=torch.float32, device=H_new.device)
+    qI = torch.empty(B, nhI * cI, dtype=H_new.dtype, device=H_new.device)
+    q = torch.empty(B, nh * c, dtype=H_new.dtype, device=H_new.device)
+    api.csa_project(H_new, W["W_H_t"], Y)  # eqs 1, 2 (+ indexer copies), 5
+    api.csa_project(H_new, W["W_w_t"], wI)  # eq 7
+    cQ = Y[:, 4 * c + 4 * cI:]
+    api.csa_project(cQ, W["W_UQI_t"], qI)  # eq 6
+    api.csa_project(cQ, W["W_UQ_t"], q)  # eq 10
+    api.csa_compress_append(Y[:, :4 * c], state.ring, W["B_a"], W["B_b"], m, state.t, state.kv_offset,
+                            state.Ccomp)  # eqs 3-4
+    api.csa_compress_append(Y[:, 4 * c:4 * c + 4 * cI], state.ring_I, W["B_aI"], W["B_bI"], m, state.t,
+                            state.kv_offset, state.KIcomp)
+    # the block a token completes is not among its own candidates (s < floor(t/m))
+    buf = decode(q.view(B, nh, c), qI.view(B, nhI, cI), wI, state.Ccomp, state.KIcomp, state.t, state.kv_offset,
+                 m, k, state.capacity, scale=scale, buf=buf)
+    state.t += 1
+    return buf

@@ -113,6 +113,38 @@ csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const voi
                         void* stream);
 
 /*
+ * csa_compress_append -- eqs 3-4 applied while decoding, one new token per
+ * sequence (section "Compressed Key-Value Entries": every m consecutive
+ * entries become one compressed entry, block i's softmax also spanning the
+ * b-rows of block i-1).
+ *
+ * Sequence b's new token is token t = t_new[b] (0-based) of that sequence.
+ * Its projected row, laid out [C^a | C^b | Z^a | Z^b] (4c values), starts at
+ * new_rows + b * ld_new.  ring [B, 2m, 4c] keeps, per sequence, the rows of
+ * its last 2m tokens (token t in slot t mod 2m); the call stores the new row
+ * there.  When t completes block i = floor(t/m) (t mod m == m - 1), the
+ * compressed entry of block i -- a-terms from the ring rows of block i,
+ * b-terms from those of block i-1 (none for i = 0) -- is written to row
+ * kv_offset[b] + i of Ccomp (leading dimension ld_out); otherwise Ccomp is
+ * not touched.  The ring must already hold the rows of tokens t-2m+1 .. t-1
+ * that exist (a prefill leaves its last 2m projected rows there); slots of
+ * tokens before 0 are never read.  The caller owns every buffer and reserves
+ * the Ccomp rows its sequences grow into.
+ *
+ *   new_rows  [B rows, >= 4c]  dtype dt, leading dimension ld_new
+ *   ring      [B, 2m, 4c]      dtype dt, contiguous, read and written
+ *   Ba, Bb    [m, c]           dtype dt, contiguous
+ *   t_new, kv_offset  [B] int64 (device)
+ *
+ * B >= 0, 1 <= m <= 64, c > 0 and a multiple of 4.  Arithmetic is fp32 and
+ * matches csa_compress on the same rows.
+ */
+csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, const void* new_rows,
+                               int64_t ld_new, void* ring, const void* Ba, const void* Bb,
+                               const int64_t* t_new, const int64_t* kv_offset, void* Ccomp,
+                               int64_t ld_out, void* stream);
+
+/*
  * csa_index_topk -- eq 8 scores and the eq 9 selection for a batch of queries.
  *
  * Query r belongs to sequence seq = q_seq[r] (q_seq NULL: 0) and sits at token

@@ -63,6 +63,24 @@ def test_compress_rejects_bad_args(L):
     assert L.csa_compress(1, 3, 4, 64, None, None, None, None, 64, None, None, None, 64, None) == api.CSA_OK
 
 
+def test_compress_append_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def call(dt=1, B=2, m=4, c=64, new=p, ldn=256, ring=p, Ba=p, Bb=p, t=p, off=p, C=p, ldo=64):
+        return L.csa_compress_append(dt, B, m, c, new, ldn, ring, Ba, Bb, t, off, C, ldo, None)
+    assert call(dt=7) == api.CSA_ERR_INVALID_ARG
+    assert call(m=0) == api.CSA_ERR_INVALID_ARG
+    assert call(m=65) == api.CSA_ERR_INVALID_ARG
+    assert call(c=6) == api.CSA_ERR_INVALID_ARG
+    assert call(t=None) == api.CSA_ERR_INVALID_ARG
+    assert call(ring=None) == api.CSA_ERR_INVALID_ARG
+    assert call(ldn=255) == api.CSA_ERR_INVALID_ARG  # a row of new_rows holds C^a|C^b|Z^a|Z^b: 4c wide
+    assert call(ldo=60) == api.CSA_ERR_INVALID_ARG
+    assert call(new=ctypes.c_void_p(18)) == api.CSA_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert call(B=0, new=None, ring=None) == api.CSA_OK  # no sequences: nothing enqueued
+
+
 def test_index_topk_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
     args = dict(dt=1, nq=4, nhI=64, cI=128, m=4, k=16, qI=p, wI=p, K=p, seq=None, pos=None, off=None,

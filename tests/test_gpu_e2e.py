@@ -5,7 +5,8 @@ import pytest
 import torch
 
 from compressed_sparse_attention_amd import synth
-from compressed_sparse_attention_amd.layer import decode, pack_prefill_params, prefill, to_device
+from compressed_sparse_attention_amd.layer import (DecodeState, decode, decode_step, pack_prefill_params,
+                                                     prefill, to_device)
 from oracle import csa_oracle as O
 from parity import assert_rows_close, check_topk, to_np64
 
@@ -71,3 +72,42 @@ def test_decode_workload_full(cfg):
     swaps = check_topk(idx, ref["scores"], w.k)
     print(f"workload {cfg}: {B} queries, band-exempt swaps {swaps}")
     _compare_o_on_matching_rows(idx, ref["idx"], to_np64(buf.o), ref["o"], 0.75)
+
+
+def test_decode_steps_with_cache_maintenance():
+    """Two sequences prefilled to different lengths (9 and 14 tokens, m = 4), then 13 decode steps with
+    cache maintenance (few-row projections, compress-and-append, indexer, top-k, MQA).  Each step's
+    output for token t must equal the oracle prefill's row t of that sequence (decode = prefill row), and
+    the compressed caches grown by the appends must equal the oracle's compression of the whole sequence."""
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS[1], name="layer_small_bf16", dtype="bf16", k=3)
+    steps, L = 13, [9, 14]
+    tot = [L[0] + steps, L[1] + steps]
+    P = synth.make_prefill(w, seed=101, n=tot[0])
+    rng = synth.rng_for(102)
+    Hs = [P["H"], synth.f32_to_bf16(rng.standard_normal((tot[1], w.d), dtype=np.float32))]
+    W = pack_prefill_params(P, w.dtype, DEV)
+    cap = max(tot) // w.m + 1
+    state = DecodeState(2, cap, w.m, w.c, w.cI, torch.bfloat16, DEV)
+    for b in range(2):
+        pb = prefill(to_device(Hs[b][:L[b]], w.dtype, DEV), W, w.m, w.k, w.nh, w.nhI)
+        state.load_prefill(b, pb, w.c, w.cI)
+    o_steps, idx_steps = [], []
+    for s in range(steps):
+        Hn = to_device(np.stack([Hs[0][L[0] + s], Hs[1][L[1] + s]]), w.dtype, DEV)
+        db = decode_step(Hn, W, state, w.m, w.k, w.nh, w.nhI)
+        o_steps.append(to_np64(db.o))
+        idx_steps.append(db.idx.cpu().numpy().copy())
+    torch.cuda.synchronize()
+    assert state.t.cpu().tolist() == tot
+    P64 = {k: _f64(v, w.dtype) for k, v in P.items()}
+    for b in range(2):
+        ref = O.prefill({**P64, "H": _f64(Hs[b], w.dtype)}, w.m, w.k, w.nh, w.nhI)
+        nb = tot[b] // w.m
+        o0 = b * cap
+        assert_rows_close(to_np64(state.Ccomp[o0:o0 + nb]), ref["Ccomp"], what="Ccomp grown by appends")
+        assert_rows_close(to_np64(state.KIcomp[o0:o0 + nb]), ref["KIcomp"], what="KIcomp grown by appends")
+        toks = [L[b] + s for s in range(steps)]
+        idx = np.stack([idx_steps[s][b] for s in range(steps)])
+        o_gpu = np.stack([o_steps[s][b] for s in range(steps)])
+        _compare_o_on_matching_rows(idx, ref["idx"][toks], o_gpu, ref["o"][toks], 0.75)

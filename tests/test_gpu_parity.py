@@ -40,6 +40,10 @@ def f64(x, dtype):
     ("bf16", "bf16", 1000, 1536, 4096),
     ("bf16", "bf16", 520, 296, 200),  # large-tile kernel: ragged M and N edges and a K tail
     ("bf16", "f32", 260, 264, 1000),
+    ("bf16", "bf16", 8, 4096, 4096),  # few-row (decode token) kernel
+    ("bf16", "f32", 3, 64, 200),
+    ("bf16", "bf16", 16, 1000, 1536),
+    ("bf16", "bf16", 1, 40, 8),
 ])
 def test_project(din, dout, M, N, K):
     rng = synth.rng_for(M * 7 + N)
@@ -118,6 +122,53 @@ def test_compress_mean_pool_exact():
 # ---------------------------------------------------------------------------
 # indexer + top-k (eqs 8-9)
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,m,c,steps", [
+    ("f32", 4, 64, 23), ("bf16", 4, 512, 21), ("bf16", 1, 128, 7), ("bf16", 8, 12, 40), ("f32", 64, 16, 140),
+    ("bf16", 2, 2560, 5), ("f32", 4, 1100, 9),
+])
+def test_compress_append(dtype, m, c, steps):
+    """One token per sequence per call: three sequences that already hold 0, 5 and 2m + 3 tokens (ring
+    holding their last 2m rows) grow by `steps` tokens; the rows the appends write must equal the oracle's
+    compression of each whole sequence, and every other cache row stays untouched."""
+    rng = synth.rng_for(m * 1000 + c)
+    pre = [0, 5, 2 * m + 3]
+    B = len(pre)
+    cp = (c + 7) // 8 * 8
+    seqs = []
+    for b in range(B):
+        n = pre[b] + steps
+        Y = draw(rng, (n, 4 * c), 1.0, dtype)
+        Yz = draw(rng, (n, 4 * c), 2.0, dtype)
+        seqs.append(np.where((np.arange(4 * c) // c)[None, :] >= 2, Yz, Y))
+    Ba = draw(rng, (m, c), 0.5, dtype)
+    Bb = draw(rng, (m, c), 0.5, dtype)
+    cap = max(pre) // m + steps // m + 2
+    Cbig = torch.full((B * cap, cp), 3.0, dtype=TD[dtype], device=DEV)
+    C = Cbig[:, :c]
+    ring = torch.zeros(B, 2 * m, 4 * c, dtype=TD[dtype], device=DEV)
+    for b in range(B):
+        for tok in range(max(0, pre[b] - 2 * m), pre[b]):
+            ring[b, tok % (2 * m)] = to_device(seqs[b][tok], dtype, DEV)
+    off = torch.arange(B, dtype=torch.int64, device=DEV) * cap
+    t = torch.tensor(pre, dtype=torch.int64, device=DEV)
+    Bad, Bbd = to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV)
+    wide = torch.zeros(B, 4 * c + 8, dtype=TD[dtype], device=DEV)  # new rows are a column slice
+    for s in range(steps):
+        wide[:, :4 * c] = to_device(np.stack([seqs[b][pre[b] + s] for b in range(B)]), dtype, DEV)
+        api.csa_compress_append(wide[:, :4 * c], ring, Bad, Bbd, m, t, off, C)
+        t += 1
+    torch.cuda.synchronize()
+    got = to_np64(C)
+    for b in range(B):
+        S = f64(seqs[b], dtype)
+        ref = O.compress(S[:, :c], S[:, c:2 * c], S[:, 2 * c:3 * c], S[:, 3 * c:], f64(Ba, dtype), f64(Bb, dtype), m)
+        lo, hi = pre[b] // m, (pre[b] + steps) // m
+        rows = got[b * cap:(b + 1) * cap]
+        assert_rows_close(rows[lo:hi], ref[lo:hi], what=f"appended rows of sequence {b}")
+        assert np.all(rows[:lo] == 3.0) and np.all(rows[hi:] == 3.0)
+    assert torch.all(Cbig[:, c:] == 3.0)
+
+
 def _run_index_topk(qI, wI, K, m, k, lens, kv_offset, dtype, prefill_mode=False):
     B = qI.shape[0]
     idx = torch.full((B, k), 123456, dtype=torch.int32, device=DEV)
