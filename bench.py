@@ -134,7 +134,7 @@ def bench_decode(args, torch, api, synth, layer):
     api.csa_timing_enable(True)
     timed(lambda i: step(i, reps), len(reps), args.steps, 0)
     api.csa_timing_enable(False)
-    kern = _kernel_stats(api, ["indexer_sweep", "topk", "mqa", "mqa_combine"])
+    kern = _kernel_stats(api, ["hist_clear", "indexer_sweep", "topk", "mqa", "mqa_combine"])
     api.csa_timing_reset()
     for n, s in kern.items():
         print(f"[bench]   {n:14s} {s['avg_us']:8.2f} us/launch", flush=True)
@@ -146,13 +146,14 @@ def bench_decode(args, torch, api, synth, layer):
     # whole decode step per query: key sweep + gathered entries + q + o + selected indices
     step_bytes = B * (2 * N * w.cI + 2 * min(w.k, N) * w.c + 2 * (w.nh * w.c + w.nhI * w.cI) + 4 * w.nhI
                       + 2 * w.nh * w.c + 4 * w.k)
-    sw = kern.get("indexer_sweep")
+    name, src = "indexer_sweep", "indexer.hip"
+    sw = kern.get(name)
     roof = None
     if sw:
         achieved = sweep_bytes / (sw["avg_us"] * 1e-6) / 1e9
-        roof = {"kernel": "indexer_sweep", "bound": "hbm", "achieved": round(achieved, 1),
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": _traffic("indexer_sweep", "indexer.hip", B),
+                "traffic": _traffic(name, src, B),
                 "algorithmic_bytes_per_launch": sweep_bytes}
     return {
         "workload": w, "B": B, "ms": ms, "ms_warm": ms_warm, "ms_eager": ms_eager, "kernels": kern, "roofline": roof,
@@ -204,6 +205,95 @@ def bench_prefill(args, torch, api, synth, layer):
             "indexer_roofline": roof}
 
 
+def bench_decode_step(args, torch, api, synth, layer):
+    """Decode with cache maintenance: the batch of 8 sequences at 131072 tokens appends one token each.
+
+    Layer sizes of the 32768-token prefill (d = 4096, d_c = 1536) with the decode batch's attention
+    sizes; the caches hold seeded synthetic entries (the state a 131072-token prefill hands over),
+    the rings random projected rows.  One step: four few-row projections (the weights are streamed
+    once), two compress-and-appends, indexer sweep, top-k and sparse MQA; positions advance, so a
+    block is appended every m steps.  Two copies of weights and state alternate (> 256 MB)."""
+    import numpy as np
+    wd, wp = synth.WORKLOADS[4], synth.WORKLOADS[3]
+    dev = "cuda:0"
+    B, L, m = wd.B, wd.L, wd.m
+    N = L // m
+    n_tok = 64  # pool of new hidden states per sequence
+    P = synth.make_prefill(wp, seed=31, n=B * n_tok)
+    Hpool = layer.to_device(P["H"], wp.dtype, dev).view(n_tok, B, wp.d)
+    del P["H"]
+    D = synth.make_decode(wd, seed=32)
+    total = 3 * (args.steps + args.warmup) + 16
+    cap = N + total // m + 8
+    dt = torch.bfloat16
+    rng = synth.rng_for(33)
+    ring = layer.to_device(synth.normal(rng, (B, 2 * m, 4 * wd.c), 1.0, "bf16"), "bf16", dev)
+    ring_I = layer.to_device(synth.normal(rng, (B, 2 * m, 4 * wd.cI), 1.0, "bf16"), "bf16", dev)
+    C = layer.to_device(D["Ccomp"], wd.dtype, dev).view(B, N, wd.c)
+    K = layer.to_device(D["KIcomp"], wd.dtype, dev).view(B, N, wd.cI)
+    del D
+    copies = []
+    for r in range(2):
+        W = layer.pack_prefill_params(P, wp.dtype, dev)
+        st = layer.DecodeState(B, cap, m, wd.c, wd.cI, dt, dev)
+        st.Ccomp.view(B, cap, wd.c)[:, :N].copy_(C)
+        st.KIcomp.view(B, cap, wd.cI)[:, :N].copy_(K)
+        st.ring.copy_(ring)
+        st.ring_I.copy_(ring_I)
+        st.t.fill_(L)
+        bufr = layer.DecodeBuffers(B, wd.k, wd.nh, wd.c, wd.nhI, cap, dt, dev)
+        copies.append((W, st, bufr))
+    del C, K, P
+
+    def step(i):
+        W, st, bufr = copies[i % 2]
+        layer.decode_step(Hpool[(i // 2) % n_tok], W, st, m, wd.k, wd.nh, wd.nhI, buf=bufr)
+
+    def run(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    run(max(1, args.warmup))
+    ms = run(args.steps)
+    api.csa_timing_reset()
+    api.csa_timing_enable(True)
+    run(args.steps)
+    api.csa_timing_enable(False)
+    names = ["gemm_smallm", "compress_append", "hist_clear", "indexer_sweep", "topk", "mqa", "mqa_combine"]
+    kern = _kernel_stats(api, names)
+    api.csa_timing_reset()
+    t_end = [int(c[1].t.max()) for c in copies]
+    if max(t_end) > cap * m:
+        raise RuntimeError("decode-step benchmark outgrew its cache capacity")
+    print(f"[bench] decode step with cache maintenance: {ms * 1000:.2f} us/step (eager)", flush=True)
+    for n, s_ in kern.items():
+        print(f"[bench]   {n:16s} {s_['total_ms'] / args.steps * 1000:8.2f} us/step "
+              f"({s_['launches'] // args.steps} launches)", flush=True)
+    # weights streamed by the four projections of one step (bf16), plus their inputs and outputs
+    d, dc, c, cI = wp.d, wp.dc, wd.c, wd.cI
+    shapes = [(4 * c + 4 * cI + dc, d, 2), (wd.nhI, d, 4), (wd.nhI * cI, dc, 2), (wd.nh * c, dc, 2)]
+    gemm_bytes = sum(n * k * 2 + B * k * 2 + B * n * ob for n, k, ob in shapes)
+    g = kern.get("gemm_smallm")
+    roof = None
+    if g:
+        t_step = g["total_ms"] / args.steps * 1e-3
+        ach = gemm_bytes / t_step / 1e9
+        roof = {"kernel": "gemm_smallm", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_step": gemm_bytes, "launches_per_step": g["launches"] // args.steps}
+    step_bytes = gemm_bytes + 2 * B * N * cI + B * (2 * wd.k * c + 2 * wd.nh * c + 4 * wd.k)
+    return {"workload": "decode_step_b8_ctx128k_d4096_bf16", "batch": B, "context": L, "d": d, "dc": dc,
+            "us_per_step": round(ms * 1000, 3), "queries_per_s": round(B / (ms * 1e-3), 1),
+            "step_hbm_fraction": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_us_per_step": {n: round(s_["total_ms"] / args.steps * 1000, 3) for n, s_ in kern.items()},
+            "projection_roofline": roof, "input_copies": 2}
+
+
 def cpu_baseline(dec, seconds):
     """The float64 oracle, as it stands, on whole queries of the same decode batch."""
     import numpy as np
@@ -253,6 +343,7 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--prefill-warmup", type=int, default=1)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode-step", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true")
@@ -271,6 +362,7 @@ def main():
 
     dec = bench_decode(args, torch, api, synth, layer)
     pre = None if args.no_prefill else bench_prefill(args, torch, api, synth, layer)
+    dstep = None if args.no_decode_step else bench_decode_step(args, torch, api, synth, layer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     w = dec["workload"]
@@ -302,6 +394,7 @@ def main():
         "graph_queries_per_s": round(dec["B"] / (dec["ms"] * 1e-3), 1),
         "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
         "prefill": pre,
+        "decode_step_with_cache": dstep,
     }
     print(json.dumps(line), flush=True)
 

@@ -3,6 +3,7 @@
 // Host code only.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -319,7 +320,7 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
     lists.gtc = k < csa::kMChunk ? k : csa::kMChunk;
   }
   hipError_t e = csa::launch_indexer(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, q_seq, q_pos, kv_offset,
-                                     max_cand, scores, ld, hist, s);
+                                     max_cand, scores, ld, hist, k, s);
   if (e != hipSuccess) return hip_fail(e, "csa_index_topk indexer launch");
   e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, multi ? &lists : nullptr, idx_out,
                        score_out, s);

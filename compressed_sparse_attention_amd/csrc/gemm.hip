@@ -335,9 +335,9 @@ hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K
   if (in_dt == CSA_BF16 && M <= 16) {
     const dim3 grid1((unsigned)((N + kSmN - 1) / kSmN));
     if (out_dt == CSA_BF16)
-      return launch("gemm", gemm_smallm_kernel<bf16_t>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+      return launch("gemm_smallm", gemm_smallm_kernel<bf16_t>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
                     (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
-    return launch("gemm", gemm_smallm_kernel<float>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+    return launch("gemm_smallm", gemm_smallm_kernel<float>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
                   (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
   }
   if (in_dt == CSA_BF16 && M >= kG2M && N >= kG2N && N % 4 == 0) {

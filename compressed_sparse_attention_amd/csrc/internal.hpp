@@ -51,13 +51,14 @@ hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void
 constexpr int kTopkL1Bits = 12;
 
 // Scores of eq 8 for every query and candidate into `scores` [n_queries, ld_sc].
-// When `hist` is not null (per-query sweep only) the kernel also adds each
-// row's level-1 key histogram into hist [n_queries, 2^kTopkL1Bits], which must
-// be zero on entry.
+// When `hist` is not null (per-query sweep only) the kernel also adds the
+// level-1 key histogram of each row with more than hist_min candidates into
+// hist [n_queries, 2^kTopkL1Bits], which must be zero on entry; the selector
+// reads those rows and leaves them zero again.
 hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, const void* qI,
                           const float* wI, const void* K, const int32_t* q_seq,
                           const int64_t* q_pos, const int64_t* kv_offset, long max_cand,
-                          float* scores, long ld_sc, uint32_t* hist, hipStream_t s);
+                          float* scores, long ld_sc, uint32_t* hist, long hist_min, hipStream_t s);
 
 hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s);
 
@@ -68,8 +69,8 @@ constexpr int kMMaxChunks = 64;
 constexpr long kMMaxWorkgroups = 4096;  // bounds the list workspace
 
 // Workspace areas of the multi-workgroup selector.  `arrive` [n_queries]
-// must be zero on entry (it is cleared together with the histogram); the
-// lists need no initialisation.  List entries hold the candidate index in
+// must be zero on entry (it is cleared together with the histogram) and is
+// zero again on exit; the lists need no initialisation.  List entries hold the candidate index in
 // the low 32 bits and the fp32 score bits (gt) or the score key (eq) above.
 struct TopkLists {
   uint32_t* arrive;  // [n_queries]
@@ -84,7 +85,7 @@ struct TopkLists {
 // histogram produced by the indexer; `lists` (nullable, needs `hist`) selects
 // the multi-workgroup path.
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
-                       const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
+                       const int64_t* q_pos, long max_cand, int k, uint32_t* hist,
                        const TopkLists* lists, int32_t* idx_out, float* score_out, hipStream_t s);
 
 bool mqa_supported_c(int c);

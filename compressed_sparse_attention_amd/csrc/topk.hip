@@ -22,346 +22,30 @@
 // the tie-break.  The result, slot order included, is deterministic.
 #include "common.hpp"
 #include "internal.hpp"
+#include "select.hpp"
 
 namespace csa {
 namespace {
-
-constexpr int kL1Bins = 1 << kTopkL1Bits;
-constexpr int kL1Shift = 32 - kTopkL1Bits;
-constexpr int kCandCap = kL1Bins / 2;  // the candidate list (index, key) reuses the level-1 histogram's LDS
-constexpr int kEPT = 32;           // keys per thread per segment
 
 __global__ void hist_clear_kernel(uint32_t* __restrict__ h, long n) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) h[i] = 0u;
 }
 
-// Inverse of score_key (a -0.0 score comes back as +0.0).
-__device__ __forceinline__ float key_score(uint32_t key) {
-  const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-  return __uint_as_float(u);
-}
-
-// Exclusive scan over the workgroup; also returns the total.  Contains barriers.
-template <int TPB>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t x = wave_incl_scan(v);
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < TPB / 64; ++w) {
-    const uint32_t t = s_wave[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  total = all;
-  return before + x - v;
-}
-
-// Scanning bins from the highest digit down, finds the bin where the running
-// count reaches `need`; writes the bin and the count strictly above it.
-template <int TPB>
-__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* s_wave,
-                         uint32_t* s_out) {
-  const int per = (nbins + TPB - 1) / TPB;
-  const int tid = threadIdx.x;
-  uint32_t local = 0;
-  for (int q = 0; q < per; ++q) {
-    const int b = nbins - 1 - (tid * per + q);
-    if (b >= 0) local += hist[b];
-  }
-  uint32_t total;
-  const uint32_t excl = block_excl_scan<TPB>(local, s_wave, total);
-  if (excl < need && excl + local >= need) {
-    uint32_t cum = excl;
-    for (int q = 0; q < per; ++q) {
-      const int b = nbins - 1 - (tid * per + q);
-      const uint32_t h = hist[b];
-      if (cum + h >= need) {
-        s_out[0] = (uint32_t)b;
-        s_out[1] = cum;
-        break;
-      }
-      cum += h;
-    }
-  }
-  __syncthreads();
-}
-
-// One wave finds the bin of a small histogram (nbins <= 256) where the count
-// from the top reaches `need`; the caller follows with a barrier.
-// nbins is 256 or 16.
-__device__ void find_bin_wave(const uint32_t* hist, int nbins, uint32_t need, uint32_t* s_out) {
-  const int lane = threadIdx.x & 63;
-  // lane l holds bins nbins-1-4l .. nbins-4-4l (highest first); lanes past the
-  // histogram hold zeros
-  uint32_t h[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int b = nbins - 1 - (4 * lane + q);
-    h[q] = b >= 0 ? hist[b] : 0u;
-  }
-  const uint32_t local = h[0] + h[1] + h[2] + h[3];
-  const uint32_t incl = wave_incl_scan(local);
-  const uint32_t excl = incl - local;
-  if (excl < need && incl >= need) {
-    uint32_t cum = excl;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (cum < need && cum + h[q] >= need) {
-        s_out[0] = (uint32_t)(nbins - 1 - (4 * lane + q));
-        s_out[1] = cum;
-      }
-      cum += h[q];
-    }
-  }
-}
-
 template <int TPB>
 __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restrict__ scores, long ld,
                                                    const int64_t* __restrict__ q_pos, long max_cand,
-                                                   int k, const uint32_t* __restrict__ hist_g,
+                                                   int k, uint32_t* __restrict__ hist_g,
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ score_out) {
-  constexpr int SEG = TPB * kEPT;     // keys per staged segment
-  constexpr int VPT = SEG / 4 / TPB;  // float4 loads per thread per segment
-  __shared__ uint32_t s_keys[SEG + SEG / 32];
-  // level-1 histogram; afterwards the candidate list: indices in [0, kCandCap),
-  // their keys in [kCandCap, 2 kCandCap)
-  __shared__ uint32_t s_hist[kL1Bins];
-  __shared__ uint32_t s_h2[3][256];  // levels 2-4
-  __shared__ uint32_t s_wave[TPB / 64];
-  __shared__ uint32_t s_res[4];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  __shared__ SelectRowSmem<TPB> sm;
   const long r = blockIdx.x;
   const long pos = q_pos ? q_pos[r] : r;
   long ncl = pos > 0 ? pos / m : 0;
   ncl = ncl < max_cand ? ncl : max_cand;
-  const int nc = (int)ncl;
-  const float* row = scores + r * ld;
-  int32_t* out = idx_out + r * k;
-  float* sout = score_out ? score_out + r * k : nullptr;
-
-  if (nc <= k) {  // every candidate is kept
-    for (int j = tid; j < k; j += TPB) {
-      const bool live = j < nc;
-      out[j] = live ? j : -1;
-      if (sout) sout[j] = live ? row[j] : -INFINITY;
-    }
-    return;
-  }
-  for (int b = tid; b < 3 * 256; b += TPB) (&s_h2[0][0])[b] = 0u;
-
-  const int nseg = (nc + SEG - 1) / SEG;
-  const int first = tid * kEPT;  // this thread's keys: [first, first + 32) of a segment
-  const uint32_t* mykeys = s_keys + first + (first >> 5);
-  // Stage segment sg: coalesced 16-byte loads (all issued first) into padded
-  // LDS.  Rows live in a workspace whose leading dimension is a multiple of 4
-  // and >= nc, so a load clamped to [0, ld-4] stays in bounds; keys past nc
-  // are staged but never used.
-  auto stage = [&](int sg) {
-    __syncthreads();
-    const long base = (long)sg * SEG;
-    float4 buf[VPT];
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const long a = base + 4L * (tid + j * TPB);
-      buf[j] = *reinterpret_cast<const float4*>(row + (a < ld - 4 ? a : ld - 4));
-    }
-    issue_fence();
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int i = 4 * (tid + j * TPB);
-      const int a = i + (i >> 5);
-      s_keys[a] = score_key(buf[j].x);
-      s_keys[a + 1] = score_key(buf[j].y);
-      s_keys[a + 2] = score_key(buf[j].z);
-      s_keys[a + 3] = score_key(buf[j].w);
-    }
-    __syncthreads();
-  };
-  auto nvalid = [&](int sg) { return max(0, min(kEPT, nc - sg * SEG - first)); };
-  auto put = [&](uint32_t slot, int i, uint32_t kv) {
-    if (slot < (uint32_t)k) {  // always true when the counts are exact; keeps writes in the row
-      out[slot] = i;
-      if (sout) sout[slot] = key_score(kv);
-    }
-  };
-  // Ordered pass over the whole row: cls(key) in {0, 1, 2}.  Each thread reads
-  // its 32 keys in one burst and records the classes as two bit masks; after
-  // the workgroup scan it visits only the set bits.  Classes 1 and 2 are
-  // numbered separately in index order and handed to emit1 / emit2.
-  auto ordered_row = [&](auto&& cls, auto&& emit1, auto&& emit2, uint32_t& tot1, uint32_t& tot2) {
-    tot1 = 0;
-    tot2 = 0;
-    for (int sg = 0; sg < nseg; ++sg) {
-      if (nseg > 1) stage(sg);
-      const int nv = nvalid(sg);
-      uint32_t m1 = 0, m2 = 0;
-#pragma unroll
-      for (int e = 0; e < kEPT; ++e) {
-        const int c = cls(mykeys[e]);
-        m1 |= (uint32_t)(c == 1 && e < nv) << e;
-        m2 |= (uint32_t)(c == 2 && e < nv) << e;
-      }
-      uint32_t tot;
-      const uint32_t ex = block_excl_scan<TPB>(__popc(m1) | (__popc(m2) << 16), s_wave, tot);
-      uint32_t p1 = tot1 + (ex & 0xFFFFu), p2 = tot2 + (ex >> 16);
-      for (uint32_t mm = m1 | m2; mm; mm &= mm - 1) {
-        const int e = __ffs(mm) - 1;
-        const uint32_t kv = mykeys[e];
-        if ((m1 >> e) & 1u)
-          emit1(sg * SEG + first + e, kv, p1++);
-        else
-          emit2(sg * SEG + first + e, kv, p2++);
-      }
-      tot1 += tot & 0xFFFFu;
-      tot2 += tot >> 16;
-    }
-  };
-
-  // the indexer's histogram is fetched together with the row
-  constexpr int HPT = kL1Bins / TPB;  // bins per thread
-  uint32_t hreg[HPT];
-  if (hist_g) {
-#pragma unroll
-    for (int q = 0; q < HPT; ++q) hreg[q] = hist_g[r * kL1Bins + q * TPB + tid];
-  }
-  if (nseg == 1) stage(0);
-
-  // ---- level 1: 12-bit digit ----------------------------------------------
-  if (hist_g) {
-#pragma unroll
-    for (int q = 0; q < HPT; ++q) s_hist[q * TPB + tid] = hreg[q];
-    __syncthreads();
-  } else {
-    for (int b = tid; b < kL1Bins; b += TPB) s_hist[b] = 0u;
-    __syncthreads();
-    for (int sg = 0; sg < nseg; ++sg) {
-      if (nseg > 1) stage(sg);
-      const int nv = nvalid(sg);
-#pragma unroll
-      for (int e = 0; e < kEPT; ++e)
-        if (e < nv) atomicAdd(&s_hist[mykeys[e] >> kL1Shift], 1u);
-    }
-    __syncthreads();
-  }
-  find_bin<TPB>(s_hist, kL1Bins, (uint32_t)k, s_wave, s_res);
-  const uint32_t b1 = s_res[0];
-  const uint32_t g1 = s_res[1];  // keys with a higher digit: all selected
-  const uint32_t need1 = (uint32_t)k - g1;
-
-  // Digit > b1: selected.  Digit == b1: candidate list, in index order.
-  uint32_t* c_idx = s_hist;
-  uint32_t* c_key = s_hist + kCandCap;
-  uint32_t n_gt1, n_cand;
-  ordered_row([&](uint32_t kv) -> int {
-        const uint32_t d = kv >> kL1Shift;
-        return d > b1 ? 1 : (d == b1 ? 2 : 0);
-      },
-      [&](int i, uint32_t kv, uint32_t p) { put(p, i, kv); },
-      [&](int i, uint32_t kv, uint32_t p) {
-        if (p < (uint32_t)kCandCap) {
-          c_idx[p] = (uint32_t)i;
-          c_key[p] = kv;
-        }
-      },
-      n_gt1, n_cand);
-  __syncthreads();
-  const bool listed = n_cand <= (uint32_t)kCandCap;
-
-  // ---- levels 2-4: 8 + 8 + 4 bits ---------------------------------------------
-  const int shifts[3] = {12, 4, 0};
-  const int widths[3] = {8, 8, 4};
-  if (listed) {
-    // The candidates fit in the list: one wave finishes the row, with wave-level
-    // scans only (no workgroup barriers).
-    if (wave != 0) return;
-    const int lane = tid & 63;
-    uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift, need = need1;
-    for (int lv = 0; lv < 3; ++lv) {
-      const int sh = shifts[lv];
-      const uint32_t dm = (1u << widths[lv]) - 1u;
-      uint32_t* h2 = s_h2[lv];
-      for (int j = lane; j < (int)n_cand; j += 64) {
-        const uint32_t kv = c_key[j];
-        if ((kv & pmask) == prefix) atomicAdd(&h2[(kv >> sh) & dm], 1u);
-      }
-      __builtin_amdgcn_wave_barrier();
-      find_bin_wave(h2, 1 << widths[lv], need, s_res);
-      __builtin_amdgcn_wave_barrier();
-      prefix |= s_res[0] << sh;
-      pmask |= dm << sh;
-      need -= s_res[1];
-    }
-    const uint32_t T = prefix;      // the k-th largest key
-    const uint32_t take_eq = need;  // ties at T to take, lowest indices first
-    const uint32_t gt2 = need1 - take_eq;
-    // list positions [cpt*lane, cpt*lane + cpt); list order is index order
-    const int cpt = ((int)n_cand + 63) / 64;
-    const int f = lane * cpt;
-    const int lim = max(0, min(cpt, (int)n_cand - f));
-    uint32_t c1 = 0, c2 = 0;
-    for (int e = 0; e < lim; ++e) {
-      const uint32_t kv = c_key[f + e];
-      c1 += kv > T;
-      c2 += kv == T;
-    }
-    const uint32_t packed = c1 | (c2 << 16);
-    const uint32_t ex = wave_incl_scan(packed) - packed;
-    uint32_t p1 = ex & 0xFFFFu, p2 = ex >> 16;
-    for (int e = 0; e < lim; ++e) {
-      const uint32_t kv = c_key[f + e];
-      const int i = (int)c_idx[f + e];
-      if (kv > T) put(g1 + p1++, i, kv);
-      if (kv == T) {
-        if (p2 < take_eq) put(g1 + gt2 + p2, i, kv);
-        ++p2;
-      }
-    }
-    return;
-  }
-
-  // More candidates than the list holds: finish over the whole row.
-  uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift, need = need1;
-  for (int lv = 0; lv < 3; ++lv) {
-    const int sh = shifts[lv];
-    const uint32_t dm = (1u << widths[lv]) - 1u;
-    uint32_t* h2 = s_h2[lv];
-    for (int sg = 0; sg < nseg; ++sg) {
-      if (nseg > 1) stage(sg);
-      const int nv = nvalid(sg);
-#pragma unroll
-      for (int e = 0; e < kEPT; ++e) {
-        const uint32_t kv = mykeys[e];
-        if (e < nv && (kv & pmask) == prefix) atomicAdd(&h2[(kv >> sh) & dm], 1u);
-      }
-    }
-    __syncthreads();
-    if (wave == 0) find_bin_wave(h2, 1 << widths[lv], need, s_res);
-    __syncthreads();
-    prefix |= s_res[0] << sh;
-    pmask |= dm << sh;
-    need -= s_res[1];
-  }
-  const uint32_t T = prefix;
-  const uint32_t take_eq = need;
-  const uint32_t gt2 = need1 - take_eq;
-  uint32_t t1, t2;
-  ordered_row([&](uint32_t kv) -> int {
-        if ((kv >> kL1Shift) != b1) return 0;
-        return kv > T ? 1 : (kv == T ? 2 : 0);
-      },
-      [&](int i, uint32_t kv, uint32_t p) { put(g1 + p, i, kv); },
-      [&](int i, uint32_t kv, uint32_t p) {
-        if (p < take_eq) put(g1 + gt2 + p, i, kv);
-      },
-      t1, t2);
+  uint32_t* hrow = hist_g ? hist_g + r * kL1Bins : nullptr;
+  select_row<TPB>(sm, scores + r * ld, ld, (int)ncl, k, hrow, hrow, idx_out + r * k,
+                  score_out ? score_out + r * k : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,35 +66,16 @@ __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restric
 // ---------------------------------------------------------------------------
 constexpr int kMTPB = 256;
 constexpr int kMEPT = 8;
-constexpr int kMSeg = 4096;   // candidates staged in LDS at once
-constexpr int kMUnroll = 8;   // list entries fetched per thread per batch
-
-// chunk holding list position e, given the exclusive prefix pre[0..P] of the
-// per-chunk counts (pre[P] = total); P <= kMMaxChunks
-__device__ __forceinline__ int chunk_of(const uint32_t* pre, int P, uint32_t e) {
-  int lo = 0, hi = P - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= e) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
     int m, const float* __restrict__ scores, long ld, const int64_t* __restrict__ q_pos, long max_cand, int k,
-    const uint32_t* __restrict__ hist_g, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
+    uint32_t* __restrict__ hist_g, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
     uint64_t* __restrict__ gt_list, uint64_t* __restrict__ eq_list, int P, int gtc, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
-  __shared__ uint32_t s_ckey[kMSeg];
-  __shared__ uint32_t s_cidx[kMSeg];
-  __shared__ uint32_t s_h2[3][256];
-  __shared__ uint32_t s_pg[kMMaxChunks + 1], s_pe[kMMaxChunks + 1];
   __shared__ uint32_t s_wave[kMTPB / 64];
-  __shared__ uint32_t s_res[4];
+  __shared__ uint32_t s_res[2];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const long r = blockIdx.x / P;
   const int j = (int)(blockIdx.x - r * P);
   const long pos = q_pos ? q_pos[r] : r;
@@ -438,42 +103,8 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
   const long a = (long)j * kMChunk + kMEPT * tid;
   const float4 v0 = *reinterpret_cast<const float4*>(row + (a < ld - 4 ? a : ld - 4));
   const float4 v1 = *reinterpret_cast<const float4*>(row + (a + 4 < ld - 4 ? a + 4 : ld - 4));
-  constexpr int HPT = kL1Bins / kMTPB;  // 16 bins per thread: [HPT*tid, HPT*tid + HPT)
-  const uint32_t* hrow = hist_g + r * kL1Bins;
-  u32x4 hv[HPT / 4];
-#pragma unroll
-  for (int q = 0; q < HPT / 4; ++q) hv[q] = *reinterpret_cast<const u32x4*>(hrow + HPT * tid + 4 * q);
-  issue_fence();
-  if (tid == 0) {
-    s_res[0] = 0u;
-    s_res[1] = 0u;
-  }
-  uint32_t hb[HPT];
-#pragma unroll
-  for (int q = 0; q < HPT / 4; ++q) {
-    hb[4 * q] = hv[q].x;
-    hb[4 * q + 1] = hv[q].y;
-    hb[4 * q + 2] = hv[q].z;
-    hb[4 * q + 3] = hv[q].w;
-  }
-  uint32_t local = 0;
-#pragma unroll
-  for (int q = 0; q < HPT; ++q) local += hb[q];
-  uint32_t tot;
-  const uint32_t excl = block_excl_scan<kMTPB>(local, s_wave, tot);
-  const uint32_t above = tot - excl - local;  // keys in bins above this thread's bins
-  if (above < (uint32_t)k && above + local >= (uint32_t)k) {
-    uint32_t cum = above;
-#pragma unroll
-    for (int q = HPT - 1; q >= 0; --q) {
-      if (cum < (uint32_t)k && cum + hb[q] >= (uint32_t)k) {
-        s_res[0] = (uint32_t)(HPT * tid + q);
-        s_res[1] = cum;
-      }
-      cum += hb[q];
-    }
-  }
-  __syncthreads();
+  // every chunk workgroup derives the threshold bin from the row's histogram
+  level1_threshold<kMTPB>(hist_g + r * kL1Bins, (uint32_t)k, s_wave, s_res);
   const uint32_t b1 = s_res[0];
   const uint32_t g1 = s_res[1];
 
@@ -515,152 +146,20 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
     s_last = __hip_atomic_fetch_add(arrive + r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(Pr - 1);
   __syncthreads();
   if (!s_last) return;
-
-  // ---- finishing phase (last chunk workgroup of the row) ----------------------
-  for (int b = tid; b < 3 * 256; b += kMTPB) (&s_h2[0][0])[b] = 0u;
-  if (wave == 0) {
-    const uint32_t cg = lane < Pr ? ld_agent(counts + (r * P + lane) * 2) : 0u;
-    const uint32_t ce = lane < Pr ? ld_agent(counts + (r * P + lane) * 2 + 1) : 0u;
-    const uint32_t ig = wave_incl_scan(cg), ie = wave_incl_scan(ce);
-    s_pg[lane] = ig - cg;
-    s_pe[lane] = ie - ce;
-    if (lane == 63) {
-      s_pg[kMMaxChunks] = ig;
-      s_pe[kMMaxChunks] = ie;
-    }
-  }
-  __syncthreads();
-  const uint32_t n_cand = s_pe[kMMaxChunks];
-  const int nseg = (int)((n_cand + kMSeg - 1) / kMSeg);
-
-  auto put = [&](uint32_t slot, uint32_t i, uint32_t key) {
-    if (slot < (uint32_t)k) {
-      out[slot] = (int32_t)i;
-      if (sout) sout[slot] = key_score(key);
-    }
-  };
-  // Both lists in one pass: a group of TPC threads serves each chunk, so list
-  // positions need no search.  Selected entries go straight to their slots
-  // (chunk order = index order); candidates go to LDS when they all fit.
+  // every chunk of the row has read its histogram: leave it and the counter
+  // zero for the next call
   {
-    int p2 = 1;
-    while (p2 < Pr) p2 <<= 1;
-    const int tpc = kMTPB / p2;  // >= 4
-    const int c = tid / tpc, sub = tid - c * tpc;
-    if (c < Pr) {
-      const uint32_t g0 = s_pg[c], ng = s_pg[c + 1] - g0;
-      const uint32_t e0c = s_pe[c], ne = s_pe[c + 1] - e0c;
-      const uint32_t nmax = nseg == 1 ? max(ng, ne) : ng;
-      const uint64_t* gsrc = gt_list + (r * P + c) * (long)gtc;
-      const uint64_t* esrc = eq_list + (r * P + c) * (long)kMChunk;
-      for (uint32_t base = sub; base < nmax; base += tpc * kMUnroll) {
-        uint64_t eg[kMUnroll], ee[kMUnroll];
-#pragma unroll
-        for (int u = 0; u < kMUnroll; ++u) {
-          const uint32_t e = base + u * tpc;
-          eg[u] = ld_agent(gsrc + (e < ng ? e : 0u));
-          ee[u] = ld_agent(esrc + (e < ne ? e : 0u));
-        }
-        issue_fence();
-#pragma unroll
-        for (int u = 0; u < kMUnroll; ++u) {
-          const uint32_t e = base + u * tpc;
-          if (e < ng && g0 + e < (uint32_t)k) {
-            out[g0 + e] = (int32_t)(uint32_t)eg[u];
-            if (sout) sout[g0 + e] = __uint_as_float((uint32_t)(eg[u] >> 32));
-          }
-          if (nseg == 1 && e < ne) {
-            s_cidx[e0c + e] = (uint32_t)ee[u];
-            s_ckey[e0c + e] = (uint32_t)(ee[u] >> 32);
-          }
-        }
-      }
-    }
+    u32x4* h = reinterpret_cast<u32x4*>(hist_g + r * kL1Bins);
+    for (int b = tid; b < kL1Bins / 4; b += kMTPB) h[b] = u32x4{0u, 0u, 0u, 0u};
+    if (tid == 0) arrive[r] = 0u;
   }
-  __syncthreads();
-
-  // More candidates than LDS holds: stage them kMSeg at a time from the lists.
-  auto stage = [&](int sg) {
-    __syncthreads();
-    const uint32_t base = (uint32_t)sg * kMSeg;
-    const uint32_t cnt = min((uint32_t)kMSeg, n_cand - base);
-    for (uint32_t el_ = tid; el_ < cnt; el_ += kMTPB) {
-      const uint32_t e = base + el_;
-      const int c = chunk_of(s_pe, Pr, e);
-      const uint64_t ent = ld_agent(eq_list + (r * P + c) * (long)kMChunk + (e - s_pe[c]));
-      s_cidx[el_] = (uint32_t)ent;
-      s_ckey[el_] = (uint32_t)(ent >> 32);
-    }
-    __syncthreads();
-  };
-  auto seg_count = [&](int sg) { return (int)min((uint32_t)kMSeg, n_cand - (uint32_t)sg * kMSeg); };
-
-  const int shifts[3] = {12, 4, 0};
-  const int widths[3] = {8, 8, 4};
-  uint32_t prefix = b1 << kL1Shift, pmask = 0xFFFFFFFFu << kL1Shift;
-  uint32_t need = (uint32_t)k - g1;
-  for (int lv = 0; lv < 3; ++lv) {
-    const int sh = shifts[lv];
-    const uint32_t dm = (1u << widths[lv]) - 1u;
-    uint32_t* h2 = s_h2[lv];
-    for (int sg = 0; sg < nseg; ++sg) {
-      if (nseg > 1) stage(sg);
-      const int cnt = seg_count(sg);
-      for (int e = tid; e < cnt; e += kMTPB) {
-        const uint32_t key = s_ckey[e];
-        if ((key & pmask) == prefix) atomicAdd(&h2[(key >> sh) & dm], 1u);
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      if (lane == 0) {
-        s_res[0] = 0u;
-        s_res[1] = 0u;
-      }
-      find_bin_wave(h2, 1 << widths[lv], need, s_res);
-    }
-    __syncthreads();
-    prefix |= s_res[0] << sh;
-    pmask |= dm << sh;
-    need -= s_res[1];
-  }
-  const uint32_t T = prefix;      // the k-th largest key
-  const uint32_t take_eq = need;  // ties at T to take, lowest indices first
-  const uint32_t gt2 = (uint32_t)k - g1 - take_eq;
-
-  uint32_t run1 = 0, run2 = 0;
-  for (int sg = 0; sg < nseg; ++sg) {
-    if (nseg > 1) stage(sg);
-    const int cnt = seg_count(sg);
-    const int cpt = (cnt + kMTPB - 1) / kMTPB;
-    const int f = tid * cpt;
-    const int lim = max(0, min(cpt, cnt - f));
-    uint32_t c1 = 0, c2 = 0;
-    for (int e = 0; e < lim; ++e) {
-      const uint32_t key = s_ckey[f + e];
-      c1 += key > T;
-      c2 += key == T;
-    }
-    uint32_t tot3;
-    const uint32_t ex3 = block_excl_scan<kMTPB>(c1 | (c2 << 16), s_wave, tot3);
-    uint32_t p1 = run1 + (ex3 & 0xFFFFu), p2 = run2 + (ex3 >> 16);
-    for (int e = 0; e < lim; ++e) {
-      const uint32_t key = s_ckey[f + e];
-      const uint32_t i = s_cidx[f + e];
-      if (key > T) put(g1 + p1++, i, key);
-      if (key == T) {
-        if (p2 < take_eq) put(g1 + gt2 + p2, i, key);
-        ++p2;
-      }
-    }
-    run1 += tot3 & 0xFFFFu;
-    run2 += tot3 >> 16;
-  }
+  finish_row<kMTPB>(Pr, k, b1, g1, counts + r * P * 2, gt_list + r * P * (long)gtc, gtc,
+                    eq_list + r * P * (long)kMChunk, kMChunk, out, sout);
 }
 
 template <int TPB>
 void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const int64_t* q_pos, long max_cand,
-            int k, const uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
+            int k, uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
   (void)csa::launch("topk", topk_kernel<TPB>, dim3((unsigned)n_queries), dim3(TPB), 0, s, m, scores, ld_sc, q_pos,
                max_cand, k, hist, idx_out, score_out);
 }
@@ -673,7 +172,7 @@ hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s) {
 }
 
 hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
-                       const int64_t* q_pos, long max_cand, int k, const uint32_t* hist,
+                       const int64_t* q_pos, long max_cand, int k, uint32_t* hist,
                        const TopkLists* lists, int32_t* idx_out, float* score_out, hipStream_t s) {
   if (n_queries == 0) return hipSuccess;
   if (hist && lists) {

@@ -115,6 +115,11 @@ def _normal(rng, shape, std, dtype):
     return x
 
 
+def normal(rng, shape, std: float = 1.0, dtype: str = "f32") -> np.ndarray:
+    """Seeded N(0, std^2) draws: fp32, or bf16 bit patterns (uint16) for dtype "bf16"."""
+    return _normal(rng, shape, std, dtype)
+
+
 # Order in which prefill parameters are drawn (after H).
 PREFILL_PARAM_ORDER = (
     "W_aKV", "W_bKV", "W_aZ", "W_bZ", "B_a", "B_b",

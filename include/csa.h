@@ -218,8 +218,10 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
  * Kernel timing (instrumentation, off by default).  While enabled, every
  * kernel the library launches is bracketed by a pair of HIP events recorded
  * on the launch stream.  csa_timing_read synchronises on the recorded events
- * and returns, for the kernel family `name` ("gemm", "compress",
- * "indexer_sweep", "indexer_prefill", "topk", "mqa", "mqa_combine"),
+ * and returns, for the kernel family `name` ("gemm", "gemm_smallm"
+ * (bf16 projections of 16 rows or fewer), "compress", "compress_append",
+ * "indexer_sweep", "indexer_prefill", "hist_clear", "topk", "mqa",
+ * "mqa_combine"),
  * the summed duration in milliseconds and the number of launches since the
  * last reset.  Unknown names give 0 launches.
  */
