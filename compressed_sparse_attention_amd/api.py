@@ -48,6 +48,9 @@ _SIGS = {
     "csa_sparse_mqa_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_sparse_mqa": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _sz, _vp]),
+    "csa_decode_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "csa_decode": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "csa_timing_reset": (ctypes.c_int, []),
     "csa_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -250,6 +253,49 @@ def csa_sparse_mqa(q, Ccomp, idx, scale: float, o, lse=None, q_seq=None, kv_offs
                                 _ptr(kv_offset), _ptr(idx), _ptr(o), _ptr(lse), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(q.device)),
            "csa_sparse_mqa")
+    return o
+
+
+def csa_decode_workspace(n_queries: int, max_cand: int, n_hI: int, n_h: int, c: int, k: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_decode_workspace(n_queries, max_cand, n_hI, n_h, c, k, ctypes.byref(b)), "csa_decode_workspace")
+    return b.value
+
+
+def csa_decode(qI, wI, KIcomp, q, Ccomp, m: int, k: int, max_cand: int, scale: float, q_pos, idx_out, o,
+               workspace, lse=None, score_out=None, q_seq=None, kv_offset=None):
+    """Eqs 8, 9 and 11 for a batch of decode queries in one call.  `workspace` (uint8, at least
+    csa_decode_workspace bytes) must be zero-filled before its first use and again whenever the
+    sizes change; every call leaves it ready for the next."""
+    nq, nhI, cI = qI.shape
+    _, nh, c = q.shape
+    for t, nm in ((qI, "qI"), (wI, "wI"), (KIcomp, "KIcomp"), (q, "q"), (Ccomp, "Ccomp"), (idx_out, "idx_out"),
+                  (o, "o"), (workspace, "workspace")):
+        _contig(t, nm)
+    if wI.dtype != torch.float32 or tuple(wI.shape) != (nq, nhI):
+        raise CSAError("csa_decode: wI must be fp32 [n_queries, n_hI]")
+    if idx_out.dtype != torch.int32 or tuple(idx_out.shape) != (nq, k):
+        raise CSAError("csa_decode: idx_out must be int32 [n_queries, k]")
+    if tuple(q.shape[:1]) != (nq,) or o.dtype != q.dtype or tuple(o.shape) != (nq, nh, c):
+        raise CSAError("csa_decode: o must match q [n_queries, n_h, c]")
+    if KIcomp.dtype != qI.dtype or Ccomp.dtype != q.dtype or q.dtype != qI.dtype:
+        raise CSAError("csa_decode: caches and queries must share one dtype")
+    if q_pos is None or q_pos.dtype != torch.int64 or q_pos.numel() != nq:
+        raise CSAError("csa_decode: q_pos must be int64 [n_queries]")
+    if q_seq is not None and (q_seq.dtype != torch.int32 or q_seq.numel() != nq):
+        raise CSAError("csa_decode: q_seq must be int32 [n_queries]")
+    if kv_offset is not None and kv_offset.dtype != torch.int64:
+        raise CSAError("csa_decode: kv_offset must be int64")
+    for t, nm, shape in ((lse, "lse", (nq, nh)), (score_out, "score_out", (nq, k))):
+        if t is not None:
+            _contig(t, nm)
+            if t.dtype != torch.float32 or tuple(t.shape) != shape:
+                raise CSAError(f"csa_decode: {nm} must be fp32 {list(shape)}")
+    _check(lib().csa_decode(_dt(q), nq, nhI, cI, nh, c, m, k, float(scale), _ptr(qI), _ptr(wI), _ptr(KIcomp),
+                            _ptr(q), _ptr(Ccomp), _ptr(q_seq), _ptr(q_pos), _ptr(kv_offset), max_cand,
+                            _ptr(idx_out), _ptr(score_out), _ptr(o), _ptr(lse), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(q.device)),
+           "csa_decode")
     return o
 
 

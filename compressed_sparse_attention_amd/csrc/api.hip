@@ -271,11 +271,15 @@ csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t
   return CSA_OK;
 }
 
-csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m,
-                          int32_t k, const void* qI, const float* wI, const void* KIcomp,
-                          const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
-                          int64_t max_cand, int32_t* idx_out, float* score_out, void* workspace,
-                          size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// csa_index_topk; `clear` zeroes the histogram and arrival counters first
+// (csa_decode relies on the selectors leaving them zero instead).
+csa_status index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m, int32_t k,
+                      const void* qI, const float* wI, const void* KIcomp, const int32_t* q_seq,
+                      const int64_t* q_pos, const int64_t* kv_offset, int64_t max_cand, int32_t* idx_out,
+                      float* score_out, void* workspace, size_t ws_bytes, void* stream, bool clear) {
   CSA_REQUIRE(dtype_ok(dt), "csa_index_topk: unknown dtype");
   CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_index_topk: bad n_queries");
   CSA_REQUIRE(n_hI >= 1 && n_hI <= 64, "csa_index_topk: n_hI must be in [1, 64] (got %d)", n_hI);
@@ -307,6 +311,8 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
   const bool multi = sweep && use_lists(n_queries, max_cand);
   if (use_hist(max_cand) && sweep) {
     hist = (uint32_t*)(ws + w.hist);
+  }
+  if (hist && clear) {
     const long words = n_queries * (1L << csa::kTopkL1Bits) + (multi ? n_queries : 0);
     hipError_t e0 = csa::launch_hist_clear(hist, words, s);
     if (e0 != hipSuccess) return hip_fail(e0, "csa_index_topk histogram clear");
@@ -325,6 +331,19 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
   e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, multi ? &lists : nullptr, idx_out,
                        score_out, s);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk top-k launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m,
+                          int32_t k, const void* qI, const float* wI, const void* KIcomp,
+                          const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
+                          int64_t max_cand, int32_t* idx_out, float* score_out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  return index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand, idx_out,
+                    score_out, workspace, ws_bytes, stream, true);
 }
 
 csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, size_t* bytes) {
@@ -362,4 +381,38 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_sparse_mqa launch");
 }
 
+csa_status csa_decode_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t n_h, int32_t c,
+                                int32_t k, size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_decode_workspace: null bytes");
+  size_t a = 0, b = 0;
+  csa_status st = csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &a);
+  if (st != CSA_OK) return st;
+  st = csa_sparse_mqa_workspace(n_queries, n_h, c, k, &b);
+  if (st != CSA_OK) return st;
+  *bytes = align256(a) + b;
+  return CSA_OK;
+}
+
+csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c, int32_t m,
+                      int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp, const void* q,
+                      const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
+                      int64_t max_cand, int32_t* idx_out, float* score_out, void* o, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(q_pos != nullptr || n_queries == 0, "csa_decode: q_pos is required");
+  CSA_REQUIRE(n_h >= 1 && n_hI >= 1 && k >= 1 && n_queries >= 0 && max_cand >= 0, "csa_decode: bad size");
+  size_t need = 0, a = 0;
+  csa_status st = csa_decode_workspace(n_queries, max_cand, n_hI, n_h, c, k, &need);
+  if (st != CSA_OK) return st;
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "csa_decode: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &a);
+  a = align256(a);
+  st = index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand, idx_out,
+                  score_out, workspace, a, stream, false);
+  if (st != CSA_OK) return st;
+  return csa_sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
+                        workspace ? (char*)workspace + a : nullptr, ws_bytes - a, stream);
+}
+
 }  // extern "C"
+

@@ -42,10 +42,11 @@ template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int 
 // Copies ROWS rows of C (row ids in lanes 0..ROWS-1 of `myid`) into LDS rows
 // row0 .. row0+ROWS-1 of Cs (pitch CPITCH elements), using one wave.  A slot
 // with id -1 receives finite filler from `fallback`; its logit is masked to
-// -inf, so it carries zero weight.  Every lane moves 16-byte pieces; up to 16 pieces per lane are loaded
-// before the first is stored, so the whole gather is one or two memory
-// round trips.  For c = 512 bf16 one wave instruction moves one 1 KiB row.
-template <typename T, int CD, int ROWS, int CPITCH>
+// -inf, so it carries zero weight.  Every lane moves 16-byte pieces; up to
+// MAXB pieces per lane are loaded before the first is stored, so the gather
+// takes ceil(pieces / MAXB) memory round trips.  For c = 512 bf16 one wave
+// instruction moves one 1 KiB row.
+template <typename T, int CD, int ROWS, int CPITCH, int MAXB = 16>
 __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, T* Cs, int row0, int lane,
                                             const void* fallback) {
   constexpr int VEC = 16 / sizeof(T);
@@ -53,7 +54,7 @@ __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, 
   if constexpr (LPR <= 64) {
     constexpr int RPI = 64 / LPR;  // rows per instruction
     constexpr int N = (ROWS + RPI - 1) / RPI;
-    constexpr int B = N < 16 ? N : 16;
+    constexpr int B = N < MAXB ? N : MAXB;
     const int sub = lane / LPR, pc = (lane % LPR) * VEC;
     for (int q0 = 0; q0 < N; q0 += B) {
       u32x4 buf[B];
@@ -80,7 +81,7 @@ __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, 
   } else {
     constexpr int IPR = LPR / 64;  // instructions per row
     constexpr int N = ROWS * IPR;
-    constexpr int B = N < 16 ? N : 16;
+    constexpr int B = N < MAXB ? N : MAXB;
     for (int q0 = 0; q0 < N; q0 += B) {
       u32x4 buf[B];
 #pragma unroll
@@ -647,7 +648,8 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
       const int raw = ch == 0 ? raw_first : idx[r * k + (slot < k ? slot : k - 1)];  // always in bounds
       const int myid = (lane < RPW && slot < k) ? raw : -1;
       if (lane < RPW) s_rows[RPW * wave + lane] = myid;
-      wave_gather<bf16_t, CD, RPW, CPITCH>(C + off * CD, myid, Cs, RPW * wave, lane, q);
+      // one wave per SIMD here: all of a wave's rows are in flight at once
+      wave_gather<bf16_t, CD, RPW, CPITCH, RPW>(C + off * CD, myid, Cs, RPW * wave, lane, q);
     }
     __syncthreads();
 
@@ -887,6 +889,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 bool mqa_supported_c(int c) { return c == 64 || c == 128 || c == 256 || c == 512 || c == 1024; }
 
 size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
+  if (n_queries <= 0) return 0;
   const Plan p = plan(n_queries, nh, c, k, bf16);
   if (p.nsplit == 1) return 0;
   return align256((size_t)n_queries * p.nsplit * nh * c * sizeof(float)) +

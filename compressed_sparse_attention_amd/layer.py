@@ -103,33 +103,33 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
 
 
 class DecodeBuffers:
+    """Outputs and the persistent workspace of decode steps of one batch shape."""
+
     def __init__(self, B: int, k: int, nh: int, c: int, nhI: int, max_cand: int, dtype, device):
         self.idx = torch.empty(B, k, dtype=torch.int32, device=device)
         self.scores = torch.empty(B, k, dtype=torch.float32, device=device)
         self.o = torch.empty(B, nh, c, dtype=dtype, device=device)
         self.lse = torch.empty(B, nh, dtype=torch.float32, device=device)
         self.q_seq = torch.arange(B, dtype=torch.int32, device=device)
-        ws_i = api.csa_index_topk_workspace(B, max_cand, nhI, k)
-        ws_m = api.csa_sparse_mqa_workspace(B, nh, c, k)
-        self.ws_index = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=device)
-        self.ws_mqa = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=device)
+        self.shape = (B, max_cand, nhI, nh, c, k)
+        ws = api.csa_decode_workspace(*self.shape)
+        # zero once: every csa_decode call leaves it ready for the next one
+        self.ws = torch.zeros(max(ws, 1), dtype=torch.uint8, device=device)
 
 
 def decode(q, qI, wI, Ccomp, KIcomp, seq_len, kv_offset, m: int, k: int, max_cand: int,
            scale: Optional[float] = None, buf: Optional[DecodeBuffers] = None) -> DecodeBuffers:
-    """One decode step: query b is appended after seq_len[b] tokens of sequence b.
+    """One decode step: query b is appended after seq_len[b] tokens of sequence b (eqs 8, 9, 11).
 
     seq_len, kv_offset: int64 device tensors [B]; max_cand >= max_b floor(seq_len[b]/m).
     """
     B, nh, c = q.shape
     nhI = qI.shape[1]
-    if buf is None:
+    if buf is None or buf.shape != (B, max_cand, nhI, nh, c, k):
         buf = DecodeBuffers(B, k, nh, c, nhI, max_cand, q.dtype, q.device)
-    api.csa_index_topk(qI, wI, KIcomp, m, k, max_cand, buf.idx, score_out=buf.scores, q_seq=buf.q_seq,
-                       q_pos=seq_len, kv_offset=kv_offset, workspace=buf.ws_index)
     sc = 1.0 / math.sqrt(c) if scale is None else scale
-    api.csa_sparse_mqa(q, Ccomp, buf.idx, sc, buf.o, buf.lse, q_seq=buf.q_seq, kv_offset=kv_offset,
-                       workspace=buf.ws_mqa)
+    api.csa_decode(qI, wI, KIcomp, q, Ccomp, m, k, max_cand, sc, seq_len, buf.idx, buf.o, buf.ws, lse=buf.lse,
+                   score_out=buf.scores, q_seq=buf.q_seq, kv_offset=kv_offset)
     return buf
 
 

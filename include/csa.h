@@ -215,6 +215,28 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa_decode -- one decode step for a batch of queries: eqs 8 and 9
+ * (csa_index_topk, per-query sweep) then eq 11 (csa_sparse_mqa) on the
+ * selected entries, in one call.  Arguments are those of the two calls
+ * (q_pos is required; idx_out receives the selection and is then read by
+ * the attention).  Results equal csa_index_topk followed by csa_sparse_mqa.
+ *
+ * Workspace protocol (this is what the call saves over the two-call
+ * sequence): the workspace must be zero-filled before its first use and
+ * again whenever n_queries, max_cand or k change; every call leaves the
+ * parts that must start at zero (score histograms, arrival counters) zero
+ * again, so back-to-back calls need no clearing pass.  Calls that share a
+ * workspace must not overlap.
+ */
+csa_status csa_decode_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t n_h, int32_t c,
+                                int32_t k, size_t* bytes);
+csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c, int32_t m,
+                      int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp, const void* q,
+                      const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
+                      int64_t max_cand, int32_t* idx_out, float* score_out, void* o, float* lse, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (instrumentation, off by default).  While enabled, every
  * kernel the library launches is bracketed by a pair of HIP events recorded
  * on the launch stream.  csa_timing_read synchronises on the recorded events

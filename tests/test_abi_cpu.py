@@ -81,6 +81,22 @@ def test_compress_append_rejects_bad_args(L):
     assert call(B=0, new=None, ring=None) == api.CSA_OK  # no sequences: nothing enqueued
 
 
+def test_decode_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def call(nq=2, q_pos=p, ws=p, wsb=1 << 30, k=64, c=128):
+        return L.csa_decode(1, nq, 8, 64, 16, c, 4, k, 0.1, p, p, p, p, p, None, q_pos, None, 1000, p, None, p, None,
+                            ws, wsb, None)
+    assert call(q_pos=None) == api.CSA_ERR_INVALID_ARG
+    assert "q_pos" in _err()
+    assert call(k=0) == api.CSA_ERR_INVALID_ARG
+    assert call(wsb=10) == api.CSA_ERR_WORKSPACE
+    assert call(ws=None) == api.CSA_ERR_WORKSPACE
+    assert call(nq=0, q_pos=None) == api.CSA_OK  # empty batch: nothing enqueued
+    assert api.csa_decode_workspace(2, 1000, 8, 16, 128, 64) >= api.csa_index_topk_workspace(2, 1000, 8, 64)
+    assert api.csa_sparse_mqa_workspace(0, 64, 512, 1024) == 0  # an empty batch needs no workspace
+
+
 def test_index_topk_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
     args = dict(dt=1, nq=4, nhI=64, cI=128, m=4, k=16, qI=p, wI=p, K=p, seq=None, pos=None, off=None,

@@ -355,3 +355,65 @@ def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
             assert np.all(np.isneginf(got))
         else:
             assert np.allclose(got, rl, rtol=1e-3, atol=1e-3)
+
+
+# ---------------------------------------------------------------------------
+# csa_decode: eqs 8, 9 and 11 in one call with a persistent workspace
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("lens,nq_rep,nhI,cI,nh,c,k", [
+    # per-chunk selector (long rows), a short row, an empty row
+    ([4 * 9000, 4 * 20000, 4 * 33000, 100, 0, 4 * 5000], 1, 8, 64, 16, 128, 512),
+    # 520 long rows of one sequence: one workgroup per row from the sweep's histogram
+    ([4 * 9100], 520, 2, 32, 4, 64, 300),
+])
+def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k):
+    """Three back-to-back csa_decode calls on one workspace (zeroed once), each with new queries, give
+    exactly the results of csa_index_topk (fresh workspace) followed by csa_sparse_mqa: the calls leave
+    the histogram and counters zero for the next one."""
+    rng = synth.rng_for(sum(lens) + nq_rep)
+    m = 4
+    if nq_rep > 1:  # many queries at different positions of one sequence
+        nb = lens[0] // m
+        pos = rng.integers(4 * 8200, 4 * nb + 1, size=nq_rep).astype(np.int64)
+        off = np.zeros(1, np.int64)
+        q_seq = torch.zeros(nq_rep, dtype=torch.int32, device=DEV)
+        rows = nb
+    else:
+        pos = np.asarray(lens, np.int64)
+        nblk = pos // m
+        off = np.zeros_like(nblk)
+        off[1:] = np.cumsum(nblk)[:-1]
+        q_seq = torch.arange(len(lens), dtype=torch.int32, device=DEV)
+        rows = max(int(nblk.sum()), 1)
+    B = len(pos)
+    max_cand = int(pos.max() // m)
+    K = to_device(draw(rng, (rows, cI), 1.0, "bf16"), "bf16", DEV)
+    C = to_device(draw(rng, (rows, c), 1.0, "bf16"), "bf16", DEV)
+    q_pos = torch.tensor(pos, device=DEV)
+    kv_off = torch.tensor(off, device=DEV)
+    ws = torch.zeros(api.csa_decode_workspace(B, max_cand, nhI, nh, c, k), dtype=torch.uint8, device=DEV)
+    scale = 1.0 / math.sqrt(c)
+    for call in range(3):
+        qI = to_device(draw(rng, (B, nhI, cI), 1.0 / math.sqrt(cI), "bf16"), "bf16", DEV)
+        wI = to_device(rng.standard_normal((B, nhI), dtype=np.float32), "f32", DEV)
+        q = to_device(draw(rng, (B, nh, c), 4.0 / math.sqrt(c), "bf16"), "bf16", DEV)
+        idx1 = torch.full((B, k), 7, dtype=torch.int32, device=DEV)
+        sc1 = torch.empty(B, k, device=DEV)
+        o1 = torch.empty(B, nh, c, dtype=torch.bfloat16, device=DEV)
+        lse1 = torch.empty(B, nh, device=DEV)
+        api.csa_decode(qI, wI, K, q, C, m, k, max_cand, scale, q_pos, idx1, o1, ws, lse=lse1, score_out=sc1,
+                       q_seq=q_seq, kv_offset=kv_off)
+        idx2 = torch.full((B, k), 9, dtype=torch.int32, device=DEV)
+        sc2 = torch.empty(B, k, device=DEV)
+        o2 = torch.empty(B, nh, c, dtype=torch.bfloat16, device=DEV)
+        lse2 = torch.empty(B, nh, device=DEV)
+        api.csa_index_topk(qI, wI, K, m, k, max_cand, idx2, score_out=sc2, q_seq=q_seq, q_pos=q_pos, kv_offset=kv_off)
+        api.csa_sparse_mqa(q, C, idx2, scale, o2, lse2, q_seq=q_seq, kv_offset=kv_off)
+        torch.cuda.synchronize()
+        assert torch.equal(idx1, idx2), f"call {call}: selections differ"
+        assert torch.equal(sc1, sc2) and torch.equal(o1, o2) and torch.equal(lse1, lse2), f"call {call}"
+    if nq_rep == 1:  # the selection itself is the oracle's
+        Kn = K.view(torch.int16).cpu().numpy().view(np.uint16)
+        qn = qI.view(torch.int16).cpu().numpy().view(np.uint16)
+        srows = _oracle_rows(qn, wI.cpu().numpy(), Kn, pos, off, m, "bf16")
+        check_topk(idx1.cpu().numpy(), srows, k)
