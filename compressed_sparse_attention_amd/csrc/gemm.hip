@@ -253,7 +253,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 // traffic.  A 256-thread workgroup owns 16 output columns over all of K; its
 // four waves split K and stream their share of the 16 weight rows straight
 // from HBM into MFMA operands (the rows of X, read from L2, are the other
-// operand; rows past M produce outputs that are not written), two 128-deep
+// operand; rows past M produce outputs that are not written), DEPTH 128-deep
 // super-steps in flight per wave.  Within a super-step lane group g covers
 // k = 32 g .. 32 g + 31 of both operands, so each lane reads 64 contiguous
 // bytes of its row.  The four partial 16x16 tiles are summed through LDS.
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 constexpr int kSmN = 16;        // output columns per workgroup
 constexpr int kSmSuper = 128;   // k per super-step
 
-template <typename TO>
+template <typename TO, int DEPTH>
 __global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, const bf16_t* __restrict__ X, long ldx,
                                                           const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y,
                                                           long ldy) {
@@ -277,16 +277,18 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, c
   const bf16_t* Wr = W + wrow * ldw + 32 * g;
   const bf16_t* Xr = X + xrow * ldx + 32 * g;
 
-  Frag<bf16_t> wb[2][4], xb[2][4];
-  // Loads of super-step ss into slot; pieces past K, and super-steps past this
-  // wave's range, read filler from the start of the operands (never used).
+  Frag<bf16_t> wb[DEPTH][4], xb[DEPTH][4];
+  // Loads of super-step ss into slot.  Super-steps past this wave's range are
+  // not fetched (a uniform branch; filler loads there would all hit one
+  // address); pieces past K read the start of the lane's own rows (never used).
   auto issue = [&](int ss, int slot) {
+    if (ss >= s1) return;
     const long k = (long)ss * kSmSuper;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bool ok = ss < s1 && k + 32 * g + 8 * kk < K;  // K % 8 == 0: a piece is all in or all out
-      wb[slot][kk].load_clamped(Wr + k + 8 * kk, ok, W);
-      xb[slot][kk].load_clamped(Xr + k + 8 * kk, ok, X);
+      const bool ok = k + 32 * g + 8 * kk < K;  // K % 8 == 0: a piece is all in or all out
+      wb[slot][kk].load_clamped(Wr + k + 8 * kk, ok, Wr);
+      xb[slot][kk].load_clamped(Xr + k + 8 * kk, ok, Xr);
     }
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -300,16 +302,16 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, c
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) mma(acc, xb[slot][kk], wb[slot][kk]);
   };
-  issue(s0, 0);
-  issue(s0 + 1, 1);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) issue(s0 + d, d);
   issue_fence();
-  for (int ss = s0; ss < s1; ss += 2) {
-    compute(ss, 0);
-    issue(ss + 2, 0);
-    issue_fence();
-    if (ss + 1 < s1) compute(ss + 1, 1);
-    issue(ss + 3, 1);
-    issue_fence();
+  for (int ss = s0; ss < s1; ss += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (ss + d < s1) compute(ss + d, d);
+      issue(ss + d + DEPTH, d);
+      issue_fence();
+    }
   }
   // acc[r] = partial of Y[4 g + r][n0 + c16]
   if (wave > 0) {
@@ -333,12 +335,19 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, c
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s) {
   if (in_dt == CSA_BF16 && M <= 16) {
+    // all of a wave's super-steps in flight when K is short (measured: up to
+    // 8% faster at K = 1536), two otherwise
     const dim3 grid1((unsigned)((N + kSmN - 1) / kSmN));
+    const bool deep = K <= 2048;
     if (out_dt == CSA_BF16)
-      return launch("gemm_smallm", gemm_smallm_kernel<bf16_t>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
-                    (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
-    return launch("gemm_smallm", gemm_smallm_kernel<float>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
-                  (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
+      return deep ? launch("gemm_smallm", gemm_smallm_kernel<bf16_t, 4>, grid1, dim3(256), 0, s, (int)M, (int)N,
+                           (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy)
+                  : launch("gemm_smallm", gemm_smallm_kernel<bf16_t, 2>, grid1, dim3(256), 0, s, (int)M, (int)N,
+                           (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
+    return deep ? launch("gemm_smallm", gemm_smallm_kernel<float, 4>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                         (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy)
+                : launch("gemm_smallm", gemm_smallm_kernel<float, 2>, grid1, dim3(256), 0, s, (int)M, (int)N, (int)K,
+                         (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
   }
   if (in_dt == CSA_BF16 && M >= kG2M && N >= kG2N && N % 4 == 0) {
     const int tm = (int)((M + kG2M - 1) / kG2M), tn = (int)((N + kG2N - 1) / kG2N);
