@@ -48,6 +48,11 @@ _SIGS = {
     "csa_sparse_mqa_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_sparse_mqa": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _sz, _vp]),
+    "csa_compress_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
+                                           _vp, _i64, _vp, _i64, _vp]),
+    "csa_index_topk_varlen_workspace": (ctypes.c_int, [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
+    "csa_index_topk_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                             _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_decode_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_decode": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -254,6 +259,68 @@ def csa_sparse_mqa(q, Ccomp, idx, scale: float, o, lse=None, q_seq=None, kv_offs
                                 workspace.numel() * workspace.element_size(), _stream(q.device)),
            "csa_sparse_mqa")
     return o
+
+
+def csa_compress_varlen(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens, block_offset, n_blocks: int, Ccomp):
+    """Eqs 3-4 for packed sequences: sequence b's rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the [n, c] column
+    slices Ca/Cb/Za/Zb (one shared leading dimension) -> Ccomp rows block_offset[b] .. block_offset[b+1]-1."""
+    c = Ca.shape[1]
+    ld = _rowmajor(Ca, "Ca")
+    for t, nm in ((Cb, "Cb"), (Za, "Za"), (Zb, "Zb")):
+        if _rowmajor(t, nm) != ld or tuple(t.shape) != tuple(Ca.shape) or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress_varlen: Ca, Cb, Za, Zb must share shape, dtype and row stride")
+    for t, nm in ((Ba, "Ba"), (Bb, "Bb")):
+        _contig(t, nm)
+        if tuple(t.shape) != (m, c) or t.dtype != Ca.dtype:
+            raise CSAError(f"csa_compress_varlen: {nm} must be [m, c] of Ca's dtype")
+    nseq = cu_seqlens.numel() - 1
+    for t, nm in ((cu_seqlens, "cu_seqlens"), (block_offset, "block_offset")):
+        if t.dtype != torch.int64 or t.numel() != nseq + 1:
+            raise CSAError(f"csa_compress_varlen: {nm} must be int64 [n_seqs + 1]")
+    if Ccomp.shape[0] < n_blocks or Ccomp.shape[1] != c or Ccomp.dtype != Ca.dtype:
+        raise CSAError("csa_compress_varlen: Ccomp must be [>= n_blocks, c] of Ca's dtype")
+    _check(lib().csa_compress_varlen(_dt(Ca), nseq, m, c, _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _ptr(Ba),
+                                     _ptr(Bb), _ptr(cu_seqlens), _ptr(block_offset), n_blocks, _ptr(Ccomp),
+                                     _rowmajor(Ccomp, "Ccomp"), _stream(Ca.device)),
+           "csa_compress_varlen")
+    return Ccomp
+
+
+def csa_index_topk_varlen_workspace(n_seqs: int, n_tokens: int, max_cand: int, k: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_index_topk_varlen_workspace(n_seqs, n_tokens, max_cand, k, ctypes.byref(b)),
+           "csa_index_topk_varlen_workspace")
+    return b.value
+
+
+def csa_index_topk_varlen(qI, wI, KIcomp, m: int, k: int, max_cand: int, cu_seqlens, kv_offset, idx_out,
+                          score_out=None, q_seq_out=None, workspace=None):
+    """Eqs 8-9 for every token of packed sequences.  qI [n, n_hI, cI], wI [n, n_hI] fp32 -> idx_out [n, k]."""
+    n, nhI, cI = qI.shape
+    for t, nm in ((qI, "qI"), (wI, "wI"), (KIcomp, "KIcomp"), (idx_out, "idx_out")):
+        _contig(t, nm)
+    if wI.dtype != torch.float32 or tuple(wI.shape) != (n, nhI):
+        raise CSAError("csa_index_topk_varlen: wI must be fp32 [n_tokens, n_hI]")
+    if idx_out.dtype != torch.int32 or tuple(idx_out.shape) != (n, k):
+        raise CSAError("csa_index_topk_varlen: idx_out must be int32 [n_tokens, k]")
+    if score_out is not None:
+        _contig(score_out, "score_out")
+        if score_out.dtype != torch.float32 or tuple(score_out.shape) != (n, k):
+            raise CSAError("csa_index_topk_varlen: score_out must be fp32 [n_tokens, k]")
+    if q_seq_out is not None and (q_seq_out.dtype != torch.int32 or q_seq_out.numel() != n):
+        raise CSAError("csa_index_topk_varlen: q_seq_out must be int32 [n_tokens]")
+    nseq = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int64 or kv_offset.dtype != torch.int64 or kv_offset.numel() < nseq:
+        raise CSAError("csa_index_topk_varlen: cu_seqlens [n_seqs + 1] and kv_offset [>= n_seqs] must be int64")
+    need = csa_index_topk_varlen_workspace(nseq, n, max_cand, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qI.device)
+    _check(lib().csa_index_topk_varlen(_dt(qI), nseq, n, nhI, cI, m, k, _ptr(qI), _ptr(wI), _ptr(KIcomp),
+                                       _ptr(cu_seqlens), _ptr(kv_offset), max_cand, _ptr(idx_out), _ptr(score_out),
+                                       _ptr(q_seq_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(qI.device)),
+           "csa_index_topk_varlen")
+    return idx_out
 
 
 def csa_decode_workspace(n_queries: int, max_cand: int, n_hI: int, n_h: int, c: int, k: int) -> int:

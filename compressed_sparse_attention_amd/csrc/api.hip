@@ -414,5 +414,86 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
                         workspace ? (char*)workspace + a : nullptr, ws_bytes - a, stream);
 }
 
+csa_status csa_compress_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca, const void* Cb,
+                               const void* Za, const void* Zb, int64_t ld_in, const void* Ba, const void* Bb,
+                               const int64_t* cu_seqlens, const int64_t* block_offset, int64_t n_blocks, void* Ccomp,
+                               int64_t ld_out, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress_varlen: unknown dtype");
+  CSA_REQUIRE(n_seqs >= 0 && n_seqs <= 0x7FFFFFFF && n_blocks >= 0, "csa_compress_varlen: bad n_seqs / n_blocks");
+  CSA_REQUIRE(m >= 1, "csa_compress_varlen: m must be >= 1 (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_varlen: c must be a positive multiple of 4 (got %d)", c);
+  if (n_seqs == 0 || n_blocks == 0) return CSA_OK;
+  CSA_REQUIRE(Ca && Cb && Za && Zb && Ba && Bb && cu_seqlens && block_offset && Ccomp,
+              "csa_compress_varlen: null pointer");
+  CSA_REQUIRE(aligned16(Ca) && aligned16(Cb) && aligned16(Za) && aligned16(Zb) && aligned16(Ba) && aligned16(Bb) &&
+                  aligned16(Ccomp),
+              "csa_compress_varlen: pointers must be 16-byte aligned");
+  const int v = vec_elems(dt);
+  CSA_REQUIRE(ld_in >= c && ld_out >= c, "csa_compress_varlen: leading dimension too small");
+  CSA_REQUIRE(ld_in % v == 0 && ld_out % v == 0,
+              "csa_compress_varlen: leading dimensions must keep rows 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_compress_varlen(dt, n_seqs, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, cu_seqlens,
+                                             block_offset, n_blocks, Ccomp, ld_out, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_varlen launch");
+}
+
+// Workspace of csa_index_topk_varlen (each area 256-byte aligned): scores
+// [n_tokens, scores_ld] fp32, q_pos [n_tokens] int64, q_seq [n_tokens] int32,
+// block table [n_seqs + 1] int32.
+csa_status csa_index_topk_varlen_workspace(int64_t n_seqs, int64_t n_tokens, int64_t max_cand, int32_t k,
+                                           size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_index_topk_varlen_workspace: null bytes");
+  CSA_REQUIRE(n_seqs >= 0 && n_tokens >= 0 && max_cand >= 0 && k >= 1, "csa_index_topk_varlen_workspace: bad size");
+  *bytes = align256((size_t)n_tokens * scores_ld(max_cand) * sizeof(float)) +
+           align256((size_t)n_tokens * sizeof(int64_t)) + align256((size_t)n_tokens * sizeof(int32_t)) +
+           align256((size_t)(n_seqs + 1) * sizeof(int32_t));
+  return CSA_OK;
+}
+
+csa_status csa_index_topk_varlen(csa_dtype dt, int64_t n_seqs, int64_t n_tokens, int32_t n_hI, int32_t cI, int32_t m,
+                                 int32_t k, const void* qI, const float* wI, const void* KIcomp,
+                                 const int64_t* cu_seqlens, const int64_t* kv_offset, int64_t max_cand,
+                                 int32_t* idx_out, float* score_out, int32_t* q_seq_out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_index_topk_varlen: unknown dtype");
+  CSA_REQUIRE(n_seqs >= 0 && n_seqs <= 0x7FFFFFFF && n_tokens >= 0 && n_tokens <= 0x7FFFFFFF,
+              "csa_index_topk_varlen: bad n_seqs / n_tokens");
+  CSA_REQUIRE(n_hI >= 1 && n_hI <= 64, "csa_index_topk_varlen: n_hI must be in [1, 64] (got %d)", n_hI);
+  CSA_REQUIRE(cI == 32 || cI == 64 || cI == 128 || cI == 256,
+              "csa_index_topk_varlen: cI must be 32, 64, 128 or 256 (got %d)", cI);
+  CSA_REQUIRE(m >= 1, "csa_index_topk_varlen: m must be >= 1");
+  CSA_REQUIRE(k >= 1 && k <= (1 << 24), "csa_index_topk_varlen: k must be in [1, 2^24]");
+  CSA_REQUIRE(max_cand >= 0 && max_cand <= 0x7FFFFFFF, "csa_index_topk_varlen: bad max_cand");
+  if (n_tokens == 0) return CSA_OK;
+  CSA_REQUIRE(n_seqs >= 1, "csa_index_topk_varlen: tokens without sequences");
+  CSA_REQUIRE(qI && wI && KIcomp && idx_out && cu_seqlens && kv_offset, "csa_index_topk_varlen: null pointer");
+  CSA_REQUIRE(aligned16(qI) && aligned16(wI) && aligned16(KIcomp) && aligned16(idx_out),
+              "csa_index_topk_varlen: pointers must be 16-byte aligned");
+  size_t need = 0;
+  csa_index_topk_varlen_workspace(n_seqs, n_tokens, max_cand, k, &need);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "csa_index_topk_varlen: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  CSA_REQUIRE(aligned16(workspace), "csa_index_topk_varlen: workspace must be 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const long ld = scores_ld(max_cand);
+  float* scores = (float*)ws;
+  size_t at = align256((size_t)n_tokens * ld * sizeof(float));
+  int64_t* q_pos = (int64_t*)(ws + at);
+  at += align256((size_t)n_tokens * sizeof(int64_t));
+  int32_t* q_seq = q_seq_out ? q_seq_out : (int32_t*)(ws + at);
+  at += align256((size_t)n_tokens * sizeof(int32_t));
+  int32_t* blk = (int32_t*)(ws + at);
+  hipError_t e = csa::launch_indexer_varlen(dt, n_seqs, n_tokens, n_hI, cI, m, qI, wI, KIcomp, cu_seqlens, kv_offset,
+                                            max_cand, scores, ld, blk, q_pos, q_seq, s);
+  if (e != hipSuccess) return hip_fail(e, "csa_index_topk_varlen indexer launch");
+  e = csa::launch_topk(n_tokens, m, scores, ld, q_pos, max_cand, k, nullptr, nullptr, idx_out, score_out, s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk_varlen top-k launch");
+}
+
 }  // extern "C"
 

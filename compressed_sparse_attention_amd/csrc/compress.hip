@@ -1,5 +1,7 @@
 // Softmax-gated overlapping compression, eqs 3-4 of "Compressed Sparse
-// Attention" (section "Compressed Key-Value Entries").
+// Attention" (section "Compressed Key-Value Entries"), for one sequence, for
+// several packed sequences (each compressed on its own, blocks never span two
+// sequences), and the decode-time append.
 //
 // One thread owns one block i and V adjacent channels.  It streams the 2m
 // (logit, value) pairs of its block -- rows m*i .. m*i+m-1 of Z^a/C^a and,
@@ -65,12 +67,26 @@ __global__ __launch_bounds__(256) void compress_kernel(long nblk, int m, int c,
                                                        const T* __restrict__ Zb, long ld,
                                                        const T* __restrict__ Ba,
                                                        const T* __restrict__ Bb, T* __restrict__ out,
-                                                       long ldo) {
+                                                       long ldo, int nseq, const int64_t* __restrict__ cu,
+                                                       const int64_t* __restrict__ boff) {
   const int groups = c / V;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long i = gid / groups;
+  const long i = gid / groups;  // output row
   if (i >= nblk) return;
   const int ch = (int)(gid - i * groups) * V;
+  // Several sequences (cu set): output row i is block il of the sequence b
+  // with boff[b] <= i < boff[b+1]; that sequence's tokens start at row cu[b]
+  // of the projections, and its block 0 has no b-terms.
+  long il = i, rbase = 0;
+  if (cu != nullptr) {
+    int lo = 0, hi = nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (boff[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    il = i - boff[lo];
+    rbase = cu[lo];
+  }
 
   float mx[V], den[V], acc[V];
   // Online softmax over the 2m pairs; logits are carried in log2 units.
@@ -98,12 +114,12 @@ __global__ __launch_bounds__(256) void compress_kernel(long nblk, int m, int c,
   };
 
   for (int r = 0; r < m; ++r) {
-    const long row = i * m + r;
+    const long row = rbase + il * m + r;
     absorb(Za + row * ld + ch, Ca + row * ld + ch, Ba + (long)r * c + ch, r == 0);
   }
-  if (i > 0) {
+  if (il > 0) {
     for (int r = 0; r < m; ++r) {
-      const long row = (i - 1) * m + r;
+      const long row = rbase + (il - 1) * m + r;
       absorb(Zb + row * ld + ch, Cb + row * ld + ch, Bb + (long)r * c + ch, false);
     }
   }
@@ -181,11 +197,23 @@ __global__ __launch_bounds__(256) void compress_append_kernel(int m, int c, cons
 template <typename T, int V>
 hipError_t run(long nblk, int m, int c, const void* Ca, const void* Cb, const void* Za,
                const void* Zb, long ld, const void* Ba, const void* Bb, void* out, long ldo,
-               hipStream_t s) {
+               int nseq, const int64_t* cu, const int64_t* boff, hipStream_t s) {
   const long threads = nblk * (c / V);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   return launch("compress", compress_kernel<T, V>, dim3(blocks), dim3(256), 0, s, nblk, m, c, (const T*)Ca,
-                (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba, (const T*)Bb, (T*)out, ldo);
+                (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba, (const T*)Bb, (T*)out, ldo, nseq, cu,
+                boff);
+}
+
+hipError_t dispatch(csa_dtype dt, long nblk, int m, int c, const void* Ca, const void* Cb, const void* Za,
+                    const void* Zb, long ld_in, const void* Ba, const void* Bb, void* out, long ld_out, int nseq,
+                    const int64_t* cu, const int64_t* boff, hipStream_t s) {
+  if (nblk == 0) return hipSuccess;
+  if (dt == CSA_F32)
+    return run<float, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, nseq, cu, boff, s);
+  if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
+    return run<bf16_t, 8>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, nseq, cu, boff, s);
+  return run<bf16_t, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, nseq, cu, boff, s);
 }
 
 }  // namespace
@@ -193,12 +221,15 @@ hipError_t run(long nblk, int m, int c, const void* Ca, const void* Cb, const vo
 hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
                            const void* Za, const void* Zb, long ld_in, const void* Ba,
                            const void* Bb, void* out, long ld_out, hipStream_t s) {
-  const long nblk = n / m;
-  if (nblk == 0) return hipSuccess;
-  if (dt == CSA_F32) return run<float, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
-  if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
-    return run<bf16_t, 8>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
-  return run<bf16_t, 4>(nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, s);
+  return dispatch(dt, n / m, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, 0, nullptr, nullptr, s);
+}
+
+hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const void* Ca, const void* Cb,
+                                  const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
+                                  const int64_t* cu, const int64_t* boff, long nblk, void* out, long ld_out,
+                                  hipStream_t s) {
+  if (nseq == 0) return hipSuccess;
+  return dispatch(dt, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, (int)nseq, cu, boff, s);
 }
 
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,

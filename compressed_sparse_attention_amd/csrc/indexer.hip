@@ -27,6 +27,7 @@
 //    Heaviest token blocks first.
 #include "common.hpp"
 #include "internal.hpp"
+#include "select.hpp"
 #include "sweep.hpp"
 
 namespace csa {
@@ -68,7 +69,9 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
                                                               const int64_t* __restrict__ kv_off,
                                                               long max_cand,
                                                               float* __restrict__ scores,
-                                                              long ld_sc) {
+                                                              long ld_sc, int nseq,
+                                                              const int64_t* __restrict__ cu,
+                                                              const int32_t* __restrict__ blk) {
   constexpr int kPfWaves = pf_waves<T, KK, NHT>();
   constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
   // keys per LDS tile: 128 (measured faster than 64) while two tiles of key
@@ -84,12 +87,34 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int nblocks = (n + kPfTokens - 1) / kPfTokens;
-  const long t0 = (long)(nblocks - 1 - (int)blockIdx.x) * kPfTokens;  // heaviest first
+  // Token block of this workgroup: positions p0 .. p0+kPfTokens-1 of one
+  // sequence of length len, whose rows start at row0 and keys at kbase.
+  // One sequence: the blocks in reverse order (heaviest first).  Several
+  // (cu set): blk[b] .. blk[b+1]-1 are sequence b's blocks; the grid may hold
+  // more workgroups than blocks.
+  long p0, len, row0 = 0, kbase = kv_off ? kv_off[0] : 0;
+  if (cu == nullptr) {
+    const int nblocks = (n + kPfTokens - 1) / kPfTokens;
+    p0 = (long)(nblocks - 1 - (int)blockIdx.x) * kPfTokens;
+    len = n;
+  } else {
+    const int total = blk[nseq];
+    if ((int)blockIdx.x >= total) return;
+    const int j = total - 1 - (int)blockIdx.x;
+    int lo = 0, hi = nseq - 1;  // the sequence b with blk[b] <= j < blk[b+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (blk[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    p0 = (long)(j - blk[lo]) * kPfTokens;
+    row0 = cu[lo];
+    len = cu[lo + 1] - row0;
+    kbase = kv_off[lo];
+  }
 
   // candidate count of the last token of this block bounds the key range
-  const long t_last = min(t0 + kPfTokens - 1, (long)n - 1);
-  long kend = t_last / m;
+  const long p_last = min(p0 + kPfTokens - 1, len - 1);
+  long kend = p_last / m;
   kend = kend < max_cand ? kend : max_cand;
   if (kend <= 0) return;
 
@@ -98,11 +123,12 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
   long tok[kPfTokPerWave], nc[kPfTokPerWave];
 #pragma unroll
   for (int tt = 0; tt < kPfTokPerWave; ++tt) {
-    const long t = t0 + wave * kPfTokPerWave + tt;
+    const long pos = p0 + wave * kPfTokPerWave + tt;
+    const bool live = pos < len;
+    const long t = row0 + (live ? pos : 0);  // the token's row in qI / wI / scores
     tok[tt] = t;
-    long c = t < n ? t / m : 0;
+    long c = live ? pos / m : 0;
     nc[tt] = c < max_cand ? c : max_cand;
-    const bool live = t < n;
 #pragma unroll
     for (int mt = 0; mt < NHT; ++mt) {
       const int head = 16 * mt + c16;
@@ -117,7 +143,7 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
     }
   }
 
-  if (kv_off) K += kv_off[0] * CI;
+  K += kbase * CI;
   const int ntiles = (int)((kend + kPfTile - 1) / kPfTile);
   constexpr int LOADS = (TILE_VECS + 64 * kPfWaves - 1) / (64 * kPfWaves);
   u32x4 stage[LOADS];
@@ -171,6 +197,88 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed sequences: per-token sequence and position, and the tiled kernel's
+// block table blk[b] = sum over b' < b of ceil(len_b' / wtok) (blk[nseq] =
+// total), from cu (the sequences' first rows, cu[nseq] = total tokens).
+// Workgroup 0 also builds the table.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void varlen_meta_kernel(int nseq, const int64_t* __restrict__ cu, long ntok, int wtok,
+                                                          int32_t* __restrict__ blk, int64_t* __restrict__ q_pos,
+                                                          int32_t* __restrict__ q_seq) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t < ntok) {
+    int lo = 0, hi = nseq - 1;  // the last sequence starting at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    q_pos[t] = t - cu[lo];
+    q_seq[t] = lo;
+  }
+  if (blockIdx.x == 0) {
+    __shared__ uint32_t s_wave[4];
+    uint32_t run = 0;
+    for (int b0 = 0; b0 < nseq; b0 += 256) {
+      const int b = b0 + (int)threadIdx.x;
+      const uint32_t v = b < nseq ? (uint32_t)((cu[b + 1] - cu[b] + wtok - 1) / wtok) : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_excl_scan<256>(v, s_wave, tot);
+      if (b < nseq) blk[b] = (int32_t)(run + ex);
+      run += tot;
+    }
+    if (threadIdx.x == 0) blk[nseq] = (int32_t)run;
+  }
+}
+
+template <typename T, int KK, int NHT>
+hipError_t run_varlen(long nseq, long ntok, int nhI, int m, const void* qI, const float* wI, const void* K,
+                      const int64_t* cu, const int32_t* blk, const int64_t* kv_off, long max_cand, float* scores,
+                      long ld_sc, hipStream_t s) {
+  constexpr int waves = pf_waves<T, KK, NHT>();
+  // every sequence adds at most one partly filled block; surplus workgroups exit
+  const long grid = (ntok + waves - 1) / waves + nseq;
+  return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3((unsigned)grid), dim3(64 * waves), 0, s,
+                (int)ntok, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc, (int)nseq, cu,
+                blk);
+}
+
+template <typename T>
+int waves_of(int nhI, int cI) {
+  const int nht = (nhI + 15) / 16;
+  switch (cI / 32) {
+    case 1: return nht == 1 ? pf_waves<T, 1, 1>() : nht == 2 ? pf_waves<T, 1, 2>() : nht == 3 ? pf_waves<T, 1, 3>() : pf_waves<T, 1, 4>();
+    case 2: return nht == 1 ? pf_waves<T, 2, 1>() : nht == 2 ? pf_waves<T, 2, 2>() : nht == 3 ? pf_waves<T, 2, 3>() : pf_waves<T, 2, 4>();
+    case 4: return nht == 1 ? pf_waves<T, 4, 1>() : nht == 2 ? pf_waves<T, 4, 2>() : nht == 3 ? pf_waves<T, 4, 3>() : pf_waves<T, 4, 4>();
+    default: return nht == 1 ? pf_waves<T, 8, 1>() : nht == 2 ? pf_waves<T, 8, 2>() : nht == 3 ? pf_waves<T, 8, 3>() : pf_waves<T, 8, 4>();
+  }
+}
+
+template <typename T, int KK>
+hipError_t varlen_nht(long nseq, long ntok, int nhI, int m, const void* qI, const float* wI, const void* K,
+                      const int64_t* cu, const int32_t* blk, const int64_t* kv_off, long max_cand, float* scores,
+                      long ld_sc, hipStream_t s) {
+  switch ((nhI + 15) / 16) {
+    case 1: return run_varlen<T, KK, 1>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    case 2: return run_varlen<T, KK, 2>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    case 3: return run_varlen<T, KK, 3>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    default: return run_varlen<T, KK, 4>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+  }
+}
+
+template <typename T>
+hipError_t varlen_kk(long nseq, long ntok, int nhI, int cI, int m, const void* qI, const float* wI, const void* K,
+                     const int64_t* cu, const int32_t* blk, const int64_t* kv_off, long max_cand, float* scores,
+                     long ld_sc, hipStream_t s) {
+  switch (cI / 32) {
+    case 1: return varlen_nht<T, 1>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    case 2: return varlen_nht<T, 2>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    case 4: return varlen_nht<T, 4>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    case 8: return varlen_nht<T, 8>(nseq, ntok, nhI, m, qI, wI, K, cu, blk, kv_off, max_cand, scores, ld_sc, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int KK, int NHT>
 hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const void* K,
                const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_off, long max_cand,
@@ -179,7 +287,8 @@ hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const v
     constexpr int waves = pf_waves<T, KK, NHT>();
     const int nblocks = (int)((nq + waves * kPfTokPerWave - 1) / (waves * kPfTokPerWave));
     return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3(nblocks), dim3(64 * waves), 0, s,
-                  (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc);
+                  (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc, 0,
+                  (const int64_t*)nullptr, (const int32_t*)nullptr);
   } else {
     const unsigned chunks = (unsigned)((max_cand + kSweepKeysPerWG - 1) / kSweepKeysPerWG);
     return launch("indexer_sweep", indexer_sweep_kernel<T, KK, NHT>, dim3(chunks * (unsigned)nq),
@@ -226,6 +335,20 @@ hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, 
                           scores, ld_sc, hist, hist_min, s);
   return pick_kk<bf16_t>(n_queries, nhI, cI, m, qI, wI, K, q_seq, q_pos, kv_offset, max_cand,
                          scores, ld_sc, hist, hist_min, s);
+}
+
+hipError_t launch_indexer_varlen(csa_dtype dt, long nseq, long ntok, int nhI, int cI, int m, const void* qI,
+                                 const float* wI, const void* K, const int64_t* cu, const int64_t* kv_offset,
+                                 long max_cand, float* scores, long ld_sc, int32_t* blk, int64_t* q_pos,
+                                 int32_t* q_seq, hipStream_t s) {
+  if (nseq == 0 || ntok == 0) return hipSuccess;
+  const int wtok = dt == CSA_F32 ? waves_of<float>(nhI, cI) : waves_of<bf16_t>(nhI, cI);
+  hipError_t e = launch("varlen_meta", varlen_meta_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, s,
+                        (int)nseq, cu, ntok, wtok, blk, q_pos, q_seq);
+  if (e != hipSuccess || max_cand == 0) return e;
+  if (dt == CSA_F32)
+    return varlen_kk<float>(nseq, ntok, nhI, cI, m, qI, wI, K, cu, blk, kv_offset, max_cand, scores, ld_sc, s);
+  return varlen_kk<bf16_t>(nseq, ntok, nhI, cI, m, qI, wI, K, cu, blk, kv_offset, max_cand, scores, ld_sc, s);
 }
 
 }  // namespace csa

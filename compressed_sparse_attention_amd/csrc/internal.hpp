@@ -41,6 +41,13 @@ hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, c
                            const void* Za, const void* Zb, long ld_in, const void* Ba,
                            const void* Bb, void* out, long ld_out, hipStream_t s);
 
+// Packed sequences: sequence b's projected rows start at cu[b]; its blocks go
+// to output rows boff[b] .. boff[b+1]-1 (nblk = boff[nseq] in total).
+hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const void* Ca, const void* Cb,
+                                  const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
+                                  const int64_t* cu, const int64_t* boff, long nblk, void* out, long ld_out,
+                                  hipStream_t s);
+
 // Decode-time append (one new token per sequence); see csa_compress_append.
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,
                                   const void* Ba, const void* Bb, const int64_t* t_new, const int64_t* kv_off,
@@ -59,6 +66,16 @@ hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, 
                           const float* wI, const void* K, const int32_t* q_seq,
                           const int64_t* q_pos, const int64_t* kv_offset, long max_cand,
                           float* scores, long ld_sc, uint32_t* hist, long hist_min, hipStream_t s);
+
+// Packed sequences (prefill of several sequences in one call): sequence b owns
+// rows cu[b] .. cu[b+1]-1 of qI / wI and keys from kv_offset[b].  Fills the
+// per-token q_pos / q_seq [ntok] and the tiled kernel's block table blk
+// [nseq + 1] (device buffers), then scores every token against its own
+// sequence's causal candidates into scores [ntok, ld_sc].
+hipError_t launch_indexer_varlen(csa_dtype dt, long nseq, long ntok, int nhI, int cI, int m, const void* qI,
+                                 const float* wI, const void* K, const int64_t* cu, const int64_t* kv_offset,
+                                 long max_cand, float* scores, long ld_sc, int32_t* blk, int64_t* q_pos,
+                                 int32_t* q_seq, hipStream_t s);
 
 hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s);
 

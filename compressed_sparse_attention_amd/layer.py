@@ -102,6 +102,70 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
     return buf
 
 
+class VarlenPrefill:
+    """Buffers and offsets of a prefill of several packed sequences (token rows of sequence b:
+    cu[b] .. cu[b+1]-1; its compressed entries: rows block_offset[b] .. block_offset[b+1]-1)."""
+
+    def __init__(self, lengths, m: int, k: int, nh: int, nhI: int, c: int, cI: int, dc: int, dtype, device):
+        cu, bo = [0], [0]
+        for L in lengths:
+            if L < 0:
+                raise ValueError("negative sequence length")
+            cu.append(cu[-1] + int(L))
+            bo.append(bo[-1] + int(L) // m)
+        self.lengths = [int(L) for L in lengths]
+        self.n, self.n_blocks = cu[-1], bo[-1]
+        self.max_cand = max([(L - 1) // m for L in self.lengths if L > 0], default=0)
+        self.cu = torch.tensor(cu, dtype=torch.int64, device=device)
+        self.block_offset = torch.tensor(bo, dtype=torch.int64, device=device)
+        n = self.n
+        width = 4 * c + 4 * cI + dc
+        self.Y_H = torch.empty(n, width, dtype=dtype, device=device)
+        self.wI = torch.empty(n, nhI, dtype=torch.float32, device=device)
+        self.qI = torch.empty(n, nhI * cI, dtype=dtype, device=device)
+        self.q = torch.empty(n, nh * c, dtype=dtype, device=device)
+        self.Ccomp = torch.empty(max(self.n_blocks, 1), c, dtype=dtype, device=device)
+        self.KIcomp = torch.empty(max(self.n_blocks, 1), cI, dtype=dtype, device=device)
+        self.idx = torch.empty(n, k, dtype=torch.int32, device=device)
+        self.o = torch.empty(n, nh, c, dtype=dtype, device=device)
+        self.lse = torch.empty(n, nh, dtype=torch.float32, device=device)
+        self.q_seq = torch.empty(max(n, 1), dtype=torch.int32, device=device)
+        ws_i = api.csa_index_topk_varlen_workspace(len(lengths), n, self.max_cand, k)
+        ws_m = api.csa_sparse_mqa_workspace(n, nh, c, k)
+        self.ws_index = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=device)
+        self.ws_mqa = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=device)
+
+
+def prefill_varlen(H: torch.Tensor, lengths, W: Dict[str, torch.Tensor], m: int, k: int, nh: int, nhI: int,
+                   scale: Optional[float] = None, buf: Optional[VarlenPrefill] = None) -> VarlenPrefill:
+    """Eqs 1-11 for several sequences packed in H [sum(lengths), d]: each sequence is a causal prefill of
+    its own (its tokens see only its own compressed entries)."""
+    c, cI, dc = W["c"], W["cI"], W["dc"]
+    if buf is None:
+        buf = VarlenPrefill(lengths, m, k, nh, nhI, c, cI, dc, H.dtype, H.device)
+    n = buf.n
+    if H.shape[0] != n:
+        raise ValueError("H must hold sum(lengths) rows")
+    Y = buf.Y_H
+    api.csa_project(H, W["W_H_t"], Y)  # eqs 1, 2 (+ indexer copies), 5
+    api.csa_project(H, W["W_w_t"], buf.wI)  # eq 7
+    cQ = Y[:, 4 * c + 4 * cI:]
+    api.csa_project(cQ, W["W_UQI_t"], buf.qI)  # eq 6
+    api.csa_compress_varlen(Y[:, 0:c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:4 * c], W["B_a"], W["B_b"], m,
+                            buf.cu, buf.block_offset, buf.n_blocks, buf.Ccomp)  # eqs 3-4
+    o = 4 * c
+    api.csa_compress_varlen(Y[:, o:o + cI], Y[:, o + cI:o + 2 * cI], Y[:, o + 2 * cI:o + 3 * cI],
+                            Y[:, o + 3 * cI:o + 4 * cI], W["B_aI"], W["B_bI"], m, buf.cu, buf.block_offset,
+                            buf.n_blocks, buf.KIcomp)
+    api.csa_index_topk_varlen(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, buf.max_cand, buf.cu,
+                              buf.block_offset, buf.idx, q_seq_out=buf.q_seq[:n], workspace=buf.ws_index)  # eqs 8-9
+    api.csa_project(cQ, W["W_UQ_t"], buf.q)  # eq 10
+    sc = 1.0 / math.sqrt(c) if scale is None else scale
+    api.csa_sparse_mqa(buf.q.view(n, nh, c), buf.Ccomp, buf.idx, sc, buf.o, buf.lse, q_seq=buf.q_seq[:n],
+                       kv_offset=buf.block_offset, workspace=buf.ws_mqa)  # eq 11
+    return buf
+
+
 class DecodeBuffers:
     """Outputs and the persistent workspace of decode steps of one batch shape."""
 

@@ -215,6 +215,41 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Packed sequences (a prefill of several sequences in one call).  Sequence b
+ * owns projected rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens: n_seqs + 1
+ * non-decreasing int64 on the device, cu_seqlens[0] = 0); each sequence is
+ * compressed and attended on its own, as if it were the only one.
+ *
+ * csa_compress_varlen -- eqs 3-4 per sequence (section "Compressed Key-Value
+ * Entries"): sequence b's floor(len_b / m) blocks go to Ccomp rows
+ * block_offset[b] .. block_offset[b+1]-1 (block_offset: n_seqs + 1 int64 on the
+ * device, the prefix sums of floor(len_b / m)); n_blocks = block_offset[n_seqs]
+ * (host value).  Block 0 of every sequence has no b-terms.  Arguments and
+ * limits otherwise as csa_compress.
+ *
+ * csa_index_topk_varlen -- eqs 8-9 for every token of every sequence (section
+ * "Lightning Indexer for Sparse Selection"): token t of sequence b (row
+ * cu_seqlens[b] + t) is a query at position t whose candidates are its own
+ * sequence's blocks s < floor(t / m), KIcomp rows kv_offset[b] + s (kv_offset:
+ * n_seqs int64 on the device, e.g. block_offset).  max_cand >= the largest
+ * floor(t / m) of the batch.  Outputs per token as csa_index_topk; q_seq_out
+ * (nullable, [n_tokens] int32) receives each token's sequence index, the
+ * q_seq that csa_sparse_mqa takes for this batch.  The workspace (size from
+ * csa_index_topk_varlen_workspace) needs no initialisation.
+ */
+csa_status csa_compress_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca, const void* Cb,
+                               const void* Za, const void* Zb, int64_t ld_in, const void* Ba, const void* Bb,
+                               const int64_t* cu_seqlens, const int64_t* block_offset, int64_t n_blocks, void* Ccomp,
+                               int64_t ld_out, void* stream);
+csa_status csa_index_topk_varlen_workspace(int64_t n_seqs, int64_t n_tokens, int64_t max_cand, int32_t k,
+                                           size_t* bytes);
+csa_status csa_index_topk_varlen(csa_dtype dt, int64_t n_seqs, int64_t n_tokens, int32_t n_hI, int32_t cI, int32_t m,
+                                 int32_t k, const void* qI, const float* wI, const void* KIcomp,
+                                 const int64_t* cu_seqlens, const int64_t* kv_offset, int64_t max_cand,
+                                 int32_t* idx_out, float* score_out, int32_t* q_seq_out, void* workspace,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * csa_decode -- one decode step for a batch of queries: eqs 8 and 9
  * (csa_index_topk, per-query sweep) then eq 11 (csa_sparse_mqa) on the
  * selected entries, in one call.  Arguments are those of the two calls
@@ -242,8 +277,8 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
  * on the launch stream.  csa_timing_read synchronises on the recorded events
  * and returns, for the kernel family `name` ("gemm", "gemm_smallm"
  * (bf16 projections of 16 rows or fewer), "compress", "compress_append",
- * "indexer_sweep", "indexer_prefill", "hist_clear", "topk", "mqa",
- * "mqa_combine"),
+ * "indexer_sweep", "indexer_prefill", "varlen_meta", "hist_clear", "topk",
+ * "mqa", "mqa_combine"),
  * the summed duration in milliseconds and the number of launches since the
  * last reset.  Unknown names give 0 launches.
  */

@@ -97,6 +97,28 @@ def test_decode_rejects_bad_args(L):
     assert api.csa_sparse_mqa_workspace(0, 64, 512, 1024) == 0  # an empty batch needs no workspace
 
 
+def test_varlen_calls_reject_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def comp(dt=1, ns=3, m=4, c=64, ld=256, nb=10, cu=p, bo=p, ldo=64):
+        return L.csa_compress_varlen(dt, ns, m, c, p, p, p, p, ld, p, p, cu, bo, nb, p, ldo, None)
+    assert comp(m=0) == api.CSA_ERR_INVALID_ARG
+    assert comp(c=6) == api.CSA_ERR_INVALID_ARG
+    assert comp(cu=None) == api.CSA_ERR_INVALID_ARG
+    assert comp(ld=60) == api.CSA_ERR_INVALID_ARG
+    assert comp(nb=0, cu=None, bo=None) == api.CSA_OK  # no complete block anywhere: nothing to do
+
+    def idx(ns=2, nt=100, nhI=8, cI=64, k=16, cu=p, ws=p, wsb=1 << 30):
+        return L.csa_index_topk_varlen(1, ns, nt, nhI, cI, 4, k, p, p, p, cu, p, 30, p, None, None, ws, wsb, None)
+    assert idx(cI=96) == api.CSA_ERR_INVALID_ARG
+    assert idx(nhI=65) == api.CSA_ERR_INVALID_ARG
+    assert idx(cu=None) == api.CSA_ERR_INVALID_ARG
+    assert idx(ns=0) == api.CSA_ERR_INVALID_ARG  # tokens without sequences
+    assert idx(wsb=8) == api.CSA_ERR_WORKSPACE
+    assert idx(nt=0, cu=None) == api.CSA_OK
+    assert api.csa_index_topk_varlen_workspace(2, 100, 30, 16) >= 100 * 32 * 4
+
+
 def test_index_topk_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
     args = dict(dt=1, nq=4, nhI=64, cI=128, m=4, k=16, qI=p, wI=p, K=p, seq=None, pos=None, off=None,

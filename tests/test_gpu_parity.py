@@ -417,3 +417,76 @@ def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k):
         qn = qI.view(torch.int16).cpu().numpy().view(np.uint16)
         srows = _oracle_rows(qn, wI.cpu().numpy(), Kn, pos, off, m, "bf16")
         check_topk(idx1.cpu().numpy(), srows, k)
+
+
+# ---------------------------------------------------------------------------
+# packed sequences: compression and indexer + top-k per sequence
+# ---------------------------------------------------------------------------
+def _packed(lengths, m):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    bo = np.concatenate([[0], np.cumsum(np.asarray(lengths) // m)]).astype(np.int64)
+    return cu, bo
+
+
+@pytest.mark.parametrize("dtype,lengths,m,c", [
+    ("f32", [0, 3, 5, 17, 64, 130], 4, 64), ("bf16", [1000, 1, 257, 4], 4, 512), ("bf16", [9, 31, 2], 8, 12),
+    ("bf16", [40, 0, 0, 7], 1, 128),
+])
+def test_compress_varlen(dtype, lengths, m, c):
+    """Each packed sequence is compressed as if alone: its rows equal the oracle's compression of its slice."""
+    rng = synth.rng_for(sum(lengths) + m + c)
+    cu, bo = _packed(lengths, m)
+    n = int(cu[-1])
+    cp = (c + 7) // 8 * 8
+    P = draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = draw(rng, (n, 4 * cp), 2.0, dtype)
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
+    Ba = draw(rng, (m, c), 0.5, dtype)
+    Bb = draw(rng, (m, c), 0.5, dtype)
+    Pd = to_device(P, dtype, DEV)
+    nb = int(bo[-1])
+    out = torch.full((nb + 2, cp), 3.0, dtype=TD[dtype], device=DEV)[:, :c]
+    sl = [Pd[:, i * cp:i * cp + c] for i in range(4)]
+    api.csa_compress_varlen(*sl, to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV), m,
+                            torch.tensor(cu, device=DEV), torch.tensor(bo, device=DEV), nb, out)
+    torch.cuda.synchronize()
+    got = to_np64(out)
+    P64 = f64(P, dtype)
+    for b in range(len(lengths)):
+        seg = P64[cu[b]:cu[b + 1]]
+        ref = O.compress(*[seg[:, i * cp:i * cp + c] for i in range(4)], f64(Ba, dtype), f64(Bb, dtype), m)
+        if ref.shape[0]:
+            assert_rows_close(got[bo[b]:bo[b + 1]], ref, what=f"sequence {b}")
+    assert np.all(got[nb:] == 3.0)  # rows past the blocks are untouched
+
+
+@pytest.mark.parametrize("dtype,lengths,m,nhI,cI,k", [
+    ("bf16", [1, 40, 257, 1000, 33], 4, 64, 128, 64),
+    ("f32", [130, 0, 77, 512], 4, 4, 32, 16),
+    ("bf16", [3000, 70], 2, 20, 64, 300),
+])
+def test_index_topk_varlen(dtype, lengths, m, nhI, cI, k):
+    """Token t of packed sequence b selects among its own sequence's first floor(t/m) blocks."""
+    rng = synth.rng_for(sum(lengths) + nhI + k)
+    cu, bo = _packed(lengths, m)
+    n, nb = int(cu[-1]), int(bo[-1])
+    K = draw(rng, (max(nb, 1), cI), 1.0, dtype)
+    qI = draw(rng, (n, nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((n, nhI), dtype=np.float32)
+    max_cand = max((L - 1) // m for L in lengths if L > 0)
+    idx = torch.full((n, k), 123456, dtype=torch.int32, device=DEV)
+    sc = torch.empty(n, k, dtype=torch.float32, device=DEV)
+    qs = torch.full((n,), -5, dtype=torch.int32, device=DEV)
+    api.csa_index_topk_varlen(to_device(qI, dtype, DEV), to_device(wI, "f32", DEV), to_device(K, dtype, DEV), m, k,
+                              max_cand, torch.tensor(cu, device=DEV), torch.tensor(bo, device=DEV), idx,
+                              score_out=sc, q_seq_out=qs)
+    torch.cuda.synchronize()
+    seq_of = np.repeat(np.arange(len(lengths)), lengths)
+    assert np.array_equal(qs.cpu().numpy(), seq_of)
+    K64, q64 = f64(K, dtype), f64(qI, dtype)
+    rows = []
+    for t in range(n):
+        b = seq_of[t]
+        nc = int((t - cu[b]) // m)
+        rows.append(O.index_scores_row(q64[t], wI[t].astype(np.float64), K64[bo[b]:bo[b] + nc], nc))
+    check_topk(idx.cpu().numpy(), rows, k)
