@@ -205,6 +205,52 @@ def bench_prefill(args, torch, api, synth, layer):
             "indexer_roofline": roof}
 
 
+def bench_prefill_varlen(args, torch, api, synth, layer):
+    """Prefill of 16 packed sequences with ragged lengths (512 .. 4096 tokens, seeded draw) at the layer
+    sizes of the 32768-token prefill: one call per stage for the whole batch, each sequence causal on its
+    own."""
+    w = synth.WORKLOADS[3]
+    dev = "cuda:0"
+    lengths = [int(x) for x in synth.ragged_lengths(synth.rng_for(41), 16, 512, 4096)]
+    n = sum(lengths)
+    P = synth.make_prefill(w, seed=42, n=n)
+    W = layer.pack_prefill_params(P, w.dtype, dev)
+    H = layer.to_device(P["H"], w.dtype, dev)
+    del P
+    buf = layer.VarlenPrefill(lengths, w.m, w.k, w.nh, w.nhI, w.c, w.cI, w.dc, H.dtype, dev)
+
+    def run(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            layer.prefill_varlen(H, lengths, W, w.m, w.k, w.nh, w.nhI, buf=buf)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    run(max(1, args.prefill_warmup))
+    ms = run(args.prefill_steps)
+    api.csa_timing_reset()
+    api.csa_timing_enable(True)
+    run(args.prefill_steps)
+    api.csa_timing_enable(False)
+    kern = _kernel_stats(api, ["gemm", "compress", "varlen_meta", "indexer_prefill", "topk", "mqa", "mqa_combine"])
+    api.csa_timing_reset()
+    print(f"[bench] packed prefill: {ms:.2f} ms for {len(lengths)} sequences, {n} tokens", flush=True)
+    pairs = sum(t // w.m for L in lengths for t in range(L))
+    idx_flops = 2.0 * pairs * w.nhI * w.cI
+    ip = kern.get("indexer_prefill")
+    roof = None
+    if ip:
+        ach = idx_flops / (ip["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": "indexer_prefill", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": idx_flops}
+    return {"workload": "prefill_varlen_16seq_512-4096_bf16", "sequences": len(lengths), "tokens": n,
+            "lengths": lengths, "ms": round(ms, 4), "tokens_per_s": round(n / (ms * 1e-3), 1),
+            "kernels_ms_per_step": {k: round(v["total_ms"] / args.prefill_steps, 4) for k, v in kern.items()},
+            "indexer_roofline": roof}
+
+
 def bench_decode_step(args, torch, api, synth, layer):
     """Decode with cache maintenance: the batch of 8 sequences at 131072 tokens appends one token each.
 
@@ -344,6 +390,7 @@ def main():
     ap.add_argument("--prefill-warmup", type=int, default=1)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode-step", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true")
@@ -363,6 +410,7 @@ def main():
     dec = bench_decode(args, torch, api, synth, layer)
     pre = None if args.no_prefill else bench_prefill(args, torch, api, synth, layer)
     dstep = None if args.no_decode_step else bench_decode_step(args, torch, api, synth, layer)
+    pvar = None if args.no_varlen else bench_prefill_varlen(args, torch, api, synth, layer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     w = dec["workload"]
@@ -395,6 +443,7 @@ def main():
         "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
         "prefill": pre,
         "decode_step_with_cache": dstep,
+        "prefill_varlen": pvar,
     }
     print(json.dumps(line), flush=True)
 

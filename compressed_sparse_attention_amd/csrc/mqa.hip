@@ -335,6 +335,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
 // LDS; O^T is split over the output dims (c/8 per wave).
 // ---------------------------------------------------------------------------
 constexpr int kG8Chunk = 64;
+constexpr int kG8MaxStaged = 2048;  // slot ids of a split staged in LDS
 
 template <int DTW>
 __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg, int nsplit, int cps,
@@ -362,6 +363,8 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
   __shared__ float s_red[2][2][kHG];
   __shared__ float s_alpha[kHG];
   __shared__ float s_l[kHG];
+  __shared__ int32_t s_ids[kG8MaxStaged];
+  __shared__ int s_ext[2][8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -376,17 +379,49 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
   const int seq = q_seq ? q_seq[r] : 0;
   const long off = kv_off ? kv_off[seq] : 0;
   const bf16_t* Cb = C + off * CD;
-  const int nch = min(cps, (k - j * cps * KS + KS - 1) / KS);  // chunks of this split (>= 1)
+  const int nch_all = min(cps, (k - j * cps * KS + KS - 1) / KS);  // chunks of this split (>= 1)
+  const int sbeg = j * cps * KS, send = min(k, sbeg + nch_all * KS);
 
   const int ht = wave & 3, kh = wave >> 2;  // S^T work: head tile, key half
   const int qhead = h0 + 16 * ht + c16;
   const bool qlive = ht < NT;
 
+  // The split's slot ids are staged in LDS once (when they fit).  Slots that
+  // hold -1 contribute nothing; when the valid ids form a prefix of the split
+  // (the selector pads rows with -1 at the end), the chunks past it are not
+  // walked at all.
+  const bool staged = send - sbeg <= kG8MaxStaged;
+  int nch = nch_all;
+  if (staged) {
+    int first_bad = 0x7FFFFFFF, last_good = -1;
+    for (int sl = sbeg + tid; sl < send; sl += 512) {
+      const int id = idx[r * k + sl];
+      s_ids[sl - sbeg] = id;
+      if (id < 0) first_bad = min(first_bad, sl); else last_good = max(last_good, sl);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      first_bad = min(first_bad, __shfl_xor(first_bad, sh));
+      last_good = max(last_good, __shfl_xor(last_good, sh));
+    }
+    if (lane == 0) {
+      s_ext[0][wave] = first_bad;
+      s_ext[1][wave] = last_good;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      first_bad = min(first_bad, s_ext[0][w]);
+      last_good = max(last_good, s_ext[1][w]);
+    }
+    if (last_good < first_bad) nch = max(0, (last_good - sbeg + KS) / KS);
+  }
+
   // row ids of chunk c for this wave's RPW rows (lane < RPW), -1 past k
   auto load_ids = [&](int c) -> int {
     const int slot = (j * cps + c) * KS + RPW * wave + lane;
-    const int raw = idx[r * k + (slot < k ? slot : k - 1)];
-    return (lane < RPW && slot < k) ? raw : -1;
+    const int raw = staged ? s_ids[min(slot, send - 1) - sbeg] : idx[r * k + (slot < k ? slot : k - 1)];
+    return (lane < RPW && slot < send) ? raw : -1;
   };
   u32x4 stg[NLD];
   auto issue_rows = [&](int ids) {

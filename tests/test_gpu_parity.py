@@ -315,19 +315,24 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
 # ---------------------------------------------------------------------------
 # sparse MQA (eq 11)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,B,nh,c,k,nblk,qmult", [
-    ("bf16", 4, 64, 512, 512, 3000, 1.0),
-    ("bf16", 3, 64, 512, 100, 700, 8.0),
-    ("bf16", 2, 128, 512, 256, 400, 32.0),
-    ("f32", 5, 8, 64, 16, 128, 1.0),
-    ("bf16", 3, 20, 128, 70, 90, 4.0),
-    ("bf16", 600, 64, 512, 200, 300, 4.0),
-    ("f32", 530, 8, 64, 70, 40, 2.0),
-    ("bf16", 64, 64, 512, 1024, 1500, 8.0),  # several 128-row chunks per split
-    ("bf16", 520, 128, 256, 130, 500, 2.0),  # long batch, two 64-head groups, c = 256
-    ("bf16", 512, 20, 128, 200, 260, 1.0),  # long batch, partial head tile, c = 128
+@pytest.mark.parametrize("dtype,B,nh,c,k,nblk,qmult,layout", [
+    ("bf16", 4, 64, 512, 512, 3000, 1.0, "prefix"),
+    ("bf16", 3, 64, 512, 100, 700, 8.0, "prefix"),
+    ("bf16", 2, 128, 512, 256, 400, 32.0, "prefix"),
+    ("f32", 5, 8, 64, 16, 128, 1.0, "prefix"),
+    ("bf16", 3, 20, 128, 70, 90, 4.0, "prefix"),
+    ("bf16", 600, 64, 512, 200, 300, 4.0, "prefix"),
+    ("f32", 530, 8, 64, 70, 40, 2.0, "prefix"),
+    ("bf16", 64, 64, 512, 1024, 1500, 8.0, "prefix"),  # several 128-row chunks per split
+    ("bf16", 520, 128, 256, 130, 500, 2.0, "prefix"),  # long batch, two 64-head groups, c = 256
+    ("bf16", 512, 20, 128, 200, 260, 1.0, "prefix"),  # long batch, partial head tile, c = 128
+    # long batch, selections of every length 0 .. 700 (trailing chunks of -1 slots are skipped)
+    ("bf16", 560, 64, 512, 512, 700, 2.0, "ragged"),
+    # -1 slots scattered between valid ones (no prefix: every chunk is walked)
+    ("bf16", 560, 64, 512, 512, 700, 2.0, "scatter"),
+    ("bf16", 4, 64, 512, 512, 700, 2.0, "scatter"),
 ])
-def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
+def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
     rng = synth.rng_for(B * nh + k)
     C = draw(rng, (B * nblk, c), 1.0, dtype)
     q = draw(rng, (B, nh, c), qmult / math.sqrt(c), dtype)
@@ -335,7 +340,12 @@ def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult):
     ncand[-1] = 0  # one query with nothing selected
     if B > 2:
         ncand[1] = min(nblk, k // 2 + 1)  # a short selection padded with -1
+    if layout != "prefix":
+        ncand = rng.integers(0, nblk + 1, size=B)
+        ncand[0] = 0
     idx = synth.random_selection(rng, ncand, k)
+    if layout == "scatter":
+        idx = np.stack([rng.permutation(row) for row in idx])
     off = np.arange(B, dtype=np.int64) * nblk
     o = torch.full((B, nh, c), 5.0, dtype=TD[dtype], device=DEV)
     lse = torch.empty(B, nh, dtype=torch.float32, device=DEV)
