@@ -48,8 +48,8 @@ def _kernel_stats(api, names):
     return out
 
 
-def _traffic(kernel: str, src: str, per_launch_units: float):
-    """HBM bytes per launch from committed counter runs, if the kernel source is unchanged."""
+def _traffic(kernel: str):
+    """HBM bytes per launch from committed counter runs, while the kernel's sources are unchanged."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -57,9 +57,11 @@ def _traffic(kernel: str, src: str, per_launch_units: float):
         rec = json.load(f).get(kernel)
     if not rec:
         return None
-    with open(os.path.join(ROOT, "compressed_sparse_attention_amd", "csrc", src), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        with open(os.path.join(ROOT, "compressed_sparse_attention_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    if rec.get("sources_sha256") != h.hexdigest():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -146,14 +148,14 @@ def bench_decode(args, torch, api, synth, layer):
     # whole decode step per query: key sweep + gathered entries + q + o + selected indices
     step_bytes = B * (2 * N * w.cI + 2 * min(w.k, N) * w.c + 2 * (w.nh * w.c + w.nhI * w.cI) + 4 * w.nhI
                       + 2 * w.nh * w.c + 4 * w.k)
-    name, src = "indexer_sweep", "indexer.hip"
+    name = "indexer_sweep"
     sw = kern.get(name)
     roof = None
     if sw:
         achieved = sweep_bytes / (sw["avg_us"] * 1e-6) / 1e9
         roof = {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": _traffic(name, src, B),
+                "traffic": _traffic(name),
                 "algorithmic_bytes_per_launch": sweep_bytes}
     return {
         "workload": w, "B": B, "ms": ms, "ms_warm": ms_warm, "ms_eager": ms_eager, "kernels": kern, "roofline": roof,
