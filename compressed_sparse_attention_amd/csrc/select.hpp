@@ -453,6 +453,23 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
 
+  // A group of tpc threads serves each chunk.  The first batch of each
+  // thread's list entries is fetched before the counts are known (positions
+  // past a list's end read filler from inside it and are ignored), so the
+  // counts and the lists take one memory round trip, not two.
+  int p2 = 1;
+  while (p2 < Pr) p2 <<= 1;
+  const int tpc = p2 >= TPB ? 1 : TPB / p2;
+  const int c_first = tid / tpc, sub = tid % tpc;
+  uint64_t spec_g[kMUnroll], spec_e[kMUnroll];
+  if (c_first < Pr) {
+#pragma unroll
+    for (int u = 0; u < kMUnroll; ++u) {
+      const long e = sub + u * tpc;
+      spec_g[u] = ld_agent(gt + c_first * gts + (e < gts ? e : gts - 1));
+      spec_e[u] = ld_agent(eq + c_first * eqs + (e < eqs ? e : eqs - 1));
+    }
+  }
   for (int b = tid; b < 3 * 256; b += TPB) (&s_h2[0][0])[b] = 0u;
   if (wave == 0) {  // exclusive prefix of the per-chunk counts, 64 chunks per step
     uint32_t run_g = 0, run_e = 0;
@@ -481,22 +498,23 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
       if (sout) sout[slot] = key_score(key);
     }
   };
-  // Both lists in one pass: a group of tpc threads serves each chunk, so list
-  // positions need no search.  Selected entries go straight to their slots
-  // (chunk order = index order); candidates go to LDS when they all fit.
-  {
-    int p2 = 1;
-    while (p2 < Pr) p2 <<= 1;
-    const int tpc = p2 >= TPB ? 1 : TPB / p2;
-    for (int c = tid / tpc; c < Pr; c += TPB / tpc) {
-      const int sub = tid % tpc;
-      const uint32_t g0 = s_pg[c], ng = s_pg[c + 1] - g0;
-      const uint32_t e0c = s_pe[c], ne = s_pe[c + 1] - e0c;
-      const uint32_t nmax = nseg == 1 ? max(ng, ne) : ng;
-      const uint64_t* gsrc = gt + c * gts;
-      const uint64_t* esrc = eq + c * eqs;
-      for (uint32_t base = sub; base < nmax; base += tpc * kMUnroll) {
-        uint64_t eg[kMUnroll], ee[kMUnroll];
+  // Both lists in one pass (chunk order = index order): selected entries go
+  // straight to their slots; candidates go to LDS when they all fit.
+  for (int c = c_first; c < Pr; c += TPB / tpc) {
+    const uint32_t g0 = s_pg[c], ng = s_pg[c + 1] - g0;
+    const uint32_t e0c = s_pe[c], ne = s_pe[c + 1] - e0c;
+    const uint32_t nmax = nseg == 1 ? max(ng, ne) : ng;
+    const uint64_t* gsrc = gt + c * gts;
+    const uint64_t* esrc = eq + c * eqs;
+    for (uint32_t base = sub; base < nmax; base += tpc * kMUnroll) {
+      uint64_t eg[kMUnroll], ee[kMUnroll];
+      if (c == c_first && base == (uint32_t)sub) {  // the batch fetched with the counts
+#pragma unroll
+        for (int u = 0; u < kMUnroll; ++u) {
+          eg[u] = spec_g[u];
+          ee[u] = spec_e[u];
+        }
+      } else {
 #pragma unroll
         for (int u = 0; u < kMUnroll; ++u) {
           const uint32_t e = base + u * tpc;
@@ -504,17 +522,17 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
           ee[u] = ld_agent(esrc + (e < ne ? e : 0u));
         }
         issue_fence();
+      }
 #pragma unroll
-        for (int u = 0; u < kMUnroll; ++u) {
-          const uint32_t e = base + u * tpc;
-          if (e < ng && g0 + e < (uint32_t)k) {
-            out[g0 + e] = (int32_t)(uint32_t)eg[u];
-            if (sout) sout[g0 + e] = __uint_as_float((uint32_t)(eg[u] >> 32));
-          }
-          if (nseg == 1 && e < ne) {
-            s_cidx[e0c + e] = (uint32_t)ee[u];
-            s_ckey[e0c + e] = (uint32_t)(ee[u] >> 32);
-          }
+      for (int u = 0; u < kMUnroll; ++u) {
+        const uint32_t e = base + u * tpc;
+        if (e < ng && g0 + e < (uint32_t)k) {
+          out[g0 + e] = (int32_t)(uint32_t)eg[u];
+          if (sout) sout[g0 + e] = __uint_as_float((uint32_t)(eg[u] >> 32));
+        }
+        if (nseg == 1 && e < ne) {
+          s_cidx[e0c + e] = (uint32_t)ee[u];
+          s_ckey[e0c + e] = (uint32_t)(ee[u] >> 32);
         }
       }
     }
