@@ -147,15 +147,18 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
 constexpr int kG2M = 256;
 constexpr int kG2N = 256;
 constexpr int kG2K = 64;               // elements per slab row (128 bytes)
-constexpr int kG2Pitch = kG2K + 8;     // padded LDS row (elements)
+// LDS slab rows are unpadded; 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7), so the 16 lanes of a fragment read (16 rows, one chunk)
+// and of a staging store (2 rows x 8 chunks) each hit 16 distinct 4-bank groups.
+__device__ __forceinline__ int g2_swz(int row, int chunk) { return row * kG2K + ((chunk ^ ((row >> 1) & 7)) << 3); }
 constexpr int kG2Group = 4;            // tile rows per group in the walk order
 
 template <typename TO>
 __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const bf16_t* __restrict__ X, long ldx,
                                                         const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y,
                                                         long ldy, int tiles_m, int tiles_n, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kG2M * kG2Pitch];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kG2N * kG2Pitch];
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kG2M * kG2K];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kG2N * kG2K];
 
   const int seq = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (seq >= tiles_m * tiles_n) return;
@@ -195,8 +198,8 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
   auto stash = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      *reinterpret_cast<u32x4*>(&As[buf][(lrow + 64 * p) * kG2Pitch + lcol]) = ra[p];
-      *reinterpret_cast<u32x4*>(&Bs[buf][(lrow + 64 * p) * kG2Pitch + lcol]) = rb[p];
+      *reinterpret_cast<u32x4*>(&As[buf][g2_swz(lrow + 64 * p, tid & 7)]) = ra[p];
+      *reinterpret_cast<u32x4*>(&Bs[buf][g2_swz(lrow + 64 * p, tid & 7)]) = rb[p];
     }
   };
 
@@ -218,12 +221,13 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 #pragma unroll
     for (int ks = 0; ks < kG2K / 32; ++ks) {
       Frag<bf16_t> fa[8], fb[4];
-      const bf16_t* Ab = &As[cur][(wm * 128 + c16) * kG2Pitch + 8 * g + 32 * ks];
-      const bf16_t* Bb = &Bs[cur][(wn * 64 + c16) * kG2Pitch + 8 * g + 32 * ks];
+      // rows wm*128 + 16 i + c16 (A) and wn*64 + 16 j + c16 (B), chunk 4 ks + g
+      const bf16_t* Ab = &As[cur][g2_swz(wm * 128 + c16, 4 * ks + g)];
+      const bf16_t* Bb = &Bs[cur][g2_swz(wn * 64 + c16, 4 * ks + g)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j].load(Bb + j * 16 * kG2Pitch);
+      for (int j = 0; j < 4; ++j) fb[j].load(Bb + j * 16 * kG2K);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i].load(Ab + i * 16 * kG2Pitch);
+      for (int i = 0; i < 8; ++i) fa[i].load(Ab + i * 16 * kG2K);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
