@@ -32,6 +32,11 @@ every step is evaluated in float64.  Readings taken where the page is silent
   compressed entries and scale = 1/sqrt(c) unless given; an empty selection
   gives o = 0 and lse = -inf.
 
+Backward functions (gradients of eqs 1-4 and 11 for training; the top-k of
+eq 9 passes no gradient, and the indexer's training objective is not on the
+page) are the chain rule of the forward definitions written out, pinned by
+central finite differences.
+
 Parity status: every function here is pinned by the CPU tests (closed forms,
 invariants, brute force and a library routine); there is no trained-model
 value to compare with, so absolute behaviour on trained weights is
@@ -47,7 +52,7 @@ import numpy as np
 __all__ = [
     "project", "compress", "compress_weights", "n_candidates", "index_scores",
     "index_scores_row", "topk", "topk_rows", "mqa", "prefill", "prefill_rows",
-    "decode",
+    "decode", "project_backward", "compress_backward", "mqa_backward", "sparse_mqa_backward",
 ]
 
 
@@ -307,3 +312,88 @@ def decode(q, qI, wI, Ccomp, KIcomp, seq_len, kv_offset, m: int, k: int,
         lse.append(lb)
     return {"scores": scores, "idx": np.stack(idx), "o": np.stack(o), "lse": np.stack(lse),
             "seqs": seqs}
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients of a scalar loss whose gradient w.r.t. the outputs is given)
+# ---------------------------------------------------------------------------
+
+
+def project_backward(X, W, dY) -> Tuple[np.ndarray, np.ndarray]:
+    """Eqs 1, 2, 5, 6, 7, 10 (Y = X W): dX = dY W^T, dW = X^T dY."""
+    X, W, dY = _f64(X), _f64(W), _f64(dY)
+    return dY @ W.T, X.T @ dY
+
+
+def compress_backward(Ca, Cb, Za, Zb, Ba, Bb, m: int, dCcomp):
+    """Gradients of eqs 3-4 given dCcomp [floor(n/m), c].
+
+    For block i and channel ch, with weights S_j (the per-channel softmax of
+    eq 3 over the 2m stacked logits) and values v_j (the C^a and C^b rows),
+    out = sum_j S_j v_j; then dv_j = S_j * dout and the logit gradient is
+    dlogit_j = S_j * dout * (v_j - out).  Each projected row is an a-row of one
+    block and a b-row of the next, so its gradients come from one block each;
+    B^a and B^b collect dlogit over all blocks.  Rows past the last complete
+    block, and the b-rows of the last block, get zero gradient.
+    Returns (dCa, dCb, dZa, dZb) [n, c] and (dBa, dBb) [m, c].
+    """
+    Ca, Cb, dC = _f64(Ca), _f64(Cb), _f64(dCcomp)
+    n, c = Ca.shape
+    N = n // m
+    out, S = compress(Ca, Cb, Za, Zb, Ba, Bb, m, return_weights=True)
+    grads = [np.zeros((n, c)) for _ in range(4)]
+    dBa, dBb = np.zeros((m, c)), np.zeros((m, c))
+    if N == 0:
+        return (*grads, dBa, dBb)
+    va = Ca[: N * m].reshape(N, m, c)
+    vb = np.zeros((N, m, c))
+    if N > 1:
+        vb[1:] = Cb[: (N - 1) * m].reshape(N - 1, m, c)
+    vals = np.concatenate([va, vb], axis=1)  # [N, 2m, c]
+    dv = S * dC[:, None, :]
+    dl = S * dC[:, None, :] * (vals - out[:, None, :])
+    dCa, dCb, dZa, dZb = grads
+    dCa[: N * m] = dv[:, :m].reshape(N * m, c)
+    dZa[: N * m] = dl[:, :m].reshape(N * m, c)
+    if N > 1:
+        dCb[: (N - 1) * m] = dv[1:, m:].reshape((N - 1) * m, c)
+        dZb[: (N - 1) * m] = dl[1:, m:].reshape((N - 1) * m, c)
+    dBa = dl[:, :m].sum(axis=0)
+    dBb = dl[1:, m:].sum(axis=0) if N > 1 else dBb
+    return dCa, dCb, dZa, dZb, dBa, dBb
+
+
+def mqa_backward(q_t, C_sel, scale: float, dO_t) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients of eq 11 for one query token: (dq [n_h, c], dC_sel [k_sel, c]).
+
+    With P = softmax(scale q C^T) (per head), o = P C and the selected entries
+    serving as both keys and values: dP = dO C^T, D = rowsum(dO * o),
+    dS = P * (dP - D), dq = scale dS C, dC = P^T dO + scale dS^T q.
+    """
+    q, C, dO = _f64(q_t), _f64(C_sel), _f64(dO_t)
+    if C.shape[0] == 0:
+        return np.zeros_like(q), np.zeros((0, q.shape[1]))
+    logits = scale * (q @ C.T)
+    P = np.exp(logits - logits.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    o = P @ C
+    dP = dO @ C.T
+    D = (dO * o).sum(axis=1, keepdims=True)
+    dS = P * (dP - D)
+    return scale * dS @ C, P.T @ dO + scale * dS.T @ q
+
+
+def sparse_mqa_backward(q, Ccomp, idx, row_offset, scale: float, dO) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients of eq 11 over a batch: dq [n, n_h, c] and dCcomp [rows, c], where
+    every selection of a compressed row (by any query) adds its share."""
+    q, dO, Cc = _f64(q), _f64(dO), _f64(Ccomp)
+    dq = np.zeros_like(q)
+    dC = np.zeros_like(Cc)
+    for r in range(q.shape[0]):
+        sel = np.asarray(idx[r])
+        sel = sel[sel >= 0]
+        rows = int(row_offset[r]) + sel
+        dq[r], dc = mqa_backward(q[r], Cc[rows], scale, dO[r])
+        np.add.at(dC, rows, dc)
+    return dq, dC
+
