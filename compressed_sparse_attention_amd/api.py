@@ -42,12 +42,18 @@ _SIGS = {
                                     _i64, _vp]),
     "csa_compress_append": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _i64, _vp]),
+    "csa_compress_backward_workspace": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "csa_compress_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
+                                             _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_index_topk": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "csa_sparse_mqa_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_sparse_mqa": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _sz, _vp]),
+    "csa_sparse_mqa_backward_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]),
+    "csa_sparse_mqa_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _i64, _vp, _vp,
+                                               _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_compress_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                            _vp, _i64, _vp, _i64, _vp]),
     "csa_index_topk_varlen_workspace": (ctypes.c_int, [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
@@ -113,7 +119,9 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _rowmajor(t: torch.Tensor, name: str) -> int:
-    """Leading dimension of a 2-D row-major view (unit column stride)."""
+    """Leading dimension of a 2-D row-major view (unit column stride; any layout when empty)."""
+    if t.dim() == 2 and t.numel() == 0:
+        return max(t.shape[1], 1)
     if t.dim() != 2 or t.stride(1) != 1:
         raise CSAError(f"{name} must be a 2-D view with unit column stride")
     return t.stride(0)
@@ -189,6 +197,44 @@ def csa_compress_append(new_rows, ring, Ba, Bb, m: int, t_new, kv_offset, Ccomp)
     return Ccomp
 
 
+def csa_compress_backward_workspace(n: int, m: int, c: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_compress_backward_workspace(n, m, c, ctypes.byref(b)), "csa_compress_backward_workspace")
+    return b.value
+
+
+def csa_compress_backward(Ca, Cb, Za, Zb, Ba, Bb, m: int, dCcomp, dCa, dCb, dZa, dZb, dBa, dBb, workspace=None):
+    """Gradients of eqs 3-4.  Forward inputs as csa_compress; dCcomp [n // m, c] fp32; outputs dCa/dCb/dZa/dZb
+    [n, c] views of the inputs' dtype sharing one leading dimension, dBa/dBb [m, c] fp32 (overwritten)."""
+    n, c = Ca.shape
+    ld = _rowmajor(Ca, "Ca")
+    for t, nm in ((Cb, "Cb"), (Za, "Za"), (Zb, "Zb")):
+        if tuple(t.shape) != (n, c) or _rowmajor(t, nm) != ld or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress_backward: Ca, Cb, Za, Zb must share shape, dtype and leading dimension")
+    ldo = _rowmajor(dCa, "dCa")
+    for t, nm in ((dCa, "dCa"), (dCb, "dCb"), (dZa, "dZa"), (dZb, "dZb")):
+        if tuple(t.shape) != (n, c) or _rowmajor(t, nm) != ldo or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress_backward: dCa, dCb, dZa, dZb must be [n, c] of the input dtype "
+                           "sharing one leading dimension")
+    for t, nm in ((Ba, "Ba"), (Bb, "Bb"), (dBa, "dBa"), (dBb, "dBb")):
+        _contig(t, nm)
+        if tuple(t.shape) != (m, c):
+            raise CSAError(f"csa_compress_backward: {nm} must be [m, c]")
+    if dBa.dtype != torch.float32 or dBb.dtype != torch.float32 or dCcomp.dtype != torch.float32:
+        raise CSAError("csa_compress_backward: dCcomp, dBa and dBb are fp32")
+    if tuple(dCcomp.shape) != (n // m, c):
+        raise CSAError("csa_compress_backward: dCcomp must be [n // m, c]")
+    need = csa_compress_backward_workspace(n, m, c)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Ca.device)
+    _check(lib().csa_compress_backward(_dt(Ca), n, m, c, _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _ptr(Ba),
+                                       _ptr(Bb), _ptr(dCcomp), _rowmajor(dCcomp, "dCcomp") if n // m else c,
+                                       _ptr(dCa), _ptr(dCb), _ptr(dZa), _ptr(dZb), ldo, _ptr(dBa), _ptr(dBb),
+                                       _ptr(workspace), workspace.numel(), _stream(Ca.device)),
+           "csa_compress_backward")
+    return dCa, dCb, dZa, dZb, dBa, dBb
+
+
 def csa_index_topk_workspace(n_queries: int, max_cand: int, n_hI: int, k: int) -> int:
     b = _sz(0)
     _check(lib().csa_index_topk_workspace(n_queries, max_cand, n_hI, k, ctypes.byref(b)),
@@ -259,6 +305,44 @@ def csa_sparse_mqa(q, Ccomp, idx, scale: float, o, lse=None, q_seq=None, kv_offs
                                 workspace.numel() * workspace.element_size(), _stream(q.device)),
            "csa_sparse_mqa")
     return o
+
+
+def csa_sparse_mqa_backward_workspace(n_queries: int, n_h: int, c: int, k: int, n_rows: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_sparse_mqa_backward_workspace(n_queries, n_h, c, k, n_rows, ctypes.byref(b)),
+           "csa_sparse_mqa_backward_workspace")
+    return b.value
+
+
+def csa_sparse_mqa_backward(q, Ccomp, idx, scale: float, o, lse, dO, dq, dCcomp, q_seq=None, kv_offset=None,
+                            workspace=None):
+    """Gradients of eq 11: q/o/dO/dq [n, n_h, c] bf16, Ccomp [rows, c] bf16, idx [n, k] int32, lse [n, n_h] fp32,
+    dCcomp [rows, c] fp32 (overwritten)."""
+    n, nh, c = q.shape
+    k = idx.shape[1]
+    rows = Ccomp.shape[0]
+    for t, nm in ((q, "q"), (o, "o"), (dO, "dO"), (dq, "dq")):
+        _contig(t, nm)
+        if tuple(t.shape) != (n, nh, c) or t.dtype != Ccomp.dtype:
+            raise CSAError(f"csa_sparse_mqa_backward: {nm} must be [n, n_h, c] of the Ccomp dtype")
+    _contig(Ccomp, "Ccomp")
+    _contig(idx, "idx")
+    _contig(lse, "lse")
+    _contig(dCcomp, "dCcomp")
+    if idx.dtype != torch.int32 or idx.shape[0] != n:
+        raise CSAError("csa_sparse_mqa_backward: idx must be int32 [n, k]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (n, nh):
+        raise CSAError("csa_sparse_mqa_backward: lse must be fp32 [n, n_h]")
+    if dCcomp.dtype != torch.float32 or tuple(dCcomp.shape) != (rows, c):
+        raise CSAError("csa_sparse_mqa_backward: dCcomp must be fp32 [rows, c]")
+    need = csa_sparse_mqa_backward_workspace(n, nh, c, k, rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().csa_sparse_mqa_backward(_dt(q), n, nh, c, k, scale, _ptr(q), _ptr(Ccomp), rows, _ptr(q_seq),
+                                         _ptr(kv_offset), _ptr(idx), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq),
+                                         _ptr(dCcomp), _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "csa_sparse_mqa_backward")
+    return dq, dCcomp
 
 
 def csa_compress_varlen(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens, block_offset, n_blocks: int, Ccomp):

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["gemm.hip", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "api.hip"]
+SOURCES = ["gemm.hip", "compress.hip", "indexer.hip", "topk.hip", "mqa.hip", "mqa_bwd.hip", "api.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

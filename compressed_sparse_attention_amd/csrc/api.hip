@@ -239,6 +239,47 @@ csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const voi
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress launch");
 }
 
+csa_status csa_compress_backward_workspace(int64_t n, int32_t m, int32_t c, size_t* bytes) {
+  CSA_REQUIRE(bytes != nullptr, "csa_compress_backward_workspace: null bytes");
+  CSA_REQUIRE(n >= 0, "csa_compress_backward_workspace: n must be >= 0");
+  CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_workspace: m must be in [1, 16] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_workspace: c must be a positive multiple of 4");
+  *bytes = csa::compress_backward_workspace_bytes(n, m, c);
+  return CSA_OK;
+}
+
+csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, const void* Ca, const void* Cb,
+                                 const void* Za, const void* Zb, int64_t ld_in, const void* Ba, const void* Bb,
+                                 const float* dCcomp, int64_t ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
+                                 int64_t ld_out, float* dBa, float* dBb, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress_backward: unknown dtype");
+  CSA_REQUIRE(n >= 0, "csa_compress_backward: n must be >= 0");
+  CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward: m must be in [1, 16] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward: c must be a positive multiple of 4 (got %d)", c);
+  CSA_REQUIRE(dBa && dBb && workspace, "csa_compress_backward: null pointer");
+  const size_t need = csa::compress_backward_workspace_bytes(n, m, c);
+  CSA_REQUIRE(ws_bytes >= need, "csa_compress_backward: workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+  CSA_REQUIRE(aligned16(workspace), "csa_compress_backward: workspace must be 16-byte aligned");
+  const int v = vec_elems(dt);
+  if (n > 0) {
+    CSA_REQUIRE(Ca && Cb && Za && Zb && Ba && Bb && dCa && dCb && dZa && dZb, "csa_compress_backward: null pointer");
+    CSA_REQUIRE(n / m == 0 || dCcomp != nullptr, "csa_compress_backward: null dCcomp");
+    CSA_REQUIRE(aligned16(Ca) && aligned16(Cb) && aligned16(Za) && aligned16(Zb) && aligned16(Ba) &&
+                    aligned16(Bb) && aligned16(dCa) && aligned16(dCb) && aligned16(dZa) && aligned16(dZb) &&
+                    (dCcomp == nullptr || aligned16(dCcomp)),
+                "csa_compress_backward: pointers must be 16-byte aligned");
+    CSA_REQUIRE(ld_in >= c && ld_out >= c && ld_dc >= c, "csa_compress_backward: leading dimension smaller than c");
+    CSA_REQUIRE(ld_in % v == 0 && ld_out % v == 0 && ld_dc % 4 == 0,
+                "csa_compress_backward: leading dimensions must keep rows 16-byte aligned");
+  }
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_compress_backward(dt, n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb,
+                                               dZa, dZb, ld_out, dBa, dBb, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_backward launch");
+}
+
 csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, const void* new_rows,
                                int64_t ld_new, void* ring, const void* Ba, const void* Bb,
                                const int64_t* t_new, const int64_t* kv_offset, void* Ccomp,
@@ -379,6 +420,48 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   hipError_t e = csa::launch_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx, o, lse,
                                  workspace, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_sparse_mqa launch");
+}
+
+csa_status csa_sparse_mqa_backward_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, int64_t n_rows,
+                                             size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_sparse_mqa_backward_workspace: null bytes");
+  CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_sparse_mqa_backward_workspace: bad n_queries");
+  CSA_REQUIRE(n_h >= 1 && n_h <= 256, "csa_sparse_mqa_backward_workspace: n_h must be in [1, 256]");
+  CSA_REQUIRE(c == 512, "csa_sparse_mqa_backward_workspace: c must be 512 (got %d)", c);
+  CSA_REQUIRE(k >= 1 && k <= (1 << 20), "csa_sparse_mqa_backward_workspace: k must be in [1, 2^20]");
+  CSA_REQUIRE(n_rows >= 0 && n_rows < 0x7FFFFFFF, "csa_sparse_mqa_backward_workspace: bad n_rows");
+  *bytes = csa::mqa_backward_workspace_bytes(n_queries, n_h, k, n_rows);
+  return CSA_OK;
+}
+
+csa_status csa_sparse_mqa_backward(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k, float scale,
+                                   const void* q, const void* Ccomp, int64_t n_rows, const int32_t* q_seq,
+                                   const int64_t* kv_offset, const int32_t* idx, const void* o, const float* lse,
+                                   const void* dO, void* dq, float* dCcomp, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_sparse_mqa_backward: unknown dtype");
+  if (dt != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "csa_sparse_mqa_backward: only bf16 is supported");
+  size_t need = 0;
+  csa_status st = csa_sparse_mqa_backward_workspace(n_queries, n_h, c, k, n_rows, &need);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(scale == scale && scale > 0.f && scale < 1e30f,
+              "csa_sparse_mqa_backward: scale must be positive and finite");
+  CSA_REQUIRE(n_rows == 0 || dCcomp, "csa_sparse_mqa_backward: null dCcomp");
+  CSA_REQUIRE(aligned16(dCcomp), "csa_sparse_mqa_backward: dCcomp must be 16-byte aligned");
+  if (n_queries > 0) {
+    CSA_REQUIRE(q && idx && o && lse && dO && dq && (n_rows == 0 || Ccomp), "csa_sparse_mqa_backward: null pointer");
+    CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(idx) && aligned16(o) && aligned16(dO) && aligned16(dq),
+                "csa_sparse_mqa_backward: pointers must be 16-byte aligned");
+    if (workspace == nullptr || ws_bytes < need)
+      return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa_backward: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    CSA_REQUIRE(aligned16(workspace), "csa_sparse_mqa_backward: workspace must be 16-byte aligned");
+  }
+  if (n_queries == 0 && n_rows == 0) return CSA_OK;
+  st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_mqa_backward(n_queries, n_h, k, scale, q, Ccomp, n_rows, q_seq, kv_offset, idx, o, lse,
+                                          dO, dq, dCcomp, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_sparse_mqa_backward launch");
 }
 
 csa_status csa_decode_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t n_h, int32_t c,

@@ -14,6 +14,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <algorithm>
+
 namespace csa {
 namespace {
 
@@ -194,6 +196,213 @@ __global__ __launch_bounds__(256) void compress_append_kernel(int m, int c, cons
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward of eqs 3-4.  For block i and channel j, with S_r the softmax
+// weights of the 2m pairs (v_r, l_r) and out = sum_r S_r v_r:
+//
+//   dv_r = S_r * dout,   dl_r = S_r * dout * (v_r - out),
+//
+// and the logit l_r = Z_r + B_r passes dl_r to both Z_r and B_r.  A projected
+// row is an a-row of exactly one block and a b-row of exactly one other, so
+// each element of dC^a, dZ^a (from its own block) and dC^b, dZ^b (from the
+// next block) is written once, by the thread that owns that block: no
+// accumulation.  The bias gradients sum dl over all blocks: each workgroup
+// adds its blocks' terms in LDS and writes one partial row set, and a second
+// kernel sums the partials in a fixed order (deterministic).
+//
+// Thread mapping: lane l of every wave owns channels V*(64*blockIdx.x + l)
+// .. +V-1 (one contiguous run per row for the wave); the 8 waves of a
+// workgroup take the blocks of its range in turn.  The extra block index N
+// (one past the last block) stands for the rows no block reads: the a-rows
+// past N*m and the b-rows past (N-1)*m get zero gradients.
+// ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 8;
+constexpr int kBwdRowGroup = 8;  // rows loaded together: all 2m rows of a block when m <= 4
+
+// V elements of a row as loaded (bf16 kept packed), converted on use.
+template <typename T, int V> struct Raw {
+  static constexpr int W = V * (int)sizeof(T) / 4;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const T* p) {
+    if constexpr (W == 4) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+      w[0] = u[0]; w[1] = u[1]; w[2] = u[2]; w[3] = u[3];
+    } else {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      w[0] = u.x; w[1] = u.y;
+    }
+  }
+  __device__ __forceinline__ float at(int q) const {
+    if constexpr (sizeof(T) == 4) return __uint_as_float(w[q]);
+    else return __uint_as_float((q & 1) ? (w[q >> 1] & 0xFFFF0000u) : (w[q >> 1] << 16));
+  }
+};
+
+template <typename T, int V>
+__global__ __launch_bounds__(64 * kBwdWaves) void compress_bwd_kernel(
+    long N, long n, int m, int c, const T* __restrict__ Ca, const T* __restrict__ Cb, const T* __restrict__ Za,
+    const T* __restrict__ Zb, long ld, const T* __restrict__ Ba, const T* __restrict__ Bb,
+    const float* __restrict__ dC, long ldd, T* __restrict__ dCa, T* __restrict__ dCb, T* __restrict__ dZa,
+    T* __restrict__ dZb, long ldo, long bpw, float* __restrict__ part) {
+  extern __shared__ float s_db[];  // [2m][64 V]: bias-gradient sums of this workgroup's blocks
+  constexpr int G = kBwdRowGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = 64 * V;
+  const int ch = (blockIdx.x * 64 + lane) * V;
+  const bool live = ch < c;
+  for (int e = tid; e < 2 * m * W; e += 64 * kBwdWaves) s_db[e] = 0.f;
+  __syncthreads();
+
+  const long i0 = (long)blockIdx.y * bpw, i1 = min(i0 + bpw, N + 1);
+  for (long i = i0 + wave; live && i < i1; i += kBwdWaves) {
+    if (i == N) {  // rows read by no block
+      const float zero[V] = {};
+      for (long row = N * m; row < n; ++row) {
+        Vec<T, V>::store(dCa + row * ldo + ch, zero);
+        Vec<T, V>::store(dZa + row * ldo + ch, zero);
+      }
+      for (long row = N > 0 ? (N - 1) * m : 0; row < n; ++row) {
+        Vec<T, V>::store(dCb + row * ldo + ch, zero);
+        Vec<T, V>::store(dZb + row * ldo + ch, zero);
+      }
+      continue;
+    }
+    // Pair p < m is a-row p of block i; pair m + r is b-row r (a row of block i-1).
+    const int npairs = i > 0 ? 2 * m : m;
+    auto row_of = [&](int p) -> long { return p < m ? i * m + p : (i - 1) * m + (p - m); };
+    Raw<T, V> z[G], v[G], b[G];
+    auto load_group = [&](int p0) {
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int p = min(p0 + u, npairs - 1);  // past the end: a repeat, never used
+        const long row = row_of(p);
+        const bool is_a = p < m;
+        z[u].load((is_a ? Za : Zb) + row * ld + ch);
+        v[u].load((is_a ? Ca : Cb) + row * ld + ch);
+        b[u].load((is_a ? Ba : Bb) + (long)(is_a ? p : p - m) * c + ch);
+      }
+    };
+    // pass 1: max (log2 units), denominator and weighted sum, as the forward
+    float mx[V], den[V], acc[V];
+    for (int p0 = 0; p0 < npairs; p0 += G) {
+      load_group(p0);
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (p0 + u >= npairs) break;
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          const float l = (z[u].at(q) + b[u].at(q)) * kLog2e;
+          const float x = v[u].at(q);
+          if (p0 + u == 0) {
+            mx[q] = l;
+            den[q] = 1.f;
+            acc[q] = x;
+          } else {
+            const float d = l - mx[q];
+            const float e = exp2_fast(-fabsf(d));
+            const bool up = d > 0.f;
+            acc[q] = up ? fmaf(acc[q], e, x) : fmaf(e, x, acc[q]);
+            den[q] = up ? fmaf(den[q], e, 1.f) : den[q] + e;
+            mx[q] = up ? l : mx[q];
+          }
+        }
+      }
+    }
+    float out[V], inv[V], dout[V];
+    Vec<float, 4>::load(dC + i * ldd + ch, dout);
+    if constexpr (V == 8) Vec<float, 4>::load(dC + i * ldd + ch + 4, dout + 4);
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      inv[q] = 1.f / den[q];
+      out[q] = acc[q] * inv[q];
+    }
+    // pass 2: per-pair gradients (rows re-read only when 2m > G)
+    for (int p0 = 0; p0 < npairs; p0 += G) {
+      if (npairs > G) load_group(p0);
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int p = p0 + u;
+        if (p >= npairs) break;
+        float gv[V], gl[V];
+#pragma unroll
+        for (int q = 0; q < V; ++q) {
+          const float S = exp2_fast((z[u].at(q) + b[u].at(q)) * kLog2e - mx[q]) * inv[q];
+          gv[q] = S * dout[q];
+          gl[q] = gv[q] * (v[u].at(q) - out[q]);
+        }
+        const long row = row_of(p);
+        const bool is_a = p < m;
+        Vec<T, V>::store((is_a ? dCa : dCb) + row * ldo + ch, gv);
+        Vec<T, V>::store((is_a ? dZa : dZb) + row * ldo + ch, gl);
+        float* sb = s_db + (long)p * W + lane * V;
+#pragma unroll
+        for (int q = 0; q < V; ++q) atomicAdd(sb + q, gl[q]);
+      }
+    }
+  }
+  __syncthreads();
+  // this workgroup's partial bias gradients: part[blockIdx.y][p][ch], p < 2m
+  for (int e = tid; e < 2 * m * 64; e += 64 * kBwdWaves) {
+    const int p = e >> 6, l = e & 63;
+    const int cc = (blockIdx.x * 64 + l) * V;
+    if (cc < c) {
+      float* dst = part + ((long)blockIdx.y * 2 * m + p) * c + cc;
+#pragma unroll
+      for (int q = 0; q < V; ++q) dst[q] = s_db[p * W + l * V + q];
+    }
+  }
+}
+
+// dBa[r][j] = sum_y part[y][r][j], dBb[r][j] = sum_y part[y][m + r][j], the
+// partials summed in a fixed order: 16 slices of y per column, then the
+// slices in index order.
+__global__ __launch_bounds__(1024) void compress_bias_reduce_kernel(long ny, int m, int c,
+                                                                    const float* __restrict__ part,
+                                                                    float* __restrict__ dBa,
+                                                                    float* __restrict__ dBb) {
+  __shared__ float s_sum[16][64];
+  const int col_l = threadIdx.x & 63, slice = threadIdx.x >> 6;
+  const long col = (long)blockIdx.x * 64 + col_l;  // over 2m * c
+  const long ncol = 2L * m * c;
+  float sum = 0.f;
+  if (col < ncol)
+    for (long y = slice; y < ny; y += 16) sum += part[y * ncol + col];
+  s_sum[slice][col_l] = sum;
+  __syncthreads();
+  if (slice == 0 && col < ncol) {
+    float t = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) t += s_sum[s][col_l];
+    const long p = col / c, j = col - p * c;
+    if (p < m) dBa[p * c + j] = t; else dBb[(p - m) * c + j] = t;
+  }
+}
+
+// Workgroup rows of the backward grid and blocks per workgroup row.
+void compress_bwd_grid(long n, int m, long* ny, long* bpw) {
+  const long units = n / m + 1;  // blocks, plus the tail unit
+  const long want = 256;
+  *bpw = std::max(1L, (units + want - 1) / want);
+  *ny = (units + *bpw - 1) / *bpw;
+}
+
+template <typename T, int V>
+hipError_t run_bwd(long n, int m, int c, const void* Ca, const void* Cb, const void* Za, const void* Zb, long ld,
+                   const void* Ba, const void* Bb, const float* dC, long ldd, void* dCa, void* dCb, void* dZa,
+                   void* dZb, long ldo, float* dBa, float* dBb, float* part, hipStream_t s) {
+  long ny, bpw;
+  compress_bwd_grid(n, m, &ny, &bpw);
+  const dim3 grid((unsigned)((c / V + 63) / 64), (unsigned)ny);
+  const uint32_t lds = (uint32_t)(2 * m * 64 * V * sizeof(float));
+  hipError_t e = launch("compress_bwd", compress_bwd_kernel<T, V>, grid, dim3(64 * kBwdWaves), lds, s, n / m, n, m,
+                        c, (const T*)Ca, (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba, (const T*)Bb,
+                        dC, ldd, (T*)dCa, (T*)dCb, (T*)dZa, (T*)dZb, ldo, bpw, part);
+  if (e != hipSuccess) return e;
+  const long ncol = 2L * m * c;
+  return launch("compress_bias_reduce", compress_bias_reduce_kernel, dim3((unsigned)((ncol + 63) / 64)),
+                dim3(1024), 0, s, ny, m, c, (const float*)part, dBa, dBb);
+}
+
 template <typename T, int V>
 hipError_t run(long nblk, int m, int c, const void* Ca, const void* Cb, const void* Za,
                const void* Zb, long ld, const void* Ba, const void* Bb, void* out, long ldo,
@@ -230,6 +439,27 @@ hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const v
                                   hipStream_t s) {
   if (nseq == 0) return hipSuccess;
   return dispatch(dt, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, (int)nseq, cu, boff, s);
+}
+
+size_t compress_backward_workspace_bytes(long n, int m, int c) {
+  long ny, bpw;
+  compress_bwd_grid(n, m, &ny, &bpw);
+  return (size_t)ny * 2 * m * c * sizeof(float);
+}
+
+hipError_t launch_compress_backward(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
+                                    const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
+                                    const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
+                                    long ld_out, float* dBa, float* dBb, void* workspace, hipStream_t s) {
+  float* part = (float*)workspace;
+  if (dt == CSA_F32)
+    return run_bwd<float, 4>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out, dBa,
+                             dBb, part, s);
+  if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
+    return run_bwd<bf16_t, 8>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
+                              dBa, dBb, part, s);
+  return run_bwd<bf16_t, 4>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out, dBa,
+                            dBb, part, s);
 }
 
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,

@@ -48,6 +48,14 @@ hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const v
                                   const int64_t* cu, const int64_t* boff, long nblk, void* out, long ld_out,
                                   hipStream_t s);
 
+// Backward of eqs 3-4 (see csa_compress_backward); the workspace holds the
+// per-workgroup partial bias gradients.
+size_t compress_backward_workspace_bytes(long n, int m, int c);
+hipError_t launch_compress_backward(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
+                                    const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
+                                    const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
+                                    long ld_out, float* dBa, float* dBb, void* workspace, hipStream_t s);
+
 // Decode-time append (one new token per sequence); see csa_compress_append.
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,
                                   const void* Ba, const void* Bb, const int64_t* t_new, const int64_t* kv_off,
@@ -111,5 +119,12 @@ hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float 
                       const void* q, const void* C, const int32_t* q_seq,
                       const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
                       void* workspace, hipStream_t s);
+
+// Backward of eq 11 (see csa_sparse_mqa_backward): bf16, c = 512.
+size_t mqa_backward_workspace_bytes(long n_queries, int nh, int k, long rows);
+hipError_t launch_mqa_backward(long nq, int nh, int k, float scale, const void* q, const void* C, long rows,
+                               const int32_t* q_seq, const int64_t* kv_off, const int32_t* idx, const void* o,
+                               const float* lse, const void* dO, void* dq, float* dC, void* workspace,
+                               hipStream_t s);
 
 }  // namespace csa

@@ -31,14 +31,6 @@ namespace {
 
 constexpr int kHG = 64;  // heads per pass (4 waves x 16)
 
-template <typename T> __device__ __forceinline__ void frag_set(Frag<T>& f, int j, T v);
-template <> __device__ __forceinline__ void frag_set<bf16_t>(Frag<bf16_t>& f, int j, bf16_t v) {
-  f.v[j] = __builtin_bit_cast(__bf16, v);
-}
-template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int j, float v) {
-  f.f[j] = v;
-}
-
 // Copies ROWS rows of C (row ids in lanes 0..ROWS-1 of `myid`) into LDS rows
 // row0 .. row0+ROWS-1 of Cs (pitch CPITCH elements), using one wave.  A slot
 // with id -1 receives finite filler from `fallback`; its logit is masked to
@@ -100,31 +92,6 @@ __device__ __forceinline__ void wave_gather(const T* __restrict__ Cb, int myid, 
       }
     }
   }
-}
-
-// A-operand fragment of C_sel^T for the output product: rows = output dims
-// dim0 .. dim0+15, contraction slots = keys key0 + 8g .. key0 + 8g + 7, taken
-// from row-major LDS rows of C_sel (pitch `pitch` elements).  bf16 uses two
-// transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane
-// s points at 4 consecutive columns dim0 + 4(s%4) of row key0 + 8g + s/4 (+4),
-// and lane j receives column dim0 + j of those four rows.  fp32 reads the 8
-// values one by one.
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-template <typename T>
-__device__ __forceinline__ Frag<T> frag_ct(const T* Cs, int pitch, int key0, int dim0, int lane) {
-  Frag<T> f;
-  const int g = lane >> 4, s = lane & 15;
-  if constexpr (sizeof(T) == 2) {
-    typedef __attribute__((address_space(3))) bf16x4 lds4;
-    const T* p0 = Cs + (key0 + 8 * g + (s >> 2)) * pitch + dim0 + 4 * (s & 3);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)p0);
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(p0 + 4 * pitch));
-    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) frag_set<T>(f, jj, Cs[(key0 + 8 * g + jj) * pitch + dim0 + (lane & 15)]);
-  }
-  return f;
 }
 
 template <typename T> __device__ __forceinline__ void store4(T* p, const float* v);

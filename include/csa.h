@@ -145,6 +145,42 @@ csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, co
                                int64_t ld_out, void* stream);
 
 /*
+ * csa_compress_backward -- gradients of eqs 3-4 (section "Compressed Key-Value
+ * Entries") for one sequence, given dCcomp = dL/dCcomp.  For block i and
+ * channel j, with S_r the softmax weights of its 2m pairs (value v_r, logit
+ * l_r = Z_r + B_r) and out = Ccomp[i, j]:
+ *
+ *   dv_r = S_r * dCcomp[i, j],   dl_r = S_r * dCcomp[i, j] * (v_r - out),
+ *
+ * dl_r going to both Z_r and B_r.  Each projected row gets its a-gradients
+ * (dCa, dZa) from its own block and its b-gradients (dCb, dZb) from the next
+ * block; rows that no block reads get zeros.  The bias gradients sum over
+ * blocks: dBa[r, j] = sum_i dl of a-row r of block i, dBb likewise over the
+ * b-rows of blocks 1 .. floor(n/m)-1.
+ *
+ *   Ca, Cb, Za, Zb      [n, c]  forward inputs, leading dimension ld_in, dtype dt
+ *   Ba, Bb              [m, c]  forward biases, contiguous, dtype dt
+ *   dCcomp              [floor(n/m), c]  fp32, leading dimension ld_dc
+ *   dCa, dCb, dZa, dZb  [n, c]  outputs, dtype dt, leading dimension ld_out
+ *                       (they may be column slices of one [n, >= 4c] gradient
+ *                       buffer, the layout of the forward projection output)
+ *   dBa, dBb            [m, c]  fp32 outputs, contiguous, overwritten
+ *   workspace           csa_compress_backward_workspace bytes, 16-byte aligned;
+ *                       per-workgroup partial bias gradients, summed by a second
+ *                       kernel in a fixed order (the result is deterministic)
+ *
+ * Arithmetic is fp32 (the forward statistics are recomputed from the inputs).
+ * n >= 0, 1 <= m <= 16, c > 0 and a multiple of 4.  Every output row is
+ * written exactly once; nothing is accumulated into the caller's buffers.
+ */
+csa_status csa_compress_backward_workspace(int64_t n, int32_t m, int32_t c, size_t* bytes);
+csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, const void* Ca, const void* Cb,
+                                 const void* Za, const void* Zb, int64_t ld_in, const void* Ba, const void* Bb,
+                                 const float* dCcomp, int64_t ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
+                                 int64_t ld_out, float* dBa, float* dBb, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * csa_index_topk -- eq 8 scores and the eq 9 selection for a batch of queries.
  *
  * Query r belongs to sequence seq = q_seq[r] (q_seq NULL: 0) and sits at token
@@ -215,6 +251,45 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa_sparse_mqa_backward -- gradients of eq 11 (section "Shared Key-Value
+ * MQA") given dO = dL/do.  With P[r, h, s] = exp(scale q[r, h] . C_s - lse[r, h])
+ * over the selected rows C_s = Ccomp[kv_offset[seq] + idx[r, s]] (the
+ * forward's softmax, from its lse) and D[r, h] = dO[r, h] . o[r, h]:
+ *
+ *   dS       = P * (dO[r, h] . C_s - D[r, h])
+ *   dq[r, h] = scale * sum_s dS C_s
+ *   dCcomp[kv_offset[seq] + idx[r, s]] += sum_h P dO[r, h] + scale * sum_h dS q[r, h]
+ *
+ * summed over every query and slot that selects a row (each selected entry
+ * is both key and value, so both paths add to it).  Slots holding -1 add
+ * nothing.
+ *
+ *   q, dO, o  [n_queries, n_h, c]  bf16, contiguous (o and lse are the forward's outputs)
+ *   lse       [n_queries, n_h]     fp32
+ *   Ccomp     [n_rows, c]          bf16, contiguous
+ *   idx, q_seq, kv_offset          as csa_sparse_mqa
+ *   dq        [n_queries, n_h, c]  bf16 output
+ *   dCcomp    [n_rows, c]          fp32 output, overwritten (rows nobody selects get 0)
+ *   workspace csa_sparse_mqa_backward_workspace bytes, 16-byte aligned
+ *
+ * Each query's key-gradient share of each selected row is written to the
+ * workspace as a bf16 row (rounded once, after fp32 accumulation); the shares
+ * are then grouped by row with a counting sort and summed in fp32.  Queries
+ * are processed in passes of at most 2^21 (query, slot) pairs per 64-head
+ * group, which bounds the workspace at about 2 GiB.  The order of the fp32
+ * additions into dCcomp is not fixed (atomic adds at segment boundaries).
+ * Supported: bf16, c = 512, 1 <= n_h <= 256, 1 <= k <= 2^20.  Entries of idx
+ * must lie in [-1, number of rows of the query's sequence).
+ */
+csa_status csa_sparse_mqa_backward_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, int64_t n_rows,
+                                             size_t* bytes);
+csa_status csa_sparse_mqa_backward(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k, float scale,
+                                   const void* q, const void* Ccomp, int64_t n_rows, const int32_t* q_seq,
+                                   const int64_t* kv_offset, const int32_t* idx, const void* o, const float* lse,
+                                   const void* dO, void* dq, float* dCcomp, void* workspace, size_t ws_bytes,
+                                   void* stream);
+
+/*
  * Packed sequences (a prefill of several sequences in one call).  Sequence b
  * owns projected rows cu_seqlens[b] .. cu_seqlens[b+1]-1 (cu_seqlens: n_seqs + 1
  * non-decreasing int64 on the device, cu_seqlens[0] = 0); each sequence is
@@ -278,7 +353,9 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
  * and returns, for the kernel family `name` ("gemm", "gemm_smallm"
  * (bf16 projections of 16 rows or fewer), "compress", "compress_append",
  * "indexer_sweep", "indexer_prefill", "varlen_meta", "hist_clear", "topk",
- * "mqa", "mqa_combine"),
+ * "mqa", "mqa_combine", and for the backward "compress_bwd",
+ * "compress_bias_reduce", "mqa_bwd", "mqa_bwd_zero", "mqa_bwd_sort",
+ * "mqa_bwd_reduce"),
  * the summed duration in milliseconds and the number of launches since the
  * last reset.  Unknown names give 0 launches.
  */

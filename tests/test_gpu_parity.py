@@ -119,6 +119,80 @@ def test_compress_mean_pool_exact():
     assert np.array_equal(out.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("dtype,n,m,c", [
+    ("f32", 64, 4, 64), ("bf16", 1030, 4, 512), ("bf16", 37, 8, 12), ("f32", 3, 4, 16), ("bf16", 4, 4, 64),
+    ("f32", 2000, 16, 40), ("bf16", 9000, 1, 128), ("bf16", 0, 4, 64), ("bf16", 70001, 4, 512),
+])
+def test_compress_backward(dtype, n, m, c):
+    """Gradients of eqs 3-4: inputs and outputs are column slices of [n, 4c'] buffers (as the forward
+    projection lays them out); the output buffer starts full of a sentinel, so every row must be written."""
+    rng = synth.rng_for(3 * n + m + c)
+    cp = (c + 7) // 8 * 8
+    P = draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = draw(rng, (n, 4 * cp), 2.0, dtype)
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
+    Ba = draw(rng, (m, c), 0.5, dtype)
+    Bb = draw(rng, (m, c), 0.5, dtype)
+    N = n // m
+    dC = rng.standard_normal(size=(N, cp), dtype=np.float32)
+    Pd = to_device(P, dtype, DEV)
+    sl = [Pd[:, i * cp:i * cp + c] for i in range(4)]
+    dCd = torch.from_numpy(dC).to(DEV)[:, :c]
+    G = torch.full((n, 4 * cp), 7.0, dtype=TD[dtype], device=DEV)
+    gs = [G[:, i * cp:i * cp + c] for i in range(4)]
+    dBa = torch.full((m, c), 7.0, device=DEV)
+    dBb = torch.full((m, c), 7.0, device=DEV)
+    api.csa_compress_backward(*sl, to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV), m, dCd, *gs, dBa, dBb)
+    torch.cuda.synchronize()
+    P64 = f64(P, dtype)
+    parts = [P64[:, i * cp:i * cp + c] for i in range(4)]
+    if n > 20000:  # the oracle on sampled blocks: blocks 0, 1, a middle one and the last two, plus the tail
+        blocks = sorted({0, 1, N // 2, N - 2, N - 1})
+        for i in blocks:
+            lo = max(i - 1, 0) * m
+            hi = min((i + 2) * m, n)  # block i's rows, the rows feeding it, and the next block (b-gradients)
+            sub = [x[lo:hi] for x in parts]
+            j = i - lo // m
+            dsub = np.zeros((hi // m - lo // m, c))
+            dsub[j] = dC[i, :c]
+            ref = O.compress_backward(*sub, f64(Ba, dtype), f64(Bb, dtype), m, dsub)
+            # rows of block i: a-gradients from block i alone (dsub is zero for its neighbours)
+            a0, a1 = i * m - lo, (i + 1) * m - lo
+            for w, gi in ((0, 0), (2, 2)):
+                assert_rows_close(to_np64(gs[gi][i * m:(i + 1) * m]), ref[w][a0:a1], what=f"block {i} a-grad {gi}")
+            if i > 0:  # block i's b-gradients land on block i-1's rows
+                b0, b1 = (i - 1) * m - lo, i * m - lo
+                for w, gi in ((1, 1), (3, 3)):
+                    got = to_np64(gs[gi][(i - 1) * m:i * m])
+                    assert_rows_close(got, ref[w][b0:b1], what=f"block {i} b-grad {gi}")
+        tail = to_np64(G[N * m:])
+        assert np.all(tail[:, :c] == 0) and np.all(tail[:, 2 * cp:2 * cp + c] == 0)
+        assert np.all(to_np64(G[(N - 1) * m:])[:, cp:cp + c] == 0)
+        # the bias gradients: the per-position sums of the dZ rows the GPU wrote (a property that holds at any
+        # size), recomputed in float64 from the GPU's own per-row gradients
+        dZa = to_np64(gs[2])[:N * m].reshape(N, m, c)
+        dZb = to_np64(gs[3])[:(N - 1) * m].reshape(N - 1, m, c)
+        for got, want, mag in ((dBa, dZa.sum(0), np.abs(dZa).sum(0)), (dBb, dZb.sum(0), np.abs(dZb).sum(0))):
+            err = np.abs(to_np64(got) - want)
+            assert np.all(err <= 1e-2 * mag + 1e-6), f"bias gradient off by {err.max()}"
+        return
+    ref = O.compress_backward(*parts, f64(Ba, dtype), f64(Bb, dtype), m, dC[:, :c].astype(np.float64))
+    for w in range(4):
+        got = to_np64(gs[w])
+        if n:
+            assert_rows_close(got, ref[w], what=f"grad {w}")
+    # bias gradients: error bounded relative to the sum of the magnitudes of the terms they add up
+    mag_a = np.abs(ref[2][:N * m]).reshape(N, m, c).sum(0) if N else np.zeros((m, c))
+    mag_b = np.abs(ref[3][:(N - 1) * m]).reshape(N - 1, m, c).sum(0) if N > 1 else np.zeros((m, c))
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    for got, want, mag in ((dBa, ref[4], mag_a), (dBb, ref[5], mag_b)):
+        err = np.abs(to_np64(got) - want)
+        assert np.all(err <= tol * mag + 1e-7), f"bias gradient off by {err.max()}"
+    if n:  # the padding columns between the slices are untouched
+        pad = to_np64(G).reshape(n, 4, cp)[:, :, c:]
+        assert np.all(pad == 7.0)
+
+
 # ---------------------------------------------------------------------------
 # indexer + top-k (eqs 8-9)
 # ---------------------------------------------------------------------------
@@ -365,6 +439,51 @@ def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
             assert np.all(np.isneginf(got))
         else:
             assert np.allclose(got, rl, rtol=1e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("B,nh,k,nblk,qps,layout", [
+    (40, 64, 64, 100, 1, "prefix"),     # one 64-head group, an empty and a short selection
+    (37, 20, 100, 150, 3, "scatter"),   # partial head tile, k not a multiple of the chunk, -1 between slots
+    (24, 128, 96, 70, 4, "ragged"),     # two head groups summed into one key gradient
+    (33, 64, 512, 700, 11, "ragged"),   # long selections; 11 queries share each sequence's rows
+    (4200, 16, 512, 600, 700, "prefix"),  # over 2^21 (query, slot) pairs: the shares are summed in two passes
+])
+def test_sparse_mqa_backward(B, nh, k, nblk, qps, layout):
+    """Gradients of eq 11 against the oracle: dq per query and head, dCcomp per compressed row (queries of a
+    sequence share its rows, so every row collects several queries' shares).  o and lse come from the
+    library's own forward, as in training."""
+    c = 512
+    rng = synth.rng_for(B * nh + k + nblk)
+    nseq = (B + qps - 1) // qps
+    C = draw(rng, (nseq * nblk, c), 1.0, "bf16")
+    q = draw(rng, (B, nh, c), 4.0 / math.sqrt(c), "bf16")
+    dO = draw(rng, (B, nh, c), 1.0, "bf16")
+    ncand = np.full(B, nblk)
+    ncand[-1] = 0
+    if B > 2:
+        ncand[1] = min(nblk, k // 2 + 1)
+    if layout != "prefix":
+        ncand = rng.integers(0, nblk + 1, size=B)
+        ncand[0] = 0
+    idx = synth.random_selection(rng, ncand, k)
+    if layout == "scatter":
+        idx = np.stack([rng.permutation(row) for row in idx])
+    q_seq = (np.arange(B) // qps).astype(np.int32)
+    off = np.arange(nseq, dtype=np.int64) * nblk
+    qd, Cd, dOd = to_device(q, "bf16", DEV), to_device(C, "bf16", DEV), to_device(dO, "bf16", DEV)
+    idxd = torch.from_numpy(idx).to(DEV)
+    qsd, offd = torch.from_numpy(q_seq).to(DEV), torch.from_numpy(off).to(DEV)
+    o = torch.empty(B, nh, c, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, nh, dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(c)
+    api.csa_sparse_mqa(qd, Cd, idxd, scale, o, lse, q_seq=qsd, kv_offset=offd)
+    dq = torch.full((B, nh, c), 9.0, dtype=torch.bfloat16, device=DEV)
+    dC = torch.full((nseq * nblk, c), 9.0, dtype=torch.float32, device=DEV)
+    api.csa_sparse_mqa_backward(qd, Cd, idxd, scale, o, lse, dOd, dq, dC, q_seq=qsd, kv_offset=offd)
+    torch.cuda.synchronize()
+    ref_dq, ref_dC = O.sparse_mqa_backward(f64(q, "bf16"), f64(C, "bf16"), idx, off[q_seq], scale, f64(dO, "bf16"))
+    assert_rows_close(to_np64(dq), ref_dq, what="dq")
+    assert_rows_close(to_np64(dC), ref_dC, what="dCcomp")
 
 
 # ---------------------------------------------------------------------------
