@@ -38,6 +38,10 @@ _SIGS = {
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_project": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                    _i64, _vp]),
+    "csa_project_backward_workspace": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.POINTER(_sz)]),
+    "csa_project_backward": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
+                                            _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "csa_compress": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                     _i64, _vp]),
     "csa_compress_append": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
@@ -153,6 +157,39 @@ def csa_project(X: torch.Tensor, Wt: torch.Tensor, Y: torch.Tensor) -> torch.Ten
                              _rowmajor(Wt, "Wt"), _ptr(Y), _rowmajor(Y, "Y"), _stream(X.device)),
            "csa_project")
     return Y
+
+
+def csa_project_backward_workspace(dtype, M: int, N: int, K: int, want_dx: bool, want_dw: bool) -> int:
+    b = _sz(0)
+    dt = CSA_F32 if dtype == torch.float32 else CSA_BF16
+    _check(lib().csa_project_backward_workspace(dt, M, N, K, int(want_dx), int(want_dw), ctypes.byref(b)),
+           "csa_project_backward_workspace")
+    return b.value
+
+
+def csa_project_backward(X, Wt, dY, dX=None, dWt=None, workspace=None):
+    """Gradients of Y = X . Wt^T: dX [M, K] = dY . Wt, dWt [N, K] = dY^T . X (either may be None; views allowed)."""
+    M, K = X.shape
+    N = Wt.shape[0]
+    if Wt.shape[1] != K or tuple(dY.shape) != (M, N) or X.dtype != Wt.dtype or dY.dtype != X.dtype:
+        raise CSAError("csa_project_backward: shape or dtype mismatch")
+    out = dX if dX is not None else dWt
+    if out is None:
+        return dX, dWt
+    if dX is not None and (tuple(dX.shape) != (M, K) or dX.dtype != out.dtype):
+        raise CSAError("csa_project_backward: dX must be [M, K]")
+    if dWt is not None and (tuple(dWt.shape) != (N, K) or dWt.dtype != out.dtype):
+        raise CSAError("csa_project_backward: dWt must be [N, K] of the dX dtype")
+    need = csa_project_backward_workspace(X.dtype, M, N, K, dX is not None, dWt is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=X.device)
+    _check(lib().csa_project_backward(_dt(X), _dt(out), M, N, K, _ptr(X), _rowmajor(X, "X"), _ptr(Wt),
+                                      _rowmajor(Wt, "Wt"), _ptr(dY), _rowmajor(dY, "dY"), _ptr(dX),
+                                      _rowmajor(dX, "dX") if dX is not None else K, _ptr(dWt),
+                                      _rowmajor(dWt, "dWt") if dWt is not None else K, _ptr(workspace),
+                                      workspace.numel(), _stream(X.device)),
+           "csa_project_backward")
+    return dX, dWt
 
 
 def csa_compress(Ca, Cb, Za, Zb, Ba, Bb, m: int, Ccomp: torch.Tensor) -> torch.Tensor:

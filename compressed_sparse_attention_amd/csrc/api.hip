@@ -216,6 +216,75 @@ csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, 
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_project launch");
 }
 
+namespace {
+// Workspace of csa_project_backward: W = Wt^T [K, N] (for dX); dY^T [N, M8] and X^T [K, M8] (for dWt).
+struct ProjBwdLayout {
+  size_t w, dyt, xt, total;
+};
+ProjBwdLayout proj_bwd_layout(csa_dtype dt, int64_t M, int64_t N, int64_t K, bool want_dx, bool want_dw) {
+  const size_t e = dt == CSA_F32 ? 4 : 2;
+  const int64_t M8 = (M + 7) / 8 * 8;
+  ProjBwdLayout L;
+  L.w = 0;
+  L.dyt = want_dx ? align256((size_t)K * N * e) : 0;
+  L.xt = L.dyt + (want_dw ? align256((size_t)N * M8 * e) : 0);
+  L.total = L.xt + (want_dw ? align256((size_t)K * M8 * e) : 0);
+  return L;
+}
+}  // namespace
+
+csa_status csa_project_backward_workspace(csa_dtype in_dt, int64_t M, int64_t N, int64_t K, int want_dx, int want_dw,
+                                          size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_project_backward_workspace: null bytes");
+  CSA_REQUIRE(dtype_ok(in_dt), "csa_project_backward_workspace: unknown dtype");
+  CSA_REQUIRE(M >= 0 && N > 0 && K > 0, "csa_project_backward_workspace: bad sizes");
+  *bytes = proj_bwd_layout(in_dt, M, N, K, want_dx != 0, want_dw != 0).total;
+  return CSA_OK;
+}
+
+csa_status csa_project_backward(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, int64_t K, const void* X,
+                                int64_t ldx, const void* Wt, int64_t ldw, const void* dY, int64_t ldy, void* dX,
+                                int64_t ld_dx, void* dWt, int64_t ld_dw, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  CSA_REQUIRE(dtype_ok(in_dt) && dtype_ok(out_dt), "csa_project_backward: unknown dtype");
+  CSA_REQUIRE(!(in_dt == CSA_F32 && out_dt == CSA_BF16),
+              "csa_project_backward: (F32 in, BF16 out) is not a supported combination");
+  CSA_REQUIRE(M >= 0 && N > 0 && K > 0, "csa_project_backward: M >= 0, N > 0, K > 0 required");
+  CSA_REQUIRE(N % 8 == 0 && K % 8 == 0, "csa_project_backward: N and K must be multiples of 8");
+  CSA_REQUIRE(dY && (dX == nullptr || Wt) && (dWt == nullptr || X), "csa_project_backward: null pointer");
+  CSA_REQUIRE(dWt == nullptr || M > 0, "csa_project_backward: dWt needs M > 0");
+  const int v = vec_elems(in_dt);
+  CSA_REQUIRE(aligned16(X) && aligned16(Wt) && aligned16(dY) && aligned16(dX) && aligned16(dWt) &&
+                  aligned16(workspace),
+              "csa_project_backward: pointers must be 16-byte aligned");
+  CSA_REQUIRE(ldx >= K && ldw >= K && ldy >= N && ld_dx >= K && ld_dw >= K,
+              "csa_project_backward: leading dimension smaller than row length");
+  CSA_REQUIRE(ldx % v == 0 && ldw % v == 0 && ldy % v == 0, "csa_project_backward: input rows must stay 16-byte aligned");
+  CSA_REQUIRE(ld_dx % vec_elems(out_dt) == 0 && ld_dw % vec_elems(out_dt) == 0,
+              "csa_project_backward: output rows must stay 16-byte aligned");
+  const ProjBwdLayout L = proj_bwd_layout(in_dt, M, N, K, dX != nullptr, dWt != nullptr);
+  if (L.total > 0 && (workspace == nullptr || ws_bytes < L.total))
+    return fail(CSA_ERR_WORKSPACE, "csa_project_backward: workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t M8 = (M + 7) / 8 * 8;
+  hipError_t e = hipSuccess;
+  if (dX && M > 0) {  // dX [M, K] = dY [M, N] . W^T, W^T stored as W = Wt^T [K, N]
+    e = csa::launch_transpose(in_dt, N, K, N, Wt, ldw, ws + L.w, N, s);
+    if (e == hipSuccess) e = csa::launch_gemm(in_dt, out_dt, M, K, N, dY, ldy, ws + L.w, N, dX, ld_dx, s);
+    if (e != hipSuccess) return hip_fail(e, "csa_project_backward (dX) launch");
+  }
+  if (dWt) {  // dWt [N, K] = dY^T [N, M] . X [M, K]; contraction over the (zero-padded) tokens
+    e = csa::launch_transpose(in_dt, M, N, M8, dY, ldy, ws + L.dyt, M8, s);
+    if (e == hipSuccess) e = csa::launch_transpose(in_dt, M, K, M8, X, ldx, ws + L.xt, M8, s);
+    if (e == hipSuccess) e = csa::launch_gemm(in_dt, out_dt, N, K, M8, ws + L.dyt, M8, ws + L.xt, M8, dWt, ld_dw, s);
+    if (e != hipSuccess) return hip_fail(e, "csa_project_backward (dWt) launch");
+  }
+  return CSA_OK;
+}
+
 csa_status csa_compress(csa_dtype dt, int64_t n, int32_t m, int32_t c, const void* Ca,
                         const void* Cb, const void* Za, const void* Zb, int64_t ld_in,
                         const void* Ba, const void* Bb, void* Ccomp, int64_t ld_out,

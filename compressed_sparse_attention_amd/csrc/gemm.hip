@@ -334,6 +334,37 @@ __global__ __launch_bounds__(256) void gemm_smallm_kernel(int M, int N, int K, c
   }
 }
 
+// ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c] for r < R, c < C, and dst[c][r] = 0 for R <= r < Rp
+// (the padded tail of each destination row).  64 x 64 tiles through LDS with
+// 16-byte loads and stores; requires C, Rp, the leading dimensions and both
+// pointers to be multiples of 16 bytes.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(long R, long C, long Rp, const T* __restrict__ src, long lds,
+                                                        T* __restrict__ dst, long ldd) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int PR = 64 / VEC;             // 16-byte pieces per 64-element row
+  constexpr int PITCH = 64 + VEC;          // padded LDS row
+  __shared__ __attribute__((aligned(16))) T tile[64 * PITCH];
+  const long r0 = (long)blockIdx.y * 64, c0 = (long)blockIdx.x * 64;
+  for (int p = threadIdx.x; p < 64 * PR; p += 256) {
+    const int r = p / PR, ch = (p % PR) * VEC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < R && c0 + ch < C) v = *reinterpret_cast<const u32x4*>(src + (r0 + r) * lds + c0 + ch);
+    *reinterpret_cast<u32x4*>(&tile[r * PITCH + ch]) = v;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < 64 * PR; p += 256) {
+    const int cc = p / PR, rc = (p % PR) * VEC;
+    if (c0 + cc >= C || r0 + rc >= Rp) continue;
+    T v[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) v[j] = tile[(rc + j) * PITCH + cc];
+    *reinterpret_cast<u32x4*>(dst + (c0 + cc) * ldd + r0 + rc) = *reinterpret_cast<const u32x4*>(v);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
@@ -372,6 +403,17 @@ hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K
                   (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
   return launch("gemm", gemm_nt_kernel<bf16_t, float>, grid, dim3(256), 0, s, (int)M, (int)N, (int)K,
                 (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
+}
+
+hipError_t launch_transpose(csa_dtype dt, long R, long C, long Rp, const void* src, long lds, void* dst, long ldd,
+                            hipStream_t s) {
+  if (R == 0 && Rp == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((Rp + 63) / 64));
+  if (dt == CSA_F32)
+    return launch("transpose", transpose_kernel<float>, grid, dim3(256), 0, s, R, C, Rp, (const float*)src, lds,
+                  (float*)dst, ldd);
+  return launch("transpose", transpose_kernel<bf16_t>, grid, dim3(256), 0, s, R, C, Rp, (const bf16_t*)src, lds,
+                (bf16_t*)dst, ldd);
 }
 
 }  // namespace csa

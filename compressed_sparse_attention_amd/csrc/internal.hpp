@@ -37,6 +37,10 @@ hipError_t launch(const char* family, F kernel, dim3 grid, dim3 block, uint32_t 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s);
 
+// dst[c][r] = src[r][c] (r < R, c < C), zeros for R <= r < Rp; 16-byte granules.
+hipError_t launch_transpose(csa_dtype dt, long R, long C, long Rp, const void* src, long lds, void* dst, long ldd,
+                            hipStream_t s);
+
 hipError_t launch_compress(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
                            const void* Za, const void* Zb, long ld_in, const void* Ba,
                            const void* Bb, void* out, long ld_out, hipStream_t s);

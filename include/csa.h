@@ -91,6 +91,30 @@ csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, 
                        int64_t ldy, void* stream);
 
 /*
+ * csa_project_backward -- gradients of Y = X . W (eqs 1, 2, 5, 6, 7 and 10)
+ * given dY, with W stored transposed as for csa_project:
+ *
+ *   dX  [M, K] = dY . W^T           (skipped when dX is NULL)
+ *   dWt [N, K] = dY^T . X  (= (dL/dW)^T, the layout of Wt; skipped when dWt is NULL)
+ *
+ *   X [M, K], Wt [N, K], dY [M, N]  dtype in_dt, row-major with leading dimensions ldx, ldw, ldy
+ *   dX, dWt                         dtype out_dt, leading dimensions ld_dx, ld_dw
+ *
+ * Both products run on the projection GEMM kernels after the operands are
+ * transposed into the workspace (csa_project_backward_workspace bytes:
+ * K x N for dX, (N + K) x roundup(M, 8) for dWt, elements of in_dt; the
+ * token axis is zero-padded to a multiple of 8).  Accumulation is fp32.
+ * Supported (in_dt, out_dt) as csa_project; N and K multiples of 8; dWt
+ * needs M > 0.
+ */
+csa_status csa_project_backward_workspace(csa_dtype in_dt, int64_t M, int64_t N, int64_t K, int want_dx, int want_dw,
+                                          size_t* bytes);
+csa_status csa_project_backward(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, int64_t K, const void* X,
+                                int64_t ldx, const void* Wt, int64_t ldw, const void* dY, int64_t ldy, void* dX,
+                                int64_t ld_dx, void* dWt, int64_t ld_dw, void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/*
  * csa_compress -- eqs 3-4: for every block i = 0 .. floor(n/m)-1 and channel j,
  * softmax over the 2m logits Z^a[m*i+r, j] + B^a[r, j] and
  * Z^b[m*(i-1)+r, j] + B^b[r, j] (r < m), then
@@ -355,7 +379,7 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
  * "indexer_sweep", "indexer_prefill", "varlen_meta", "hist_clear", "topk",
  * "mqa", "mqa_combine", and for the backward "compress_bwd",
  * "compress_bias_reduce", "mqa_bwd", "mqa_bwd_zero", "mqa_bwd_sort",
- * "mqa_bwd_reduce"),
+ * "mqa_bwd_reduce", "transpose"),
  * the summed duration in milliseconds and the number of launches since the
  * last reset.  Unknown names give 0 launches.
  */

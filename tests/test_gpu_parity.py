@@ -57,6 +57,30 @@ def test_project(din, dout, M, N, K):
     assert_rows_close(to_np64(Y), O.project(f64(X, din), f64(W, din)), what="project")
 
 
+@pytest.mark.parametrize("din,dout,M,N,K", [
+    ("f32", "f32", 77, 40, 24),          # token count not a multiple of 8 (zero-padded contraction)
+    ("bf16", "bf16", 1000, 1536, 4096),  # large-tile kernels for both products
+    ("bf16", "f32", 130, 64, 200),
+    ("bf16", "bf16", 8, 4096, 4096),     # few-row kernel for dX
+    ("bf16", "bf16", 3, 64, 200),
+])
+def test_project_backward(din, dout, M, N, K):
+    """dX = dY W^T and dW^T = dY^T X against the oracle's gradients of Y = X W."""
+    rng = synth.rng_for(M * 5 + N + K)
+    X = draw(rng, (M, K), 1.0, din)
+    W = draw(rng, (K, N), 1.0 / math.sqrt(K), din)
+    dY = draw(rng, (M, N), 1.0, din)
+    Xd, dYd = to_device(X, din, DEV), to_device(dY, din, DEV)
+    Wt = to_device(np.ascontiguousarray(W.T), din, DEV)
+    dX = torch.full((M, K), 7.0, dtype=TD[dout], device=DEV)
+    dWt = torch.full((N, K), 7.0, dtype=TD[dout], device=DEV)
+    api.csa_project_backward(Xd, Wt, dYd, dX, dWt)
+    torch.cuda.synchronize()
+    ref_dX, ref_dW = O.project_backward(f64(X, din), f64(W, din), f64(dY, din))
+    assert_rows_close(to_np64(dX), ref_dX, what="dX")
+    assert_rows_close(to_np64(dWt), ref_dW.T, what="dWt")
+
+
 def test_project_strided_views():
     """Input column slice (ldx > K) and output column slice of a wider buffer (ldy > N)."""
     rng = synth.rng_for(99)
