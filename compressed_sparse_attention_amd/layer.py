@@ -102,6 +102,55 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
     return buf
 
 
+class PrefillGrads:
+    """Gradient buffers of one prefill shape (reused across calls).  Weight gradients are kept in the
+    transposed layout of the weights they belong to (W_H_t, W_UQ_t); bias gradients are fp32."""
+
+    def __init__(self, n: int, m: int, k: int, nh: int, c: int, cI: int, dc: int, d: int, dtype, device):
+        width = 4 * c + 4 * cI + dc
+        N = n // m
+        self.dO = None
+        self.dq = torch.empty(n, nh * c, dtype=dtype, device=device)
+        self.dCcomp = torch.empty(max(N, 1), c, dtype=torch.float32, device=device)[:N]
+        self.dY_H = torch.zeros(n, width, dtype=dtype, device=device)  # indexer columns stay zero
+        self.dH = torch.empty(n, d, dtype=dtype, device=device)
+        self.dW_H_t = torch.empty(width, d, dtype=dtype, device=device)
+        self.dW_UQ_t = torch.empty(nh * c, dc, dtype=dtype, device=device)
+        self.dB_a = torch.empty(m, c, dtype=torch.float32, device=device)
+        self.dB_b = torch.empty(m, c, dtype=torch.float32, device=device)
+        ws = max(api.csa_sparse_mqa_backward_workspace(n, nh, c, k, N),
+                 api.csa_compress_backward_workspace(n, m, c),
+                 api.csa_project_backward_workspace(dtype, n, nh * c, dc, True, True),
+                 api.csa_project_backward_workspace(dtype, n, width, d, True, True))
+        self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
+
+
+def prefill_backward(H: torch.Tensor, W: Dict[str, torch.Tensor], buf: PrefillBuffers, dO: torch.Tensor, m: int,
+                     k: int, nh: int, scale: Optional[float] = None,
+                     grads: Optional[PrefillGrads] = None) -> PrefillGrads:
+    """Gradients of sum(dO * o) after ``prefill`` filled ``buf``: eq 11, eqs 3-4, eq 10, then eqs 1, 2, 5.
+
+    The selection (eqs 6-9) passes no gradient, so the indexer's columns of dY_H stay zero and its
+    weights get none.
+    """
+    n, d = H.shape
+    c, cI, dc = W["c"], W["cI"], W["dc"]
+    if grads is None:
+        grads = PrefillGrads(n, m, k, nh, c, cI, dc, d, H.dtype, H.device)
+    g = grads
+    sc = 1.0 / math.sqrt(c) if scale is None else scale
+    api.csa_sparse_mqa_backward(buf.q.view(n, nh, c), buf.Ccomp, buf.idx, sc, buf.o, buf.lse, dO,
+                                g.dq.view(n, nh, c), g.dCcomp, workspace=g.ws)  # eq 11
+    Y, dY = buf.Y_H, g.dY_H
+    api.csa_compress_backward(Y[:, 0:c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:4 * c], W["B_a"], W["B_b"], m,
+                              g.dCcomp, dY[:, 0:c], dY[:, c:2 * c], dY[:, 2 * c:3 * c], dY[:, 3 * c:4 * c],
+                              g.dB_a, g.dB_b, workspace=g.ws)  # eqs 3-4
+    o = 4 * c + 4 * cI
+    api.csa_project_backward(Y[:, o:], W["W_UQ_t"], g.dq, dX=dY[:, o:], dWt=g.dW_UQ_t, workspace=g.ws)  # eq 10
+    api.csa_project_backward(H, W["W_H_t"], dY, dX=g.dH, dWt=g.dW_H_t, workspace=g.ws)  # eqs 1, 2, 5
+    return g
+
+
 class VarlenPrefill:
     """Buffers and offsets of a prefill of several packed sequences (token rows of sequence b:
     cu[b] .. cu[b+1]-1; its compressed entries: rows block_offset[b] .. block_offset[b+1]-1)."""

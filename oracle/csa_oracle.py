@@ -53,6 +53,7 @@ __all__ = [
     "project", "compress", "compress_weights", "n_candidates", "index_scores",
     "index_scores_row", "topk", "topk_rows", "mqa", "prefill", "prefill_rows",
     "decode", "project_backward", "compress_backward", "mqa_backward", "sparse_mqa_backward",
+    "prefill_backward",
 ]
 
 
@@ -396,4 +397,35 @@ def sparse_mqa_backward(q, Ccomp, idx, row_offset, scale: float, dO) -> Tuple[np
         dq[r], dc = mqa_backward(q[r], Cc[rows], scale, dO[r])
         np.add.at(dC, rows, dc)
     return dq, dC
+
+
+def prefill_backward(P: Dict[str, np.ndarray], m: int, k: int, n_h: int, n_hI: int, dO,
+                     scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(dO * o) for the prefill of ``prefill`` (eqs 1-11).
+
+    The selection of eq 9 is piecewise constant in every input, so no
+    gradient flows through eqs 6-9 (the indexer's own training objective is
+    not part of the method as described): the indexer weights get none, and
+    H collects the gradients of eqs 1-2 (through compression, eqs 3-4) and of
+    eq 5 (through the attention queries, eq 10).  Returns dH, the gradients of
+    W_aKV, W_bKV, W_aZ, W_bZ, B_a, B_b, W_DQ and W_UQ, plus dq and dCcomp.
+    """
+    H = _f64(P["H"])
+    n = H.shape[0]
+    fwd = prefill(P, m, k, n_h, n_hI, scale)
+    c = fwd["Ccomp"].shape[1]
+    sc = default_scale(c) if scale is None else scale
+    dq, dCcomp = sparse_mqa_backward(fwd["q"], fwd["Ccomp"], fwd["idx"], np.zeros(n, np.int64), sc, dO)
+    proj = {name: project(H, P[name]) for name in ("W_aKV", "W_bKV", "W_aZ", "W_bZ")}
+    dCa, dCb, dZa, dZb, dBa, dBb = compress_backward(proj["W_aKV"], proj["W_bKV"], proj["W_aZ"], proj["W_bZ"],
+                                                     P["B_a"], P["B_b"], m, dCcomp)
+    dcQ, dW_UQ = project_backward(fwd["cQ"], P["W_UQ"], dq.reshape(n, n_h * c))
+    g = {"dq": dq, "dCcomp": dCcomp, "B_a": dBa, "B_b": dBb, "W_UQ": dW_UQ}
+    dH = np.zeros_like(H)
+    for name, dY in (("W_aKV", dCa), ("W_bKV", dCb), ("W_aZ", dZa), ("W_bZ", dZb), ("W_DQ", dcQ)):
+        dX, dW = project_backward(H, P[name], dY)
+        dH += dX
+        g[name] = dW
+    g["H"] = dH
+    return g
 

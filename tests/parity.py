@@ -4,6 +4,14 @@
   compared per row: max_j |gpu - ref| / max_j |ref| <= 2e-2 (fp32
   accumulation, bf16 storage).  Rows whose reference is all zero must be
   within 1e-6 absolutely.
+* Gradients that are sums over tokens (weight gradients X^T dY) are
+  compared against the size of their terms: max_j |gpu - ref| <= 2e-2 *
+  max_j (|X|^T |dY|) per row, since cancellation between tokens can make a
+  row's maximum far smaller than the bf16 rounding of the terms it sums.
+* dq of the attention backward: the library forms D = dO . o from the
+  stored (bf16) forward output, which moves dq by up to
+  scale |dO|_2 |o - o_bf16|_2 max|o| <= scale |dO|_2 2^-8 |o|_2 max|o|
+  per head; that bound is added to the row tolerance.
 * Top-k index sets: with tau the reference's k-th largest score of a row and
   eps = 1e-3 |tau| + 1e-6 max|score|, the GPU set G must hold every
   candidate scoring above tau + eps and nothing scoring below tau - eps;
@@ -44,6 +52,33 @@ def assert_rows_close(gpu, ref, tol=ROW_TOL, what=""):
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} rows exceed {tol}; "
                            f"worst row {worst} rel {rel[worst]:.3e}")
     return float(rel.max()) if rel.size else 0.0
+
+
+def assert_sum_rows_close(gpu, ref, term_scale, tol=ROW_TOL, what=""):
+    """Rows of a sum over tokens: error within tol of the row's largest |X|^T |dY| entry."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(-1, np.shape(gpu)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(gpu.shape)
+    scale = np.asarray(term_scale, dtype=np.float64).reshape(gpu.shape).max(axis=1)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    rel = np.abs(gpu - ref).max(axis=1) / np.where(scale > 0, scale, 1.0)
+    worst = int(np.argmax(rel))
+    assert np.all(rel <= tol), f"{what}: worst row {worst} rel {rel[worst]:.3e} of its term scale"
+    return float(rel.max())
+
+
+def assert_dq_close(gpu, ref, dO, o, scale, tol=ROW_TOL, what="dq"):
+    """dq rows [.., heads, c]: row tolerance plus the bound of the stored-output rounding (see above)."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(-1, np.shape(gpu)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(gpu.shape)
+    dO = np.asarray(dO, dtype=np.float64).reshape(gpu.shape)
+    o = np.asarray(o, dtype=np.float64).reshape(gpu.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU output"
+    extra = scale * np.linalg.norm(dO, axis=1) * 2.0 ** -8 * np.linalg.norm(o, axis=1) * np.abs(o).max(axis=1)
+    err = np.abs(gpu - ref).max(axis=1)
+    allowed = tol * np.abs(ref).max(axis=1) + extra + 1e-7
+    worst = int(np.argmax(err / allowed))
+    assert np.all(err <= allowed), f"{what}: row {worst} off by {err[worst]:.3e} (allowed {allowed[worst]:.3e})"
+    return float((err / allowed).max())
 
 
 def check_topk_row(sel_row: np.ndarray, scores: np.ndarray, k: int, rel: float = TOPK_REL):

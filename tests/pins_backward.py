@@ -20,9 +20,10 @@ import numpy as np
 
 def backward_ns():
     from oracle import csa_oracle as O
-    return SimpleNamespace(compress=O.compress, mqa=O.mqa, project=O.project,
+    return SimpleNamespace(compress=O.compress, mqa=O.mqa, project=O.project, prefill=O.prefill,
                            compress_backward=O.compress_backward, mqa_backward=O.mqa_backward,
-                           sparse_mqa_backward=O.sparse_mqa_backward, project_backward=O.project_backward)
+                           sparse_mqa_backward=O.sparse_mqa_backward, project_backward=O.project_backward,
+                           prefill_backward=O.prefill_backward)
 
 
 def _fd_grad(loss, args, which, h=1e-5):
@@ -224,6 +225,39 @@ def check_project_backward(ns, rng):
     _close((dW * W).sum(), s, "bilinear (W)")
 
 
+# ---------------------------------------------------------------------------
+# whole layer: the composed gradient against central differences of the prefill
+# ---------------------------------------------------------------------------
+
+
+def check_prefill_backward_fd(ns, rng):
+    """Every parameter that reaches the output, perturbed element by element; the selection must not
+    move under the perturbation (it is piecewise constant), which the check verifies."""
+    from pins import tiny_params
+    n, d, c, cI, m, dc, nh, nhI, k = 13, 4, 3, 2, 2, 3, 2, 2, 3
+    P = tiny_params(rng, n, d, c, cI, m, dc, nh, nhI)
+    dO = rng.standard_normal((n, nh, c))
+    base = ns.prefill(P, m, k, nh, nhI)
+    g = ns.prefill_backward(P, m, k, nh, nhI, dO)
+
+    def loss_for(name):
+        def loss(x):
+            Q = dict(P)
+            Q[name] = x
+            out = ns.prefill(Q, m, k, nh, nhI)
+            assert np.array_equal(out["idx"], base["idx"]), "selection moved under the perturbation"
+            return float((dO * out["o"]).sum())
+        return loss
+
+    for name in ("H", "W_aKV", "W_bKV", "W_aZ", "W_bZ", "B_a", "B_b", "W_DQ", "W_UQ"):
+        fd = _fd_grad(lambda x: loss_for(name)(x), [P[name]], 0, h=1e-6)
+        np.testing.assert_allclose(g[name], fd, rtol=1e-5, atol=1e-7, err_msg=name)
+    # the indexer's parameters do not reach the output (the selection is piecewise constant)
+    for name in ("W_UQI", "W_w", "W_aKV_I"):
+        fd = _fd_grad(lambda x: loss_for(name)(x), [P[name]], 0, h=1e-6)
+        np.testing.assert_allclose(fd, 0.0, atol=1e-7, err_msg=name)
+
+
 ALL_BACKWARD_CHECKS = [
     ("compress_backward_fd", check_compress_backward_fd),
     ("compress_backward_identities", check_compress_backward_identities),
@@ -232,4 +266,5 @@ ALL_BACKWARD_CHECKS = [
     ("mqa_backward_special", check_mqa_backward_special),
     ("sparse_mqa_backward", check_sparse_mqa_backward),
     ("project_backward", check_project_backward),
+    ("prefill_backward_fd", check_prefill_backward_fd),
 ]

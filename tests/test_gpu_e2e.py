@@ -6,9 +6,9 @@ import torch
 
 from compressed_sparse_attention_amd import synth
 from compressed_sparse_attention_amd.layer import (DecodeState, decode, decode_step, pack_prefill_params,
-                                                     prefill, prefill_varlen, to_device)
+                                                     prefill, prefill_backward, prefill_varlen, to_device)
 from oracle import csa_oracle as O
-from parity import assert_rows_close, check_topk, to_np64
+from parity import assert_dq_close, assert_rows_close, assert_sum_rows_close, check_topk, to_np64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -50,6 +50,59 @@ def test_prefill_workload1_fp32():
     lse = buf.lse.cpu().numpy()
     assert np.all(np.isneginf(lse[: w.m]))  # tokens t < m select nothing
     assert np.all(to_np64(buf.o)[: w.m] == 0)
+
+
+def test_prefill_backward_layer():
+    """Gradients of the whole layer (eq 11, eqs 3-4, eq 10, eqs 1, 2, 5) against the oracle's chain rule.
+
+    512 tokens with k = 128 > floor(511 / 4): every query selects all of its candidates, so the GPU and the
+    oracle attend over identical sets and the gradients are comparable row by row (a selection that
+    differed on a near-tie would move a whole row's gradient)."""
+    w = synth.Workload("prefill_grad_n512_bf16", "prefill", "bf16", m=4, c=512, cI=64, nhI=4, nh=16, k=128,
+                       n=512, d=256, dc=128)
+    P = synth.make_prefill(w, seed=11)
+    rng = synth.rng_for(12)
+    dO = synth.normal(rng, (w.n, w.nh, w.c), 1.0, "bf16")
+    W = pack_prefill_params(P, w.dtype, DEV)
+    H = to_device(P["H"], w.dtype, DEV)
+    buf = prefill(H, W, w.m, w.k, w.nh, w.nhI)
+    g = prefill_backward(H, W, buf, to_device(dO, "bf16", DEV), w.m, w.k, w.nh)
+    torch.cuda.synchronize()
+    P64 = {k: _f64(v, w.dtype) for k, v in P.items()}
+    ref = O.prefill_backward(P64, w.m, w.k, w.nh, w.nhI, _f64(dO, "bf16"))
+    n, c, cI, d = w.n, w.c, w.cI, w.d
+    fwd = O.prefill(P64, w.m, w.k, w.nh, w.nhI)
+    dO64 = _f64(dO, "bf16")
+    H64 = P64["H"]
+    results = {}
+
+    def check(fn, *args, what):
+        try:
+            results[what] = fn(*args, what=what)
+        except AssertionError as e:
+            results[what] = str(e)
+
+    check(assert_dq_close, to_np64(g.dq).reshape(n, w.nh, c), ref["dq"], dO64, fwd["o"], 1.0 / np.sqrt(c), what="dq")
+    check(assert_rows_close, to_np64(g.dCcomp), ref["dCcomp"], what="dCcomp")
+    check(assert_rows_close, to_np64(g.dB_a), ref["B_a"], what="dB_a")
+    check(assert_rows_close, to_np64(g.dB_b), ref["B_b"], what="dB_b")
+    check(assert_rows_close, to_np64(g.dH), ref["H"], what="dH")
+    # weight gradients are sums over the 512 tokens: compared against the size of their terms
+    dq_flat = ref["dq"].reshape(n, w.nh * c)
+    check(assert_sum_rows_close, to_np64(g.dW_UQ_t), ref["W_UQ"].T, np.abs(dq_flat).T @ np.abs(fwd["cQ"]),
+          what="dW_UQ")
+    dCa, dCb, dZa, dZb, _, _ = O.compress_backward(*(O.project(H64, P64[nm]) for nm in ("W_aKV", "W_bKV", "W_aZ",
+                                                                                         "W_bZ")),
+                                                   P64["B_a"], P64["B_b"], w.m, ref["dCcomp"])
+    dWH = to_np64(g.dW_H_t)
+    for i, (name, dY) in enumerate((("W_aKV", dCa), ("W_bKV", dCb), ("W_aZ", dZa), ("W_bZ", dZb))):
+        check(assert_sum_rows_close, dWH[i * c:(i + 1) * c], ref[name].T, np.abs(dY).T @ np.abs(H64),
+              what=f"d{name}")
+    dcQ = dq_flat @ P64["W_UQ"].T
+    check(assert_sum_rows_close, dWH[4 * c + 4 * cI:], ref["W_DQ"].T, np.abs(dcQ).T @ np.abs(H64), what="dW_DQ")
+    assert np.all(dWH[4 * c:4 * c + 4 * cI] == 0)  # the indexer's projections get no gradient
+    print(results)
+    assert all(isinstance(v, float) for v in results.values()), results
 
 
 @pytest.mark.parametrize("cfg", [2, 4, 5])

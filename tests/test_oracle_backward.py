@@ -80,6 +80,12 @@ def _project_token_mean(X, W, dY):  # weight gradient averaged over tokens inste
     return dX, dW / np.shape(X)[0]
 
 
+def _prefill_no_query_weight(P, m, k, nh, nhI, dO, scale=None):  # W_DQ's gradient dropped
+    g = dict(O.prefill_backward(P, m, k, nh, nhI, dO, scale))
+    g["W_DQ"] = np.zeros_like(g["W_DQ"])
+    return g
+
+
 MUTANTS = {
     "mqa_drop_D": dict(mqa_backward=_mqa_bwd(drop_D=True)),
     "mqa_drop_q_term": dict(mqa_backward=_mqa_bwd(drop_q_term=True)),
@@ -90,6 +96,7 @@ MUTANTS = {
     "compress_bias_mean": dict(compress_backward=_compress_bwd("bias_mean")),
     "sparse_overwrite": dict(sparse_mqa_backward=_sparse_overwrite),
     "project_token_mean": dict(project_backward=_project_token_mean),
+    "prefill_no_query_weight": dict(prefill_backward=_prefill_no_query_weight),
 }
 
 
