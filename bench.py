@@ -207,6 +207,62 @@ def bench_prefill(args, torch, api, synth, layer):
             "indexer_roofline": roof}
 
 
+def bench_prefill_backward(args, torch, api, synth, layer):
+    """Backward of the 32768-token prefill (training): sparse-MQA gradients (dq and the key-gradient shares,
+    grouped and summed per compressed entry), compression gradients, and the eq 10 and eqs 1, 2, 5 projection
+    gradients (dX and dW), given a seeded random dL/do."""
+    w = synth.WORKLOADS[3]
+    dev = "cuda:0"
+    P = synth.make_prefill(w)
+    W = layer.pack_prefill_params(P, w.dtype, dev)
+    H = layer.to_device(P["H"], w.dtype, dev)
+    del P
+    buf = layer.prefill(H, W, w.m, w.k, w.nh, w.nhI)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    dO = torch.randn(w.n, w.nh, w.c, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    grads = layer.PrefillGrads(w.n, w.m, w.k, w.nh, w.c, w.cI, w.dc, w.d, H.dtype, dev)
+
+    def run(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            layer.prefill_backward(H, W, buf, dO, w.m, w.k, w.nh, grads=grads)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    run(max(1, args.prefill_warmup))
+    ms = run(args.prefill_steps)
+    api.csa_timing_reset()
+    api.csa_timing_enable(True)
+    run(args.prefill_steps)
+    api.csa_timing_enable(False)
+    names = ["mqa_bwd", "mqa_bwd_zero", "mqa_bwd_sort", "mqa_bwd_reduce", "compress_bwd", "compress_bias_reduce",
+             "transpose", "gemm"]
+    kern = _kernel_stats(api, names)
+    api.csa_timing_reset()
+    print(f"[bench] prefill backward: {ms:.2f} ms per {w.n}-token sequence", flush=True)
+    for n, st in kern.items():
+        print(f"[bench]   {n:20s} {st['total_ms'] / args.prefill_steps:9.3f} ms/step "
+              f"({st['launches'] // args.prefill_steps} launches)", flush=True)
+    pairs = sum(min(w.k, t // w.m) for t in range(w.n))
+    flops = 10.0 * w.nh * w.c * pairs  # S, dP, dq (nh c MACs each) and the two key-gradient paths (2 nh c)
+    mb = kern.get("mqa_bwd")
+    roof = None
+    if mb:
+        per_launch = mb["total_ms"] / mb["launches"]
+        launches_per_step = mb["launches"] // args.prefill_steps
+        ach = flops / launches_per_step / (per_launch * 1e-3) / 1e12
+        roof = {"kernel": "mqa_bwd", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "algorithmic_flops_per_step": flops, "launches_per_step": launches_per_step}
+    return {"workload": w.name + "_backward", "tokens": w.n, "ms": round(ms, 4),
+            "tokens_per_s": round(w.n / (ms * 1e-3), 1),
+            "kernels_ms_per_step": {n: round(st["total_ms"] / args.prefill_steps, 4) for n, st in kern.items()},
+            "mqa_bwd_roofline": roof}
+
+
 def bench_prefill_varlen(args, torch, api, synth, layer):
     """Prefill of 16 packed sequences with ragged lengths (512 .. 4096 tokens, seeded draw) at the layer
     sizes of the 32768-token prefill: one call per stage for the whole batch, each sequence causal on its
@@ -393,6 +449,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode-step", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true")
@@ -413,6 +470,7 @@ def main():
     pre = None if args.no_prefill else bench_prefill(args, torch, api, synth, layer)
     dstep = None if args.no_decode_step else bench_decode_step(args, torch, api, synth, layer)
     pvar = None if args.no_varlen else bench_prefill_varlen(args, torch, api, synth, layer)
+    pbwd = None if args.no_backward else bench_prefill_backward(args, torch, api, synth, layer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     w = dec["workload"]
@@ -446,6 +504,7 @@ def main():
         "prefill": pre,
         "decode_step_with_cache": dstep,
         "prefill_varlen": pvar,
+        "prefill_backward": pbwd,
     }
     print(json.dumps(line), flush=True)
 

@@ -33,8 +33,27 @@
 namespace csa {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void glb_void;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Row gather straight into LDS: lane l's 16 bytes at `src` land at LDS byte
+// offset `lds_base` + 16 l (global_load_lds_dwordx4; m0 holds the base).
+// Issued from asm so that the compiler does not treat every later LDS read
+// as a possible reader of these writes (it would wait for the whole gather
+// right after issuing it); the kernel waits for them itself, with vmcnt, at
+// the top of the next chunk.  No register is written, so nothing is left for
+// the compiler to misread as already loaded.
+__device__ __forceinline__ void gather_row_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have
+// completed; vector memory operations may still be in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(1): every vector memory operation of this wave except the
+// newest one has completed (the counter drains in issue order).
+__device__ __forceinline__ void wait_vm_all_but_one() { __builtin_amdgcn_s_waitcnt(0x0F71); }
 
 constexpr int kBwdCD = 512;             // c
 constexpr int kBwdHeads = 64;           // heads per workgroup
@@ -58,6 +77,30 @@ __device__ __forceinline__ void store4_bf16(bf16_t* p, float a, float b, float c
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// dO of the 64 heads stays in LDS for the whole sweep, rows of 512 without
+// padding, 16-byte chunk j of row h stored at position j ^ f(h).  f is a
+// bijection on the low four bits that sends 16 consecutive rows to 16
+// distinct positions (16-lane reads of one chunk from 16 rows: all banks
+// distinct) and keeps f(h) >> 1 distinct over any 4 aligned consecutive rows
+// (the transposing reads of 4 rows x 2 adjacent chunks: 8 distinct positions).
+__device__ __forceinline__ int dos_at(int row, int col) {
+  const int f = ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+  return row * kBwdCD + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}
+
+// frag_ct over the swizzled dO rows: fragment row j = column dim0 + j,
+// contraction slots = rows row0 + 8g .. row0 + 8g + 7.
+__device__ __forceinline__ Frag<bf16_t> frag_ct_dos(const bf16_t* D, int row0, int dim0, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds4;
+  const int g = lane >> 4, s = lane & 15;
+  const int row = row0 + 8 * g + (s >> 2), col = dim0 + 4 * (s & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + dos_at(row, col)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + dos_at(row + 4, col)));
+  Frag<bf16_t> f;
+  f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return f;
+}
+
 __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, float scale, const bf16_t* __restrict__ q,
                                                       const bf16_t* __restrict__ C, const int32_t* __restrict__ q_seq,
                                                       const int64_t* __restrict__ kv_off,
@@ -67,8 +110,9 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
                                                       long nqc) {
   constexpr int CD = kBwdCD, P = kBwdPitch, KC = kBwdChunk;
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
+  __shared__ __attribute__((aligned(16))) bf16_t s_dO[kBwdHeads * kBwdCD];
   __shared__ float s_D[kBwdHeads], s_lse2[kBwdHeads];
-  __shared__ int32_t s_ids[2][KC];
+  __shared__ int32_t s_ids[3][KC];  // slot ids of chunks ch - 1, ch, ch + 1 (by ch mod 3)
   __shared__ int s_ext[2][8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -86,7 +130,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
   // ---- prologue: q and dO into registers (through LDS), D and lse per head
   const int ht = wave & 3, half = wave >> 2;  // phase A: head tile, dims half
   Frag<bf16_t> qB[8], dB[8];                  // [16 heads of tile ht] x [256 dims of half], by 32-dim step
-  Frag<bf16_t> xA[4][4];                      // [16 dims] x [32 head slots]: wave's dims tiles; dO slots 0..63, q 64..127
+  Frag<bf16_t> xA[4][2];                      // [16 dims] x [32 heads] of q^T: the wave's dims tiles (dO^T: from LDS)
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const bf16_t* src = pass == 0 ? q : dO;
@@ -97,7 +141,8 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
       const bool live = h0 + head < nh;
       const long base = ((long)r * nh + h0 + head) * CD + 8 * lane;
       const u32x4 v = load16_clamped(src + base, live, src);
-      *reinterpret_cast<u32x4*>(&sm.X[head * P + 8 * lane]) = live ? v : u32x4{0u, 0u, 0u, 0u};
+      bf16_t* dst = pass == 0 ? &sm.X[head * P + 8 * lane] : &s_dO[dos_at(head, 8 * lane)];
+      *reinterpret_cast<u32x4*>(dst) = live ? v : u32x4{0u, 0u, 0u, 0u};
       dsum[i] = 0.f;
       if (pass == 1) {
         const u32x4 ov = load16_clamped(o + base, live, o);
@@ -121,15 +166,18 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
         s_lse2[tid] = h0 + tid < nh ? lse[(long)r * nh + h0 + tid] * kLog2e : INFINITY;  // dead heads: P = 0
     }
     __syncthreads();
-    Frag<bf16_t>* B = pass == 0 ? qB : dB;
+    if (pass == 0) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) B[kk].load(&sm.X[(16 * ht + c16) * P + 256 * half + 32 * kk + 8 * g]);
+      for (int kk = 0; kk < 8; ++kk) qB[kk].load(&sm.X[(16 * ht + c16) * P + 256 * half + 32 * kk + 8 * g]);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        xA[dt][2 * (1 - pass) + h2] = frag_ct<bf16_t>(sm.X, P, 32 * h2, 64 * wave + 16 * dt, lane);
-    __syncthreads();
+        for (int h2 = 0; h2 < 2; ++h2) xA[dt][h2] = frag_ct<bf16_t>(sm.X, P, 32 * h2, 64 * wave + 16 * dt, lane);
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) dB[kk].load(&s_dO[dos_at(16 * ht + c16, 256 * half + 32 * kk + 8 * g)]);
+    }
   }
 
   // Chunks to walk: when the valid slots form a prefix (the selector pads
@@ -158,15 +206,53 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
 
   // Gather of chunk ch into buffer b: wave w brings slots 4w .. 4w+3, one
   // 1 KiB row per instruction (lane l's 16 bytes land at row offset 16 l).
-  auto gather = [&](int ch, int b) {
+  // The slot ids come from `ids` (lane j < 4: slot 4w + j of the chunk),
+  // loaded one chunk ahead so that no gather waits for its own id.
+  // (always one load instruction: the id load is the newest vector memory
+  // operation of a chunk, which the wait at the top of the next chunk counts
+  // on).  The raw value is kept as loaded (slots past k are masked when the
+  // ids are used) so that nothing waits for the load where it is issued.
+  auto load_ids = [&](int ch) -> int {
+    const int sl = min(ch, nch - 1) * KC + 4 * wave + (lane & 3);
+    return idx[r * k + min(sl, k - 1)];
+  };
+  auto gather = [&](int ch, int raw) {
+    const int ids = ch * KC + 4 * wave + (lane & 3) < k ? raw : -1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int sl = ch * KC + 4 * wave + j;
-      const int id = sl < k ? idx[r * k + sl] : -1;
+      const int id = __builtin_amdgcn_readlane(ids, j);
       const bf16_t* row = id >= 0 ? Cb + (long)id * CD : q;  // -1: finite filler, weight 0
-      __builtin_amdgcn_global_load_lds((glb_void*)(row + 8 * lane), (lds_void*)&sm.loop.C[b][(4 * wave + j) * P],
-                                       16, 0, 0);
-      if (lane == 0) s_ids[b][4 * wave + j] = id;
+      const uint32_t base = (uint32_t)(size_t)(lds_char*)&sm.loop.C[ch & 1][(4 * wave + j) * P];
+      gather_row_lds(row + 8 * lane, __builtin_amdgcn_readfirstlane(base));
+    }
+    if (lane < 4) s_ids[ch % 3][4 * wave + lane] = ids;
+  };
+
+  // D: the key-gradient shares of chunk pc (from its [P | scale dS] rows in
+  // LDS), 16 keys at a time, stored as bf16 rows of the workspace.
+  auto shares = [&](int pc) {
+    const int* ids = s_ids[pc % 3];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        Frag<bf16_t> b;
+        b.load(&sm.loop.W[(16 * kt + c16) * kBwdWPitch + 32 * kk + 8 * g]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          if (kk < 2) mma(acc[dt], frag_ct_dos(s_dO, 32 * kk, 64 * wave + 16 * dt, lane), b);
+          else mma(acc[dt], xA[dt][kk - 2], b);
+        }
+      }
+      if (ids[16 * kt + c16] >= 0) {
+        const int slot = pc * KC + 16 * kt + c16;
+        bf16_t* dst = part + (((long)hg * nqc + rl) * k + slot) * CD + 64 * wave + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) store4_bf16(dst + 16 * dt, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+      }
     }
   };
 
@@ -176,12 +262,24 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc_dq[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nch > 0) gather(0, 0);
+  int ids_next = 0;
+  if (nch > 0) {
+    const int ids0 = load_ids(0);
+    gather(0, ids0);
+    ids_next = load_ids(1);
+  }
+  // Chunk ch: the shares of chunk ch - 1 are computed and stored first, so
+  // that their writes have a whole chunk of work to drain before the next
+  // wait for this wave's memory operations (the gathers share that counter).
   for (int ch = 0; ch < nch; ++ch) {
-    const int cur = ch & 1;
-    wait_stores();  // this wave's gathers (and earlier share stores) have completed
-    __syncthreads();
-    if (ch + 1 < nch) gather(ch + 1, cur ^ 1);
+    const int cur = ch & 1, sid = ch % 3;
+    // this wave's gathers of chunk ch and the share stores issued after them
+    // have completed; only the id load issued last may be pending
+    wait_vm_all_but_one();
+    lds_barrier();
+    if (ch + 1 < nch) gather(ch + 1, ids_next);
+    if (ch > 0) shares(ch - 1);
+    if (ch + 1 < nch) ids_next = load_ids(ch + 2);
     const bf16_t* Cs = sm.loop.C[cur];
 
     // ---- A: partial S^T, dP^T over this wave's 256 dims, both key tiles
@@ -210,7 +308,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
         x[(4 + rr) * 64] = ad[1 - half][rr];
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- B: P and dS for key tile `half`, heads of tile ht
     {
       const float* x = &sm.loop.xch[ht][half][0][lane];
@@ -222,14 +320,14 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
         const int key = 16 * half + 4 * g + rr;
         const float sv = as[half][rr] + x[rr * 64];
         const float dp = ad[half][rr] + x[(4 + rr) * 64];
-        const float p = s_ids[cur][key] >= 0 ? exp2_fast(sv * scale_log2 - l2) : 0.f;
+        const float p = s_ids[sid][key] >= 0 ? exp2_fast(sv * scale_log2 - l2) : 0.f;
         dsv[rr] = p * (dp - Dh);
         sm.loop.W[key * kBwdWPitch + hl] = f2bf(p);
         sm.loop.W[key * kBwdWPitch + 64 + hl] = f2bf(scale * dsv[rr]);
       }
       store4_bf16(&sm.loop.dS[hl * kBwdSPitch + 16 * half + 4 * g], dsv[0], dsv[1], dsv[2], dsv[3]);
     }
-    __syncthreads();
+    lds_barrier();
     // ---- C: dq^T += C_sel^T dS^T  (wave's 64 dims x 64 heads, 32 keys)
     {
       Frag<bf16_t> bs[4];
@@ -243,26 +341,11 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
           if (nt < NT) mma(acc_dq[dt][nt], a, bs[nt]);
       }
     }
-    // ---- D: the chunk's key-gradient shares, 16 keys at a time
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x4 acc[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        Frag<bf16_t> b;
-        b.load(&sm.loop.W[(16 * kt + c16) * kBwdWPitch + 32 * kk + 8 * g]);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) mma(acc[dt], xA[dt][kk], b);
-      }
-      const int slot = ch * KC + 16 * kt + c16;
-      if (s_ids[cur][16 * kt + c16] >= 0) {
-        bf16_t* dst = part + (((long)hg * nqc + rl) * k + slot) * CD + 64 * wave + 4 * g;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) store4_bf16(dst + 16 * dt, acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-      }
-    }
+  }
+
+  if (nch > 0) {
+    __syncthreads();  // the last chunk's [P | scale dS] rows are complete
+    shares(nch - 1);
   }
 
   // ---- dq = scale * acc  (lane: head 16 nt + c16, dims 4g .. 4g+3 of each tile)
@@ -345,12 +428,60 @@ __global__ __launch_bounds__(256) void pair_fill_kernel(long nqc, int k, long q0
   pkey[pos] = (int32_t)e;
 }
 
+// The same two steps with the counting done in LDS first (entries < kLdsRows):
+// a workgroup histograms kPairsPerWG pairs in LDS and adds each nonzero bin
+// to the global count once, so a popular entry (early blocks are selected
+// by almost every query) takes one global atomic per workgroup instead of
+// one per query.  The fill reserves each bin's run in the entry's list with
+// one global atomic and hands out positions inside it with LDS atomics.
+constexpr int kLdsRows = 16384;
+constexpr int kPairsPerWG = 32768;
+
+template <bool FILL>
+__global__ __launch_bounds__(1024) void pair_bins_kernel(long nqc, int k, long q0, long rows,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ q_seq,
+                                                         const int64_t* __restrict__ kv_off,
+                                                         int32_t* __restrict__ cnt_or_cursor,
+                                                         int32_t* __restrict__ pair, int32_t* __restrict__ pkey) {
+  __shared__ int32_t s_bin[kLdsRows];
+  const int t = threadIdx.x;
+  const long total = nqc * k;
+  const long p0 = (long)blockIdx.x * kPairsPerWG, p1 = min(total, p0 + kPairsPerWG);
+  for (long e = t; e < rows; e += 1024) s_bin[e] = 0;
+  __syncthreads();
+  for (long p = p0 + t; p < p1; p += 1024) {
+    const int id = idx[q0 * k + p];
+    if (id < 0) continue;
+    const long e = entry_of((int)(q0 + p / k), id, q_seq, kv_off);
+    if (e < rows) atomicAdd(&s_bin[e], 1);
+  }
+  __syncthreads();
+  for (long e = t; e < rows; e += 1024) {
+    const int c = s_bin[e];
+    if (c == 0) continue;
+    const int base = atomicAdd(&cnt_or_cursor[e], c);
+    if (FILL) s_bin[e] = base;
+  }
+  if (!FILL) return;
+  __syncthreads();
+  for (long p = p0 + t; p < p1; p += 1024) {
+    const int id = idx[q0 * k + p];
+    if (id < 0) continue;
+    const long e = entry_of((int)(q0 + p / k), id, q_seq, kv_off);
+    if (e >= rows) continue;
+    const int pos = atomicAdd(&s_bin[e], 1);
+    pair[pos] = (int32_t)p;
+    pkey[pos] = (int32_t)e;
+  }
+}
+
 // One wave per segment of kSegPairs consecutive sorted pairs: lane l sums
 // dims 8l .. 8l+7 of the share rows of each entry in the segment (over all
 // head groups) and adds the sum into dC (fp32) when the entry changes, so an
 // entry gets one atomic add per segment it spans.
 constexpr int kSegPairs = 512;
-constexpr int kSegBatch = 4;
+constexpr int kSegBatch = 8;
 
 __global__ __launch_bounds__(256) void share_reduce_kernel(int k, int nhg, long nqc, const int32_t* __restrict__ start,
                                                            long rows, const int32_t* __restrict__ pair,
@@ -474,14 +605,20 @@ hipError_t launch_mqa_backward(long nq, int nh, int k, float scale, const void* 
     if (rows == 0) continue;
     e = zero_words(cnt, rows, s);
     if (e != hipSuccess) return e;
+    const bool lds_bins = rows <= kLdsRows;
     const unsigned pblocks = (unsigned)((nqc * k + 255) / 256);
-    e = launch("mqa_bwd_sort", pair_count_kernel, dim3(pblocks), dim3(256), 0, s, nqc, k, q0, rows, idx, q_seq, kv_off,
-               cnt);
+    const unsigned bblocks = (unsigned)((nqc * k + kPairsPerWG - 1) / kPairsPerWG);
+    e = lds_bins ? launch("mqa_bwd_sort", pair_bins_kernel<false>, dim3(bblocks), dim3(1024), 0, s, nqc, k, q0, rows,
+                          idx, q_seq, kv_off, cnt, (int32_t*)nullptr, (int32_t*)nullptr)
+                 : launch("mqa_bwd_sort", pair_count_kernel, dim3(pblocks), dim3(256), 0, s, nqc, k, q0, rows, idx,
+                          q_seq, kv_off, cnt);
     if (e != hipSuccess) return e;
     e = launch("mqa_bwd_sort", pair_scan_kernel, dim3(1), dim3(1024), 0, s, rows, (const int32_t*)cnt, start, cursor);
     if (e != hipSuccess) return e;
-    e = launch("mqa_bwd_sort", pair_fill_kernel, dim3(pblocks), dim3(256), 0, s, nqc, k, q0, rows, idx, q_seq, kv_off,
-               cursor, pair, pkey);
+    e = lds_bins ? launch("mqa_bwd_sort", pair_bins_kernel<true>, dim3(bblocks), dim3(1024), 0, s, nqc, k, q0, rows,
+                          idx, q_seq, kv_off, cursor, pair, pkey)
+                 : launch("mqa_bwd_sort", pair_fill_kernel, dim3(pblocks), dim3(256), 0, s, nqc, k, q0, rows, idx,
+                          q_seq, kv_off, cursor, pair, pkey);
     if (e != hipSuccess) return e;
     const long segs = (nqc * k + kSegPairs - 1) / kSegPairs;
     e = launch("mqa_bwd_reduce", share_reduce_kernel, dim3((unsigned)((segs + 3) / 4)), dim3(256), 0, s, k, nhg, nqc,

@@ -471,6 +471,7 @@ def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
     (24, 128, 96, 70, 4, "ragged"),     # two head groups summed into one key gradient
     (33, 64, 512, 700, 11, "ragged"),   # long selections; 11 queries share each sequence's rows
     (4200, 16, 512, 600, 700, "prefix"),  # over 2^21 (query, slot) pairs: the shares are summed in two passes
+    (40, 16, 64, 500, 1, "scatter"),    # 20000 compressed rows: the sort counts in global memory, not in LDS
 ])
 def test_sparse_mqa_backward(B, nh, k, nblk, qps, layout):
     """Gradients of eq 11 against the oracle: dq per query and head, dCcomp per compressed row (queries of a
