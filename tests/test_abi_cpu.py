@@ -168,3 +168,50 @@ def test_timing_interface(L):
     api.csa_timing_reset()
     assert api.csa_timing_read("gemm") == (0.0, 0)
     api.csa_timing_enable(False)
+
+
+def test_backward_calls_reject_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def mqa(dt=1, nq=4, nh=64, c=512, k=64, scale=0.05, rows=100, dC=p, ws=p, wsb=1 << 30):
+        return L.csa_sparse_mqa_backward(dt, nq, nh, c, k, scale, p, p, rows, None, None, p, p, p, p, p, dC, ws, wsb,
+                                         None)
+    assert mqa(dt=0) == api.CSA_ERR_UNSUPPORTED  # fp32 attention backward is not built
+    assert mqa(c=256) == api.CSA_ERR_INVALID_ARG
+    assert "512" in _err()
+    assert mqa(nh=0) == api.CSA_ERR_INVALID_ARG
+    assert mqa(k=0) == api.CSA_ERR_INVALID_ARG
+    assert mqa(scale=0.0) == api.CSA_ERR_INVALID_ARG
+    assert mqa(dC=None) == api.CSA_ERR_INVALID_ARG
+    assert mqa(wsb=100) == api.CSA_ERR_WORKSPACE
+    assert mqa(nq=0, rows=0, ws=None) == api.CSA_OK  # nothing to do
+    # the share rows of one pass: at most 2^21 (query, slot) pairs of c bf16 values per head group
+    assert api.csa_sparse_mqa_backward_workspace(4096, 64, 512, 512, 8192) >= (1 << 21) * 512 * 2
+    assert api.csa_sparse_mqa_backward_workspace(100000, 64, 512, 512, 8192) < (1 << 21) * 512 * 2 + (64 << 20)
+
+    def comp(dt=1, n=64, m=4, c=64, ldi=256, ldd=64, ldo=256, ws=p, wsb=1 << 30):
+        return L.csa_compress_backward(dt, n, m, c, p, p, p, p, ldi, p, p, p, ldd, p, p, p, p, ldo, p, p, ws, wsb,
+                                       None)
+    assert comp(m=0) == api.CSA_ERR_INVALID_ARG
+    assert comp(m=17) == api.CSA_ERR_INVALID_ARG  # the bias sums live in LDS: m <= 16
+    assert comp(c=6) == api.CSA_ERR_INVALID_ARG
+    assert comp(ldi=60) == api.CSA_ERR_INVALID_ARG
+    assert comp(ldd=62) == api.CSA_ERR_INVALID_ARG
+    assert comp(wsb=8) == api.CSA_ERR_INVALID_ARG
+    assert "workspace" in _err()
+
+    def proj(M=64, N=64, K=64, dX=p, dW=p, ws=p, wsb=1 << 30, ind=1, outd=1):
+        return L.csa_project_backward(ind, outd, M, N, K, p, K, p, K, p, N, dX, K, dW, K, ws, wsb, None)
+    assert proj(N=60) == api.CSA_ERR_INVALID_ARG
+    assert proj(K=12) == api.CSA_ERR_INVALID_ARG
+    assert proj(M=0) == api.CSA_ERR_INVALID_ARG  # dW needs tokens
+    assert proj(ind=0, outd=1) == api.CSA_ERR_INVALID_ARG  # fp32 in, bf16 out is not a GEMM combination
+    assert proj(wsb=16) == api.CSA_ERR_WORKSPACE
+    # workspace: W^T for dX, dY^T and X^T (tokens padded to 8) for dW
+    assert api.csa_project_backward_workspace(torch_bf16(), 10, 64, 32, True, False) >= 64 * 32 * 2
+    assert api.csa_project_backward_workspace(torch_bf16(), 10, 64, 32, False, True) >= (64 + 32) * 16 * 2
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
