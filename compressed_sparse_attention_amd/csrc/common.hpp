@@ -64,6 +64,14 @@ __device__ __forceinline__ T ld_agent(const T* p) {
 // s_waitcnt vmcnt(0): this thread's loads and stores have completed.
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have
+// completed; its vector memory operations may still be in flight.  (The
+// compiler drains every counter before a plain s_barrier on this target, so
+// a prefetch issued just before __syncthreads() would be waited for there.)
+// Loads whose results are consumed later are still waited for by the
+// compiler at their first use.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Guarded 16-byte load without control flow: loads from p, or from
 // `fallback` (any readable address holding finite input values) when !pred.
 // The value loaded for !pred is NOT zeroed: every caller discards or masks
@@ -165,6 +173,44 @@ __device__ __forceinline__ Frag<T> frag_ct(const T* Cs, int pitch, int key0, int
     for (int jj = 0; jj < 8; ++jj) frag_set<T>(f, jj, Cs[(key0 + 8 * g + jj) * pitch + dim0 + (lane & 15)]);
   }
   return f;
+}
+
+// Rows of 512 bf16 in LDS without padding: 16-byte chunk j of row h is stored
+// at position j ^ f(h).  f is a
+// bijection on the low four bits that sends 16 consecutive rows to 16
+// distinct positions (16-lane reads of one chunk from 16 rows: all banks
+// distinct) and keeps f(h) >> 1 distinct over any 4 aligned consecutive rows
+// (the transposing reads of 4 rows x 2 adjacent chunks: 8 distinct positions).
+__device__ __forceinline__ int swz512_at(int row, int col) {
+  const int f = ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+  return row * 512 + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}
+
+// frag_ct over swizzled 512-column rows: fragment row j = column dim0 + j,
+// contraction slots = rows row0 + 8g .. row0 + 8g + 7.
+__device__ __forceinline__ Frag<bf16_t> frag_ct_swz512(const bf16_t* D, int row0, int dim0, int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds4;
+  const int g = lane >> 4, s = lane & 15;
+  const int row = row0 + 8 * g + (s >> 2), col = dim0 + 4 * (s & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + swz512_at(row, col)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + swz512_at(row + 4, col)));
+  Frag<bf16_t> f;
+  f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return f;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Row gather straight into LDS: lane l's 16 bytes at `src` land at LDS byte
+// offset `lds_base` + 16 l (global_load_lds_dwordx4; m0 holds the base).
+// Issued from asm so that the compiler does not treat every later LDS read
+// as a possible reader of these writes (it would wait for the whole gather
+// right after issuing it); the kernel waits for them itself, with vmcnt, at
+// the top of the next chunk.  No register is written, so nothing is left for
+// the compiler to misread as already loaded.
+__device__ __forceinline__ void gather_row_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);

@@ -297,7 +297,8 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
 // (query, 64-head group), 64-slot chunks, double buffered.  While chunk i is
 // scored and accumulated from one LDS buffer, the rows of chunk i+1 are in
 // flight into registers (and the ids of chunk i+2 are being read), and are
-// stored into the other buffer after the output update.  S^T is split over
+// stored into the other buffer after the output update (the loop's barriers
+// cover LDS only, so those loads stay in flight through them).  S^T is split over
 // (16-head tile, 32-key half) with the per-head max and sum exchanged through
 // LDS; O^T is split over the output dims (c/8 per wave).
 // ---------------------------------------------------------------------------
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
       cm = wave_max_xor_16_32(cm);
       if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
     }
-    __syncthreads();
+    lds_barrier();
     // Lazy rescaling: the reference maximum m_run moves only when a chunk's
     // maximum exceeds it by more than 2^8, so the exponentials stay below 256
     // (exact in the fp32 sums and within bf16's range) and the O^T
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
       }
       m_run = m_new;
     }
-    __syncthreads();
+    lds_barrier();
     if (qlive) {
       const int hl = 16 * ht + c16;
       l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
@@ -524,7 +525,7 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
     }
     // ---- rows of chunk ch+1 land in the other buffer; chunk ch+2 goes in flight
     if (ch + 1 < nch) store_rows(cur ^ 1, ids_nxt);
-    __syncthreads();
+    lds_barrier();
     if (ch + 2 < nch) {
       issue_rows(ids_nn);
       ids_nxt = ids_nn;

@@ -33,24 +33,6 @@
 namespace csa {
 namespace {
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Row gather straight into LDS: lane l's 16 bytes at `src` land at LDS byte
-// offset `lds_base` + 16 l (global_load_lds_dwordx4; m0 holds the base).
-// Issued from asm so that the compiler does not treat every later LDS read
-// as a possible reader of these writes (it would wait for the whole gather
-// right after issuing it); the kernel waits for them itself, with vmcnt, at
-// the top of the next chunk.  No register is written, so nothing is left for
-// the compiler to misread as already loaded.
-__device__ __forceinline__ void gather_row_lds(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Workgroup barrier for LDS traffic only: this wave's LDS operations have
-// completed; vector memory operations may still be in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // s_waitcnt vmcnt(1): every vector memory operation of this wave except the
 // newest one has completed (the counter drains in issue order).
 __device__ __forceinline__ void wait_vm_all_but_one() { __builtin_amdgcn_s_waitcnt(0x0F71); }
@@ -77,29 +59,8 @@ __device__ __forceinline__ void store4_bf16(bf16_t* p, float a, float b, float c
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-// dO of the 64 heads stays in LDS for the whole sweep, rows of 512 without
-// padding, 16-byte chunk j of row h stored at position j ^ f(h).  f is a
-// bijection on the low four bits that sends 16 consecutive rows to 16
-// distinct positions (16-lane reads of one chunk from 16 rows: all banks
-// distinct) and keeps f(h) >> 1 distinct over any 4 aligned consecutive rows
-// (the transposing reads of 4 rows x 2 adjacent chunks: 8 distinct positions).
-__device__ __forceinline__ int dos_at(int row, int col) {
-  const int f = ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
-  return row * kBwdCD + ((((col >> 3) ^ f)) << 3) + (col & 7);
-}
-
-// frag_ct over the swizzled dO rows: fragment row j = column dim0 + j,
-// contraction slots = rows row0 + 8g .. row0 + 8g + 7.
-__device__ __forceinline__ Frag<bf16_t> frag_ct_dos(const bf16_t* D, int row0, int dim0, int lane) {
-  typedef __attribute__((address_space(3))) bf16x4 lds4;
-  const int g = lane >> 4, s = lane & 15;
-  const int row = row0 + 8 * g + (s >> 2), col = dim0 + 4 * (s & 3);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + dos_at(row, col)));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds4*)(D + dos_at(row + 4, col)));
-  Frag<bf16_t> f;
-  f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return f;
-}
+// dO of the 64 heads stays in LDS for the whole sweep in the swizzled
+// 512-column row layout of swz512_at (no padding).
 
 __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, float scale, const bf16_t* __restrict__ q,
                                                       const bf16_t* __restrict__ C, const int32_t* __restrict__ q_seq,
@@ -141,7 +102,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
       const bool live = h0 + head < nh;
       const long base = ((long)r * nh + h0 + head) * CD + 8 * lane;
       const u32x4 v = load16_clamped(src + base, live, src);
-      bf16_t* dst = pass == 0 ? &sm.X[head * P + 8 * lane] : &s_dO[dos_at(head, 8 * lane)];
+      bf16_t* dst = pass == 0 ? &sm.X[head * P + 8 * lane] : &s_dO[swz512_at(head, 8 * lane)];
       *reinterpret_cast<u32x4*>(dst) = live ? v : u32x4{0u, 0u, 0u, 0u};
       dsum[i] = 0.f;
       if (pass == 1) {
@@ -176,7 +137,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
       __syncthreads();
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) dB[kk].load(&s_dO[dos_at(16 * ht + c16, 256 * half + 32 * kk + 8 * g)]);
+      for (int kk = 0; kk < 8; ++kk) dB[kk].load(&s_dO[swz512_at(16 * ht + c16, 256 * half + 32 * kk + 8 * g)]);
     }
   }
 
@@ -243,7 +204,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
         b.load(&sm.loop.W[(16 * kt + c16) * kBwdWPitch + 32 * kk + 8 * g]);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          if (kk < 2) mma(acc[dt], frag_ct_dos(s_dO, 32 * kk, 64 * wave + 16 * dt, lane), b);
+          if (kk < 2) mma(acc[dt], frag_ct_swz512(s_dO, 32 * kk, 64 * wave + 16 * dt, lane), b);
           else mma(acc[dt], xA[dt][kk - 2], b);
         }
       }

@@ -429,6 +429,9 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
     # -1 slots scattered between valid ones (no prefix: every chunk is walked)
     ("bf16", 560, 64, 512, 512, 700, 2.0, "scatter"),
     ("bf16", 4, 64, 512, 512, 700, 2.0, "scatter"),
+    # long batch, c = 512, a partial head group (20 heads) and k not a multiple of the 64-slot chunk
+    ("bf16", 600, 20, 512, 96, 120, 2.0, "scatter"),
+    ("bf16", 530, 100, 512, 200, 250, 4.0, "ragged"),  # two head groups, the second partial
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
     rng = synth.rng_for(B * nh + k)
