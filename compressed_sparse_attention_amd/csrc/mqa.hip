@@ -415,13 +415,17 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
     if (lane < RPW) s_rows[buf][RPW * wave + lane] = ids;
   };
 
-  // prologue: chunk 0 into buffer 0, chunk 1 in flight, ids of chunk 2 requested
-  int ids_cur = load_ids(0);
-  int ids_nxt = nch > 1 ? load_ids(1) : -1;
-  issue_rows(ids_cur);
+  // prologue: chunk 0 into buffer 0, chunk 1 in flight, ids of chunk 2
+  // requested.  The query fragments are loaded before the first rows: their
+  // wait (for the rows, which come later in issue order) then happens here,
+  // not inside the chunk loop, where it would also wait for the loop's
+  // prefetch of the next chunk.
   Frag<bf16_t> qf[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) qf[kk].load_clamped(q + (r * nh + qhead) * CD + 32 * kk + 8 * g, qlive && qhead < nh, q);
+  int ids_cur = load_ids(0);
+  int ids_nxt = nch > 1 ? load_ids(1) : -1;
+  issue_rows(ids_cur);
   store_rows(0, ids_cur);
   if (nch > 1) issue_rows(ids_nxt);
   int ids_nn = nch > 2 ? load_ids(2) : -1;
@@ -625,15 +629,19 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
   // gather depends on them, the fragments are needed only after it
   const int slot_first = (j * cps) * kTileRows + (kTileRows / 4) * wave + lane;
   int raw_first = idx[r * k + (slot_first < k ? slot_first : k - 1)];
-  // the tile's 16 query heads: each wave stages 4 of them in LDS (16-byte pieces)
-  {
-    constexpr int QCH = CD / 8;
+  // the tile's 16 query heads: each wave stages 4 of them in LDS (16-byte
+  // pieces).  The pieces are loaded here but written to LDS only after the
+  // first chunk's gather has been issued, so that their round trip overlaps
+  // the gather's instead of preceding it.
+  constexpr int QCH = CD / 8;
+  constexpr int QN = (4 * QCH + 63) / 64;
+  u32x4 qv[QN];
 #pragma unroll
-    for (int v = lane; v < 4 * QCH; v += 64) {
-      const int hl = 4 * wave + v / QCH, pc = (v % QCH) * 8;
-      const int hh = 16 * ht + hl;
-      *reinterpret_cast<u32x4*>(&s_q[hl * CPITCH + pc]) = load16_clamped(q + (r * nh + hh) * CD + pc, hh < nh, q);
-    }
+  for (int i = 0; i < QN; ++i) {
+    const int v = lane + 64 * i;
+    const int hl = 4 * wave + v / QCH, pc = (v % QCH) * 8;
+    const int hh = 16 * ht + hl;
+    qv[i] = load16_clamped(q + (r * nh + hh) * CD + pc, v < 4 * QCH && hh < nh, q);
   }
   Frag<bf16_t> qf[KSTEPS];
 
@@ -653,6 +661,13 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
       if (lane < RPW) s_rows[RPW * wave + lane] = myid;
       // one wave per SIMD here: all of a wave's rows are in flight at once
       wave_gather<bf16_t, CD, RPW, CPITCH, RPW>(C + off * CD, myid, Cs, RPW * wave, lane, q);
+    }
+    if (ch == 0) {
+#pragma unroll
+      for (int i = 0; i < QN; ++i) {
+        const int v = lane + 64 * i;
+        if (v < 4 * QCH) *reinterpret_cast<u32x4*>(&s_q[(4 * wave + v / QCH) * CPITCH + (v % QCH) * 8]) = qv[i];
+      }
     }
     __syncthreads();
 
