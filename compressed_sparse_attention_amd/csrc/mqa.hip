@@ -26,6 +26,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <algorithm>
+
 namespace csa {
 namespace {
 
@@ -579,6 +581,323 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
 }
 
 // ---------------------------------------------------------------------------
+// Persistent form of the kernel above for c = 512 (long bf16 batches whose
+// splits' slot ids fit in LDS).  One workgroup per CU walks the units
+// u = blockIdx.x, blockIdx.x + gridDim.x, ... (unit = query, 64-head group,
+// split) and keeps the chunk pipeline running across unit boundaries, so a
+// unit's start does not pay its two dependent memory round trips (slot ids,
+// then rows) with the CU otherwise idle: the next unit's slot ids are fetched
+// during the current unit's first chunk and staged after it, its query
+// fragments are fetched after the current unit's last S^T, and its first
+// rows are gathered during the current unit's last chunk.  Rows go straight
+// into LDS (global_load_lds issued from asm, one 1 KiB row per instruction),
+// one chunk ahead; the top of each chunk waits for them explicitly.  A unit
+// whose first rows could not be prefetched (the unit before had a single
+// chunk) gathers them when it starts.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxStaged = 512;  // slot ids of a unit staged in LDS
+
+struct G8Unit {
+  long r;
+  int h0, j, sbeg, send, nch, sb;  // sb: the s_ids buffer holding the unit's slot ids
+  const bf16_t* Cb;
+};
+
+__global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, int k, int nhg, int nsplit, int cps,
+                                                         float scale_log2, const bf16_t* __restrict__ q,
+                                                         const bf16_t* __restrict__ C,
+                                                         const int32_t* __restrict__ q_seq,
+                                                         const int64_t* __restrict__ kv_off,
+                                                         const int32_t* __restrict__ idx,
+                                                         bf16_t* __restrict__ o, float* __restrict__ lse,
+                                                         float* __restrict__ part_o,
+                                                         float* __restrict__ part_ml) {
+  constexpr int CD = 512;
+  constexpr int KS = kG8Chunk;
+  constexpr int CPITCH = CD + 8;
+  constexpr int PPITCH = KS + 8;
+  constexpr int KSTEPS = CD / 32;
+  constexpr int DTPW = CD / 16 / 8;
+  constexpr int RPW = KS / 8;  // rows gathered per wave per chunk
+  __shared__ __attribute__((aligned(16))) bf16_t Cs[2][KS * CPITCH];
+  __shared__ __attribute__((aligned(16))) bf16_t Ps[kHG * PPITCH];
+  __shared__ int32_t s_rows[2][KS];
+  __shared__ float s_red[2][2][kHG];
+  __shared__ float s_alpha[kHG];
+  __shared__ float s_l[kHG];
+  __shared__ int32_t s_ids[2][kStreamMaxStaged];
+  __shared__ int s_ext[2][8];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int ht = wave & 3, kh = wave >> 2;
+  const long stride = gridDim.x;
+
+  auto describe = [&](long u, int sb) -> G8Unit {
+    G8Unit d;
+    d.j = (int)(u % nsplit);
+    const long rest = u / nsplit;
+    d.h0 = (int)(rest % nhg) * kHG;
+    d.r = rest / nhg;
+    const int seq = q_seq ? q_seq[d.r] : 0;
+    d.Cb = C + (kv_off ? kv_off[seq] : 0) * CD;
+    const int nch_all = min(cps, (k - d.j * cps * KS + KS - 1) / KS);
+    d.sbeg = d.j * cps * KS;
+    d.send = min(k, d.sbeg + nch_all * KS);
+    d.nch = nch_all;
+    d.sb = sb;
+    return d;
+  };
+  // slot ids: fetched into a register, staged in LDS (with the test of a
+  // -1-padded prefix that trims trailing chunks), then counted after a barrier
+  int nid = -1;
+  auto fetch_ids = [&](const G8Unit& d) { nid = idx[d.r * k + min(d.sbeg + tid, d.send - 1)]; };
+  auto stage_ids = [&](const G8Unit& d) {
+    const int sl = d.sbeg + tid;
+    int first_bad = 0x7FFFFFFF, last_good = -1;
+    if (sl < d.send) {
+      s_ids[d.sb][tid] = nid;
+      if (nid < 0) first_bad = sl; else last_good = sl;
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      first_bad = min(first_bad, __shfl_xor(first_bad, sh));
+      last_good = max(last_good, __shfl_xor(last_good, sh));
+    }
+    if (lane == 0) {
+      s_ext[0][wave] = first_bad;
+      s_ext[1][wave] = last_good;
+    }
+  };
+  auto count_chunks = [&](G8Unit& d) {
+    int first_bad = 0x7FFFFFFF, last_good = -1;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      first_bad = min(first_bad, s_ext[0][w]);
+      last_good = max(last_good, s_ext[1][w]);
+    }
+    if (last_good < first_bad) d.nch = max(0, (last_good - d.sbeg + KS) / KS);
+  };
+  // rows of chunk c of unit d into buffer b: wave w brings rows RPW w .. +RPW-1
+  auto gather = [&](const G8Unit& d, int c, int b) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = RPW * wave + i;
+      const int sl = d.sbeg + c * KS + row;
+      const int id = __builtin_amdgcn_readfirstlane(sl < d.send ? s_ids[d.sb][sl - d.sbeg] : -1);
+      const bf16_t* src = id >= 0 ? d.Cb + (long)id * CD : q;  // -1: finite filler, weight 0
+      const uint32_t base = (uint32_t)(size_t)(lds_char*)&Cs[b][row * CPITCH];
+      gather_row_lds(src + 8 * lane, __builtin_amdgcn_readfirstlane(base));
+      if (lane == 0) s_rows[b][row] = id;
+    }
+  };
+  Frag<bf16_t> qf[KSTEPS];
+  auto load_q = [&](const G8Unit& d) {
+    const int qhead = d.h0 + 16 * ht + c16;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk].load_clamped(q + (d.r * nh + qhead) * CD + 32 * kk + 8 * g, qhead < nh, q);
+  };
+
+  long u = blockIdx.x;
+  if (u >= nunits) return;
+  G8Unit cu = describe(u, 0), nu;
+  fetch_ids(cu);
+  stage_ids(cu);
+  __syncthreads();
+  count_chunks(cu);
+  bool has_nu = u + stride < nunits, nu_staged = false;
+  if (has_nu) nu = describe(u + stride, 1);
+  load_q(cu);
+  bool q_loaded = true;
+  int bufc = 0;
+  bool first_in_buf = false;  // the current unit's chunk 0 is already in Cs[bufc] (or in flight to it)
+
+  while (true) {
+    if (!q_loaded) load_q(cu);
+    q_loaded = false;
+    if (cu.nch > 0 && !first_in_buf) gather(cu, 0, bufc);
+    first_in_buf = false;
+    const int NT = min(4, (nh - cu.h0 + 15) / 16);
+    const int qhead = cu.h0 + 16 * ht + c16;
+    const bool qlive = ht < NT;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc_o[DTPW][4];
+#pragma unroll
+    for (int dt = 0; dt < DTPW; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc_o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int ch = 0; ch < cu.nch; ++ch) {
+      const int cur = bufc;
+      // this wave's gathers of chunk ch (and everything it issued before
+      // them) have landed; after the barrier, every wave's have
+      wait_stores();
+      lds_barrier();
+      // the next chunk goes in flight into the other buffer (free: chunk
+      // ch - 1 was read before the barrier); the next unit's slot ids are
+      // requested once this unit has started
+      if (ch + 1 < cu.nch) {
+        gather(cu, ch + 1, cur ^ 1);
+      } else if (has_nu && nu_staged && nu.nch > 0) {
+        gather(nu, 0, cur ^ 1);
+        first_in_buf = true;
+      }
+      if (ch == 0 && has_nu) fetch_ids(nu);
+      const bf16_t* Cc = Cs[cur];
+      float x[2][4];
+      float cm = -INFINITY;
+      if (qlive) {
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            Frag<bf16_t> ac;
+            ac.load(&Cc[(32 * kh + 16 * t + c16) * CPITCH + 32 * kk + 8 * g]);
+            mma(acc[t], ac, qf[kk]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int key = 32 * kh + 16 * t + 4 * g + rr;
+            x[t][rr] = s_rows[cur][key] >= 0 ? acc[t][rr] * scale_log2 : -INFINITY;
+            cm = fmaxf(cm, x[t][rr]);
+          }
+        cm = wave_max_xor_16_32(cm);
+        if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
+      }
+      if (ch == cu.nch - 1 && has_nu) {  // the last S^T of this unit: the next unit's query fragments
+        load_q(nu);
+        q_loaded = true;
+      }
+      // the next unit's slot ids are staged behind this unit's first chunk
+      const bool staging = ch == 0 && has_nu;
+      if (staging) stage_ids(nu);
+      lds_barrier();
+      if (staging) {
+        count_chunks(nu);
+        nu_staged = true;
+      }
+      float alpha = 1.f;
+      if (qlive) {
+        const int hl = 16 * ht + c16;
+        const float cmax = fmaxf(s_red[0][0][hl], s_red[0][1][hl]);
+        const float m_new = (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
+        const bool none = (m_new == -INFINITY);
+        alpha = none ? 1.f : exp2_fast(m_run - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float p[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            p[rr] = none ? 0.f : exp2_fast(x[t][rr] - m_new);
+            ps += p[rr];
+          }
+          *reinterpret_cast<uint2*>(&Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g]) =
+              make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+        }
+        ps = wave_sum_xor_16_32(ps);
+        if (g == 0) {
+          s_red[1][kh][hl] = ps;
+          if (kh == 0) s_alpha[hl] = alpha;
+        }
+        m_run = m_new;
+      }
+      lds_barrier();
+      if (qlive) {
+        const int hl = 16 * ht + c16;
+        l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt < NT) {
+          const float a = s_alpha[16 * nt + c16];
+          if (__builtin_amdgcn_read_exec() & __ballot(a != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+          }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS / 32; ++kk) {
+        Frag<bf16_t> bp[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          if (nt < NT) bp[nt].load(&Ps[(16 * nt + c16) * PPITCH + 32 * kk + 8 * g]);
+#pragma unroll
+        for (int dt = 0; dt < DTPW; ++dt) {
+          const Frag<bf16_t> ac = frag_ct<bf16_t>(Cc, CPITCH, 32 * kk, (wave * DTPW + dt) * 16, lane);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            if (nt < NT) mma(acc_o[dt][nt], ac, bp[nt]);
+        }
+      }
+      bufc ^= 1;
+    }
+
+    // ---- finish the unit
+    if (nsplit == 1) {
+      if (qlive && kh == 0 && g == 0) {
+        s_l[16 * ht + c16] = l_run;
+        if (lse && qhead < nh)
+          lse[cu.r * nh + qhead] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int head = cu.h0 + 16 * nt + c16;
+        if (nt < NT && head < nh) {
+          const float l = s_l[16 * nt + c16];
+          const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < DTPW; ++dt) {
+            float v[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) v[rr] = acc_o[dt][nt][rr] * inv;
+            store4<bf16_t>(o + (cu.r * nh + head) * CD + (wave * DTPW + dt) * 16 + 4 * g, v);
+          }
+        }
+      }
+    } else {
+      const long pbase = (cu.r * nsplit + cu.j) * (long)nh;
+      if (qlive && kh == 0 && g == 0 && qhead < nh) {
+        part_ml[(pbase + qhead) * 2] = m_run;
+        part_ml[(pbase + qhead) * 2 + 1] = l_run;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int head = cu.h0 + 16 * nt + c16;
+        if (nt < NT && head < nh) {
+#pragma unroll
+          for (int dt = 0; dt < DTPW; ++dt)
+            *reinterpret_cast<float4*>(part_o + (pbase + head) * CD + (wave * DTPW + dt) * 16 + 4 * g) =
+                make_float4(acc_o[dt][nt][0], acc_o[dt][nt][1], acc_o[dt][nt][2], acc_o[dt][nt][3]);
+        }
+      }
+    }
+    if (!has_nu) break;
+    // ---- switch to the next unit
+    u += stride;
+    if (!nu_staged) {  // this unit had no chunk to stage it behind
+      fetch_ids(nu);
+      stage_ids(nu);
+      __syncthreads();
+      count_chunks(nu);
+    }
+    cu = nu;
+    __syncthreads();  // s_l, s_ext and the other s_ids buffer are free again
+    has_nu = u + stride < nunits;
+    nu_staged = false;
+    if (has_nu) nu = describe(u + stride, cu.sb ^ 1);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Short batches (decode): one workgroup per (query, 16-head tile, split).
 // The split's slots are walked in chunks of kTileRows gathered rows; the four
 // waves share the chunk's keys for S^T (32 keys each, the per-head max and sum
@@ -814,6 +1133,18 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
   if (d4 == 0 && lse) lse[rh] = (M == -INFINITY) ? -INFINITY : (M + log2f(L)) * 0.6931471805599453f;
 }
 
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
+
 struct Plan {
   bool tile;    // short-batch kernel (16-head tiles) instead of the 64-head-group kernels
   bool group8;  // eight-wave double-buffered 64-head-group kernel (bf16, 128 <= c <= 512)
@@ -869,6 +1200,14 @@ hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C
     }
   }
   if constexpr (sizeof(T) == 2 && DTW >= 2 && DTW <= 8) {
+    if (!done && p.group8 && DTW == 8 && (long)p.cps * kG8Chunk <= kStreamMaxStaged) {
+      const long units = nq * p.nhg * p.nsplit;
+      const long grid = std::min(units, (long)compute_units());
+      e = launch("mqa", mqa_stream_kernel, dim3((unsigned)grid), dim3(512), 0, s, units, nh, k, p.nhg, p.nsplit,
+                 p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx, (bf16_t*)o, lse,
+                 part_o, part_ml);
+      done = true;
+    }
     if (!done && p.group8) {
       e = launch("mqa", mqa_group8_kernel<DTW>, dim3((unsigned)(nq * p.nhg * p.nsplit)), dim3(512), 0, s, nh, k,
                  p.nhg, p.nsplit, p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx,
