@@ -16,17 +16,20 @@
 // segmented sum over the sorted pairs.
 //
 // Main kernel: one workgroup of 8 waves per (query, 64-head group), c = 512,
-// bf16.  The query's q and dO stay in registers for the whole sweep, in the
-// two layouts the products need (dims as the contraction axis for the scores,
-// heads as the contraction axis for the key gradient); dq accumulates in
-// registers.  The selection is walked in chunks of 32 slots whose rows are
-// gathered straight into LDS (global_load_lds), double buffered.  Per chunk:
+// bf16.  q and dO stay resident for the whole sweep in the two layouts the
+// products need: dims as the contraction axis for the scores (q and dO
+// fragments in registers) and heads as the contraction axis for the key
+// gradient (q^T fragments in registers, dO^T read from a swizzled LDS copy);
+// dq accumulates in registers.  The selection is walked in chunks of 32 slots
+// whose rows are gathered straight into LDS (asm-issued global_load_lds, one
+// chunk ahead, double buffered; each chunk waits for its rows once).  Per chunk:
 //   A. S^T and dP^T [32 keys x 16 heads] per wave, the 512 dims split in two
 //      halves between wave pairs (partial sums exchanged through LDS);
 //   B. P and dS (the softmax is the forward's: exp(scale q.C - lse));
 //   C. dq^T += C_sel^T dS^T  (dims x heads, contraction over the 32 keys);
 //   D. dC_sel^T = [dO; q]^T [P; scale dS]  (dims x keys, contraction over
-//      the 128 head slots), stored as the chunk's 32 bf16 share rows.
+//      the 128 head slots), stored as the chunk's 32 bf16 share rows at the
+//      top of the next chunk (so that the stores drain during a whole chunk).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -229,9 +232,10 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
     gather(0, ids0);
     ids_next = load_ids(1);
   }
-  // Chunk ch: the shares of chunk ch - 1 are computed and stored first, so
-  // that their writes have a whole chunk of work to drain before the next
-  // wait for this wave's memory operations (the gathers share that counter).
+  // Chunk ch starts by issuing the gather of chunk ch + 1, then computes and
+  // stores the shares of chunk ch - 1: those writes then have a whole chunk of
+  // work to drain before the next wait for this wave's memory operations (the
+  // gathers share that counter), and the id load of chunk ch + 2 comes last.
   for (int ch = 0; ch < nch; ++ch) {
     const int cur = ch & 1, sid = ch % 3;
     // this wave's gathers of chunk ch and the share stores issued after them
