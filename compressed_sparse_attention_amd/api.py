@@ -60,6 +60,10 @@ _SIGS = {
                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "csa_compress_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp,
                                            _vp, _i64, _vp, _i64, _vp]),
+    "csa_compress_backward_varlen_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "csa_compress_backward_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp,
+                                                    _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp,
+                                                    _vp, _vp, _sz, _vp]),
     "csa_index_topk_varlen_workspace": (ctypes.c_int, [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
     "csa_index_topk_varlen": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                              _vp, _i64, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -405,6 +409,51 @@ def csa_compress_varlen(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens, block_offset
                                      _rowmajor(Ccomp, "Ccomp"), _stream(Ca.device)),
            "csa_compress_varlen")
     return Ccomp
+
+
+def csa_compress_backward_varlen_workspace(n_seqs: int, n_blocks: int, m: int, c: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_compress_backward_varlen_workspace(n_seqs, n_blocks, m, c, ctypes.byref(b)),
+           "csa_compress_backward_varlen_workspace")
+    return b.value
+
+
+def csa_compress_backward_varlen(Ca, Cb, Za, Zb, Ba, Bb, m: int, cu_seqlens, block_offset, n_blocks: int, dCcomp,
+                                 dCa, dCb, dZa, dZb, dBa, dBb, workspace=None):
+    """Gradients of eqs 3-4 for packed sequences (the layout of csa_compress_varlen): dCcomp [>= n_blocks, c] fp32;
+    dCa/dCb/dZa/dZb shaped like Ca and sharing one leading dimension; dBa/dBb [m, c] fp32 summed over every
+    sequence's blocks (overwritten)."""
+    n, c = Ca.shape
+    ld = _rowmajor(Ca, "Ca")
+    for t, nm in ((Cb, "Cb"), (Za, "Za"), (Zb, "Zb")):
+        if tuple(t.shape) != (n, c) or _rowmajor(t, nm) != ld or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress_backward_varlen: Ca, Cb, Za, Zb must share shape, dtype and row stride")
+    ldo = _rowmajor(dCa, "dCa")
+    for t, nm in ((dCa, "dCa"), (dCb, "dCb"), (dZa, "dZa"), (dZb, "dZb")):
+        if tuple(t.shape) != (n, c) or _rowmajor(t, nm) != ldo or t.dtype != Ca.dtype:
+            raise CSAError("csa_compress_backward_varlen: dCa, dCb, dZa, dZb must be shaped like Ca, of its dtype, "
+                           "sharing one leading dimension")
+    for t, nm in ((Ba, "Ba"), (Bb, "Bb"), (dBa, "dBa"), (dBb, "dBb")):
+        _contig(t, nm)
+        if tuple(t.shape) != (m, c):
+            raise CSAError(f"csa_compress_backward_varlen: {nm} must be [m, c]")
+    if dBa.dtype != torch.float32 or dBb.dtype != torch.float32 or dCcomp.dtype != torch.float32:
+        raise CSAError("csa_compress_backward_varlen: dCcomp, dBa and dBb are fp32")
+    nseq = cu_seqlens.numel() - 1
+    for t, nm in ((cu_seqlens, "cu_seqlens"), (block_offset, "block_offset")):
+        if t.dtype != torch.int64 or t.numel() != nseq + 1:
+            raise CSAError(f"csa_compress_backward_varlen: {nm} must be int64 [n_seqs + 1]")
+    if dCcomp.dim() != 2 or dCcomp.shape[0] < n_blocks or dCcomp.shape[1] != c:
+        raise CSAError("csa_compress_backward_varlen: dCcomp must be [>= n_blocks, c]")
+    need = csa_compress_backward_varlen_workspace(nseq, n_blocks, m, c)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Ca.device)
+    _check(lib().csa_compress_backward_varlen(
+        _dt(Ca), nseq, m, c, _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), ld, _ptr(Ba), _ptr(Bb), _ptr(cu_seqlens),
+        _ptr(block_offset), n_blocks, _ptr(dCcomp), _rowmajor(dCcomp, "dCcomp") if dCcomp.shape[0] else c,
+        _ptr(dCa), _ptr(dCb), _ptr(dZa), _ptr(dZb), ldo, _ptr(dBa), _ptr(dBb), _ptr(workspace), workspace.numel(),
+        _stream(Ca.device)), "csa_compress_backward_varlen")
+    return dCa, dCb, dZa, dZb, dBa, dBb
 
 
 def csa_index_topk_varlen_workspace(n_seqs: int, n_tokens: int, max_cand: int, k: int) -> int:

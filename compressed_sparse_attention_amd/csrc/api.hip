@@ -313,7 +313,7 @@ csa_status csa_compress_backward_workspace(int64_t n, int32_t m, int32_t c, size
   CSA_REQUIRE(n >= 0, "csa_compress_backward_workspace: n must be >= 0");
   CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_workspace: m must be in [1, 16] (got %d)", m);
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_workspace: c must be a positive multiple of 4");
-  *bytes = csa::compress_backward_workspace_bytes(n, m, c);
+  *bytes = csa::compress_backward_workspace_bytes(n, m, c, 0, 0, false);
   return CSA_OK;
 }
 
@@ -327,7 +327,7 @@ csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, 
   CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward: m must be in [1, 16] (got %d)", m);
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward: c must be a positive multiple of 4 (got %d)", c);
   CSA_REQUIRE(dBa && dBb && workspace, "csa_compress_backward: null pointer");
-  const size_t need = csa::compress_backward_workspace_bytes(n, m, c);
+  const size_t need = csa::compress_backward_workspace_bytes(n, m, c, 0, 0, false);
   CSA_REQUIRE(ws_bytes >= need, "csa_compress_backward: workspace of %zu bytes is smaller than %zu", ws_bytes, need);
   CSA_REQUIRE(aligned16(workspace), "csa_compress_backward: workspace must be 16-byte aligned");
   const int v = vec_elems(dt);
@@ -347,6 +347,55 @@ csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, 
   hipError_t e = csa::launch_compress_backward(dt, n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb,
                                                dZa, dZb, ld_out, dBa, dBb, workspace, (hipStream_t)stream);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_backward launch");
+}
+
+csa_status csa_compress_backward_varlen_workspace(int64_t n_seqs, int64_t n_blocks, int32_t m, int32_t c,
+                                                 size_t* bytes) {
+  CSA_REQUIRE(bytes != nullptr, "csa_compress_backward_varlen_workspace: null bytes");
+  CSA_REQUIRE(n_seqs >= 0 && n_seqs <= 0x7FFFFFFF && n_blocks >= 0,
+              "csa_compress_backward_varlen_workspace: bad n_seqs / n_blocks");
+  CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_varlen_workspace: m must be in [1, 16] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_varlen_workspace: c must be a positive multiple of 4");
+  *bytes = csa::compress_backward_workspace_bytes(0, m, c, n_seqs, n_blocks, true);
+  return CSA_OK;
+}
+
+csa_status csa_compress_backward_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca,
+                                        const void* Cb, const void* Za, const void* Zb, int64_t ld_in,
+                                        const void* Ba, const void* Bb, const int64_t* cu_seqlens,
+                                        const int64_t* block_offset, int64_t n_blocks, const float* dCcomp,
+                                        int64_t ld_dc, void* dCa, void* dCb, void* dZa, void* dZb, int64_t ld_out,
+                                        float* dBa, float* dBb, void* workspace, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress_backward_varlen: unknown dtype");
+  CSA_REQUIRE(n_seqs >= 0 && n_seqs <= 0x7FFFFFFF && n_blocks >= 0, "csa_compress_backward_varlen: bad n_seqs / n_blocks");
+  CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_varlen: m must be in [1, 16] (got %d)", m);
+  CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_varlen: c must be a positive multiple of 4 (got %d)", c);
+  CSA_REQUIRE(dBa && dBb && workspace, "csa_compress_backward_varlen: null pointer");
+  const size_t need = csa::compress_backward_workspace_bytes(0, m, c, n_seqs, n_blocks, true);
+  CSA_REQUIRE(ws_bytes >= need, "csa_compress_backward_varlen: workspace of %zu bytes is smaller than %zu", ws_bytes,
+              need);
+  CSA_REQUIRE(aligned16(workspace), "csa_compress_backward_varlen: workspace must be 16-byte aligned");
+  CSA_REQUIRE(n_seqs > 0 || n_blocks == 0, "csa_compress_backward_varlen: blocks without sequences");
+  const int v = vec_elems(dt);
+  if (n_seqs > 0) {
+    CSA_REQUIRE(Ca && Cb && Za && Zb && Ba && Bb && dCa && dCb && dZa && dZb && cu_seqlens && block_offset,
+                "csa_compress_backward_varlen: null pointer");
+    CSA_REQUIRE(n_blocks == 0 || dCcomp != nullptr, "csa_compress_backward_varlen: null dCcomp");
+    CSA_REQUIRE(aligned16(Ca) && aligned16(Cb) && aligned16(Za) && aligned16(Zb) && aligned16(Ba) &&
+                    aligned16(Bb) && aligned16(dCa) && aligned16(dCb) && aligned16(dZa) && aligned16(dZb) &&
+                    (dCcomp == nullptr || aligned16(dCcomp)),
+                "csa_compress_backward_varlen: pointers must be 16-byte aligned");
+    CSA_REQUIRE(ld_in >= c && ld_out >= c && ld_dc >= c,
+                "csa_compress_backward_varlen: leading dimension smaller than c");
+    CSA_REQUIRE(ld_in % v == 0 && ld_out % v == 0 && ld_dc % 4 == 0,
+                "csa_compress_backward_varlen: leading dimensions must keep rows 16-byte aligned");
+  }
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_compress_backward_varlen(dt, n_seqs, n_blocks, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb,
+                                                      cu_seqlens, block_offset, dCcomp, ld_dc, dCa, dCb, dZa, dZb,
+                                                      ld_out, dBa, dBb, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_backward_varlen launch");
 }
 
 csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, const void* new_rows,

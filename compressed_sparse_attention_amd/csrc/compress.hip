@@ -243,7 +243,8 @@ __global__ __launch_bounds__(64 * kBwdWaves) void compress_bwd_kernel(
     long N, long n, int m, int c, const T* __restrict__ Ca, const T* __restrict__ Cb, const T* __restrict__ Za,
     const T* __restrict__ Zb, long ld, const T* __restrict__ Ba, const T* __restrict__ Bb,
     const float* __restrict__ dC, long ldd, T* __restrict__ dCa, T* __restrict__ dCb, T* __restrict__ dZa,
-    T* __restrict__ dZb, long ldo, long bpw, float* __restrict__ part) {
+    T* __restrict__ dZb, long ldo, long bpw, float* __restrict__ part, int nseq, const int64_t* __restrict__ cu,
+    const int64_t* __restrict__ boff) {
   extern __shared__ float s_db[];  // [2m][64 V]: bias-gradient sums of this workgroup's blocks
   constexpr int G = kBwdRowGroup;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -253,23 +254,42 @@ __global__ __launch_bounds__(64 * kBwdWaves) void compress_bwd_kernel(
   for (int e = tid; e < 2 * m * W; e += 64 * kBwdWaves) s_db[e] = 0.f;
   __syncthreads();
 
-  const long i0 = (long)blockIdx.y * bpw, i1 = min(i0 + bpw, N + 1);
+  // Units 0 .. N-1 are the blocks; then one tail unit per sequence (one in all
+  // without cu) writes zeros to the rows that no block reads.
+  const long units = N + (cu != nullptr ? nseq : 1);
+  const long i0 = (long)blockIdx.y * bpw, i1 = min(i0 + bpw, units);
   for (long i = i0 + wave; live && i < i1; i += kBwdWaves) {
-    if (i == N) {  // rows read by no block
+    long il = i, rbase = 0;  // block index within its sequence, the sequence's first token row
+    if (i >= N) {
+      long len = n;
+      if (cu != nullptr) {
+        rbase = cu[i - N];
+        len = cu[i - N + 1] - rbase;
+      }
+      const long nb = len / m, end = rbase + len;
       const float zero[V] = {};
-      for (long row = N * m; row < n; ++row) {
+      for (long row = rbase + nb * m; row < end; ++row) {
         Vec<T, V>::store(dCa + row * ldo + ch, zero);
         Vec<T, V>::store(dZa + row * ldo + ch, zero);
       }
-      for (long row = N > 0 ? (N - 1) * m : 0; row < n; ++row) {
+      for (long row = rbase + (nb > 0 ? (nb - 1) * m : 0); row < end; ++row) {
         Vec<T, V>::store(dCb + row * ldo + ch, zero);
         Vec<T, V>::store(dZb + row * ldo + ch, zero);
       }
       continue;
     }
+    if (cu != nullptr) {  // block i is block il of the sequence b with boff[b] <= i < boff[b+1]
+      int lo = 0, hi = nseq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (boff[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      il = i - boff[lo];
+      rbase = cu[lo];
+    }
     // Pair p < m is a-row p of block i; pair m + r is b-row r (a row of block i-1).
-    const int npairs = i > 0 ? 2 * m : m;
-    auto row_of = [&](int p) -> long { return p < m ? i * m + p : (i - 1) * m + (p - m); };
+    const int npairs = il > 0 ? 2 * m : m;
+    auto row_of = [&](int p) -> long { return rbase + (p < m ? il * m + p : (il - 1) * m + (p - m)); };
     Raw<T, V> z[G], v[G], b[G];
     auto load_group = [&](int p0) {
 #pragma unroll
@@ -379,24 +399,28 @@ __global__ __launch_bounds__(1024) void compress_bias_reduce_kernel(long ny, int
 }
 
 // Workgroup rows of the backward grid and blocks per workgroup row.
-void compress_bwd_grid(long n, int m, long* ny, long* bpw) {
-  const long units = n / m + 1;  // blocks, plus the tail unit
+void compress_bwd_grid(long units, long* ny, long* bpw) {
   const long want = 256;
   *bpw = std::max(1L, (units + want - 1) / want);
-  *ny = (units + *bpw - 1) / *bpw;
+  *ny = std::max(1L, (units + *bpw - 1) / *bpw);  // one row even with no units: it writes the zero partials
 }
 
+// Backward units: the blocks, then one tail unit per sequence (a single
+// sequence when cu is null).
+long compress_bwd_units(long n, int m, long nseq, long nblk, bool varlen) { return varlen ? nblk + nseq : n / m + 1; }
+
 template <typename T, int V>
-hipError_t run_bwd(long n, int m, int c, const void* Ca, const void* Cb, const void* Za, const void* Zb, long ld,
-                   const void* Ba, const void* Bb, const float* dC, long ldd, void* dCa, void* dCb, void* dZa,
-                   void* dZb, long ldo, float* dBa, float* dBb, float* part, hipStream_t s) {
+hipError_t run_bwd(long n, long nblk, int m, int c, const void* Ca, const void* Cb, const void* Za, const void* Zb,
+                   long ld, const void* Ba, const void* Bb, const float* dC, long ldd, void* dCa, void* dCb,
+                   void* dZa, void* dZb, long ldo, float* dBa, float* dBb, float* part, int nseq, const int64_t* cu,
+                   const int64_t* boff, hipStream_t s) {
   long ny, bpw;
-  compress_bwd_grid(n, m, &ny, &bpw);
+  compress_bwd_grid(compress_bwd_units(n, m, nseq, nblk, cu != nullptr), &ny, &bpw);
   const dim3 grid((unsigned)((c / V + 63) / 64), (unsigned)ny);
   const uint32_t lds = (uint32_t)(2 * m * 64 * V * sizeof(float));
-  hipError_t e = launch("compress_bwd", compress_bwd_kernel<T, V>, grid, dim3(64 * kBwdWaves), lds, s, n / m, n, m,
+  hipError_t e = launch("compress_bwd", compress_bwd_kernel<T, V>, grid, dim3(64 * kBwdWaves), lds, s, nblk, n, m,
                         c, (const T*)Ca, (const T*)Cb, (const T*)Za, (const T*)Zb, ld, (const T*)Ba, (const T*)Bb,
-                        dC, ldd, (T*)dCa, (T*)dCb, (T*)dZa, (T*)dZb, ldo, bpw, part);
+                        dC, ldd, (T*)dCa, (T*)dCb, (T*)dZa, (T*)dZb, ldo, bpw, part, nseq, cu, boff);
   if (e != hipSuccess) return e;
   const long ncol = 2L * m * c;
   return launch("compress_bias_reduce", compress_bias_reduce_kernel, dim3((unsigned)((ncol + 63) / 64)),
@@ -441,25 +465,46 @@ hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const v
   return dispatch(dt, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, out, ld_out, (int)nseq, cu, boff, s);
 }
 
-size_t compress_backward_workspace_bytes(long n, int m, int c) {
+size_t compress_backward_workspace_bytes(long n, int m, int c, long nseq, long nblk, bool varlen) {
   long ny, bpw;
-  compress_bwd_grid(n, m, &ny, &bpw);
+  compress_bwd_grid(compress_bwd_units(n, m, nseq, nblk, varlen), &ny, &bpw);
   return (size_t)ny * 2 * m * c * sizeof(float);
 }
+
+namespace {
+hipError_t dispatch_bwd(csa_dtype dt, long n, long nblk, int m, int c, const void* Ca, const void* Cb,
+                        const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
+                        const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa, void* dZb, long ld_out,
+                        float* dBa, float* dBb, void* workspace, int nseq, const int64_t* cu, const int64_t* boff,
+                        hipStream_t s) {
+  float* part = (float*)workspace;
+  if (dt == CSA_F32)
+    return run_bwd<float, 4>(n, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
+                             dBa, dBb, part, nseq, cu, boff, s);
+  if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
+    return run_bwd<bf16_t, 8>(n, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb,
+                              ld_out, dBa, dBb, part, nseq, cu, boff, s);
+  return run_bwd<bf16_t, 4>(n, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
+                            dBa, dBb, part, nseq, cu, boff, s);
+}
+}  // namespace
 
 hipError_t launch_compress_backward(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
                                     const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
                                     const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
                                     long ld_out, float* dBa, float* dBb, void* workspace, hipStream_t s) {
-  float* part = (float*)workspace;
-  if (dt == CSA_F32)
-    return run_bwd<float, 4>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out, dBa,
-                             dBb, part, s);
-  if (c % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0)
-    return run_bwd<bf16_t, 8>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
-                              dBa, dBb, part, s);
-  return run_bwd<bf16_t, 4>(n, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out, dBa,
-                            dBb, part, s);
+  return dispatch_bwd(dt, n, n / m, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
+                      dBa, dBb, workspace, 0, nullptr, nullptr, s);
+}
+
+hipError_t launch_compress_backward_varlen(csa_dtype dt, long nseq, long nblk, int m, int c, const void* Ca,
+                                           const void* Cb, const void* Za, const void* Zb, long ld_in,
+                                           const void* Ba, const void* Bb, const int64_t* cu, const int64_t* boff,
+                                           const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa,
+                                           void* dZb, long ld_out, float* dBa, float* dBb, void* workspace,
+                                           hipStream_t s) {
+  return dispatch_bwd(dt, 0, nblk, m, c, Ca, Cb, Za, Zb, ld_in, Ba, Bb, dCcomp, ld_dc, dCa, dCb, dZa, dZb, ld_out,
+                      dBa, dBb, workspace, (int)nseq, cu, boff, s);
 }
 
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,

@@ -52,13 +52,20 @@ hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const v
                                   const int64_t* cu, const int64_t* boff, long nblk, void* out, long ld_out,
                                   hipStream_t s);
 
-// Backward of eqs 3-4 (see csa_compress_backward); the workspace holds the
-// per-workgroup partial bias gradients.
-size_t compress_backward_workspace_bytes(long n, int m, int c);
+// Backward of eqs 3-4 (see csa_compress_backward and its _varlen form); the
+// workspace holds the per-workgroup partial bias gradients.  The size is that
+// of one sequence of n tokens, or (varlen) of nseq sequences with nblk blocks.
+size_t compress_backward_workspace_bytes(long n, int m, int c, long nseq, long nblk, bool varlen);
 hipError_t launch_compress_backward(csa_dtype dt, long n, int m, int c, const void* Ca, const void* Cb,
                                     const void* Za, const void* Zb, long ld_in, const void* Ba, const void* Bb,
                                     const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa, void* dZb,
                                     long ld_out, float* dBa, float* dBb, void* workspace, hipStream_t s);
+hipError_t launch_compress_backward_varlen(csa_dtype dt, long nseq, long nblk, int m, int c, const void* Ca,
+                                           const void* Cb, const void* Za, const void* Zb, long ld_in,
+                                           const void* Ba, const void* Bb, const int64_t* cu, const int64_t* boff,
+                                           const float* dCcomp, long ld_dc, void* dCa, void* dCb, void* dZa,
+                                           void* dZb, long ld_out, float* dBa, float* dBb, void* workspace,
+                                           hipStream_t s);
 
 // Decode-time append (one new token per sequence); see csa_compress_append.
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,

@@ -106,10 +106,11 @@ class PrefillGrads:
     """Gradient buffers of one prefill shape (reused across calls).  Weight gradients are kept in the
     transposed layout of the weights they belong to (W_H_t, W_UQ_t); bias gradients are fp32."""
 
-    def __init__(self, n: int, m: int, k: int, nh: int, c: int, cI: int, dc: int, d: int, dtype, device):
+    def __init__(self, n: int, m: int, k: int, nh: int, c: int, cI: int, dc: int, d: int, dtype, device,
+                 n_seqs: Optional[int] = None, n_blocks: Optional[int] = None):
+        """One sequence of n tokens, or (n_seqs and n_blocks given) n tokens of packed sequences."""
         width = 4 * c + 4 * cI + dc
-        N = n // m
-        self.dO = None
+        N = n // m if n_seqs is None else n_blocks
         self.dq = torch.empty(n, nh * c, dtype=dtype, device=device)
         self.dCcomp = torch.empty(max(N, 1), c, dtype=torch.float32, device=device)[:N]
         self.dY_H = torch.zeros(n, width, dtype=dtype, device=device)  # indexer columns stay zero
@@ -118,8 +119,9 @@ class PrefillGrads:
         self.dW_UQ_t = torch.empty(nh * c, dc, dtype=dtype, device=device)
         self.dB_a = torch.empty(m, c, dtype=torch.float32, device=device)
         self.dB_b = torch.empty(m, c, dtype=torch.float32, device=device)
-        ws = max(api.csa_sparse_mqa_backward_workspace(n, nh, c, k, N),
-                 api.csa_compress_backward_workspace(n, m, c),
+        ws_c = (api.csa_compress_backward_workspace(n, m, c) if n_seqs is None
+                else api.csa_compress_backward_varlen_workspace(n_seqs, N, m, c))
+        ws = max(api.csa_sparse_mqa_backward_workspace(n, nh, c, k, N), ws_c,
                  api.csa_project_backward_workspace(dtype, n, nh * c, dc, True, True),
                  api.csa_project_backward_workspace(dtype, n, width, d, True, True))
         self.ws = torch.empty(max(ws, 16), dtype=torch.uint8, device=device)
@@ -213,6 +215,37 @@ def prefill_varlen(H: torch.Tensor, lengths, W: Dict[str, torch.Tensor], m: int,
     api.csa_sparse_mqa(buf.q.view(n, nh, c), buf.Ccomp, buf.idx, sc, buf.o, buf.lse, q_seq=buf.q_seq[:n],
                        kv_offset=buf.block_offset, workspace=buf.ws_mqa)  # eq 11
     return buf
+
+
+def prefill_varlen_backward(H: torch.Tensor, W: Dict[str, torch.Tensor], buf: VarlenPrefill, dO: torch.Tensor,
+                            m: int, k: int, nh: int, scale: Optional[float] = None,
+                            grads: Optional[PrefillGrads] = None) -> PrefillGrads:
+    """Gradients of sum(dO * o) after ``prefill_varlen`` filled ``buf``; the order of ``prefill_backward``.
+
+    Per-token gradients (dq, dH and the projection rows) follow each token's own sequence; the weight and
+    bias gradients are shared parameters and sum over every sequence.
+    """
+    n, d = H.shape
+    c, cI, dc = W["c"], W["cI"], W["dc"]
+    if n != buf.n:
+        raise ValueError("H must hold sum(lengths) rows")
+    if grads is None:
+        grads = PrefillGrads(n, m, k, nh, c, cI, dc, d, H.dtype, H.device, n_seqs=len(buf.lengths),
+                             n_blocks=buf.n_blocks)
+    g = grads
+    sc = 1.0 / math.sqrt(c) if scale is None else scale
+    api.csa_sparse_mqa_backward(buf.q.view(n, nh, c), buf.Ccomp[:buf.n_blocks], buf.idx, sc, buf.o, buf.lse, dO,
+                                g.dq.view(n, nh, c), g.dCcomp, q_seq=buf.q_seq[:n], kv_offset=buf.block_offset,
+                                workspace=g.ws)  # eq 11
+    Y, dY = buf.Y_H, g.dY_H
+    api.csa_compress_backward_varlen(Y[:, 0:c], Y[:, c:2 * c], Y[:, 2 * c:3 * c], Y[:, 3 * c:4 * c], W["B_a"],
+                                     W["B_b"], m, buf.cu, buf.block_offset, buf.n_blocks, g.dCcomp, dY[:, 0:c],
+                                     dY[:, c:2 * c], dY[:, 2 * c:3 * c], dY[:, 3 * c:4 * c], g.dB_a, g.dB_b,
+                                     workspace=g.ws)  # eqs 3-4
+    o = 4 * c + 4 * cI
+    api.csa_project_backward(Y[:, o:], W["W_UQ_t"], g.dq, dX=dY[:, o:], dWt=g.dW_UQ_t, workspace=g.ws)  # eq 10
+    api.csa_project_backward(H, W["W_H_t"], dY, dX=g.dH, dWt=g.dW_H_t, workspace=g.ws)  # eqs 1, 2, 5
+    return g
 
 
 class DecodeBuffers:

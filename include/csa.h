@@ -205,6 +205,31 @@ csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, 
                                  void* stream);
 
 /*
+ * csa_compress_backward_varlen -- csa_compress_backward for several sequences
+ * packed the way csa_compress_varlen takes them (same section and equations):
+ * sequence b owns token rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of Ca, Cb, Za,
+ * Zb and of the four gradient outputs, and rows block_offset[b] ..
+ * block_offset[b+1]-1 of dCcomp (its blocks, block_offset[b+1] - block_offset[b]
+ * = floor(length / m), n_blocks = block_offset[n_seqs]).  Each sequence's
+ * gradients are those of csa_compress_backward on its own rows (its block 0
+ * has no b-terms; its rows that none of its blocks reads get zeros); dBa and
+ * dBb sum over the blocks of every sequence, since the biases are shared.
+ * Rows outside every sequence are not written.  cu_seqlens [n_seqs+1] and
+ * block_offset [n_seqs+1] are int64 in device memory and must agree as stated;
+ * they are not checked.  Other arguments, limits and the workspace rules as
+ * csa_compress_backward, with the workspace sized by
+ * csa_compress_backward_varlen_workspace.  n_seqs = 0 writes zero bias gradients.
+ */
+csa_status csa_compress_backward_varlen_workspace(int64_t n_seqs, int64_t n_blocks, int32_t m, int32_t c,
+                                                 size_t* bytes);
+csa_status csa_compress_backward_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca,
+                                        const void* Cb, const void* Za, const void* Zb, int64_t ld_in,
+                                        const void* Ba, const void* Bb, const int64_t* cu_seqlens,
+                                        const int64_t* block_offset, int64_t n_blocks, const float* dCcomp,
+                                        int64_t ld_dc, void* dCa, void* dCb, void* dZa, void* dZb, int64_t ld_out,
+                                        float* dBa, float* dBb, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * csa_index_topk -- eq 8 scores and the eq 9 selection for a batch of queries.
  *
  * Query r belongs to sequence seq = q_seq[r] (q_seq NULL: 0) and sits at token

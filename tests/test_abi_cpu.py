@@ -200,6 +200,20 @@ def test_backward_calls_reject_bad_args(L):
     assert comp(wsb=8) == api.CSA_ERR_INVALID_ARG
     assert "workspace" in _err()
 
+    def compv(dt=1, ns=3, m=4, c=64, nb=10, cu=p, ldd=64, ws=p, wsb=1 << 30):
+        return L.csa_compress_backward_varlen(dt, ns, m, c, p, p, p, p, 256, p, p, cu, p, nb, p, ldd, p, p, p, p, 256,
+                                              p, p, ws, wsb, None)
+    assert compv(m=17) == api.CSA_ERR_INVALID_ARG
+    assert compv(ns=-1) == api.CSA_ERR_INVALID_ARG
+    assert compv(ns=0, nb=3) == api.CSA_ERR_INVALID_ARG  # blocks without sequences
+    assert compv(cu=None) == api.CSA_ERR_INVALID_ARG
+    assert compv(ldd=60) == api.CSA_ERR_INVALID_ARG
+    assert compv(wsb=8) == api.CSA_ERR_INVALID_ARG
+    assert "workspace" in _err()
+    # one partial-sum row of 2m x c fp32 per workgroup row, at least one row even with nothing to do
+    assert api.csa_compress_backward_varlen_workspace(0, 0, 4, 64) == 2 * 4 * 64 * 4
+    assert api.csa_compress_backward_varlen_workspace(300, 3000, 4, 64) >= 2 * 4 * 64 * 4
+
     def proj(M=64, N=64, K=64, dX=p, dW=p, ws=p, wsb=1 << 30, ind=1, outd=1):
         return L.csa_project_backward(ind, outd, M, N, K, p, K, p, K, p, N, dX, K, dW, K, ws, wsb, None)
     assert proj(N=60) == api.CSA_ERR_INVALID_ARG

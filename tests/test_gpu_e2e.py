@@ -6,7 +6,8 @@ import torch
 
 from compressed_sparse_attention_amd import synth
 from compressed_sparse_attention_amd.layer import (DecodeState, decode, decode_step, pack_prefill_params,
-                                                     prefill, prefill_backward, prefill_varlen, to_device)
+                                                     prefill, prefill_backward, prefill_varlen,
+                                                     prefill_varlen_backward, to_device)
 from oracle import csa_oracle as O
 from parity import assert_dq_close, assert_rows_close, assert_sum_rows_close, check_topk, to_np64
 
@@ -52,6 +53,51 @@ def test_prefill_workload1_fp32():
     assert np.all(to_np64(buf.o)[: w.m] == 0)
 
 
+def _layer_grad_refs(P64, w, dO64):
+    """The oracle's layer gradients of one sequence, with the term scales of the weight gradients (sums of
+    |dY|^T |X| over its tokens) that their tolerances are measured against."""
+    ref = O.prefill_backward(P64, w.m, w.k, w.nh, w.nhI, dO64)
+    fwd = O.prefill(P64, w.m, w.k, w.nh, w.nhI)
+    n, c, cI = P64["H"].shape[0], w.c, w.cI
+    H64 = P64["H"]
+    dq_flat = ref["dq"].reshape(n, w.nh * c)
+    scales = {"W_UQ": np.abs(dq_flat).T @ np.abs(fwd["cQ"])}
+    dY = O.compress_backward(*(O.project(H64, P64[nm]) for nm in ("W_aKV", "W_bKV", "W_aZ", "W_bZ")),
+                             P64["B_a"], P64["B_b"], w.m, ref["dCcomp"])[:4]
+    for name, g in zip(("W_aKV", "W_bKV", "W_aZ", "W_bZ"), dY):
+        scales[name] = np.abs(g).T @ np.abs(H64)
+    scales["W_DQ"] = np.abs(dq_flat @ P64["W_UQ"].T).T @ np.abs(H64)
+    return ref, fwd, scales
+
+
+def _check_layer_grads(g, w, n, dq_ref, dO64, o_ref, dCcomp_ref, dH_ref, wref, scales):
+    """GPU layer gradients against the oracle's: per-token ones row by row, weight sums against their term
+    scales; every comparison runs and the failures are reported together."""
+    c, cI = w.c, w.cI
+    results = {}
+
+    def check(fn, *args, what):
+        try:
+            results[what] = fn(*args, what=what)
+        except AssertionError as e:
+            results[what] = str(e)
+
+    check(assert_dq_close, to_np64(g.dq).reshape(n, w.nh, c), dq_ref, dO64, o_ref, 1.0 / np.sqrt(c), what="dq")
+    if dCcomp_ref.shape[0]:
+        check(assert_rows_close, to_np64(g.dCcomp), dCcomp_ref, what="dCcomp")
+    check(assert_rows_close, to_np64(g.dB_a), wref["B_a"], what="dB_a")
+    check(assert_rows_close, to_np64(g.dB_b), wref["B_b"], what="dB_b")
+    check(assert_rows_close, to_np64(g.dH), dH_ref, what="dH")
+    check(assert_sum_rows_close, to_np64(g.dW_UQ_t), wref["W_UQ"].T, scales["W_UQ"], what="dW_UQ")
+    dWH = to_np64(g.dW_H_t)
+    for i, name in enumerate(("W_aKV", "W_bKV", "W_aZ", "W_bZ")):
+        check(assert_sum_rows_close, dWH[i * c:(i + 1) * c], wref[name].T, scales[name], what=f"d{name}")
+    check(assert_sum_rows_close, dWH[4 * c + 4 * cI:], wref["W_DQ"].T, scales["W_DQ"], what="dW_DQ")
+    assert np.all(dWH[4 * c:4 * c + 4 * cI] == 0)  # the indexer's projections get no gradient
+    print(results)
+    assert all(isinstance(v, float) for v in results.values()), results
+
+
 def test_prefill_backward_layer():
     """Gradients of the whole layer (eq 11, eqs 3-4, eq 10, eqs 1, 2, 5) against the oracle's chain rule.
 
@@ -69,40 +115,47 @@ def test_prefill_backward_layer():
     g = prefill_backward(H, W, buf, to_device(dO, "bf16", DEV), w.m, w.k, w.nh)
     torch.cuda.synchronize()
     P64 = {k: _f64(v, w.dtype) for k, v in P.items()}
-    ref = O.prefill_backward(P64, w.m, w.k, w.nh, w.nhI, _f64(dO, "bf16"))
-    n, c, cI, d = w.n, w.c, w.cI, w.d
-    fwd = O.prefill(P64, w.m, w.k, w.nh, w.nhI)
     dO64 = _f64(dO, "bf16")
-    H64 = P64["H"]
-    results = {}
+    ref, fwd, scales = _layer_grad_refs(P64, w, dO64)
+    _check_layer_grads(g, w, w.n, ref["dq"], dO64, fwd["o"], ref["dCcomp"], ref["H"], ref, scales)
 
-    def check(fn, *args, what):
-        try:
-            results[what] = fn(*args, what=what)
-        except AssertionError as e:
-            results[what] = str(e)
 
-    check(assert_dq_close, to_np64(g.dq).reshape(n, w.nh, c), ref["dq"], dO64, fwd["o"], 1.0 / np.sqrt(c), what="dq")
-    check(assert_rows_close, to_np64(g.dCcomp), ref["dCcomp"], what="dCcomp")
-    check(assert_rows_close, to_np64(g.dB_a), ref["B_a"], what="dB_a")
-    check(assert_rows_close, to_np64(g.dB_b), ref["B_b"], what="dB_b")
-    check(assert_rows_close, to_np64(g.dH), ref["H"], what="dH")
-    # weight gradients are sums over the 512 tokens: compared against the size of their terms
-    dq_flat = ref["dq"].reshape(n, w.nh * c)
-    check(assert_sum_rows_close, to_np64(g.dW_UQ_t), ref["W_UQ"].T, np.abs(dq_flat).T @ np.abs(fwd["cQ"]),
-          what="dW_UQ")
-    dCa, dCb, dZa, dZb, _, _ = O.compress_backward(*(O.project(H64, P64[nm]) for nm in ("W_aKV", "W_bKV", "W_aZ",
-                                                                                         "W_bZ")),
-                                                   P64["B_a"], P64["B_b"], w.m, ref["dCcomp"])
-    dWH = to_np64(g.dW_H_t)
-    for i, (name, dY) in enumerate((("W_aKV", dCa), ("W_bKV", dCb), ("W_aZ", dZa), ("W_bZ", dZb))):
-        check(assert_sum_rows_close, dWH[i * c:(i + 1) * c], ref[name].T, np.abs(dY).T @ np.abs(H64),
-              what=f"d{name}")
-    dcQ = dq_flat @ P64["W_UQ"].T
-    check(assert_sum_rows_close, dWH[4 * c + 4 * cI:], ref["W_DQ"].T, np.abs(dcQ).T @ np.abs(H64), what="dW_DQ")
-    assert np.all(dWH[4 * c:4 * c + 4 * cI] == 0)  # the indexer's projections get no gradient
-    print(results)
-    assert all(isinstance(v, float) for v in results.values()), results
+def test_prefill_varlen_backward_layer():
+    """Layer gradients of four packed sequences (200, 3, 131 and 178 tokens): each token's gradients equal
+    those of the oracle run on its sequence alone, and the weight and bias gradients equal the sum over the
+    sequences.  Every sequence is at most 512 tokens with k = 128, so every query selects all its candidates
+    (as in the single-sequence test)."""
+    w = synth.Workload("prefill_grad_packed_bf16", "prefill", "bf16", m=4, c=512, cI=64, nhI=4, nh=16, k=128,
+                       n=512, d=256, dc=128)
+    lengths = [200, 3, 131, 178]
+    n = sum(lengths)
+    P = synth.make_prefill(w, seed=21, n=n)
+    rng = synth.rng_for(22)
+    dO = synth.normal(rng, (n, w.nh, w.c), 1.0, "bf16")
+    W = pack_prefill_params(P, w.dtype, DEV)
+    H = to_device(P["H"], w.dtype, DEV)
+    buf = prefill_varlen(H, lengths, W, w.m, w.k, w.nh, w.nhI)
+    g = prefill_varlen_backward(H, W, buf, to_device(dO, "bf16", DEV), w.m, w.k, w.nh)
+    torch.cuda.synchronize()
+    P64 = {k: _f64(v, w.dtype) for k, v in P.items()}
+    dO64 = _f64(dO, "bf16")
+    dq, o, dC, dH = [], [], [], []
+    wsum, ssum = {}, {}
+    t0 = 0
+    for L in lengths:
+        sl = slice(t0, t0 + L)
+        ref, fwd, scales = _layer_grad_refs({**P64, "H": P64["H"][sl]}, w, dO64[sl])
+        dq.append(ref["dq"])
+        o.append(fwd["o"])
+        dC.append(ref["dCcomp"])
+        dH.append(ref["H"])
+        for name in ("B_a", "B_b", "W_UQ", "W_aKV", "W_bKV", "W_aZ", "W_bZ", "W_DQ"):
+            wsum[name] = wsum.get(name, 0.0) + ref[name]
+        for name, v in scales.items():
+            ssum[name] = ssum.get(name, 0.0) + v
+        t0 += L
+    _check_layer_grads(g, w, n, np.concatenate(dq), dO64, np.concatenate(o), np.concatenate(dC),
+                       np.concatenate(dH), wsum, ssum)
 
 
 @pytest.mark.parametrize("cfg", [2, 4, 5])

@@ -617,6 +617,62 @@ def test_compress_varlen(dtype, lengths, m, c):
     assert np.all(got[nb:] == 3.0)  # rows past the blocks are untouched
 
 
+@pytest.mark.parametrize("dtype,lengths,m,c,lead", [
+    ("f32", [0, 3, 5, 17, 64, 130], 4, 64, 0), ("bf16", [1000, 1, 257, 4], 4, 512, 3), ("bf16", [9, 31, 2], 8, 12, 0),
+    ("bf16", [40, 0, 0, 7], 1, 128, 5), ("bf16", "many", 4, 128, 2), ("f32", [], 4, 16, 0), ("bf16", [2, 3], 4, 64, 1),
+])
+def test_compress_backward_varlen(dtype, lengths, m, c, lead):
+    """Gradients of eqs 3-4 for packed sequences: each sequence's rows get the oracle's gradients of its own slice,
+    the bias gradients sum over every sequence, and rows outside the sequences (the first `lead` rows and two rows
+    after the last sequence) keep their sentinel."""
+    if lengths == "many":  # 300 sequences: several units per workgroup and a deep sequence search
+        lengths = [int(x) for x in synth.rng_for(77).integers(0, 40, size=300)]
+    rng = synth.rng_for(sum(lengths) + 7 * m + c + lead)
+    cu, bo = _packed(lengths, m)
+    cu = cu + lead
+    n = int(cu[-1]) + 2
+    nb = int(bo[-1])
+    cp = (c + 7) // 8 * 8
+    P = draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = draw(rng, (n, 4 * cp), 2.0, dtype)
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
+    Ba = draw(rng, (m, c), 0.5, dtype)
+    Bb = draw(rng, (m, c), 0.5, dtype)
+    dC = rng.standard_normal(size=(nb, cp), dtype=np.float32)
+    Pd = to_device(P, dtype, DEV)
+    sl = [Pd[:, i * cp:i * cp + c] for i in range(4)]
+    G = torch.full((n, 4 * cp), 7.0, dtype=TD[dtype], device=DEV)
+    gs = [G[:, i * cp:i * cp + c] for i in range(4)]
+    dBa = torch.full((m, c), 7.0, device=DEV)
+    dBb = torch.full((m, c), 7.0, device=DEV)
+    api.csa_compress_backward_varlen(*sl, to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV), m,
+                                     torch.tensor(cu, device=DEV), torch.tensor(bo, device=DEV), nb,
+                                     torch.from_numpy(dC).to(DEV)[:, :c], *gs, dBa, dBb)
+    torch.cuda.synchronize()
+    got = to_np64(G).reshape(n, 4, cp)
+    P64 = f64(P, dtype)
+    sum_a, sum_b = np.zeros((m, c)), np.zeros((m, c))
+    mag_a, mag_b = np.zeros((m, c)), np.zeros((m, c))
+    for b in range(len(lengths)):
+        seg = P64[cu[b]:cu[b + 1]]
+        ref = O.compress_backward(*[seg[:, i * cp:i * cp + c] for i in range(4)], f64(Ba, dtype), f64(Bb, dtype), m,
+                                  dC[bo[b]:bo[b + 1], :c].astype(np.float64))
+        if seg.shape[0]:
+            for w in range(4):
+                assert_rows_close(got[cu[b]:cu[b + 1], w, :c], ref[w], what=f"sequence {b} grad {w}")
+        N = bo[b + 1] - bo[b]
+        sum_a += ref[4]
+        sum_b += ref[5]
+        mag_a += np.abs(ref[2][:N * m]).reshape(N, m, c).sum(0) if N else 0.0
+        mag_b += np.abs(ref[3][:(N - 1) * m]).reshape(N - 1, m, c).sum(0) if N > 1 else 0.0
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    for gpu, want, mag in ((dBa, sum_a, mag_a), (dBb, sum_b, mag_b)):
+        err = np.abs(to_np64(gpu) - want)
+        assert np.all(err <= tol * mag + 1e-7), f"bias gradient off by {err.max()}"
+    assert np.all(got[:lead] == 7.0) and np.all(got[int(cu[-1]):] == 7.0)  # rows outside the sequences
+    assert np.all(got[:, :, c:] == 7.0)  # the padding columns between the slices
+
+
 @pytest.mark.parametrize("dtype,lengths,m,nhI,cI,k", [
     ("bf16", [1, 40, 257, 1000, 33], 4, 64, 128, 64),
     ("f32", [130, 0, 77, 512], 4, 4, 32, 16),
