@@ -4,8 +4,9 @@
 // row-vector projections of this form.  Both operands are K-contiguous, so
 // each 16x16x32 MFMA operand is one 16-byte LDS read per lane.
 //
-// Three kernels: gemm_smallm (below) for bf16 with M <= 16, gemm256 (below)
-// for bf16 operands with M, N >= 256, and the general gemm_nt (fp32 too, any
+// Four kernels: gemm_smallm (below) for bf16 with M <= 16, gemm256 and its
+// copy-pipelined form gemm256_dma (K a multiple of 64) (below) for bf16
+// operands with M, N >= 256, and the general gemm_nt (fp32 too, any
 // shape): 128x128 output tile per 256-thread
 // workgroup (4 waves in 2x2, each 64x64 = 4x4 MFMA tiles), K staged through
 // LDS in 128-byte slabs, double buffered: the next slab is fetched into
@@ -253,6 +254,190 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 }
 
 // ---------------------------------------------------------------------------
+// The same 256x256 tile and wave layout for K a multiple of 64, with the
+// operands brought in by direct global-to-LDS copies (global_load_lds, no
+// VGPR staging) into a ring of kDmaStages 32-deep stages, and each wave's
+// fragments for stage kt+1 read from LDS while its MFMAs on stage kt run.
+//
+// Per stage a workgroup's LDS traffic is 96 KiB of fragment reads and 32 KiB
+// of copies for 8 x 32 MFMAs, about 125 bytes per clock at full MFMA rate,
+// against ~140 bytes per clock measured for 16-byte LDS reads from eight
+// waves: this tile shape is LDS-bound, and the ring and the prefetch recover
+// what the barrier-synchronised register staging left idle (W_H at
+// 32768x4096x4096 1.04 -> 1.00 ms, W_UQ at 32768x32768x1536 3.55 -> 3.32 ms).
+// bf16 outputs are staged through LDS and written as 512-byte row segments
+// (the MFMA layout alone gives 32-byte pieces of 16 rows per store).
+//
+// Copy layout: wave w copies 16-row blocks 2w and 2w+1 of both operands per
+// stage; lane l lands at byte 16 l of its block, i.e. row l/4 and stored
+// chunk l%4, which holds the row's source chunk (l%4) ^ ((l/16)%4).  A
+// fragment read (16 rows, one chunk) then hits 16 distinct 4-bank groups.
+// The copies are asm (the compiler does not track them): each wave waits
+// for its own with an explicit vmcnt, then the workgroup meets at a barrier.
+// ---------------------------------------------------------------------------
+constexpr int kDmaStages = 3;
+constexpr int kDmaK = 32;  // k per stage
+
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// LDS wait the compiler can see (it then knows earlier LDS reads are done,
+// instead of waiting for the next batch at the first use), then a barrier
+// with no wait for vector memory.
+__device__ __forceinline__ void lds_wait_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <typename TO>
+__global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, const bf16_t* __restrict__ X,
+                                                            long ldx, const bf16_t* __restrict__ W, long ldw,
+                                                            TO* __restrict__ Y, long ldy, int tiles_m, int tiles_n,
+                                                            int per_xcd) {
+  constexpr int S = kDmaStages;
+  constexpr int STAGE = 2 * 256 * kDmaK;  // elements: the A block, then the B block
+  constexpr int OP = kG2N + 8;            // pitch of the staged output tile
+  constexpr int SM = S * STAGE > kG2M * OP ? S * STAGE : kG2M * OP;
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SM];
+
+  const int seq = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (seq >= tiles_m * tiles_n) return;
+  const int in_group = kG2Group * tiles_n;
+  const int first_m = (seq / in_group) * kG2Group;
+  const int gsize = min(kG2Group, tiles_m - first_m);
+  const int r = seq % in_group;
+  const long m0 = (long)(first_m + r % gsize) * kG2M;
+  const long n0 = (long)(r / gsize) * kG2N;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
+  const int g = lane >> 4, c16 = lane & 15;
+  const int KT = K / kDmaK;  // even
+
+  // copy sources: rows past M or N repeat the last row (their outputs are not written)
+  const int rl = lane >> 2;
+  const int schunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const bf16_t* src[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const long ra = m0 + 16 * (2 * wave + j) + rl;
+    const long rb = n0 + 16 * (2 * wave + j) + rl;
+    src[0][j] = X + (ra < M ? ra : M - 1) * ldx + schunk * 8;
+    src[1][j] = W + (rb < N ? rb : N - 1) * ldw + schunk * 8;
+  }
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_char*)smem;
+  auto issue = [&](int kt) {  // four 1 KiB copies per wave
+    const int buf = kt % S;
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t dst = lds0 + 2u * (uint32_t)(buf * STAGE + op * 256 * kDmaK + (2 * wave + j) * 16 * kDmaK);
+        gather_row_lds(src[op][j] + (long)kt * kDmaK, __builtin_amdgcn_readfirstlane(dst));
+      }
+  };
+  auto wait_later = [&](int later) {  // this wave's copies, but for `later` stages, have landed
+    if (later >= 2) wait_vm_n<8>();
+    else if (later == 1) wait_vm_n<4>();
+    else wait_vm_n<0>();
+  };
+  // fragment rows: A wm*128 + 16 i + c16, B wn*64 + 16 j + c16; their chunk
+  // g is stored at g ^ ((row / 4) % 4) = g ^ (c16 / 4)
+  const int fchunk = (g ^ (c16 >> 2)) * 8;
+  auto read_frags = [&](int kt, Frag<bf16_t>(&fa)[8], Frag<bf16_t>(&fb)[4]) {
+    const bf16_t* As = smem + (kt % S) * STAGE;
+    const bf16_t* Bs = As + 256 * kDmaK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j].load(Bs + (wn * 64 + 16 * j + c16) * kDmaK + fchunk);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa[i].load(As + (wm * 128 + 16 * i + c16) * kDmaK + fchunk);
+  };
+
+  // acc[j][i] = (W tile j) x (X tile i)^T, as in gemm256_kernel
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    if (st < KT) issue(st);
+  Frag<bf16_t> fa0[8], fb0[4], fa1[8], fb1[4];
+  wait_later(min(S - 1, KT - 1));
+  lds_wait_barrier();
+  read_frags(0, fa0, fb0);
+  // Step kt: stage kt's fragments are in registers.  Once stage kt+1 has
+  // landed for every wave (which also means stage kt's buffer is no longer
+  // read), stage kt+S is copied into that buffer and stage kt+1's fragments
+  // are read while stage kt's MFMAs run.  On the last step the read is of a
+  // stale buffer and unused: a branch around it would make the compiler wait
+  // for those reads before the MFMAs.
+  auto step = [&](int kt, Frag<bf16_t>(&fa)[8], Frag<bf16_t>(&fb)[4], Frag<bf16_t>(&na)[8],
+                  Frag<bf16_t>(&nb)[4]) {
+    wait_later(min(S - 2, KT - 2 - kt));
+    lds_wait_barrier();
+    if (kt + S < KT) issue(kt + S);
+    read_frags(kt + 1, na, nb);
+    issue_fence();  // the reads go out before the MFMAs (the scheduler would sink them below)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mma(acc[j][i], fb[j], fa[i]);
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, fa0, fb0, fa1, fb1);
+    step(kt + 1, fa1, fb1, fa0, fb0);
+  }
+
+  if constexpr (sizeof(TO) == 2) {
+    lds_wait_barrier();  // every wave's last fragment reads are done before the tile is staged over them
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = wm * 128 + i * 16 + c16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[4] = {acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
+        store4<bf16_t>(&smem[row * OP + wn * 64 + j * 16 + 4 * g], v);
+      }
+    }
+    lds_wait_barrier();
+    // 32 lanes per row, 16 bytes each; N % 4 == 0, so a half chunk is all in or all out
+#pragma unroll 4
+    for (int it = 0; it < kG2M / 16; ++it) {
+      const int row = it * 16 + (tid >> 5), ch = (tid & 31) * 8;
+      const long grow = m0 + row, gcol = n0 + ch;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&smem[row * OP + ch]);
+      if (grow < M) {
+        if (gcol + 8 <= N) {
+          *reinterpret_cast<u32x4*>(Y + grow * ldy + gcol) = v;
+        } else if (gcol < N) {
+          *reinterpret_cast<uint2*>(Y + grow * ldy + gcol) = make_uint2(v[0], v[1]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const long row = m0 + wm * 128 + i * 16 + c16;
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long col = n0 + wn * 64 + j * 16 + 4 * g;
+        if (col < N) {
+          float v[4] = {acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]};
+          store4<TO>(Y + row * ldy + col, v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Few rows (M <= 16: one decode token per sequence): the weights are the
 // traffic.  A 256-thread workgroup owns 16 output columns over all of K; its
 // four waves split K and stream their share of the 16 weight rows straight
@@ -388,6 +573,13 @@ hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K
     const int tm = (int)((M + kG2M - 1) / kG2M), tn = (int)((N + kG2N - 1) / kG2N);
     const int per_xcd = (tm * tn + 7) / 8;
     const dim3 grid2((unsigned)(8 * per_xcd));
+    if (K % (2 * kDmaK) == 0) {  // rows are 16-byte aligned (checked by csa_project)
+      if (out_dt == CSA_BF16)
+        return launch("gemm", gemm256_dma_kernel<bf16_t>, grid2, dim3(512), 0, s, (int)M, (int)N, (int)K,
+                      (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy, tm, tn, per_xcd);
+      return launch("gemm", gemm256_dma_kernel<float>, grid2, dim3(512), 0, s, (int)M, (int)N, (int)K,
+                    (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy, tm, tn, per_xcd);
+    }
     if (out_dt == CSA_BF16)
       return launch("gemm", gemm256_kernel<bf16_t>, grid2, dim3(512), 0, s, (int)M, (int)N, (int)K,
                     (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy, tm, tn, per_xcd);

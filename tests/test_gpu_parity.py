@@ -40,6 +40,11 @@ def f64(x, dtype):
     ("bf16", "bf16", 1000, 1536, 4096),
     ("bf16", "bf16", 520, 296, 200),  # large-tile kernel: ragged M and N edges and a K tail
     ("bf16", "f32", 260, 264, 1000),
+    # K a multiple of 64: the copy-pipelined large-tile kernel (two stages up to many, ragged edges)
+    ("bf16", "bf16", 256, 256, 64),
+    ("bf16", "bf16", 520, 296, 192),
+    ("bf16", "f32", 260, 260, 1024),
+    ("bf16", "bf16", 777, 1032, 1536),
     ("bf16", "bf16", 8, 4096, 4096),  # few-row (decode token) kernel
     ("bf16", "f32", 3, 64, 200),
     ("bf16", "bf16", 16, 1000, 1536),
@@ -81,10 +86,10 @@ def test_project_backward(din, dout, M, N, K):
     assert_rows_close(to_np64(dWt), ref_dW.T, what="dWt")
 
 
-def test_project_strided_views():
+@pytest.mark.parametrize("M,K,N", [(257, 128, 96), (300, 128, 264)])
+def test_project_strided_views(M, K, N):
     """Input column slice (ldx > K) and output column slice of a wider buffer (ldy > N)."""
-    rng = synth.rng_for(99)
-    M, K, N = 257, 128, 96
+    rng = synth.rng_for(99 + M)
     X = draw(rng, (M, 3 * K), 1.0, "bf16")
     W = draw(rng, (K, N), 0.1, "bf16")
     Xd = to_device(X, "bf16", DEV)
@@ -96,6 +101,20 @@ def test_project_strided_views():
     assert_rows_close(to_np64(Ybig[:, N:2 * N]), ref, what="project slice")
     untouched = torch.cat([Ybig[:, :N], Ybig[:, 2 * N:]], 1)
     assert torch.all(untouched == 7.0)
+
+
+def test_project_output_half_chunk():
+    """bf16 output with N % 8 == 4 (possible only with ldy > N): the last 4 columns of each row are a half
+    16-byte chunk; the columns between N and ldy keep their sentinel."""
+    rng = synth.rng_for(123)
+    M, K, N = 300, 128, 260
+    X = draw(rng, (M, K), 1.0, "bf16")
+    W = draw(rng, (K, N), 0.1, "bf16")
+    Ybig = torch.full((M, N + 4), 7.0, dtype=torch.bfloat16, device=DEV)
+    api.csa_project(to_device(X, "bf16", DEV), to_device(np.ascontiguousarray(W.T), "bf16", DEV), Ybig[:, :N])
+    torch.cuda.synchronize()
+    assert_rows_close(to_np64(Ybig[:, :N]), O.project(f64(X, "bf16"), f64(W, "bf16")), what="project")
+    assert torch.all(Ybig[:, N:] == 7.0)
 
 
 # ---------------------------------------------------------------------------
