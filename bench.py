@@ -204,7 +204,35 @@ def bench_prefill(args, torch, api, synth, layer):
                 "algorithmic_flops_per_launch": idx_flops}
     return {"workload": w.name, "tokens": w.n, "ms": ms, "tokens_per_s": w.n / (ms * 1e-3),
             "kernels_ms_per_step": {n: round(s["total_ms"] / args.prefill_steps, 4) for n, s in kern.items()},
-            "indexer_roofline": roof}
+            "indexer_roofline": roof, "stage_rooflines": _prefill_stage_rooflines(w, kern, args.prefill_steps)}
+
+
+def _prefill_stage_rooflines(w, kern, steps):
+    """Algorithmic work of the other prefill stages per pass against their bound: the projections (eqs 1, 2, 5,
+    6, 7, 10) and the attention (eq 11) on bf16 MFMA; compression (eqs 3-4, main and indexer) and the top-k
+    (eq 9: reading each token's causal scores, writing its k indices) on HBM."""
+    n, d, m, k = w.n, w.d, w.m, w.k
+    width = 4 * w.c + 4 * w.cI + w.dc
+    ncand = [t // m for t in range(n)]
+    work = {
+        "projections": ("gemm", "mfma", 2.0 * n * (d * width + d * w.nhI + w.dc * w.nhI * w.cI + w.dc * w.nh * w.c)),
+        "compression": ("compress", "hbm", 2.0 * (4 * n * (w.c + w.cI) + (n // m) * (w.c + w.cI))),
+        "topk": ("topk", "hbm", 4.0 * sum(ncand) + 4.0 * n * k),
+        "mqa": ("mqa", "mfma", 4.0 * sum(min(k, x) for x in ncand) * w.nh * w.c),
+    }
+    out = {}
+    for stage, (fam, bound, amount) in work.items():
+        st = kern.get(fam)
+        if not st:
+            continue
+        sec = st["total_ms"] / steps * 1e-3
+        if bound == "mfma":
+            ach, peak, unit, key = amount / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s", "algorithmic_flops_per_step"
+        else:
+            ach, peak, unit, key = amount / sec / 1e9, HBM_PEAK_GBS, "GB/s", "algorithmic_bytes_per_step"
+        out[stage] = {"kernels": fam, "bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                      "frac": round(ach / peak, 4), key: amount}
+    return out
 
 
 def bench_prefill_backward(args, torch, api, synth, layer):
