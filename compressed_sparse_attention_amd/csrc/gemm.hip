@@ -262,9 +262,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 // Per stage a workgroup's LDS traffic is 96 KiB of fragment reads and 32 KiB
 // of copies for 8 x 32 MFMAs, about 125 bytes per clock at full MFMA rate,
 // against ~140 bytes per clock measured for 16-byte LDS reads from eight
-// waves: this tile shape is LDS-bound, and the ring and the prefetch recover
-// what the barrier-synchronised register staging left idle (W_H at
-// 32768x4096x4096 1.04 -> 1.00 ms, W_UQ at 32768x32768x1536 3.55 -> 3.32 ms).
+// waves; the ring, the prefetch and spreading the copies and reads over the
+// MFMAs recover part of what the barrier-synchronised register staging left
+// idle (W_H at 32768x4096x4096 1.04 -> 0.94 ms, W_UQ at 32768x32768x1536
+// 3.55 -> 3.18 ms).
 // bf16 outputs are staged through LDS and written as 512-byte row segments
 // (the MFMA layout alone gives 32-byte pieces of 16 rows per store).
 //
@@ -377,17 +378,35 @@ __global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, c
   // are read while stage kt's MFMAs run.  On the last step the read is of a
   // stale buffer and unused: a branch around it would make the compiler wait
   // for those reads before the MFMAs.
+  //
+  // The copy and the reads are spread over the MFMAs, one copy and three
+  // fragment reads before each group of 8 MFMAs: issued all at once after the
+  // barrier, they held both waves of a SIMD (which leave the barrier
+  // together) off the MFMA pipe (measured 6-8% slower).  Fences keep the
+  // scheduler from regrouping them.
   auto step = [&](int kt, Frag<bf16_t>(&fa)[8], Frag<bf16_t>(&fb)[4], Frag<bf16_t>(&na)[8],
                   Frag<bf16_t>(&nb)[4]) {
     wait_later(min(S - 2, KT - 2 - kt));
     lds_wait_barrier();
-    if (kt + S < KT) issue(kt + S);
-    read_frags(kt + 1, na, nb);
-    issue_fence();  // the reads go out before the MFMAs (the scheduler would sink them below)
+    const bool more = kt + S < KT;
+    const int buf = (kt + S) % S;
+    const bf16_t* As = smem + ((kt + 1) % S) * STAGE;
+    const bf16_t* Bs = As + 256 * kDmaK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      if (more) {  // copy j of stage kt+S: operand j / 2, this wave's block j % 2
+        const int op = j >> 1, jj = j & 1;
+        const uint32_t dst = lds0 + 2u * (uint32_t)(buf * STAGE + op * 256 * kDmaK + (2 * wave + jj) * 16 * kDmaK);
+        gather_row_lds(src[op][jj] + (long)(kt + S) * kDmaK, __builtin_amdgcn_readfirstlane(dst));
+      }
+      nb[j].load(Bs + (wn * 64 + 16 * j + c16) * kDmaK + fchunk);
+      na[2 * j].load(As + (wm * 128 + 16 * (2 * j) + c16) * kDmaK + fchunk);
+      na[2 * j + 1].load(As + (wm * 128 + 16 * (2 * j + 1) + c16) * kDmaK + fchunk);
+      issue_fence();
 #pragma unroll
       for (int i = 0; i < 8; ++i) mma(acc[j][i], fb[j], fa[i]);
+      issue_fence();
+    }
   };
   for (int kt = 0; kt < KT; kt += 2) {
     step(kt, fa0, fb0, fa1, fb1);
