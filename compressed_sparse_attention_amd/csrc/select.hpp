@@ -154,10 +154,11 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_
   __syncthreads();
 }
 
-// LDS of select_row.
-template <int TPB>
+// LDS of select_row.  REGS: rows of at most 32 x TPB keys, held in registers
+// (no key staging area: about a third of the LDS, so more rows per CU).
+template <int TPB, bool REGS = false>
 struct SelectRowSmem {
-  uint32_t keys[TPB * kEPT + TPB * kEPT / 32];
+  uint32_t keys[REGS ? 1 : TPB * kEPT + TPB * kEPT / 32];
   // level-1 histogram; afterwards the candidate list: indices in [0, kCandCap),
   // their keys in [kCandCap, 2 kCandCap)
   uint32_t hist[kL1Bins];
@@ -183,11 +184,17 @@ struct SelectRowSmem {
 // into a candidate list; levels 2-4 run over the list (or, when it
 // overflows, over the whole row again).  Not every thread returns at the
 // same point: callers add nothing after it that needs a barrier.
-template <int TPB>
-__device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* __restrict__ row, long ld, int nc, int k,
-                           const uint32_t* hist_g, uint32_t* hist_zero,
-                           int32_t* __restrict__ out, float* __restrict__ sout) {
-  constexpr int SEG = TPB * kEPT;     // keys per staged segment
+//
+// REGS (rows of at most 32 x TPB keys): thread t loads its 32 keys straight
+// into registers (eight 16-byte loads 128 bytes apart) instead of staging the
+// row in LDS; every pass reads them there, with loop indices that unroll to
+// constants.  Results are identical.
+template <int TPB, bool REGS = false, int EPT = kEPT>
+__device__ __forceinline__ void select_row(SelectRowSmem<TPB, REGS>& sm, const float* __restrict__ row, long ld,
+                                           int nc, int k, const uint32_t* hist_g, uint32_t* hist_zero,
+                                           int32_t* __restrict__ out, float* __restrict__ sout) {
+  static_assert(EPT % 4 == 0 && EPT <= 32 && (REGS || EPT == kEPT), "staging in LDS assumes 32 keys per thread");
+  constexpr int SEG = TPB * EPT;     // keys per staged segment
   constexpr int VPT = SEG / 4 / TPB;  // float4 loads per thread per segment
   uint32_t* s_keys = sm.keys;
   uint32_t* s_hist = sm.hist;
@@ -206,16 +213,41 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
     }
     return;
   }
+  const int first = tid * EPT;  // this thread's keys: [first, first + EPT) of a segment
+  // a vector value, not an array: a run-time index into it becomes register
+  // selects (an indexed array would be placed in scratch memory)
+  typedef uint32_t KeyRun __attribute__((ext_vector_type(EPT)));
+  KeyRun kreg;
+  if constexpr (REGS) {  // loads clamped into the row as in stage(); keys past nc are never used
+    float4 v[EPT / 4];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const long a = first + 4L * j;
+      v[j] = *reinterpret_cast<const float4*>(row + (a < ld - 4 ? a : ld - 4));
+    }
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      kreg[4 * j] = score_key(v[j].x);
+      kreg[4 * j + 1] = score_key(v[j].y);
+      kreg[4 * j + 2] = score_key(v[j].z);
+      kreg[4 * j + 3] = score_key(v[j].w);
+    }
+  }
   for (int b = tid; b < 3 * 256; b += TPB) (&s_h2[0][0])[b] = 0u;
 
-  const int nseg = (nc + SEG - 1) / SEG;
-  const int first = tid * kEPT;  // this thread's keys: [first, first + 32) of a segment
-  const uint32_t* mykeys = s_keys + first + (first >> 5);
+  const int nseg = (nc + SEG - 1) / SEG;  // 1 when REGS
+  const uint32_t* mykeys = s_keys + (REGS ? 0 : first + (first >> 5));
+  // key e of this thread's run (e a constant after unrolling when REGS)
+  auto key_at = [&](int e) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (REGS) return kreg[e];
+    else return mykeys[e];
+  };
   // Stage segment sg: coalesced 16-byte loads (all issued first) into padded
   // LDS.  Rows live in a workspace whose leading dimension is a multiple of 4
   // and >= nc, so a load clamped to [0, ld-4] stays in bounds; keys past nc
   // are staged but never used.
   auto stage = [&](int sg) {
+    if constexpr (REGS) return;  // never called: a REGS row is one segment, already in registers
     __syncthreads();
     const long base = (long)sg * SEG;
     float4 buf[VPT];
@@ -236,7 +268,7 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
     }
     __syncthreads();
   };
-  auto nvalid = [&](int sg) { return max(0, min(kEPT, nc - sg * SEG - first)); };
+  auto nvalid = [&](int sg) { return max(0, min(EPT, nc - sg * SEG - first)); };
   auto put = [&](uint32_t slot, int i, uint32_t kv) {
     if (slot < (uint32_t)k) {  // always true when the counts are exact; keeps writes in the row
       out[slot] = i;
@@ -247,7 +279,8 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
   // its 32 keys in one burst and records the classes as two bit masks; after
   // the workgroup scan it visits only the set bits.  Classes 1 and 2 are
   // numbered separately in index order and handed to emit1 / emit2.
-  auto ordered_row = [&](auto&& cls, auto&& emit1, auto&& emit2, uint32_t& tot1, uint32_t& tot2) {
+  auto ordered_row = [&](auto&& cls, auto&& emit1, auto&& emit2, uint32_t& tot1,
+                         uint32_t& tot2) __attribute__((always_inline)) {
     tot1 = 0;
     tot2 = 0;
     for (int sg = 0; sg < nseg; ++sg) {
@@ -255,8 +288,8 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
       const int nv = nvalid(sg);
       uint32_t m1 = 0, m2 = 0;
 #pragma unroll
-      for (int e = 0; e < kEPT; ++e) {
-        const int c = cls(mykeys[e]);
+      for (int e = 0; e < EPT; ++e) {
+        const int c = cls(key_at(e));
         m1 |= (uint32_t)(c == 1 && e < nv) << e;
         m2 |= (uint32_t)(c == 2 && e < nv) << e;
       }
@@ -265,7 +298,12 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
       uint32_t p1 = tot1 + (ex & 0xFFFFu), p2 = tot2 + (ex >> 16);
       for (uint32_t mm = m1 | m2; mm; mm &= mm - 1) {
         const int e = __ffs(mm) - 1;
-        const uint32_t kv = mykeys[e];
+        uint32_t kv;
+        if constexpr (REGS) {
+          kv = kreg[e];
+        } else {
+          kv = mykeys[e];
+        }
         if ((m1 >> e) & 1u)
           emit1(sg * SEG + first + e, kv, p1++);
         else
@@ -283,7 +321,7 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
 #pragma unroll
     for (int q = 0; q < HPT; ++q) hreg[q] = hist_g[q * TPB + tid];
   }
-  if (nseg == 1) stage(0);
+  if (!REGS && nseg == 1) stage(0);
 
   // ---- level 1: 12-bit digit ----------------------------------------------
   if (hist_g) {
@@ -301,8 +339,8 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
       if (nseg > 1) stage(sg);
       const int nv = nvalid(sg);
 #pragma unroll
-      for (int e = 0; e < kEPT; ++e)
-        if (e < nv) atomicAdd(&s_hist[mykeys[e] >> kL1Shift], 1u);
+      for (int e = 0; e < EPT; ++e)
+        if (e < nv) atomicAdd(&s_hist[key_at(e) >> kL1Shift], 1u);
     }
     __syncthreads();
   }
@@ -392,8 +430,8 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB>& sm, const float* 
       if (nseg > 1) stage(sg);
       const int nv = nvalid(sg);
 #pragma unroll
-      for (int e = 0; e < kEPT; ++e) {
-        const uint32_t kv = mykeys[e];
+      for (int e = 0; e < EPT; ++e) {
+        const uint32_t kv = key_at(e);
         if (e < nv && (kv & pmask) == prefix) atomicAdd(&h2[(kv >> sh) & dm], 1u);
       }
     }

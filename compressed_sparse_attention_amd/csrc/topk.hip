@@ -12,10 +12,11 @@
 //            into a small candidate list;
 //   levels 2-4: 8+8+4-bit histograms over the candidates only, then one
 //            ordered pass over the candidates.
-// The row is staged in LDS in segments of 32 x TPB keys (coalesced loads; one
-// padding word per 32 keys, so the 64 lanes of a wave reading "their" 32
-// consecutive keys hit 64 different banks).  Thread t owns keys [32t, 32t+32)
-// of a segment, so thread order is index order: an ordered pass is one burst
+// Rows of up to 8192 candidates are held in registers, 32 consecutive keys per
+// thread; longer rows are staged in LDS in segments of 32 x TPB keys
+// (coalesced loads; one padding word per 32 keys, so the 64 lanes of a wave
+// reading "their" 32 consecutive keys hit 64 different banks).  Thread t owns
+// keys [32t, 32t+32) of a segment, so thread order is index order: an ordered pass is one burst
 // read and classification per thread, one workgroup-wide exclusive scan, and
 // an emit of the (few) selected keys.  Keys > T fill the
 // first slots; among keys == T the lowest indices fill the rest, which is
@@ -32,19 +33,26 @@ __global__ void hist_clear_kernel(uint32_t* __restrict__ h, long n) {
   if (i < n) h[i] = 0u;
 }
 
-template <int TPB>
+// REGS: rows of at most EPT x TPB candidates (max_cand bounds them), keys in
+// registers.  Rows of up to 8192 candidates (every prefill row here) take
+// 256 threads x 32 keys: at 19.5 KB of LDS and 93 VGPRs five rows share a
+// CU, against three with the row staged in LDS (0.53 -> 0.38 ms for the
+// 32768-token prefill; 512 x 16 and 1024 x 8 measured 0.41 and 0.65 ms).
+constexpr int kShortTPB = 256;
+constexpr int kShortEPT = 32;
+template <int TPB, bool REGS, int EPT>
 __global__ __launch_bounds__(TPB) void topk_kernel(int m, const float* __restrict__ scores, long ld,
                                                    const int64_t* __restrict__ q_pos, long max_cand,
                                                    int k, uint32_t* __restrict__ hist_g,
                                                    int32_t* __restrict__ idx_out,
                                                    float* __restrict__ score_out) {
-  __shared__ SelectRowSmem<TPB> sm;
+  __shared__ SelectRowSmem<TPB, REGS> sm;
   const long r = blockIdx.x;
   const long pos = q_pos ? q_pos[r] : r;
   long ncl = pos > 0 ? pos / m : 0;
   ncl = ncl < max_cand ? ncl : max_cand;
   uint32_t* hrow = hist_g ? hist_g + r * kL1Bins : nullptr;
-  select_row<TPB>(sm, scores + r * ld, ld, (int)ncl, k, hrow, hrow, idx_out + r * k,
+  select_row<TPB, REGS, EPT>(sm, scores + r * ld, ld, (int)ncl, k, hrow, hrow, idx_out + r * k,
                   score_out ? score_out + r * k : nullptr);
 }
 
@@ -157,11 +165,11 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
                     eq_list + r * P * (long)kMChunk, kMChunk, out, sout);
 }
 
-template <int TPB>
+template <int TPB, bool REGS, int EPT>
 void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const int64_t* q_pos, long max_cand,
             int k, uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
-  (void)csa::launch("topk", topk_kernel<TPB>, dim3((unsigned)n_queries), dim3(TPB), 0, s, m, scores, ld_sc, q_pos,
-               max_cand, k, hist, idx_out, score_out);
+  (void)csa::launch("topk", topk_kernel<TPB, REGS, EPT>, dim3((unsigned)n_queries), dim3(TPB), 0, s, m, scores, ld_sc,
+                    q_pos, max_cand, k, hist, idx_out, score_out);
 }
 
 }  // namespace
@@ -181,10 +189,11 @@ hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
                       lists->P, lists->gtc, idx_out, score_out);
     return hipGetLastError();
   }
-  if (max_cand <= 8192)
-    launch_rows<256>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
+  if (max_cand <= kShortTPB * kShortEPT)  // every row fits in registers
+    launch_rows<kShortTPB, true, kShortEPT>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out,
+                                             score_out, s);
   else
-    launch_rows<1024>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
+    launch_rows<1024, false, kEPT>(n_queries, m, scores, ld_sc, q_pos, max_cand, k, hist, idx_out, score_out, s);
   return hipGetLastError();
 }
 
