@@ -32,6 +32,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -232,6 +234,77 @@ def _prefill_stage_rooflines(w, kern, steps):
             ach, peak, unit, key = amount / sec / 1e9, HBM_PEAK_GBS, "GB/s", "algorithmic_bytes_per_step"
         out[stage] = {"kernels": fam, "bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
                       "frac": round(ach / peak, 4), key: amount}
+    return out
+
+
+def bench_other_configs(args, torch, api, synth, layer):
+    """The other seeded workloads, timed on their own: the 512-token fp32 prefill (a parity-sized case, launch
+    bound), the 32 x 8K decode batch and the ragged 64-sequence decode batch (m = 8, 128 heads).  Decode steps are
+    eager launches over enough input copies to exceed the 256 MB last-level cache; their HBM fraction is the
+    step's algorithmic bytes (every candidate key, the selected entries, queries, outputs and indices) over the
+    step time against 8 TB/s."""
+    dev = "cuda:0"
+    out = {}
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    w = synth.WORKLOADS[1]
+    P = synth.make_prefill(w)
+    W = layer.pack_prefill_params(P, w.dtype, dev)
+    H = layer.to_device(P["H"], w.dtype, dev)
+    buf = layer.PrefillBuffers(w.n, w.m, w.k, w.nh, w.nhI, w.c, w.cI, w.dc, H.dtype, dev)
+    ms = timed(lambda i: layer.prefill(H, W, w.m, w.k, w.nh, w.nhI, buf=buf), 50, 5)
+    out[w.name] = {"kind": "prefill", "tokens": w.n, "ms": round(ms, 4), "tokens_per_s": round(w.n / (ms * 1e-3), 1)}
+    print(f"[bench] {w.name}: {ms * 1000:.1f} us per {w.n}-token prefill", flush=True)
+
+    for cfg in (2, 5):
+        w = synth.WORKLOADS[cfg]
+        D = synth.make_decode(w)
+        B = int(D["seq_len"].shape[0])
+        nb = D["n_blocks"].astype(np.int64)
+        max_cand = int(nb.max())
+        base = {"q": layer.to_device(D["q"], w.dtype, dev), "qI": layer.to_device(D["qI"], w.dtype, dev),
+                "wI": layer.to_device(D["wI"], "f32", dev), "C": layer.to_device(D["Ccomp"], w.dtype, dev),
+                "K": layer.to_device(D["KIcomp"], w.dtype, dev)}
+        per_copy = sum(t.numel() * t.element_size() for t in base.values())
+        copies = max(1, min(8, -(-(320 << 20) // per_copy)))
+        reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+        seq_len = torch.from_numpy(D["seq_len"]).to(dev)
+        off = torch.from_numpy(D["kv_offset"]).to(dev)
+        dbuf = layer.DecodeBuffers(B, w.k, w.nh, w.c, w.nhI, max_cand, base["q"].dtype, dev)
+
+        def step(i):
+            r = reps[i % len(reps)]
+            layer.decode(r["q"], r["qI"], r["wI"], r["C"], r["K"], seq_len, off, w.m, w.k, max_cand, buf=dbuf)
+
+        ms = timed(step, 100, 10)
+        api.csa_timing_reset()
+        api.csa_timing_enable(True)
+        timed(step, 50, 0)
+        api.csa_timing_enable(False)
+        kern = _kernel_stats(api, ["hist_clear", "indexer_sweep", "topk", "mqa", "mqa_combine"])
+        api.csa_timing_reset()
+        sel = np.minimum(nb, w.k)
+        step_bytes = int((2 * nb * w.cI + 2 * sel * w.c + 2 * (w.nh * w.c + w.nhI * w.cI) + 4 * w.nhI
+                          + 2 * w.nh * w.c + 4 * w.k).sum())
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        out[w.name] = {"kind": "decode", "batch": B, "us_per_step": round(ms * 1000, 3),
+                       "queries_per_s": round(B / (ms * 1e-3), 1), "step_bytes": step_bytes,
+                       "step_hbm_fraction": round(gbs / HBM_PEAK_GBS, 4), "input_copies": copies,
+                       "kernels_us": {n: round(st["avg_us"], 3) for n, st in kern.items()}}
+        print(f"[bench] {w.name}: {ms * 1000:.2f} us/step, {B / (ms * 1e-3):.0f} queries/s, "
+              f"{gbs:.0f} GB/s of step bytes", flush=True)
+        del reps, base, dbuf
     return out
 
 
@@ -478,6 +551,7 @@ def main():
     ap.add_argument("--no-decode-step", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true")
@@ -499,6 +573,7 @@ def main():
     dstep = None if args.no_decode_step else bench_decode_step(args, torch, api, synth, layer)
     pvar = None if args.no_varlen else bench_prefill_varlen(args, torch, api, synth, layer)
     pbwd = None if args.no_backward else bench_prefill_backward(args, torch, api, synth, layer)
+    other = None if args.no_other_configs else bench_other_configs(args, torch, api, synth, layer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec, args.cpu_seconds)
 
     w = dec["workload"]
@@ -533,6 +608,7 @@ def main():
         "decode_step_with_cache": dstep,
         "prefill_varlen": pvar,
         "prefill_backward": pbwd,
+        "other_configs": other,
     }
     print(json.dumps(line), flush=True)
 
