@@ -1,0 +1,178 @@
+"""Seeded random-shape GPU parity: the compression, selection, attention, compression-gradient and projection
+calls on shapes drawn at random (sizes, ragged edges, head counts, k, column pitches), each against the oracle
+as in the hand-picked cases.  Every case is fixed by its index, so a failure names a reproducible shape."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_amd import api, synth
+from compressed_sparse_attention_amd.layer import to_device
+from oracle import csa_oracle as O
+from parity import assert_rows_close, check_topk, to_np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _rng(tag, i):
+    return synth.rng_for(1000 * tag + i)
+
+
+def _draw(rng, shape, std, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    return synth.f32_to_bf16(x) if dtype == "bf16" else x
+
+
+def _f64(x, dtype):
+    return synth.to_f64(x, dtype)
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_compress(i):
+    rng = _rng(1, i)
+    dtype = ["f32", "bf16"][i % 2]
+    m = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16]))
+    c = 4 * int(rng.integers(1, 161))
+    n = int(rng.integers(0, 2500)) if i % 5 else int(rng.integers(0, 3 * m))
+    cp = (c + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))  # column pitch of the four slices
+    print(f"compress case {i}: {dtype} n={n} m={m} c={c} pitch={cp}", flush=True)
+    P = _draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = _draw(rng, (n, 4 * cp), 2.0, dtype)
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
+    Ba, Bb = _draw(rng, (m, c), 0.5, dtype), _draw(rng, (m, c), 0.5, dtype)
+    Pd = to_device(P, dtype, DEV)
+    N = n // m
+    out = torch.full((max(N, 1), cp), 3.0, dtype=TD[dtype], device=DEV)[:N, :c]  # rows 16-byte aligned
+    api.csa_compress(*[Pd[:, j * cp:j * cp + c] for j in range(4)], to_device(Ba, dtype, DEV),
+                     to_device(Bb, dtype, DEV), m, out)
+    torch.cuda.synchronize()
+    if N:
+        P64 = _f64(P, dtype)
+        ref = O.compress(*[P64[:, j * cp:j * cp + c] for j in range(4)], _f64(Ba, dtype), _f64(Bb, dtype), m)
+        assert_rows_close(to_np64(out), ref, what=f"compress case {i}")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_index_topk_decode(i):
+    rng = _rng(2, i)
+    dtype = "f32" if i % 6 == 5 else "bf16"
+    m = int(rng.choice([1, 2, 4, 8]))
+    nhI = int(rng.integers(1, 65))
+    cI = int(rng.choice([32, 64, 128, 256]))
+    k = int(rng.integers(1, 1500))
+    B = int(rng.integers(1, 9))
+    lens = rng.integers(0, 4 * 8000, size=B).astype(np.int64)
+    lens[rng.random(B) < 0.2] = int(rng.integers(0, 4 * m))  # some sequences with no or few blocks
+    print(f"index_topk case {i}: {dtype} m={m} nhI={nhI} cI={cI} k={k} lens={lens.tolist()}", flush=True)
+    nblk = lens // m
+    off = np.zeros_like(nblk)
+    off[1:] = np.cumsum(nblk)[:-1]
+    K = _draw(rng, (max(int(nblk.sum()), 1), cI), 1.0, dtype)
+    qI = _draw(rng, (B, nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((B, nhI), dtype=np.float32)
+    idx = torch.full((B, k), 123456, dtype=torch.int32, device=DEV)
+    max_cand = int(nblk.max())
+    api.csa_index_topk(to_device(qI, dtype, DEV), to_device(wI, "f32", DEV), to_device(K, dtype, DEV), m, k,
+                       max_cand, idx, q_seq=torch.arange(B, dtype=torch.int32, device=DEV),
+                       q_pos=torch.tensor(lens, device=DEV), kv_offset=torch.tensor(off, device=DEV))
+    torch.cuda.synchronize()
+    K64 = _f64(K, dtype)
+    rows = [O.index_scores_row(_f64(qI[b], dtype), wI[b].astype(np.float64), K64[off[b]:off[b] + nblk[b]],
+                               int(nblk[b])) for b in range(B)]
+    check_topk(idx.cpu().numpy(), rows, k)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_sparse_mqa(i):
+    rng = _rng(3, i)
+    dtype = "f32" if i % 4 == 3 else "bf16"
+    c = int(rng.choice([64, 128, 256, 512]))
+    nh = int(rng.integers(1, 131))
+    k = int(rng.integers(1, 701))
+    nblk = int(rng.integers(1, 801))
+    # short batches (split slots) and long ones (one workgroup per query and head group), kept to a size the
+    # oracle finishes quickly
+    B = int(rng.integers(1, 41)) if i % 3 else int(rng.integers(520, 641))
+    while B * nh * min(k, nblk) * c > 3e8 and nh > 1:
+        nh = max(1, nh // 2)
+    qmult = float(rng.choice([1.0, 4.0, 16.0]))
+    print(f"sparse_mqa case {i}: {dtype} B={B} nh={nh} c={c} k={k} nblk={nblk} q x{qmult}", flush=True)
+    C = _draw(rng, (B * nblk, c), 1.0, dtype)
+    q = _draw(rng, (B, nh, c), qmult / math.sqrt(c), dtype)
+    ncand = rng.integers(0, nblk + 1, size=B)
+    idx = synth.random_selection(rng, ncand, k)
+    if i % 2:
+        idx = np.stack([rng.permutation(row) for row in idx])  # -1 slots between valid ones
+    off = np.arange(B, dtype=np.int64) * nblk
+    o = torch.full((B, nh, c), 5.0, dtype=TD[dtype], device=DEV)
+    lse = torch.empty(B, nh, dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(c)
+    api.csa_sparse_mqa(to_device(q, dtype, DEV), to_device(C, dtype, DEV), torch.from_numpy(idx).to(DEV), scale, o,
+                       lse, q_seq=torch.arange(B, dtype=torch.int32, device=DEV),
+                       kv_offset=torch.from_numpy(off).to(DEV))
+    torch.cuda.synchronize()
+    C64, q64 = _f64(C, dtype), _f64(q, dtype)
+    o_np, lse_np = to_np64(o), lse.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        sel = idx[b][idx[b] >= 0]
+        ro, rl = O.mqa(q64[b], C64[off[b] + sel], scale)
+        assert_rows_close(o_np[b], ro, what=f"mqa case {i} o[{b}]")
+        if sel.size == 0:
+            assert np.all(np.isneginf(lse_np[b]))
+        else:
+            assert np.allclose(lse_np[b], rl, rtol=1e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_compress_backward(i):
+    rng = _rng(4, i)
+    dtype = ["f32", "bf16"][i % 2]
+    m = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    c = 4 * int(rng.integers(1, 161))
+    n = int(rng.integers(0, 2000))
+    cp = (c + 7) // 8 * 8 + 8 * int(rng.integers(0, 3))
+    print(f"compress_backward case {i}: {dtype} n={n} m={m} c={c} pitch={cp}", flush=True)
+    P = _draw(rng, (n, 4 * cp), 1.0, dtype)
+    Pz = _draw(rng, (n, 4 * cp), 2.0, dtype)
+    P = np.where((np.arange(4 * cp) // cp)[None, :] >= 2, Pz, P)
+    Ba, Bb = _draw(rng, (m, c), 0.5, dtype), _draw(rng, (m, c), 0.5, dtype)
+    N = n // m
+    dC = rng.standard_normal(size=(N, c)).astype(np.float32)
+    Pd = to_device(P, dtype, DEV)
+    G = torch.full((n, 4 * cp), 7.0, dtype=TD[dtype], device=DEV)
+    gs = [G[:, j * cp:j * cp + c] for j in range(4)]
+    dBa = torch.full((m, c), 7.0, device=DEV)
+    dBb = torch.full((m, c), 7.0, device=DEV)
+    api.csa_compress_backward(*[Pd[:, j * cp:j * cp + c] for j in range(4)], to_device(Ba, dtype, DEV),
+                              to_device(Bb, dtype, DEV), m, torch.from_numpy(dC).to(DEV), *gs, dBa, dBb)
+    torch.cuda.synchronize()
+    P64 = _f64(P, dtype)
+    ref = O.compress_backward(*[P64[:, j * cp:j * cp + c] for j in range(4)], _f64(Ba, dtype), _f64(Bb, dtype), m,
+                              dC.astype(np.float64))
+    if n:
+        for w in range(4):
+            assert_rows_close(to_np64(gs[w]), ref[w], what=f"compress_backward case {i} grad {w}")
+    mag_a = np.abs(ref[2][:N * m]).reshape(N, m, c).sum(0) if N else np.zeros((m, c))
+    mag_b = np.abs(ref[3][:(N - 1) * m]).reshape(N - 1, m, c).sum(0) if N > 1 else np.zeros((m, c))
+    tol = 1e-5 if dtype == "f32" else 1e-4
+    for got, want, mag in ((dBa, ref[4], mag_a), (dBb, ref[5], mag_b)):
+        assert np.all(np.abs(to_np64(got) - want) <= tol * mag + 1e-7), f"compress_backward case {i} bias"
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_project(i):
+    rng = _rng(5, i)
+    din, dout = [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")][i % 3]
+    M = int(rng.integers(1, 1200))
+    N = 8 * int(rng.integers(1, 200))
+    K = 8 * int(rng.integers(1, 300)) if i % 2 else 64 * int(rng.integers(1, 40))
+    print(f"project case {i}: {din}->{dout} M={M} N={N} K={K}", flush=True)
+    X = _draw(rng, (M, K), 1.0, din)
+    W = _draw(rng, (K, N), 1.0 / math.sqrt(K), din)
+    Y = torch.empty(M, N, dtype=TD[dout], device=DEV)
+    api.csa_project(to_device(X, din, DEV), to_device(np.ascontiguousarray(W.T), din, DEV), Y)
+    torch.cuda.synchronize()
+    assert_rows_close(to_np64(Y), O.project(_f64(X, din), _f64(W, din)), what=f"project case {i}")
