@@ -349,3 +349,87 @@ def test_random_decode(i):
     check_topk(idx, score_rows, k)
     ref_o = _mqa_ref(_f64(q, "bf16"), _f64(C, "bf16"), idx, off, 1.0 / math.sqrt(c))
     assert_rows_close(to_np64(buf.o), ref_o, what=f"decode case {i} o")
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_compress_append(i):
+    """Decode-time cache maintenance on random shapes: sequences that already hold a random number of tokens
+    grow one token per call; the appended compressed rows equal the oracle's compression of the whole
+    sequences, and no other cache row is touched."""
+    rng = _rng(10, i)
+    dtype = ["bf16", "f32"][i % 2]
+    m = int(rng.choice([1, 2, 4, 8, 16]))
+    c = 4 * int(rng.integers(1, 150))
+    B = int(rng.integers(1, 6))
+    steps = int(rng.integers(1, 41))
+    pre = [int(x) for x in rng.integers(0, 3 * m + 6, size=B)]
+    print(f"compress_append case {i}: {dtype} m={m} c={c} B={B} steps={steps} pre={pre}", flush=True)
+    cp = (c + 7) // 8 * 8
+    seqs = []
+    for b in range(B):
+        n = pre[b] + steps
+        Y = _draw(rng, (n, 4 * c), 1.0, dtype)
+        Yz = _draw(rng, (n, 4 * c), 2.0, dtype)
+        seqs.append(np.where((np.arange(4 * c) // c)[None, :] >= 2, Yz, Y))
+    Ba, Bb = _draw(rng, (m, c), 0.5, dtype), _draw(rng, (m, c), 0.5, dtype)
+    cap = max(pre) // m + steps // m + 2
+    Cbig = torch.full((B * cap, cp), 3.0, dtype=TD[dtype], device=DEV)
+    C = Cbig[:, :c]
+    ring = torch.zeros(B, 2 * m, 4 * c, dtype=TD[dtype], device=DEV)
+    for b in range(B):
+        for tok in range(max(0, pre[b] - 2 * m), pre[b]):
+            ring[b, tok % (2 * m)] = to_device(seqs[b][tok], dtype, DEV)
+    off = torch.arange(B, dtype=torch.int64, device=DEV) * cap
+    t = torch.tensor(pre, dtype=torch.int64, device=DEV)
+    Bad, Bbd = to_device(Ba, dtype, DEV), to_device(Bb, dtype, DEV)
+    new_rows = torch.zeros(B, 4 * c, dtype=TD[dtype], device=DEV)
+    for s in range(steps):
+        new_rows.copy_(to_device(np.stack([seqs[b][pre[b] + s] for b in range(B)]), dtype, DEV))
+        api.csa_compress_append(new_rows, ring, Bad, Bbd, m, t, off, C)
+        t += 1
+    torch.cuda.synchronize()
+    got = to_np64(C)
+    for b in range(B):
+        S = _f64(seqs[b], dtype)
+        ref = O.compress(S[:, :c], S[:, c:2 * c], S[:, 2 * c:3 * c], S[:, 3 * c:], _f64(Ba, dtype), _f64(Bb, dtype), m)
+        lo, hi = pre[b] // m, (pre[b] + steps) // m
+        rows = got[b * cap:(b + 1) * cap]
+        if hi > lo:
+            assert_rows_close(rows[lo:hi], ref[lo:hi], what=f"compress_append case {i} sequence {b}")
+        assert np.all(rows[:lo] == 3.0) and np.all(rows[hi:] == 3.0)
+    assert torch.all(Cbig[:, c:] == 3.0)
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_random_index_topk_varlen(i):
+    rng = _rng(11, i)
+    dtype = "f32" if i == 4 else "bf16"
+    m = int(rng.choice([1, 2, 4, 8]))
+    nhI = int(rng.integers(1, 65))
+    cI = int(rng.choice([32, 64, 128, 256]))
+    k = int(rng.integers(1, 300))
+    lengths = [int(x) for x in rng.integers(0, 600, size=int(rng.integers(1, 6)))]
+    print(f"index_topk_varlen case {i}: {dtype} m={m} nhI={nhI} cI={cI} k={k} lengths={lengths}", flush=True)
+    cu, bo = _packed(lengths, m, 0)
+    n, nb = int(cu[-1]), int(bo[-1])
+    if n == 0:
+        return
+    K = _draw(rng, (max(nb, 1), cI), 1.0, dtype)
+    qI = _draw(rng, (n, nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((n, nhI), dtype=np.float32)
+    max_cand = max([(L - 1) // m for L in lengths if L > 0], default=0)
+    idx = torch.full((n, k), 123456, dtype=torch.int32, device=DEV)
+    qs = torch.full((n,), -5, dtype=torch.int32, device=DEV)
+    api.csa_index_topk_varlen(to_device(qI, dtype, DEV), to_device(wI, "f32", DEV), to_device(K, dtype, DEV), m, k,
+                              max_cand, torch.tensor(cu, device=DEV), torch.tensor(bo, device=DEV), idx,
+                              q_seq_out=qs)
+    torch.cuda.synchronize()
+    seq_of = np.repeat(np.arange(len(lengths)), lengths)
+    assert np.array_equal(qs.cpu().numpy(), seq_of)
+    K64, q64 = _f64(K, dtype), _f64(qI, dtype)
+    rows = []
+    for t in range(n):
+        b = seq_of[t]
+        nc = int((t - cu[b]) // m)
+        rows.append(O.index_scores_row(q64[t], wI[t].astype(np.float64), K64[bo[b]:bo[b] + nc], nc))
+    check_topk(idx.cpu().numpy(), rows, k)
