@@ -479,7 +479,7 @@ def bench_decode_step(args, torch, api, synth, layer):
     for n, s_ in kern.items():
         print(f"[bench]   {n:16s} {s_['total_ms'] / args.steps * 1000:8.2f} us/step "
               f"({s_['launches'] // args.steps} launches)", flush=True)
-    # weights streamed by the four projections of one step (bf16), plus their inputs and outputs
+    # weights streamed by the four projections of one step (bf16, two paired launches), plus their inputs and outputs
     d, dc, c, cI = wp.d, wp.dc, wd.c, wd.cI
     shapes = [(4 * c + 4 * cI + dc, d, 2), (wd.nhI, d, 4), (wd.nhI * cI, dc, 2), (wd.nh * c, dc, 2)]
     gemm_bytes = sum(n * k * 2 + B * k * 2 + B * n * ob for n, k, ob in shapes)

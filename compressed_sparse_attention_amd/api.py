@@ -38,6 +38,8 @@ _SIGS = {
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_project": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                    _i64, _vp]),
+    "csa_project_pair": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _vp, _i64, ctypes.c_int, _i64, _vp, _i64, _vp,
+                                         _i64, ctypes.c_int, _i64, _vp, _i64, _vp, _i64, _vp]),
     "csa_project_backward_workspace": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                                       ctypes.POINTER(_sz)]),
     "csa_project_backward": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
@@ -161,6 +163,21 @@ def csa_project(X: torch.Tensor, Wt: torch.Tensor, Y: torch.Tensor) -> torch.Ten
                              _rowmajor(Wt, "Wt"), _ptr(Y), _rowmajor(Y, "Y"), _stream(X.device)),
            "csa_project")
     return Y
+
+
+def csa_project_pair(X: torch.Tensor, Wt1: torch.Tensor, Y1: torch.Tensor, Wt2: torch.Tensor,
+                     Y2: torch.Tensor) -> None:
+    """Y1 = X . Wt1^T and Y2 = X . Wt2^T, one launch when X has at most 16 bf16 rows (views allowed)."""
+    M, K = X.shape
+    N1, N2 = Wt1.shape[0], Wt2.shape[0]
+    if Wt1.shape[1] != K or Wt2.shape[1] != K or tuple(Y1.shape) != (M, N1) or tuple(Y2.shape) != (M, N2):
+        raise CSAError("csa_project_pair: shape mismatch")
+    if X.dtype != Wt1.dtype or X.dtype != Wt2.dtype:
+        raise CSAError("csa_project_pair: X and weight dtypes differ")
+    _check(lib().csa_project_pair(_dt(X), M, K, _ptr(X), _rowmajor(X, "X"), _dt(Y1), N1, _ptr(Wt1),
+                                  _rowmajor(Wt1, "Wt1"), _ptr(Y1), _rowmajor(Y1, "Y1"), _dt(Y2), N2, _ptr(Wt2),
+                                  _rowmajor(Wt2, "Wt2"), _ptr(Y2), _rowmajor(Y2, "Y2"), _stream(X.device)),
+           "csa_project_pair")
 
 
 def csa_project_backward_workspace(dtype, M: int, N: int, K: int, want_dx: bool, want_dw: bool) -> int:

@@ -216,6 +216,33 @@ csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, 
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_project launch");
 }
 
+csa_status csa_project_pair(csa_dtype in_dt, int64_t M, int64_t K, const void* X, int64_t ldx, csa_dtype out_dt1,
+                            int64_t N1, const void* Wt1, int64_t ldw1, void* Y1, int64_t ldy1, csa_dtype out_dt2,
+                            int64_t N2, const void* Wt2, int64_t ldw2, void* Y2, int64_t ldy2, void* stream) {
+  CSA_REQUIRE(dtype_ok(in_dt) && dtype_ok(out_dt1) && dtype_ok(out_dt2), "csa_project_pair: unknown dtype");
+  CSA_REQUIRE(!(in_dt == CSA_F32 && (out_dt1 == CSA_BF16 || out_dt2 == CSA_BF16)),
+              "csa_project_pair: fp32 input with bf16 output is not supported");
+  CSA_REQUIRE(M > 0 && K > 0 && N1 > 0 && N2 > 0, "csa_project_pair: M, K, N1, N2 must be positive");
+  CSA_REQUIRE(M <= 0x7FFFFFFF && K <= 0x7FFFFFFF && N1 <= 0x7FFFFFFF && N2 <= 0x7FFFFFFF,
+              "csa_project_pair: size exceeds 2^31-1");
+  CSA_REQUIRE(K % 8 == 0, "csa_project_pair: K must be a multiple of 8 (got %lld)", (long long)K);
+  CSA_REQUIRE(X && Wt1 && Y1 && Wt2 && Y2, "csa_project_pair: null pointer");
+  CSA_REQUIRE(aligned16(X) && aligned16(Wt1) && aligned16(Y1) && aligned16(Wt2) && aligned16(Y2),
+              "csa_project_pair: pointers must be 16-byte aligned");
+  const int v = vec_elems(in_dt);
+  CSA_REQUIRE(ldx >= K && ldw1 >= K && ldw2 >= K && ldy1 >= N1 && ldy2 >= N2,
+              "csa_project_pair: leading dimension smaller than row length");
+  CSA_REQUIRE(ldx % v == 0 && ldw1 % v == 0 && ldw2 % v == 0,
+              "csa_project_pair: ldx/ldw must keep rows 16-byte aligned");
+  CSA_REQUIRE(ldy1 % vec_elems(out_dt1) == 0 && ldy2 % vec_elems(out_dt2) == 0,
+              "csa_project_pair: ldy must keep rows 16-byte aligned");
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  hipError_t e = csa::launch_gemm_pair(in_dt, M, K, X, ldx, out_dt1, N1, Wt1, ldw1, Y1, ldy1, out_dt2, N2, Wt2, ldw2,
+                                       Y2, ldy2, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_project_pair launch");
+}
+
 namespace {
 // Workspace of csa_project_backward: W = Wt^T [K, N] (for dX); dY^T [N, M8] and X^T [K, M8] (for dWt).
 struct ProjBwdLayout {

@@ -37,6 +37,11 @@ hipError_t launch(const char* family, F kernel, dim3 grid, dim3 block, uint32_t 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s);
 
+// Y1 = X W1 and Y2 = X W2 (one launch when X has at most 16 bf16 rows).
+hipError_t launch_gemm_pair(csa_dtype in_dt, long M, long K, const void* X, long ldx, csa_dtype out1, long N1,
+                            const void* W1, long ldw1, void* Y1, long ldy1, csa_dtype out2, long N2, const void* W2,
+                            long ldw2, void* Y2, long ldy2, hipStream_t s);
+
 // dst[c][r] = src[r][c] (r < R, c < C), zeros for R <= r < Rp; 16-byte granules.
 hipError_t launch_transpose(csa_dtype dt, long R, long C, long Rp, const void* src, long lds, void* dst, long ldd,
                             hipStream_t s);

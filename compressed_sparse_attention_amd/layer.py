@@ -317,8 +317,9 @@ class DecodeState:
 def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeState, m: int, k: int, nh: int,
                 nhI: int, scale: Optional[float] = None, buf: Optional[DecodeBuffers] = None) -> DecodeBuffers:
     """One decode step with cache maintenance: every sequence b appends token state.t[b] with hidden
-    state H_new[b].  Eqs 1, 2, 5, 6, 7, 10 for the new tokens (few-row GEMMs), eqs 3-4 appended to the
-    compressed caches when a block completes, then eqs 8, 9, 11 for the new tokens; positions advance."""
+    state H_new[b].  Eqs 1, 2, 5, 6, 7, 10 for the new tokens (two paired few-row GEMM launches), eqs 3-4
+    appended to the compressed caches when a block completes, then eqs 8, 9, 11 for the new tokens; positions
+    advance."""
     B = H_new.shape[0]
     c, cI = W["c"], W["cI"]
     width = 4 * c + 4 * cI + W["dc"]
@@ -326,11 +327,9 @@ def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeSt
     wI = torch.empty(B, nhI, dtype=torch.float32, device=H_new.device)
     qI = torch.empty(B, nhI * cI, dtype=H_new.dtype, device=H_new.device)
     q = torch.empty(B, nh * c, dtype=H_new.dtype, device=H_new.device)
-    api.csa_project(H_new, W["W_H_t"], Y)  # eqs 1, 2 (+ indexer copies), 5
-    api.csa_project(H_new, W["W_w_t"], wI)  # eq 7
+    api.csa_project_pair(H_new, W["W_H_t"], Y, W["W_w_t"], wI)  # eqs 1, 2 (+ indexer copies), 5; eq 7
     cQ = Y[:, 4 * c + 4 * cI:]
-    api.csa_project(cQ, W["W_UQI_t"], qI)  # eq 6
-    api.csa_project(cQ, W["W_UQ_t"], q)  # eq 10
+    api.csa_project_pair(cQ, W["W_UQ_t"], q, W["W_UQI_t"], qI)  # eq 10; eq 6
     api.csa_compress_append(Y[:, :4 * c], state.ring, W["B_a"], W["B_b"], m, state.t, state.kv_offset,
                             state.Ccomp)  # eqs 3-4
     api.csa_compress_append(Y[:, 4 * c:4 * c + 4 * cI], state.ring_I, W["B_aI"], W["B_bI"], m, state.t,

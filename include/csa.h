@@ -91,6 +91,27 @@ csa_status csa_project(csa_dtype in_dt, csa_dtype out_dt, int64_t M, int64_t N, 
                        int64_t ldy, void* stream);
 
 /*
+ * csa_project_pair -- Y1 = X . W1 and Y2 = X . W2 for two projections of the
+ * same rows X whose outputs cannot share one stacked call (different output
+ * dtypes or separate buffers): eqs 1, 2, 5 with eq 7 (H times the stacked
+ * W^aKV | W^bKV | W^aZ | W^bZ | W^DQ, and H W^w), or eq 6 with eq 10 (c^Q W^UQ
+ * of the indexer and of the attention).
+ *
+ *   X    [M, K]   row-major, leading dimension ldx, dtype in_dt
+ *   Wt1  [N1, K]  W1 transposed as for csa_project, leading dimension ldw1
+ *   Y1   [M, N1]  leading dimension ldy1, dtype out_dt1
+ *   Wt2, Y2       likewise with N2, ldw2, ldy2, out_dt2
+ *
+ * Results are those of two csa_project calls.  With at most 16 bf16 rows
+ * (one decode token per sequence) both products run in one launch, so a
+ * small one (W^w) costs no launch of its own.  The same requirements as
+ * csa_project hold for each product; the two outputs must not overlap.
+ */
+csa_status csa_project_pair(csa_dtype in_dt, int64_t M, int64_t K, const void* X, int64_t ldx, csa_dtype out_dt1,
+                            int64_t N1, const void* Wt1, int64_t ldw1, void* Y1, int64_t ldy1, csa_dtype out_dt2,
+                            int64_t N2, const void* Wt2, int64_t ldw2, void* Y2, int64_t ldy2, void* stream);
+
+/*
  * csa_project_backward -- gradients of Y = X . W (eqs 1, 2, 5, 6, 7 and 10)
  * given dY, with W stored transposed as for csa_project:
  *

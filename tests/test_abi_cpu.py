@@ -53,6 +53,26 @@ def test_project_rejects_bad_args(L):
     assert L.csa_project(1, 1, 8, 8, 8, p, 4, p, 8, p, 8, None) == api.CSA_ERR_INVALID_ARG
 
 
+def test_project_pair_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def call(ind=1, M=8, K=8, X=p, ldx=8, o1=1, N1=8, W1=p, ldw1=8, Y1=p, ldy1=8, o2=1, N2=8, W2=p, ldw2=8, Y2=p,
+             ldy2=8):
+        return L.csa_project_pair(ind, M, K, X, ldx, o1, N1, W1, ldw1, Y1, ldy1, o2, N2, W2, ldw2, Y2, ldy2, None)
+
+    assert call(N2=0) == api.CSA_ERR_INVALID_ARG
+    assert "positive" in _err()
+    assert call(K=12, ldx=16, ldw1=16, ldw2=16) == api.CSA_ERR_INVALID_ARG
+    assert "multiple of 8" in _err()
+    assert call(W2=None) == api.CSA_ERR_INVALID_ARG
+    assert call(Y2=ctypes.c_void_p(18)) == api.CSA_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert call(ind=0, o1=0, o2=1) == api.CSA_ERR_INVALID_ARG
+    assert call(o2=7) == api.CSA_ERR_INVALID_ARG
+    assert call(ldw2=4) == api.CSA_ERR_INVALID_ARG
+    assert call(ldy1=4, N1=8) == api.CSA_ERR_INVALID_ARG
+
+
 def test_compress_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
     assert L.csa_compress(1, 64, 0, 64, p, p, p, p, 256, p, p, p, 64, None) == api.CSA_ERR_INVALID_ARG

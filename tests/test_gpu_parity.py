@@ -62,6 +62,30 @@ def test_project(din, dout, M, N, K):
     assert_rows_close(to_np64(Y), O.project(f64(X, din), f64(W, din)), what="project")
 
 
+@pytest.mark.parametrize("din,d1,d2,M,N1,N2,K", [
+    ("bf16", "bf16", "f32", 8, 4096, 64, 4096),    # one launch: a stacked H-side weight with the w^I head weights
+    ("bf16", "bf16", "bf16", 8, 1000, 264, 1536),  # one launch, ragged column blocks in both products
+    ("bf16", "f32", "bf16", 3, 40, 24, 200),       # one launch, K tail
+    ("bf16", "bf16", "f32", 40, 296, 64, 200),     # more than 16 rows: two launches
+    ("f32", "f32", "f32", 5, 48, 16, 24),
+])
+def test_project_pair(din, d1, d2, M, N1, N2, K):
+    """Both products of csa_project_pair against the oracle's projection."""
+    rng = synth.rng_for(M * 11 + N1 + 3 * N2)
+    X = draw(rng, (M, K), 1.0, din)
+    W1 = draw(rng, (K, N1), 1.0 / math.sqrt(K), din)
+    W2 = draw(rng, (K, N2), 1.0 / math.sqrt(K), din)
+    Xd = to_device(X, din, DEV)
+    Wt1 = to_device(np.ascontiguousarray(W1.T), din, DEV)
+    Wt2 = to_device(np.ascontiguousarray(W2.T), din, DEV)
+    Y1 = torch.empty(M, N1, dtype=TD[d1], device=DEV)
+    Y2 = torch.empty(M, N2, dtype=TD[d2], device=DEV)
+    api.csa_project_pair(Xd, Wt1, Y1, Wt2, Y2)
+    torch.cuda.synchronize()
+    assert_rows_close(to_np64(Y1), O.project(f64(X, din), f64(W1, din)), what="project_pair Y1")
+    assert_rows_close(to_np64(Y2), O.project(f64(X, din), f64(W2, din)), what="project_pair Y2")
+
+
 @pytest.mark.parametrize("din,dout,M,N,K", [
     ("f32", "f32", 77, 40, 24),          # token count not a multiple of 8 (zero-padded contraction)
     ("bf16", "bf16", 1000, 1536, 4096),  # large-tile kernels for both products
