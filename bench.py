@@ -68,6 +68,21 @@ def _traffic(kernel: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def per_step_stats(torch, run_one, n_pool, steps):
+    """Per-step durations (us) of `steps` back-to-back steps, from an event recorded on the launch stream
+    after every step: median and 10th / 90th percentiles."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        run_one(i % n_pool)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(steps)])
+    return {"n": steps, "median_us": round(float(np.median(t)), 3), "p10_us": round(float(np.percentile(t, 10)), 3),
+            "p90_us": round(float(np.percentile(t, 90)), 3), "mean_us": round(float(t.mean()), 3)}
+
+
 def bench_decode(args, torch, api, synth, layer):
     w = synth.WORKLOADS[4]
     dev = "cuda:0"
@@ -132,6 +147,12 @@ def bench_decode(args, torch, api, synth, layer):
           f"({len(reps)} input copies); eager launches {ms_eager * 1000:.2f} us/step", flush=True)
     ms_warm = timed(lambda i: graphs[0].replay(), 1, args.steps, args.warmup)
     print(f"[bench] decode warm cache: {ms_warm * 1000:.2f} us/step", flush=True)
+    n_dist = max(100, args.steps)
+    dist = {"eager": per_step_stats(torch, lambda i: step(i, reps), len(reps), n_dist),
+            "graph": per_step_stats(torch, lambda i: graphs[i].replay(), len(reps), n_dist)}
+    for k_, d_ in dist.items():
+        print(f"[bench] decode {k_} per step over {d_['n']} steps: median {d_['median_us']:.2f} us, "
+              f"p10 {d_['p10_us']:.2f}, p90 {d_['p90_us']:.2f}", flush=True)
 
     # second pass over the same steps with per-kernel HIP events on the launch stream
     api.csa_timing_reset()
@@ -161,6 +182,7 @@ def bench_decode(args, torch, api, synth, layer):
                 "algorithmic_bytes_per_launch": sweep_bytes}
     return {
         "workload": w, "B": B, "ms": ms, "ms_warm": ms_warm, "ms_eager": ms_eager, "kernels": kern, "roofline": roof,
+        "dist": dist,
         "step_bytes": step_bytes, "max_cand": max_cand, "D": D,
     }
 
@@ -446,6 +468,7 @@ def bench_decode_step(args, torch, api, synth, layer):
         st.ring.copy_(ring)
         st.ring_I.copy_(ring_I)
         st.t.fill_(L)
+        st.t_host[:] = L
         bufr = layer.DecodeBuffers(B, wd.k, wd.nh, wd.c, wd.nhI, cap, dt, dev)
         copies.append((W, st, bufr))
     del C, K, P
@@ -603,6 +626,8 @@ def main():
         "warm_cache_queries_per_s": round(dec["B"] / (dec["ms_warm"] * 1e-3), 1),
         "eager_queries_per_s": round(dec["B"] / (dec["ms_eager"] * 1e-3), 1),
         "graph_queries_per_s": round(dec["B"] / (dec["ms"] * 1e-3), 1),
+        "step_time_stats": dec["dist"][launch],
+        "step_time_stats_other_launch": dec["dist"]["eager" if launch == "graph" else "graph"],
         "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
         "prefill": pre,
         "decode_step_with_cache": dstep,

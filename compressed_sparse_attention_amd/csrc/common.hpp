@@ -206,11 +206,23 @@ typedef __attribute__((address_space(3))) char lds_char;
 // Issued from asm so that the compiler does not treat every later LDS read
 // as a possible reader of these writes (it would wait for the whole gather
 // right after issuing it); the kernel waits for them itself, with vmcnt, at
-// the top of the next chunk.  No register is written, so nothing is left for
-// the compiler to misread as already loaded.
+// the top of the next chunk.  No vector register is written, so nothing is
+// left for the compiler to misread as already loaded.  m0 is a register the
+// compiler reserves (it may hold a live value across this statement), so the
+// block saves it in an SGPR and puts it back after the load has been issued
+// (the load reads m0 at issue; s_nop 0 is the one wait state an m0 write needs
+// before an LDS-DMA load reads it).
 __device__ __forceinline__ void gather_row_lds(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory", "m0");
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "v"(src), "s"(lds_base)
+      : "memory");
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);

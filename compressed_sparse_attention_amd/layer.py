@@ -286,7 +286,13 @@ class DecodeState:
       sequence; sequence b's rows start at kv_offset[b] = b * capacity.
     * ring / ring_I: the projected rows [C^a|C^b|Z^a|Z^b] of each sequence's last
       2m tokens (token t in slot t mod 2m), main and indexer widths.
-    * t: position of each sequence's next token (int64, device).
+    * t: position of each sequence's next token (int64, device), mirrored on
+      the host in t_host so that a step can be refused before it launches.
+
+    Sequence b may hold tokens 0 .. capacity * m - 1.  Token t belongs to block
+    floor(t/m), so token capacity * m would eventually write row capacity of its
+    sequence -- the next sequence's first row, or past the end of the buffer --
+    and ``decode_step`` raises before any sequence reaches it.
     """
 
     def __init__(self, B: int, capacity: int, m: int, c: int, cI: int, dtype, device):
@@ -297,6 +303,16 @@ class DecodeState:
         self.ring = torch.zeros(B, 2 * m, 4 * c, dtype=dtype, device=device)
         self.ring_I = torch.zeros(B, 2 * m, 4 * cI, dtype=dtype, device=device)
         self.t = torch.zeros(B, dtype=torch.int64, device=device)
+        self.t_host = np.zeros(B, dtype=np.int64)
+
+    def check_room(self):
+        """Raises if some sequence's next token would not fit in its cache rows."""
+        full = np.nonzero(self.t_host >= self.capacity * self.m)[0]
+        if full.size:
+            b = int(full[0])
+            raise ValueError(f"sequence {b} is at token {int(self.t_host[b])}: its cache holds "
+                             f"{self.capacity} blocks of {self.m} tokens (tokens 0 .. "
+                             f"{self.capacity * self.m - 1})")
 
     def load_prefill(self, b: int, buf: "PrefillBuffers", c: int, cI: int):
         """Hand sequence b over from a prefill of its first L tokens (copies only)."""
@@ -312,6 +328,7 @@ class DecodeState:
             self.ring[b, slot].copy_(buf.Y_H[tok, :4 * c])
             self.ring_I[b, slot].copy_(buf.Y_H[tok, 4 * c:4 * c + 4 * cI])
         self.t[b] = L
+        self.t_host[b] = L
 
 
 def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeState, m: int, k: int, nh: int,
@@ -321,6 +338,9 @@ def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeSt
     appended to the compressed caches when a block completes, then eqs 8, 9, 11 for the new tokens; positions
     advance."""
     B = H_new.shape[0]
+    if B != state.B:
+        raise ValueError("H_new must hold one row per sequence of the state")
+    state.check_room()
     c, cI = W["c"], W["cI"]
     width = 4 * c + 4 * cI + W["dc"]
     Y = torch.empty(B, width, dtype=H_new.dtype, device=H_new.device)
@@ -337,5 +357,8 @@ def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeSt
     # the block a token completes is not among its own candidates (s < floor(t/m))
     buf = decode(q.view(B, nh, c), qI.view(B, nhI, cI), wI, state.Ccomp, state.KIcomp, state.t, state.kv_offset,
                  m, k, state.capacity, scale=scale, buf=buf)
+    # this step's projected queries (eqs 6, 7, 10), kept for inspection until the next step
+    buf.q_in, buf.qI_in, buf.wI_in = q.view(B, nh, c), qI.view(B, nhI, cI), wI
     state.t += 1
+    state.t_host += 1
     return buf

@@ -31,7 +31,8 @@ def oracle_ns():
     from oracle import csa_oracle as O
     return SimpleNamespace(compress=O.compress, compress_weights=O.compress_weights,
                            index_scores_row=O.index_scores_row, topk=O.topk, mqa=O.mqa,
-                           prefill=O.prefill, decode=O.decode, project=O.project)
+                           prefill=O.prefill, prefill_rows=O.prefill_rows, decode=O.decode,
+                           project=O.project)
 
 
 # ---------------------------------------------------------------------------
@@ -374,6 +375,36 @@ def check_decode_matches_prefill_row(ns, rng):
     np.testing.assert_allclose(dec2["o"][0], full["o"][L], rtol=1e-12, atol=1e-14)
 
 
+def check_rows_match_brute(ns, brute, rng):
+    """The sampled-row form of eqs 1-11 (compression over the prefix the rows need, the query side on the
+    chosen rows only) equals the pure-loop evaluation of the whole layer on those rows: compressed entries,
+    scores, selections, outputs and lse.  Rows include tokens t < m (no candidates), the last token, rows
+    given out of order and a repeated row; m in {1, 2, 4}.  The second case has c = c^I and n_h = n_h^I, so
+    a swap of the eq 6 and eq 10 up-projections runs without a shape error and must show in the values."""
+    for (n, d, c, cI, m, dc, nh, nhI, k, rows) in (
+            (21, 5, 3, 2, 1, 4, 2, 3, 4, [20, 0, 7, 13, 7]),
+            (30, 6, 4, 4, 2, 5, 2, 2, 3, [1, 29, 0, 17, 4, 16]),
+            (37, 7, 5, 3, 4, 4, 3, 2, 3, [3, 2, 36, 35, 12, 19, 8]),
+            (9, 4, 3, 3, 4, 3, 2, 2, 2, [0, 3]),  # every row before the first complete block
+            (9, 4, 3, 3, 4, 3, 2, 2, 2, [])):
+        P = tiny_params(rng, n, d, c, cI, m, dc, nh, nhI)
+        got = ns.prefill_rows(P, m, k, nh, nhI, rows)
+        ref = brute.prefill({key: v.tolist() for key, v in P.items()}, m, k, nh, nhI)
+        N_used = max(rows) // m if rows else 0
+        assert got["Ccomp"].shape == (N_used, c) and got["KIcomp"].shape == (N_used, cI)
+        np.testing.assert_allclose(got["Ccomp"], np.array(ref["Ccomp"]).reshape(-1, c)[:N_used],
+                                   rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(got["KIcomp"], np.array(ref["KIcomp"]).reshape(-1, cI)[:N_used],
+                                   rtol=1e-11, atol=1e-12)
+        assert len(got["scores"]) == len(rows) and got["idx"].shape == (len(rows), k)
+        for j, t in enumerate(rows):
+            assert got["scores"][j].shape == (t // m,)
+            np.testing.assert_allclose(got["scores"][j], ref["scores"][t], rtol=1e-10, atol=1e-12)
+            assert [int(x) for x in got["idx"][j] if x >= 0] == ref["idx"][t]
+            np.testing.assert_allclose(got["o"][j], np.array(ref["o"][t]), rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(got["lse"][j], ref["lse"][t], rtol=1e-10)
+
+
 ALL_CHECKS = [
     ("compress_golden", lambda ns, b, r: check_compress_golden(ns)),
     ("compress_constant_rows", lambda ns, b, r: check_compress_constant_rows(ns, r)),
@@ -397,4 +428,5 @@ ALL_CHECKS = [
     ("prefill_brute", lambda ns, b, r: check_prefill_brute(ns, b, r)),
     ("prefill_dense_limit", lambda ns, b, r: check_prefill_dense_limit(ns, r)),
     ("decode_matches_prefill_row", lambda ns, b, r: check_decode_matches_prefill_row(ns, r)),
+    ("rows_match_brute", lambda ns, b, r: check_rows_match_brute(ns, b, r)),
 ]

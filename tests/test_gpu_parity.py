@@ -557,6 +557,53 @@ def test_sparse_mqa_backward(B, nh, k, nblk, qps, layout):
     assert_rows_close(to_np64(dC), ref_dC, what="dCcomp")
 
 
+def test_sparse_mqa_backward_run_twice():
+    """The key gradient's fp32 sums are not in a fixed order (shares of one compressed row that span several
+    sorted segments meet in atomic adds), so two runs on the same inputs may differ in rounding only: per
+    row by at most (number of shares + 1) * 2^-23 times the sum of the shares' magnitudes (from the
+    oracle's per-query gradients).  dq is summed inside one workgroup per query and must be bit-identical.
+    1200 queries share two sequences' 600 rows (about 600 shares per row, several 512-pair segments)."""
+    B, nh, k, nblk, qps, c = 1200, 16, 512, 600, 600, 512
+    rng = synth.rng_for(4242)
+    nseq = B // qps
+    C = draw(rng, (nseq * nblk, c), 1.0, "bf16")
+    q = draw(rng, (B, nh, c), 4.0 / math.sqrt(c), "bf16")
+    dO = draw(rng, (B, nh, c), 1.0, "bf16")
+    idx = synth.random_selection(rng, rng.integers(k // 2, nblk + 1, size=B), k)
+    q_seq = (np.arange(B) // qps).astype(np.int32)
+    off = np.arange(nseq, dtype=np.int64) * nblk
+    qd, Cd, dOd = to_device(q, "bf16", DEV), to_device(C, "bf16", DEV), to_device(dO, "bf16", DEV)
+    idxd = torch.from_numpy(idx).to(DEV)
+    qsd, offd = torch.from_numpy(q_seq).to(DEV), torch.from_numpy(off).to(DEV)
+    o = torch.empty(B, nh, c, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, nh, dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(c)
+    api.csa_sparse_mqa(qd, Cd, idxd, scale, o, lse, q_seq=qsd, kv_offset=offd)
+    runs = []
+    for _ in range(2):
+        dq = torch.empty(B, nh, c, dtype=torch.bfloat16, device=DEV)
+        dC = torch.empty(nseq * nblk, c, dtype=torch.float32, device=DEV)
+        api.csa_sparse_mqa_backward(qd, Cd, idxd, scale, o, lse, dOd, dq, dC, q_seq=qsd, kv_offset=offd)
+        runs.append((dq.cpu(), dC.cpu().numpy().astype(np.float64)))
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0].view(torch.int16), runs[1][0].view(torch.int16)), "dq differs between runs"
+    q64, C64, dO64 = f64(q, "bf16"), f64(C, "bf16"), f64(dO, "bf16")
+    abs_sum = np.zeros((nseq * nblk, c))
+    count = np.zeros(nseq * nblk)
+    for r in range(B):
+        sel = idx[r][idx[r] >= 0]
+        rows = off[q_seq[r]] + sel
+        _, dc = O.mqa_backward(q64[r], C64[rows], scale, dO64[r])
+        np.add.at(abs_sum, rows, np.abs(dc))
+        np.add.at(count, rows, 1)
+    diff = np.abs(runs[0][1] - runs[1][1])
+    bound = (count[:, None] + 1) * 2.0 ** -23 * abs_sum
+    worst = np.unravel_index(np.argmax(diff - bound), diff.shape)
+    print(f"dCcomp run-to-run: {int((diff > 0).any(axis=1).sum())} of {diff.shape[0]} rows differ, "
+          f"max |diff| {diff.max():.3e}; up to {int(count.max())} shares per row")
+    assert np.all(diff <= bound), f"row {worst[0]}: runs differ by {diff[worst]:.3e} > {bound[worst]:.3e}"
+
+
 # ---------------------------------------------------------------------------
 # csa_decode: eqs 8, 9 and 11 in one call with a persistent workspace
 # ---------------------------------------------------------------------------

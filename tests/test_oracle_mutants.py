@@ -133,6 +133,36 @@ def _mqa_lse_no_max(q, C, scale):
     return o, np.log(np.exp(lg - lg.max(1, keepdims=True)).sum(1))
 
 
+def _rows_variant(prefix_blocks=lambda rows, m: int(max(rows)) // m if len(rows) else 0,
+                  swap_uq=False, query_row_shift=0, positions_from_order=False):
+    """prefill_rows rebuilt from the oracle's parts with one planted slip (the defaults give the correct
+    function): the prefix of blocks compressed, eq 6 / eq 10 up-projections swapped, the query side read
+    from the wrong hidden-state rows, or candidate counts taken from the rows' order instead of their
+    token positions."""
+    def prefill_rows(P, m, k, n_h, n_hI, rows, scale=None):
+        H = np.asarray(P["H"], float)
+        rows = np.asarray(rows, dtype=np.int64)
+        Hc = H[:prefix_blocks(rows, m) * m]
+        proj = lambda X, names: [O.project(X, P[nm]) for nm in names]  # noqa: E731
+        Ccomp = O.compress(*proj(Hc, ("W_aKV", "W_bKV", "W_aZ", "W_bZ")), P["B_a"], P["B_b"], m)
+        KIcomp = O.compress(*proj(Hc, ("W_aKV_I", "W_bKV_I", "W_aZ_I", "W_bZ_I")), P["B_aI"], P["B_bI"], m)
+        Hr = H[np.clip(rows + query_row_shift, 0, H.shape[0] - 1)]
+        cQ = O.project(Hr, P["W_DQ"])
+        cI, c = np.shape(P["B_aI"])[1], np.shape(P["B_a"])[1]
+        wUQI, wUQ = (P["W_UQ"], P["W_UQI"]) if swap_uq else (P["W_UQI"], P["W_UQ"])
+        qI = O.project(cQ, wUQI).reshape(len(rows), n_hI, cI)
+        wI = O.project(Hr, P["W_w"])
+        q = O.project(cQ, wUQ).reshape(len(rows), n_h, c)
+        ncand = O.n_candidates(np.arange(len(rows)) if positions_from_order else rows, m)
+        scores = O.index_scores(qI, wI, KIcomp, ncand)
+        idx = O.topk_rows(scores, k)
+        o, lse = O._mqa_rows(q, Ccomp, idx, np.zeros(len(rows), np.int64),
+                             O.default_scale(c) if scale is None else scale)
+        return {"Ccomp": Ccomp, "KIcomp": KIcomp, "qI": qI, "wI": wI, "q": q, "scores": scores,
+                "idx": idx, "o": o, "lse": lse}
+    return prefill_rows
+
+
 MUTANTS = {
     "compress_wrong_axis": dict(compress=_compress_with(_weights_wrong_axis),
                                 compress_weights=_weights_wrong_axis),
@@ -155,11 +185,25 @@ MUTANTS = {
     "mqa_no_scale": dict(mqa=_mqa_no_scale),
     "mqa_head_softmax": dict(mqa=_mqa_head_softmax),
     "mqa_lse_no_max": dict(mqa=_mqa_lse_no_max),
+    "rows_prefix_one_block_short": dict(prefill_rows=_rows_variant(
+        prefix_blocks=lambda rows, m: max(int(max(rows)) // m - 1, 0) if len(rows) else 0)),
+    "rows_prefix_whole_rows": dict(prefill_rows=_rows_variant(
+        prefix_blocks=lambda rows, m: (int(max(rows)) + 1) // m if len(rows) else 0)),
+    "rows_swapped_up_projections": dict(prefill_rows=_rows_variant(swap_uq=True)),
+    "rows_query_from_previous_token": dict(prefill_rows=_rows_variant(query_row_shift=-1)),
+    "rows_positions_from_order": dict(prefill_rows=_rows_variant(positions_from_order=True)),
 }
 
 # checks that exercise only a single function; the whole-layer checks call
 # the real module's composites and so cannot see a mutant of a part
 _PART_CHECKS = [(n, c) for n, c in ALL_CHECKS if not n.startswith(("prefill", "decode"))]
+
+
+def test_rows_variant_without_slip_passes():
+    """The rebuilt prefill_rows with no planted slip passes the pin, so the mutants above fail it for
+    their slip alone."""
+    from pins import check_rows_match_brute
+    check_rows_match_brute(_ns(prefill_rows=_rows_variant()), brute, np.random.Generator(np.random.PCG64(5)))
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
