@@ -621,13 +621,37 @@ csa_status csa_decode_workspace(int64_t n_queries, int64_t max_cand, int32_t n_h
   return CSA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of csa_decode (and csa_decode_noalloc) that its two stages would
+// otherwise make one after the other: the attention's are made here too, so a
+// bad argument is refused before the selection launches anything.
+csa_status decode_checks(const char* fn, int64_t n_queries, int32_t n_hI, int32_t n_h, int32_t c, int32_t k,
+                         float scale, const void* q, const void* Ccomp, const int64_t* q_pos, int64_t max_cand,
+                         const void* o) {
+  CSA_REQUIRE(q_pos != nullptr || n_queries == 0, "%s: q_pos is required", fn);
+  CSA_REQUIRE(n_h >= 1 && n_hI >= 1 && k >= 1 && n_queries >= 0 && max_cand >= 0, "%s: bad size", fn);
+  CSA_REQUIRE(n_h <= 256, "%s: n_h must be in [1, 256] (got %d)", fn, n_h);
+  CSA_REQUIRE(csa::mqa_supported_c(c), "%s: c must be 64, 128, 256, 512 or 1024 (got %d)", fn, c);
+  CSA_REQUIRE(scale == scale && scale > 0.f && scale < 1e30f, "%s: scale must be positive and finite", fn);
+  CSA_REQUIRE(n_queries == 0 || (q && Ccomp && o), "%s: null pointer", fn);
+  CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(o), "%s: pointers must be 16-byte aligned", fn);
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c, int32_t m,
                       int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp, const void* q,
                       const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos, const int64_t* kv_offset,
                       int64_t max_cand, int32_t* idx_out, float* score_out, void* o, float* lse, void* workspace,
                       size_t ws_bytes, void* stream) {
-  CSA_REQUIRE(q_pos != nullptr || n_queries == 0, "csa_decode: q_pos is required");
-  CSA_REQUIRE(n_h >= 1 && n_hI >= 1 && k >= 1 && n_queries >= 0 && max_cand >= 0, "csa_decode: bad size");
+  csa_status st0 = decode_checks("csa_decode", n_queries, n_hI, n_h, c, k, scale, q, Ccomp, q_pos, max_cand, o);
+  if (st0 != CSA_OK) return st0;
   size_t need = 0, a = 0;
   csa_status st = csa_decode_workspace(n_queries, max_cand, n_hI, n_h, c, k, &need);
   if (st != CSA_OK) return st;
