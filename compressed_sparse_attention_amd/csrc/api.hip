@@ -641,6 +641,34 @@ csa_status decode_checks(const char* fn, int64_t n_queries, int32_t n_hI, int32_
   return CSA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of csa_decode_noalloc: a file-scope device array, one copy per GPU
+// (each holds it until the process ends).  Host code never passes the
+// array's name: its device address is looked up once per device, with that
+// device current, and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+csa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "csa_decode_noalloc: address of the static scratch");
+    if (p == nullptr) return fail(CSA_ERR_HIP, "csa_decode_noalloc: the static scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -664,6 +692,40 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
   if (st != CSA_OK) return st;
   return csa_sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
                         workspace ? (char*)workspace + a : nullptr, ws_bytes - a, stream);
+}
+
+csa_status csa_decode_noalloc(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c,
+                              int32_t m, int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp,
+                              const void* q, const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos,
+                              const int64_t* kv_offset, int64_t max_cand, int32_t* idx_out, float* score_out,
+                              void* o, float* lse, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_decode_noalloc: unknown dtype");
+  csa_status st =
+      decode_checks("csa_decode_noalloc", n_queries, n_hI, n_h, c, k, scale, q, Ccomp, q_pos, max_cand, o);
+  if (st != CSA_OK) return st;
+  if (n_queries == 0) return CSA_OK;
+  // this dtype's own needs (csa_decode_workspace covers both dtypes)
+  size_t a = 0;
+  st = csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &a);
+  if (st != CSA_OK) return st;
+  a = align256(a);
+  const size_t b = csa::mqa_workspace_bytes(n_queries, n_h, c, k, dt == CSA_BF16);
+  if (a + b > kScratchBytes)
+    return fail(CSA_ERR_WORKSPACE, "csa_decode_noalloc: these sizes need %zu bytes of scratch; the static scratch "
+                "holds %zu (use csa_decode with a workspace)", a + b, kScratchBytes);
+  st = check_device();
+  if (st != CSA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != CSA_OK) return st;
+  // the scratch keeps whatever the last call left, laid out for that call's
+  // sizes: the selection clears its histogram and counters first (a kernel,
+  // not a memset)
+  st = index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand, idx_out,
+                  score_out, ws, a, stream, true);
+  if (st != CSA_OK) return st;
+  return csa_sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
+                        (char*)ws + a, b, stream);
 }
 
 csa_status csa_compress_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca, const void* Cb,

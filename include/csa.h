@@ -417,6 +417,30 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
                       size_t ws_bytes, void* stream);
 
 /*
+ * csa_decode_noalloc -- csa_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  It calls no hipMalloc,
+ * hipFree or allocating library routine.  Its scratch is one static device
+ * array of 32 MiB per GPU, which the library holds until the process ends;
+ * sizes whose scratch would not fit (the csa_index_topk workspace plus the
+ * csa_sparse_mqa workspace for dt) are refused with CSA_ERR_WORKSPACE before
+ * anything is launched.  The 8 x 131072-token, 32 x 8192-token and ragged
+ * 64-sequence decode batches of c = 512 fit.
+ *
+ * Every call on a GPU shares that GPU's array, which keeps what the last call
+ * left: each call first clears the parts that must start at zero (with a
+ * kernel, so it may be captured in a graph), then proceeds as csa_decode.
+ * Calls that overlap on one GPU (other streams, other host threads) race on
+ * the array; serialise them.  Arguments, limits and results otherwise as
+ * csa_decode (results are identical to it).
+ */
+csa_status csa_decode_noalloc(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c,
+                              int32_t m, int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp,
+                              const void* q, const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos,
+                              const int64_t* kv_offset, int64_t max_cand, int32_t* idx_out, float* score_out,
+                              void* o, float* lse, void* stream);
+
+/*
  * Kernel timing (instrumentation, off by default).  While enabled, every
  * kernel the library launches is bracketed by a pair of HIP events recorded
  * on the launch stream.  csa_timing_read synchronises on the recorded events
