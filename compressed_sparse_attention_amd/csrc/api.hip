@@ -106,23 +106,26 @@ struct IndexWs {
   size_t scores = 0, hist = 0, arrive = 0, counts = 0, gt = 0, eq = 0, total = 0;
 };
 IndexWs index_ws(long n_queries, long max_cand, int k) {
+  using csa::ws_add;
+  using csa::ws_align;
+  using csa::ws_bytes;
   IndexWs w;
-  size_t at = align256((size_t)n_queries * scores_ld(max_cand) * sizeof(float));
+  size_t at = ws_align(ws_bytes(n_queries, scores_ld(max_cand), sizeof(float)));
   if (use_hist(max_cand)) {
     w.hist = at;
-    at += (size_t)n_queries * (1u << csa::kTopkL1Bits) * sizeof(uint32_t);
+    at = ws_add(at, ws_bytes(n_queries, 1u << csa::kTopkL1Bits, sizeof(uint32_t)));
     w.arrive = at;  // contiguous with hist: one clear covers both
-    at = align256(at + (use_lists(n_queries, max_cand) ? (size_t)n_queries * sizeof(uint32_t) : 0));
+    at = ws_align(ws_add(at, use_lists(n_queries, max_cand) ? ws_bytes(n_queries, sizeof(uint32_t)) : 0));
   }
   if (use_lists(n_queries, max_cand)) {
     const size_t P = (size_t)topk_chunks(max_cand);
     const size_t gtc = (size_t)(k < csa::kMChunk ? k : csa::kMChunk);
     w.counts = at;
-    at = align256(at + (size_t)n_queries * P * 2 * sizeof(uint32_t));
+    at = ws_align(ws_add(at, ws_bytes(n_queries, P, 2 * sizeof(uint32_t))));
     w.gt = at;
-    at = align256(at + (size_t)n_queries * P * gtc * sizeof(uint64_t));
+    at = ws_align(ws_add(at, ws_bytes(n_queries, P, gtc, sizeof(uint64_t))));
     w.eq = at;
-    at = align256(at + (size_t)n_queries * P * csa::kMChunk * sizeof(uint64_t));
+    at = ws_align(ws_add(at, ws_bytes(n_queries, P, csa::kMChunk, sizeof(uint64_t))));
   }
   w.total = at;
   return w;
@@ -249,13 +252,16 @@ struct ProjBwdLayout {
   size_t w, dyt, xt, total;
 };
 ProjBwdLayout proj_bwd_layout(csa_dtype dt, int64_t M, int64_t N, int64_t K, bool want_dx, bool want_dw) {
+  using csa::ws_add;
+  using csa::ws_align;
+  using csa::ws_bytes;
   const size_t e = dt == CSA_F32 ? 4 : 2;
-  const int64_t M8 = (M + 7) / 8 * 8;
+  const uint64_t M8 = ((uint64_t)M + 7) / 8 * 8;
   ProjBwdLayout L;
   L.w = 0;
-  L.dyt = want_dx ? align256((size_t)K * N * e) : 0;
-  L.xt = L.dyt + (want_dw ? align256((size_t)N * M8 * e) : 0);
-  L.total = L.xt + (want_dw ? align256((size_t)K * M8 * e) : 0);
+  L.dyt = want_dx ? ws_align(ws_bytes(K, N, e)) : 0;
+  L.xt = ws_add(L.dyt, want_dw ? ws_align(ws_bytes(N, M8, e)) : 0);
+  L.total = ws_add(L.xt, want_dw ? ws_align(ws_bytes(K, M8, e)) : 0);
   return L;
 }
 }  // namespace
@@ -266,6 +272,7 @@ csa_status csa_project_backward_workspace(csa_dtype in_dt, int64_t M, int64_t N,
   CSA_REQUIRE(dtype_ok(in_dt), "csa_project_backward_workspace: unknown dtype");
   CSA_REQUIRE(M >= 0 && N > 0 && K > 0, "csa_project_backward_workspace: bad sizes");
   *bytes = proj_bwd_layout(in_dt, M, N, K, want_dx != 0, want_dw != 0).total;
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_project_backward_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -290,6 +297,7 @@ csa_status csa_project_backward(csa_dtype in_dt, csa_dtype out_dt, int64_t M, in
   CSA_REQUIRE(ld_dx % vec_elems(out_dt) == 0 && ld_dw % vec_elems(out_dt) == 0,
               "csa_project_backward: output rows must stay 16-byte aligned");
   const ProjBwdLayout L = proj_bwd_layout(in_dt, M, N, K, dX != nullptr, dWt != nullptr);
+  CSA_REQUIRE(L.total < csa::kWorkspaceTooBig, "csa_project_backward: sizes too large");
   if (L.total > 0 && (workspace == nullptr || ws_bytes < L.total))
     return fail(CSA_ERR_WORKSPACE, "csa_project_backward: workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
   csa_status st = check_device();
@@ -341,6 +349,7 @@ csa_status csa_compress_backward_workspace(int64_t n, int32_t m, int32_t c, size
   CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_workspace: m must be in [1, 16] (got %d)", m);
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_workspace: c must be a positive multiple of 4");
   *bytes = csa::compress_backward_workspace_bytes(n, m, c, 0, 0, false);
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_compress_backward_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -355,6 +364,7 @@ csa_status csa_compress_backward(csa_dtype dt, int64_t n, int32_t m, int32_t c, 
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward: c must be a positive multiple of 4 (got %d)", c);
   CSA_REQUIRE(dBa && dBb && workspace, "csa_compress_backward: null pointer");
   const size_t need = csa::compress_backward_workspace_bytes(n, m, c, 0, 0, false);
+  CSA_REQUIRE(need < csa::kWorkspaceTooBig, "csa_compress_backward: sizes too large");
   CSA_REQUIRE(ws_bytes >= need, "csa_compress_backward: workspace of %zu bytes is smaller than %zu", ws_bytes, need);
   CSA_REQUIRE(aligned16(workspace), "csa_compress_backward: workspace must be 16-byte aligned");
   const int v = vec_elems(dt);
@@ -384,6 +394,7 @@ csa_status csa_compress_backward_varlen_workspace(int64_t n_seqs, int64_t n_bloc
   CSA_REQUIRE(m >= 1 && m <= 16, "csa_compress_backward_varlen_workspace: m must be in [1, 16] (got %d)", m);
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_varlen_workspace: c must be a positive multiple of 4");
   *bytes = csa::compress_backward_workspace_bytes(0, m, c, n_seqs, n_blocks, true);
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_compress_backward_varlen_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -399,6 +410,7 @@ csa_status csa_compress_backward_varlen(csa_dtype dt, int64_t n_seqs, int32_t m,
   CSA_REQUIRE(c > 0 && c % 4 == 0, "csa_compress_backward_varlen: c must be a positive multiple of 4 (got %d)", c);
   CSA_REQUIRE(dBa && dBb && workspace, "csa_compress_backward_varlen: null pointer");
   const size_t need = csa::compress_backward_workspace_bytes(0, m, c, n_seqs, n_blocks, true);
+  CSA_REQUIRE(need < csa::kWorkspaceTooBig, "csa_compress_backward_varlen: sizes too large");
   CSA_REQUIRE(ws_bytes >= need, "csa_compress_backward_varlen: workspace of %zu bytes is smaller than %zu", ws_bytes,
               need);
   CSA_REQUIRE(aligned16(workspace), "csa_compress_backward_varlen: workspace must be 16-byte aligned");
@@ -454,6 +466,7 @@ csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t
   CSA_REQUIRE(n_queries >= 0 && max_cand >= 0, "csa_index_topk_workspace: negative size");
   CSA_REQUIRE(n_hI >= 1 && k >= 1, "csa_index_topk_workspace: n_hI and k must be >= 1");
   *bytes = index_ws(n_queries, max_cand, k).total;
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_index_topk_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -479,7 +492,8 @@ csa_status index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
   CSA_REQUIRE(aligned16(qI) && aligned16(wI) && aligned16(KIcomp) && aligned16(idx_out),
               "csa_index_topk: pointers must be 16-byte aligned");
   size_t need = 0;
-  csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &need);
+  csa_status st0 = csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &need);
+  if (st0 != CSA_OK) return st0;
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "csa_index_topk: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   CSA_REQUIRE(workspace == nullptr || aligned16(workspace), "csa_index_topk: workspace must be 16-byte aligned");
@@ -539,6 +553,7 @@ csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, i
   const size_t a = csa::mqa_workspace_bytes(n_queries, n_h, c, k, true);
   const size_t b = csa::mqa_workspace_bytes(n_queries, n_h, c, k, false);
   *bytes = a > b ? a : b;
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_sparse_mqa_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -557,6 +572,7 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   CSA_REQUIRE(aligned16(q) && aligned16(Ccomp) && aligned16(idx) && aligned16(o),
               "csa_sparse_mqa: pointers must be 16-byte aligned");
   const size_t need = csa::mqa_workspace_bytes(n_queries, n_h, c, k, dt == CSA_BF16);
+  CSA_REQUIRE(need < csa::kWorkspaceTooBig, "csa_sparse_mqa: sizes too large");
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(CSA_ERR_WORKSPACE, "csa_sparse_mqa: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   CSA_REQUIRE(aligned16(workspace), "csa_sparse_mqa: workspace must be 16-byte aligned");
@@ -576,6 +592,7 @@ csa_status csa_sparse_mqa_backward_workspace(int64_t n_queries, int32_t n_h, int
   CSA_REQUIRE(k >= 1 && k <= (1 << 20), "csa_sparse_mqa_backward_workspace: k must be in [1, 2^20]");
   CSA_REQUIRE(n_rows >= 0 && n_rows < 0x7FFFFFFF, "csa_sparse_mqa_backward_workspace: bad n_rows");
   *bytes = csa::mqa_backward_workspace_bytes(n_queries, n_h, k, n_rows);
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_sparse_mqa_backward_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -617,7 +634,8 @@ csa_status csa_decode_workspace(int64_t n_queries, int64_t max_cand, int32_t n_h
   if (st != CSA_OK) return st;
   st = csa_sparse_mqa_workspace(n_queries, n_h, c, k, &b);
   if (st != CSA_OK) return st;
-  *bytes = align256(a) + b;
+  *bytes = csa::ws_add(csa::ws_align(a), b);
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_decode_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -710,7 +728,7 @@ csa_status csa_decode_noalloc(csa_dtype dt, int64_t n_queries, int32_t n_hI, int
   if (st != CSA_OK) return st;
   a = align256(a);
   const size_t b = csa::mqa_workspace_bytes(n_queries, n_h, c, k, dt == CSA_BF16);
-  if (a + b > kScratchBytes)
+  if (csa::ws_add(a, b) > kScratchBytes)
     return fail(CSA_ERR_WORKSPACE, "csa_decode_noalloc: these sizes need %zu bytes of scratch; the static scratch "
                 "holds %zu (use csa_decode with a workspace)", a + b, kScratchBytes);
   st = check_device();
@@ -760,9 +778,13 @@ csa_status csa_index_topk_varlen_workspace(int64_t n_seqs, int64_t n_tokens, int
                                            size_t* bytes) {
   CSA_REQUIRE(bytes, "csa_index_topk_varlen_workspace: null bytes");
   CSA_REQUIRE(n_seqs >= 0 && n_tokens >= 0 && max_cand >= 0 && k >= 1, "csa_index_topk_varlen_workspace: bad size");
-  *bytes = align256((size_t)n_tokens * scores_ld(max_cand) * sizeof(float)) +
-           align256((size_t)n_tokens * sizeof(int64_t)) + align256((size_t)n_tokens * sizeof(int32_t)) +
-           align256((size_t)(n_seqs + 1) * sizeof(int32_t));
+  using csa::ws_add;
+  using csa::ws_align;
+  using csa::ws_bytes;
+  *bytes = ws_add(ws_add(ws_align(ws_bytes(n_tokens, scores_ld(max_cand), sizeof(float))),
+                         ws_align(ws_bytes(n_tokens, sizeof(int64_t)))),
+                  ws_add(ws_align(ws_bytes(n_tokens, sizeof(int32_t))), ws_align(ws_bytes(n_seqs + 1, sizeof(int32_t)))));
+  CSA_REQUIRE(*bytes < csa::kWorkspaceTooBig, "csa_index_topk_varlen_workspace: sizes too large");
   return CSA_OK;
 }
 
@@ -786,7 +808,8 @@ csa_status csa_index_topk_varlen(csa_dtype dt, int64_t n_seqs, int64_t n_tokens,
   CSA_REQUIRE(aligned16(qI) && aligned16(wI) && aligned16(KIcomp) && aligned16(idx_out),
               "csa_index_topk_varlen: pointers must be 16-byte aligned");
   size_t need = 0;
-  csa_index_topk_varlen_workspace(n_seqs, n_tokens, max_cand, k, &need);
+  csa_status st0 = csa_index_topk_varlen_workspace(n_seqs, n_tokens, max_cand, k, &need);
+  if (st0 != CSA_OK) return st0;
   if (workspace == nullptr || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "csa_index_topk_varlen: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   CSA_REQUIRE(aligned16(workspace), "csa_index_topk_varlen: workspace must be 16-byte aligned");

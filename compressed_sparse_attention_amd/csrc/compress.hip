@@ -468,7 +468,7 @@ hipError_t launch_compress_varlen(csa_dtype dt, long nseq, int m, int c, const v
 size_t compress_backward_workspace_bytes(long n, int m, int c, long nseq, long nblk, bool varlen) {
   long ny, bpw;
   compress_bwd_grid(compress_bwd_units(n, m, nseq, nblk, varlen), &ny, &bpw);
-  return (size_t)ny * 2 * m * c * sizeof(float);
+  return ws_bytes(ny, 2 * m, c, sizeof(float));
 }
 
 namespace {

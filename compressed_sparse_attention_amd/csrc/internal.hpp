@@ -9,6 +9,20 @@
 
 namespace csa {
 
+// Workspace sizes use saturating arithmetic with 128-bit intermediates: a
+// size that reaches kWorkspaceTooBig (far beyond any device) stays there, and
+// every size query and every call refuses it, so no query returns a size that
+// wrapped around.  Arguments are non-negative (checked before).
+constexpr size_t kWorkspaceTooBig = (size_t)1 << 56;
+inline size_t ws_sat(unsigned __int128 v) { return v >= kWorkspaceTooBig ? kWorkspaceTooBig : (size_t)v; }
+inline size_t ws_bytes(uint64_t a, uint64_t b, uint64_t c = 1, uint64_t d = 1) {
+  size_t v = ws_sat((unsigned __int128)a * b);
+  v = ws_sat((unsigned __int128)v * c);
+  return ws_sat((unsigned __int128)v * d);
+}
+inline size_t ws_add(size_t a, size_t b) { return ws_sat((unsigned __int128)a + b); }
+inline size_t ws_align(size_t b) { return ws_sat(((unsigned __int128)b + 255) & ~(unsigned __int128)255); }
+
 // Kernel timing (csa_timing_*): when enabled, launches carry a start/stop
 // event pair in their own dispatch packet, so the elapsed time is the
 // kernel's execution time, without the queueing before it.

@@ -1249,8 +1249,8 @@ size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
   if (n_queries <= 0) return 0;
   const Plan p = plan(n_queries, nh, c, k, bf16);
   if (p.nsplit == 1) return 0;
-  return align256((size_t)n_queries * p.nsplit * nh * c * sizeof(float)) +
-         align256((size_t)n_queries * p.nsplit * nh * 2 * sizeof(float));
+  return ws_add(ws_align(ws_bytes(n_queries, p.nsplit, (uint64_t)nh * c, sizeof(float))),
+                ws_align(ws_bytes(n_queries, p.nsplit, (uint64_t)nh * 2, sizeof(float))));
 }
 
 hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float scale,

@@ -516,20 +516,20 @@ struct BwdLayout {
   size_t part, cnt, start, cursor, pair, pkey, total;
 };
 
-size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 BwdLayout bwd_layout(long nq, int nh, int k, long rows) {
   BwdLayout L;
   const long nhg = (nh + kBwdHeads - 1) / kBwdHeads;
   L.qc = std::max(1L, std::min(nq, kMaxPairsPerPass / ((long)k * nhg)));
-  const size_t pairs = (size_t)L.qc * k;
+  const size_t pairs = ws_bytes(L.qc, k);
+  const size_t row_words = ws_align(ws_bytes(rows + 1, sizeof(int32_t)));
   L.part = 0;
-  L.cnt = a256(pairs * nhg * kBwdCD * sizeof(bf16_t));
-  L.start = L.cnt + a256((rows + 1) * sizeof(int32_t));
-  L.cursor = L.start + a256((rows + 1) * sizeof(int32_t));
-  L.pair = L.cursor + a256((rows + 1) * sizeof(int32_t));
-  L.pkey = L.pair + a256(pairs * sizeof(int32_t));
-  L.total = L.pkey + a256(pairs * sizeof(int32_t));
+  L.cnt = ws_align(ws_bytes(pairs, nhg, kBwdCD, sizeof(bf16_t)));
+  L.start = ws_add(L.cnt, row_words);
+  L.cursor = ws_add(L.start, row_words);
+  L.pair = ws_add(L.cursor, row_words);
+  L.pkey = ws_add(L.pair, ws_align(ws_bytes(pairs, sizeof(int32_t))));
+  L.total = ws_add(L.pkey, ws_align(ws_bytes(pairs, sizeof(int32_t))));
   return L;
 }
 

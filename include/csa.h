@@ -60,7 +60,11 @@ typedef enum {
 
 typedef enum {
   CSA_F32 = 0, /* IEEE binary32 */
-  CSA_BF16 = 1 /* bfloat16 (upper half of binary32), round-to-nearest-even on store */
+  CSA_BF16 = 1, /* bfloat16 (upper half of binary32), round-to-nearest-even on store */
+  /* not dtypes: they make every int32 a value of this type, so an unknown
+     dtype passed by a caller is refused (CSA_ERR_INVALID_ARG), not undefined */
+  CSA_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  CSA_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } csa_dtype;
 
 /* Version of this interface (CSA_ABI_VERSION of the built library). */
