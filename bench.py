@@ -187,14 +187,17 @@ def bench_decode(args, torch, api, synth, layer):
     }
 
 
-def bench_prefill(args, torch, api, synth, layer):
+def bench_prefill(args, torch, api, synth, layer, selection="dense", HW=None):
+    """The 32768-token prefill; selection "dense" (score matrix, then selector) or "stream" (the indexer
+    keeps only selectable scores).  HW: (H, W) already on the device, or None."""
     w = synth.WORKLOADS[3]
     dev = "cuda:0"
-    P = synth.make_prefill(w)
-    W = layer.pack_prefill_params(P, w.dtype, dev)
-    H = layer.to_device(P["H"], w.dtype, dev)
-    del P
-    buf = layer.PrefillBuffers(w.n, w.m, w.k, w.nh, w.nhI, w.c, w.cI, w.dc, H.dtype, dev)
+    if HW is None:
+        P = synth.make_prefill(w)
+        HW = (layer.to_device(P["H"], w.dtype, dev), layer.pack_prefill_params(P, w.dtype, dev))
+        del P
+    H, W = HW
+    buf = layer.PrefillBuffers(w.n, w.m, w.k, w.nh, w.nhI, w.c, w.cI, w.dc, H.dtype, dev, selection=selection)
 
     def run(steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,7 +216,7 @@ def bench_prefill(args, torch, api, synth, layer):
     api.csa_timing_enable(False)
     kern = _kernel_stats(api, ["gemm", "compress", "indexer_prefill", "topk", "mqa", "mqa_combine"])
     api.csa_timing_reset()
-    print(f"[bench] prefill: {ms:.2f} ms per {w.n}-token sequence", flush=True)
+    print(f"[bench] prefill ({selection} selection): {ms:.2f} ms per {w.n}-token sequence", flush=True)
     for n, s in kern.items():
         print(f"[bench]   {n:16s} {s['total_ms'] / args.prefill_steps:9.3f} ms/step "
               f"({s['launches'] // args.prefill_steps} launches)", flush=True)
@@ -226,9 +229,62 @@ def bench_prefill(args, torch, api, synth, layer):
         roof = {"kernel": "indexer_prefill", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": idx_flops}
-    return {"workload": w.name, "tokens": w.n, "ms": ms, "tokens_per_s": w.n / (ms * 1e-3),
-            "kernels_ms_per_step": {n: round(s["total_ms"] / args.prefill_steps, 4) for n, s in kern.items()},
-            "indexer_roofline": roof, "stage_rooflines": _prefill_stage_rooflines(w, kern, args.prefill_steps)}
+    out = {"workload": w.name, "selection": selection, "tokens": w.n, "ms": ms, "tokens_per_s": w.n / (ms * 1e-3),
+           "kernels_ms_per_step": {n: round(s["total_ms"] / args.prefill_steps, 4) for n, s in kern.items()},
+           "indexer_roofline": roof, "stage_rooflines": _prefill_stage_rooflines(w, kern, args.prefill_steps)}
+    del buf
+    return out, HW
+
+
+def bench_selection_long(args, torch, api, synth, layer):
+    """Eqs 8-9 alone on one longer sequence, materialised against streaming selection: 65536 query tokens,
+    16384 compressed blocks (m = 4), the 32768-token layer's indexer widths (64 heads of 128) and k = 512.
+    Inputs are drawn on the GPU from a seeded generator (queries std 128^-1/2, keys and head weights N(0, 1));
+    the two paths' selections are compared as sets on every row (they must agree except within the top-k
+    comparison band, which on these continuous scores means equality)."""
+    dev = "cuda:0"
+    n, m, nhI, cI, k = 65536, 4, 64, 128, 512
+    N = n // m
+    g = torch.Generator(device=dev)
+    g.manual_seed(51)
+    qI = (torch.randn(n, nhI, cI, generator=g, device=dev) / math.sqrt(cI)).to(torch.bfloat16)
+    K = torch.randn(N, cI, generator=g, device=dev).to(torch.bfloat16)
+    wI = torch.randn(n, nhI, generator=g, device=dev)
+    out = {}
+    idx = {}
+    for sel in ("dense", "stream"):
+        ix = torch.empty(n, k, dtype=torch.int32, device=dev)
+        if sel == "dense":
+            ws = torch.empty(api.csa_index_topk_workspace(n, N, nhI, k), dtype=torch.uint8, device=dev)
+            fn = lambda: api.csa_index_topk(qI, wI, K, m, k, N, ix, workspace=ws)  # noqa: E731
+        else:
+            ws = torch.empty(api.csa_index_topk_stream_workspace(n, N), dtype=torch.uint8, device=dev)
+            fn = lambda: api.csa_index_topk_stream(qI, wI, K, m, k, N, ix, workspace=ws)  # noqa: E731
+        fn()
+        torch.cuda.synchronize()
+        api.csa_timing_reset()
+        api.csa_timing_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.prefill_steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        api.csa_timing_enable(False)
+        kern = _kernel_stats(api, ["indexer_prefill", "topk"])
+        api.csa_timing_reset()
+        ms = e0.elapsed_time(e1) / args.prefill_steps
+        out[sel] = {"ms": round(ms, 4), "kernels_ms": {kk: round(v["total_ms"] / args.prefill_steps, 4)
+                                                       for kk, v in kern.items()}}
+        print(f"[bench] selection of {n} tokens x {N} blocks, {sel}: {ms:.3f} ms "
+              f"{out[sel]['kernels_ms']}", flush=True)
+        idx[sel] = ix
+        del ws
+    a = torch.sort(idx["dense"], dim=1).values
+    b = torch.sort(idx["stream"], dim=1).values
+    out["rows_with_equal_sets"] = int((a == b).all(dim=1).sum())
+    out["workload"] = f"selection_n{n}_N{N}_k{k}_bf16"
+    return out
 
 
 def _prefill_stage_rooflines(w, kern, steps):
@@ -592,7 +648,12 @@ def main():
     api.lib()
 
     dec = bench_decode(args, torch, api, synth, layer)
-    pre = None if args.no_prefill else bench_prefill(args, torch, api, synth, layer)
+    pre = pre_stream = sel_long = None
+    if not args.no_prefill:
+        pre, HW = bench_prefill(args, torch, api, synth, layer, "dense")
+        pre_stream, HW = bench_prefill(args, torch, api, synth, layer, "stream", HW)
+        del HW
+        sel_long = bench_selection_long(args, torch, api, synth, layer)
     dstep = None if args.no_decode_step else bench_decode_step(args, torch, api, synth, layer)
     pvar = None if args.no_varlen else bench_prefill_varlen(args, torch, api, synth, layer)
     pbwd = None if args.no_backward else bench_prefill_backward(args, torch, api, synth, layer)
@@ -630,6 +691,8 @@ def main():
         "step_time_stats_other_launch": dec["dist"]["eager" if launch == "graph" else "graph"],
         "decode_kernels_us": {n: round(s["avg_us"], 3) for n, s in dec["kernels"].items()},
         "prefill": pre,
+        "prefill_stream_selection": pre_stream,
+        "selection_long": sel_long,
         "decode_step_with_cache": dstep,
         "prefill_varlen": pvar,
         "prefill_backward": pbwd,

@@ -54,6 +54,9 @@ _SIGS = {
     "csa_index_topk_workspace": (ctypes.c_int, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_index_topk": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "csa_index_topk_stream_workspace": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_sz)]),
+    "csa_index_topk_stream": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i64, _vp,
+                                             _vp, _vp, _sz, _vp]),
     "csa_sparse_mqa_workspace": (ctypes.c_int, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_sparse_mqa": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _sz, _vp]),
@@ -300,6 +303,38 @@ def csa_index_topk_workspace(n_queries: int, max_cand: int, n_hI: int, k: int) -
     _check(lib().csa_index_topk_workspace(n_queries, max_cand, n_hI, k, ctypes.byref(b)),
            "csa_index_topk_workspace")
     return b.value
+
+
+def csa_index_topk_stream_workspace(n_queries: int, max_cand: int) -> int:
+    b = _sz(0)
+    _check(lib().csa_index_topk_stream_workspace(n_queries, max_cand, ctypes.byref(b)),
+           "csa_index_topk_stream_workspace")
+    return b.value
+
+
+def csa_index_topk_stream(qI, wI, KIcomp, m: int, k: int, max_cand: int, idx_out, score_out=None,
+                          workspace=None):
+    """Eqs 8-9 for one sequence's prefill (query t at position t) without the causal score matrix.
+    qI [n, n_hI, cI], wI [n, n_hI] fp32, KIcomp [rows, cI] -> idx_out [n, k] (each row in index order)."""
+    nq, nhI, cI = qI.shape
+    for t, nm in ((qI, "qI"), (wI, "wI"), (KIcomp, "KIcomp"), (idx_out, "idx_out")):
+        _contig(t, nm)
+    if wI.dtype != torch.float32 or tuple(wI.shape) != (nq, nhI):
+        raise CSAError("csa_index_topk_stream: wI must be fp32 [n_queries, n_hI]")
+    if idx_out.dtype != torch.int32 or tuple(idx_out.shape) != (nq, k):
+        raise CSAError("csa_index_topk_stream: idx_out must be int32 [n_queries, k]")
+    if score_out is not None:
+        _contig(score_out, "score_out")
+        if score_out.dtype != torch.float32 or tuple(score_out.shape) != (nq, k):
+            raise CSAError("csa_index_topk_stream: score_out must be fp32 [n_queries, k]")
+    need = csa_index_topk_stream_workspace(nq, max_cand)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qI.device)
+    _check(lib().csa_index_topk_stream(_dt(qI), nq, nhI, cI, m, k, _ptr(qI), _ptr(wI), _ptr(KIcomp), max_cand,
+                                       _ptr(idx_out), _ptr(score_out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(qI.device)),
+           "csa_index_topk_stream")
+    return idx_out
 
 
 def csa_index_topk(qI, wI, KIcomp, m: int, k: int, max_cand: int, idx_out, score_out=None,

@@ -546,6 +546,57 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
                     score_out, workspace, ws_bytes, stream, true);
 }
 
+// Workspace of csa_index_topk_stream (each area 256-byte aligned): lists
+// [n_queries, stream_ld(max_cand)] uint64, per-query state [n_queries, 4] uint32.
+long stream_ld(long max_cand) { return (max_cand + 1) & ~1L; }
+
+csa_status csa_index_topk_stream_workspace(int64_t n_queries, int64_t max_cand, size_t* bytes) {
+  CSA_REQUIRE(bytes, "csa_index_topk_stream_workspace: null bytes");
+  CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF && max_cand >= 0 && max_cand <= 65535,
+              "csa_index_topk_stream_workspace: bad size (max_cand <= 65535)");
+  *bytes = csa::ws_add(csa::ws_align(csa::ws_bytes(n_queries, stream_ld(max_cand), sizeof(uint64_t))),
+                       csa::ws_align(csa::ws_bytes(n_queries, 4 * sizeof(uint32_t))));
+  return CSA_OK;
+}
+
+csa_status csa_index_topk_stream(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m, int32_t k,
+                                 const void* qI, const float* wI, const void* KIcomp, int64_t max_cand,
+                                 int32_t* idx_out, float* score_out, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_index_topk_stream: unknown dtype");
+  CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_index_topk_stream: bad n_queries");
+  CSA_REQUIRE(n_hI >= 1 && n_hI <= 64, "csa_index_topk_stream: n_hI must be in [1, 64] (got %d)", n_hI);
+  CSA_REQUIRE(cI == 32 || cI == 64 || cI == 128 || cI == 256,
+              "csa_index_topk_stream: cI must be 32, 64, 128 or 256 (got %d)", cI);
+  CSA_REQUIRE(m >= 1, "csa_index_topk_stream: m must be >= 1");
+  CSA_REQUIRE(k >= 1 && k <= (1 << 24), "csa_index_topk_stream: k must be in [1, 2^24]");
+  CSA_REQUIRE(max_cand >= 0 && max_cand <= 65535, "csa_index_topk_stream: max_cand must be in [0, 65535]");
+  if (n_queries == 0) return CSA_OK;
+  CSA_REQUIRE(qI && wI && KIcomp && idx_out, "csa_index_topk_stream: null pointer");
+  CSA_REQUIRE(aligned16(qI) && aligned16(wI) && aligned16(KIcomp) && aligned16(idx_out) && aligned16(score_out),
+              "csa_index_topk_stream: pointers must be 16-byte aligned");
+  if (!csa::indexer_stream_supported(dt, n_hI, cI, max_cand))
+    return fail(CSA_ERR_UNSUPPORTED, "csa_index_topk_stream: n_hI = %d, cI = %d does not fit the streaming kernel",
+                n_hI, cI);
+  size_t need = 0;
+  csa_status st = csa_index_topk_stream_workspace(n_queries, max_cand, &need);
+  if (st != CSA_OK) return st;
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "csa_index_topk_stream: workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  CSA_REQUIRE(aligned16(workspace), "csa_index_topk_stream: workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != CSA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const long ld = stream_ld(max_cand);
+  uint64_t* lists = (uint64_t*)workspace;
+  uint32_t* meta = (uint32_t*)((char*)workspace + csa::ws_align(csa::ws_bytes(n_queries, ld, sizeof(uint64_t))));
+  hipError_t e = csa::launch_indexer_stream(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, nullptr, max_cand, lists,
+                                            ld, meta, k, s);
+  if (e != hipSuccess) return hip_fail(e, "csa_index_topk_stream indexer launch");
+  e = csa::launch_topk_lists(n_queries, m, max_cand, k, lists, ld, meta, idx_out, score_out, s);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk_stream top-k launch");
+}
+
 csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, size_t* bytes) {
   CSA_REQUIRE(bytes, "csa_sparse_mqa_workspace: null bytes");
   CSA_REQUIRE(n_queries >= 0 && n_h >= 1 && c >= 1 && k >= 1, "csa_sparse_mqa_workspace: bad size");

@@ -55,14 +55,49 @@ constexpr int kPfTokPerWave = 1;
 
 // Waves (= tokens) per workgroup, from the VGPRs a token's q^I fragments take:
 // 16 waves (128-VGPR budget each) up to 64, 8 waves (256) up to 96, else 4.
-template <typename T, int KK, int NHT>
+template <typename T, int KK, int NHT, bool STREAM = false>
 constexpr int pf_waves() {
   constexpr int v = NHT * KK * (sizeof(T) == 2 ? 4 : 8);
-  return v <= 64 ? 16 : (v <= 96 ? 8 : 4);
+  constexpr int w = v <= 64 ? 16 : (v <= 96 ? 8 : 4);
+  // streaming keeps more state per wave: at most 8 waves (256 VGPRs each)
+  return STREAM && w > 8 ? 8 : w;
 }
 
-template <typename T, int KK, int NHT>
-__global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill_kernel(int n, int nhI, int m,
+// keys per LDS tile of the prefill kernel: 128 (measured faster than 64)
+// while two tiles of key rows stay well inside LDS, else 64
+template <typename T, int KK>
+constexpr int pf_tile() {
+  return 32 * KK * sizeof(T) <= 512 ? 128 : 64;
+}
+
+// Streaming selection (STREAM): each wave keeps, for its token, a histogram
+// of 2^kStreamBits bins of the top bits of the score keys (score_key), two
+// 16-bit counts per LDS word, and a running threshold bin b: the highest bin
+// such that at least k of the scores seen so far lie in bins >= b.  b only
+// rises, and every score of the final top-k lies in a bin >= the final b >=
+// every earlier b, so a score below the current b can never be selected and
+// is dropped; the others are appended, in index order, to the token's list as
+// (index, score) entries.  The histogram counts only appended scores, which
+// are all the scores of bins >= b: exact where it is read.
+constexpr int kStreamBits = kStreamBitsTopk;
+constexpr int kStreamBins = 1 << kStreamBits;
+constexpr int kStreamWords = kStreamBins / 2;
+
+// LDS of the prefill kernel: two key tiles, plus one histogram per wave when
+// streaming.
+template <typename T, int KK, int NHT, bool STREAM>
+constexpr size_t pf_lds_bytes() {
+  return 2 * (size_t)pf_tile<T, KK>() * (32 * KK + 16 / sizeof(T)) * sizeof(T) +
+         (STREAM ? (size_t)pf_waves<T, KK, NHT, STREAM>() * kStreamWords * 4 : 0);
+}
+
+template <typename T, int KK, int NHT, bool STREAM>
+constexpr bool pf_fits() {
+  return pf_lds_bytes<T, KK, NHT, STREAM>() <= 160 * 1024;
+}
+
+template <typename T, int KK, int NHT, bool STREAM = false>
+__global__ __launch_bounds__((64 * pf_waves<T, KK, NHT, STREAM>())) void indexer_prefill_kernel(int n, int nhI, int m,
                                                               const T* __restrict__ qI,
                                                               const float* __restrict__ wI,
                                                               const T* __restrict__ K,
@@ -71,18 +106,20 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
                                                               float* __restrict__ scores,
                                                               long ld_sc, int nseq,
                                                               const int64_t* __restrict__ cu,
-                                                              const int32_t* __restrict__ blk) {
-  constexpr int kPfWaves = pf_waves<T, KK, NHT>();
+                                                              const int32_t* __restrict__ blk,
+                                                              uint64_t* __restrict__ lists, uint32_t* __restrict__ meta,
+                                                              int k) {
+  constexpr int kPfWaves = pf_waves<T, KK, NHT, STREAM>();
   constexpr int kPfTokens = kPfWaves * kPfTokPerWave;
-  // keys per LDS tile: 128 (measured faster than 64) while two tiles of key
-  // rows stay well inside LDS, else 64
-  constexpr int kPfTile = 32 * KK * sizeof(T) <= 512 ? 128 : 64;
+  constexpr int kPfTile = pf_tile<T, KK>();
   constexpr int CI = 32 * KK;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int PITCH = CI + VEC;  // padded LDS row (elements)
   constexpr int CHUNKS = CI / VEC;
   constexpr int TILE_VECS = kPfTile * CHUNKS;
+  static_assert(!STREAM || (pf_fits<T, KK, NHT, STREAM>() && kPfTokPerWave == 1), "streaming layout");
   __shared__ __attribute__((aligned(16))) T Ks[2][kPfTile * PITCH];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[STREAM ? kPfWaves * kStreamWords : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -143,6 +180,17 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
     }
   }
 
+  // streaming state of this wave's token (wave-uniform)
+  uint32_t* whist = s_hist + (STREAM ? wave * kStreamWords : 0);
+  // (a token with at most k candidates never raises its threshold: all its scores are listed)
+  const bool stream_tok = STREAM && nc[0] > 0;
+  uint32_t bstar = 0, above = 0, nlist = 0;
+  uint64_t* lrow = lists + (STREAM ? tok[0] * ld_sc : 0);
+  if constexpr (STREAM) {
+    for (int i = lane; i < kStreamWords / 4; i += 64)
+      reinterpret_cast<u32x4*>(whist)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+
   K += kbase * CI;
   const int ntiles = (int)((kend + kPfTile - 1) / kPfTile);
   constexpr int LOADS = (TILE_VECS + 64 * kPfWaves - 1) / (64 * kPfWaves);
@@ -189,11 +237,79 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT>())) void indexer_prefill
           for (int rr = 0; rr < 4; ++rr) part = fmaf(wv[tt][mt][rr], relu(acc[rr]), part);
         }
         part = wave_sum_xor_16_32(part);
-        if (g == 0 && s < nc[tt]) scores[tok[tt] * ld_sc + s] = part;
+        if constexpr (!STREAM) {
+          if (g == 0 && s < nc[tt]) scores[tok[tt] * ld_sc + s] = part;
+        } else if (stream_tok) {
+          const uint32_t bin = score_key(part) >> (32 - kStreamBits);
+          const bool pass = g == 0 && s < nc[tt] && bin >= bstar;
+          const uint64_t bal = __ballot(pass);  // lanes 0..15 only: key order
+          if (pass) {
+            const uint32_t at = nlist + __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u);
+            if (at < (uint32_t)ld_sc) lrow[at] = (uint64_t)s | ((uint64_t)__float_as_uint(part) << 32);
+            atomicAdd(&whist[bin >> 1], 1u << ((bin & 1u) * 16));
+          }
+          const uint32_t np = __builtin_amdgcn_readfirstlane((uint32_t)__popcll(bal));
+          nlist += np;
+          above += np;
+        }
+      }
+    }
+    if constexpr (STREAM) {
+      // Raise the threshold bin to the highest bin with at least k listed
+      // scores at or above it, once at least k are listed.  One wave-parallel
+      // search over the histogram: lane l sums bins 32l .. 32l+31, a suffix
+      // scan from the top finds the lane where the count reaches k, and that
+      // lane walks its 32 bins.  (This wave's LDS operations complete in
+      // order: the counts include the additions above.)  Bins below the
+      // current threshold hold partial counts, but the search stops at or
+      // above it: the count at and above it is already >= k.
+      if (stream_tok && above >= (uint32_t)k) {
+        const u32x4* hw = reinterpret_cast<const u32x4*>(whist) + 4 * lane;
+        uint32_t lsum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = hw[q];
+          lsum += ((v.x & 0xFFFFu) + (v.x >> 16)) + ((v.y & 0xFFFFu) + (v.y >> 16)) +
+                  ((v.z & 0xFFFFu) + (v.z >> 16)) + ((v.w & 0xFFFFu) + (v.w >> 16));
+        }
+        // counts at or above this lane's bins: total minus the inclusive prefix below
+        const uint32_t incl = wave_incl_scan(lsum);
+        const uint32_t total = wave_last(incl);
+        const uint32_t from_me = total - incl + lsum;  // bins >= 32 lane
+        const uint32_t above_me = from_me - lsum;      // bins >= 32 (lane + 1)
+        const uint64_t hit = __ballot(above_me < (uint32_t)k && from_me >= (uint32_t)k);
+        const int hl = __builtin_ctzll(hit | (1ull << 63));  // exactly one lane holds the crossing
+        uint32_t nb = 0, nab = 0;
+        if (lane == hl) {  // walk this lane's 32 bins from the top (its words read again)
+          uint32_t cum = above_me;
+          bool found = false;
+          for (int wdi = 15; wdi >= 0 && !found; --wdi) {
+            const uint32_t wd = whist[16 * lane + wdi];
+            for (int half = 1; half >= 0 && !found; --half) {
+              const uint32_t c = half ? (wd >> 16) : (wd & 0xFFFFu);
+              if (cum + c >= (uint32_t)k) {
+                nb = (uint32_t)(32 * lane + 2 * wdi + half);
+                nab = cum + c;
+                found = true;
+              }
+              cum += c;
+            }
+          }
+        }
+        bstar = __builtin_amdgcn_readlane(nb, hl);
+        above = __builtin_amdgcn_readlane(nab, hl);
       }
     }
     if (tile + 1 < ntiles) stash(cur ^ 1);
     __syncthreads();
+  }
+  if constexpr (STREAM) {
+    // per token: threshold bin, count strictly above it, list length
+    if (lane == 0 && p0 + wave < len) {
+      uint32_t g1 = 0;
+      if (stream_tok) g1 = above - ((whist[bstar >> 1] >> ((bstar & 1u) * 16)) & 0xFFFFu);
+      *reinterpret_cast<u32x4*>(meta + 4 * tok[0]) = u32x4{bstar, g1, nlist, stream_tok ? 1u : 0u};
+    }
   }
 }
 
@@ -240,7 +356,7 @@ hipError_t run_varlen(long nseq, long ntok, int nhI, int m, const void* qI, cons
   const long grid = (ntok + waves - 1) / waves + nseq;
   return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3((unsigned)grid), dim3(64 * waves), 0, s,
                 (int)ntok, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc, (int)nseq, cu,
-                blk);
+                blk, (uint64_t*)nullptr, (uint32_t*)nullptr, 0);
 }
 
 template <typename T>
@@ -288,7 +404,7 @@ hipError_t run(long nq, int nhI, int m, const void* qI, const float* wI, const v
     const int nblocks = (int)((nq + waves * kPfTokPerWave - 1) / (waves * kPfTokPerWave));
     return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT>, dim3(nblocks), dim3(64 * waves), 0, s,
                   (int)nq, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, scores, ld_sc, 0,
-                  (const int64_t*)nullptr, (const int32_t*)nullptr);
+                  (const int64_t*)nullptr, (const int32_t*)nullptr, (uint64_t*)nullptr, (uint32_t*)nullptr, 0);
   } else {
     const unsigned chunks = (unsigned)((max_cand + kSweepKeysPerWG - 1) / kSweepKeysPerWG);
     return launch("indexer_sweep", indexer_sweep_kernel<T, KK, NHT>, dim3(chunks * (unsigned)nq),
@@ -323,7 +439,77 @@ hipError_t pick_kk(long nq, int nhI, int cI, int m, const void* qI, const float*
   }
 }
 
+template <typename T, int KK, int NHT>
+hipError_t run_stream(long n, int nhI, int m, const void* qI, const float* wI, const void* K, const int64_t* kv_off,
+                      long max_cand, uint64_t* lists, long ld_list, uint32_t* meta, int k, hipStream_t s) {
+  if constexpr (!pf_fits<T, KK, NHT, true>()) {
+    return hipErrorInvalidValue;  // the host checks stream_supported first
+  } else {
+    constexpr int waves = pf_waves<T, KK, NHT, true>();
+    const int nblocks = (int)((n + waves - 1) / waves);
+    return launch("indexer_prefill", indexer_prefill_kernel<T, KK, NHT, true>, dim3(nblocks), dim3(64 * waves), 0, s,
+                  (int)n, nhI, m, (const T*)qI, wI, (const T*)K, kv_off, max_cand, (float*)nullptr, ld_list, 0,
+                  (const int64_t*)nullptr, (const int32_t*)nullptr, lists, meta, k);
+  }
+}
+
+template <typename T, int KK>
+hipError_t stream_nht(long n, int nhI, int m, const void* qI, const float* wI, const void* K, const int64_t* kv_off,
+                      long max_cand, uint64_t* lists, long ld_list, uint32_t* meta, int k, hipStream_t s) {
+  switch ((nhI + 15) / 16) {
+    case 1: return run_stream<T, KK, 1>(n, nhI, m, qI, wI, K, kv_off, max_cand, lists, ld_list, meta, k, s);
+    case 2: return run_stream<T, KK, 2>(n, nhI, m, qI, wI, K, kv_off, max_cand, lists, ld_list, meta, k, s);
+    case 3: return run_stream<T, KK, 3>(n, nhI, m, qI, wI, K, kv_off, max_cand, lists, ld_list, meta, k, s);
+    default: return run_stream<T, KK, 4>(n, nhI, m, qI, wI, K, kv_off, max_cand, lists, ld_list, meta, k, s);
+  }
+}
+
+template <typename T, int KK>
+bool fits_nht(int nhI) {
+  switch ((nhI + 15) / 16) {
+    case 1: return pf_fits<T, KK, 1, true>();
+    case 2: return pf_fits<T, KK, 2, true>();
+    case 3: return pf_fits<T, KK, 3, true>();
+    default: return pf_fits<T, KK, 4, true>();
+  }
+}
+
+template <typename T>
+bool fits_kk(int nhI, int cI) {
+  switch (cI / 32) {
+    case 1: return fits_nht<T, 1>(nhI);
+    case 2: return fits_nht<T, 2>(nhI);
+    case 4: return fits_nht<T, 4>(nhI);
+    case 8: return fits_nht<T, 8>(nhI);
+    default: return false;
+  }
+}
+
 }  // namespace
+
+bool indexer_stream_supported(csa_dtype dt, int nhI, int cI, long max_cand) {
+  // the streaming histogram counts up to 65535 scores per bin
+  if (max_cand > 65535) return false;
+  return dt == CSA_F32 ? fits_kk<float>(nhI, cI) : fits_kk<bf16_t>(nhI, cI);
+}
+
+hipError_t launch_indexer_stream(csa_dtype dt, long n, int nhI, int cI, int m, const void* qI, const float* wI,
+                                 const void* K, const int64_t* kv_offset, long max_cand, uint64_t* lists,
+                                 long ld_list, uint32_t* meta, int k, hipStream_t s) {
+  if (n == 0 || max_cand == 0) return hipSuccess;
+  const bool f32 = dt == CSA_F32;
+  switch (cI / 32) {
+    case 1: return f32 ? stream_nht<float, 1>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s)
+                       : stream_nht<bf16_t, 1>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s);
+    case 2: return f32 ? stream_nht<float, 2>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s)
+                       : stream_nht<bf16_t, 2>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s);
+    case 4: return f32 ? stream_nht<float, 4>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s)
+                       : stream_nht<bf16_t, 4>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s);
+    case 8: return f32 ? stream_nht<float, 8>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s)
+                       : stream_nht<bf16_t, 8>(n, nhI, m, qI, wI, K, kv_offset, max_cand, lists, ld_list, meta, k, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_indexer(csa_dtype dt, long n_queries, int nhI, int cI, int m, const void* qI,
                           const float* wI, const void* K, const int32_t* q_seq,

@@ -117,6 +117,22 @@ hipError_t launch_indexer_varlen(csa_dtype dt, long nseq, long ntok, int nhI, in
 
 hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s);
 
+// bits of the streaming indexer's histogram bins (top bits of score_key)
+constexpr int kStreamBitsTopk = 11;
+
+// Streaming prefill selection (one sequence, query t at position t): the
+// indexer appends to lists [n, ld_list] (index | score bits << 32) only the
+// scores that can still be selected and writes per token meta [n, 4] =
+// (threshold bin, count above it, list length, streamed); the list selector
+// finishes the top-k from them.  indexer_stream_supported says whether the
+// kernel's LDS holds the sizes.
+bool indexer_stream_supported(csa_dtype dt, int nhI, int cI, long max_cand);
+hipError_t launch_indexer_stream(csa_dtype dt, long n, int nhI, int cI, int m, const void* qI, const float* wI,
+                                 const void* K, const int64_t* kv_offset, long max_cand, uint64_t* lists,
+                                 long ld_list, uint32_t* meta, int k, hipStream_t s);
+hipError_t launch_topk_lists(long n, int m, long max_cand, int k, const uint64_t* lists, long ld_list,
+                             const uint32_t* meta, int32_t* idx_out, float* score_out, hipStream_t s);
+
 // Long rows (with the indexer's histogram) can be selected by many
 // workgroups per row: chunks of kMChunk keys, at most kMMaxChunks per row.
 constexpr int kMChunk = 2048;

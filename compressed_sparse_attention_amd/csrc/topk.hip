@@ -165,6 +165,170 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
                     eq_list + r * P * (long)kMChunk, kMChunk, out, sout);
 }
 
+// ---------------------------------------------------------------------------
+// Streaming prefill selection, finishing phase.  Row r (the query at position
+// r) exists only as the list the indexer appended (index | score bits << 32,
+// in index order), with the threshold bin b of its running histogram (the
+// k-th largest score lies in bin b), the count g1 of entries in higher bins
+// and the list length.  Entries below b are dropped, those above are
+// selected, and the k - g1 still needed come from bin b: levels of 8 + 8 + 5
+// bits over bin b's entries (staged in LDS) find the k-th largest key T and
+// how many entries equal to T to take (the lowest indices).  The emit is one
+// ordered pass over the list: every selected entry, in index order.  Lists
+// longer than kLTPB x kLEPT entries are walked in segments (re-read from
+// global memory), and bin b's entries are staged in LDS while they fit
+// (otherwise the levels re-read the list too).
+// ---------------------------------------------------------------------------
+constexpr int kLTPB = 256;
+constexpr int kLEPT = 32;
+constexpr int kLSeg = kLTPB * kLEPT;
+constexpr int kLCap = 4096;
+constexpr int kLShift = 32 - kStreamBitsTopk;
+
+__global__ __launch_bounds__(kLTPB) void topk_list_kernel(int m, long max_cand, int k, const uint64_t* __restrict__ lists,
+                                                         long ld_list, const uint32_t* __restrict__ meta,
+                                                         int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t s_ckey[kLCap];
+  __shared__ uint32_t s_cidx[kLCap];
+  __shared__ uint32_t s_h[3][256];
+  __shared__ uint32_t s_wave[kLTPB / 64];
+  __shared__ uint32_t s_res[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long r = blockIdx.x;
+  long nc = r / m;
+  nc = nc < max_cand ? nc : max_cand;
+  int32_t* out = idx_out + r * k;
+  float* sout = score_out ? score_out + r * k : nullptr;
+  if (nc <= k) {  // every candidate is kept: the list holds all of them, entry e = candidate e
+    for (int e = tid; e < k; e += kLTPB) {
+      const bool live = e < nc;
+      out[e] = live ? e : -1;
+      if (sout) sout[e] = live ? __uint_as_float((uint32_t)(lists[r * ld_list + e] >> 32)) : -INFINITY;
+    }
+    return;
+  }
+  const u32x4 mt = *reinterpret_cast<const u32x4*>(meta + 4 * r);
+  const uint32_t bstar = mt.x, g1 = mt.y;
+  const long len = (long)mt.z < ld_list ? (long)mt.z : ld_list;
+  const uint64_t* row = lists + r * ld_list;
+  const int nseg = (int)((len + kLSeg - 1) / kLSeg);
+  const int first = tid * kLEPT;
+
+  // this thread's entries of segment sg: [sg * kLSeg + first, + kLEPT), 16-byte loads clamped into the list
+  uint64_t ent[kLEPT];
+  // Pairs (a, a + 1), a even: rows have an even pitch, so a pair whose first
+  // entry is in the list lies inside the row (its second entry, if past the
+  // list, is masked); pairs wholly past the list read the list's first pair
+  // (every listed row has at least k + 1 >= 2 entries) and are masked.
+  auto load_seg = [&](int sg) {
+    const long base = (long)sg * kLSeg + first;
+#pragma unroll
+    for (int j = 0; j < kLEPT / 2; ++j) {
+      const long a = base + 2 * j;
+      const long at = a < len ? a : 0;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(row + at);
+      ent[2 * j] = (uint64_t)v.x | ((uint64_t)v.y << 32);
+      ent[2 * j + 1] = (uint64_t)v.z | ((uint64_t)v.w << 32);
+    }
+  };
+  auto nvalid = [&](int sg) { return (int)max(0L, min((long)kLEPT, len - (long)sg * kLSeg - first)); };
+  auto key_of = [](uint64_t e) { return score_key(__uint_as_float((uint32_t)(e >> 32))); };
+
+  // ---- bin b's entries to LDS (index order), counted ------------------------------
+  uint32_t n_eq = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    load_seg(sg);
+    const int nv = nvalid(sg);
+    uint32_t me = 0;
+#pragma unroll
+    for (int e = 0; e < kLEPT; ++e) me |= (uint32_t)(e < nv && (key_of(ent[e]) >> kLShift) == bstar) << e;
+    uint32_t tot;
+    uint32_t p = n_eq + block_excl_scan<kLTPB>(__popc(me), s_wave, tot);
+#pragma unroll
+    for (int e = 0; e < kLEPT; ++e)
+      if ((me >> e) & 1u) {
+        if (p < (uint32_t)kLCap) {
+          s_cidx[p] = (uint32_t)ent[e];
+          s_ckey[p] = key_of(ent[e]);
+        }
+        ++p;
+      }
+    n_eq += tot;
+  }
+  for (int b = tid; b < 3 * 256; b += kLTPB) (&s_h[0][0])[b] = 0u;
+  __syncthreads();
+  const bool staged = n_eq <= (uint32_t)kLCap;
+
+  // ---- levels over bin b's entries: 8, 8 and 5 more bits -----------------------------
+  const int shifts[3] = {kLShift - 8, kLShift - 16, 0};
+  const int widths[3] = {8, 8, kLShift - 16};
+  uint32_t prefix = bstar << kLShift, pmask = 0xFFFFFFFFu << kLShift, need = (uint32_t)k - g1;
+  for (int lv = 0; lv < 3; ++lv) {
+    const int sh = shifts[lv];
+    const uint32_t dm = (1u << widths[lv]) - 1u;
+    uint32_t* h = s_h[lv];
+    if (staged) {
+      for (uint32_t e = tid; e < n_eq; e += kLTPB) {
+        const uint32_t key = s_ckey[e];
+        if ((key & pmask) == prefix) atomicAdd(&h[(key >> sh) & dm], 1u);
+      }
+    } else {
+      for (int sg = 0; sg < nseg; ++sg) {
+        load_seg(sg);
+        const int nv = nvalid(sg);
+#pragma unroll
+        for (int e = 0; e < kLEPT; ++e) {
+          const uint32_t key = key_of(ent[e]);
+          if (e < nv && (key & pmask) == prefix) atomicAdd(&h[(key >> sh) & dm], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      if (lane == 0) {
+        s_res[0] = 0u;
+        s_res[1] = 0u;
+      }
+      find_bin_wave(h, 1 << widths[lv], need, s_res);
+    }
+    __syncthreads();
+    prefix |= s_res[0] << sh;
+    pmask |= dm << sh;
+    need -= s_res[1];
+  }
+  const uint32_t T = prefix;      // the k-th largest key
+  const uint32_t take_eq = need;  // entries equal to T to take, lowest indices first
+
+  // ---- ordered emit: every entry above T, and the first take_eq equal to T ----------
+  uint32_t run1 = 0, run2 = 0;
+  for (int sg = 0; sg < nseg; ++sg) {
+    if (nseg > 1 || !staged) load_seg(sg);
+    const int nv = nvalid(sg);
+    uint32_t m1 = 0, m2 = 0;
+#pragma unroll
+    for (int e = 0; e < kLEPT; ++e) {
+      const uint32_t key = key_of(ent[e]);
+      m1 |= (uint32_t)(e < nv && key > T) << e;
+      m2 |= (uint32_t)(e < nv && key == T) << e;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kLTPB>(__popc(m1) | (__popc(m2) << 16), s_wave, tot);
+    uint32_t p1 = run1 + (ex & 0xFFFFu), p2 = run2 + (ex >> 16);
+    for (uint32_t mm = m1 | m2; mm; mm &= mm - 1) {
+      const int e = __ffs(mm) - 1;
+      const bool eq = (m2 >> e) & 1u;
+      const uint32_t slot = eq ? (p2 < take_eq ? p1 + p2 : 0xFFFFFFFFu) : p1 + min(p2, take_eq);
+      if (slot < (uint32_t)k) {
+        out[slot] = (int32_t)(uint32_t)ent[e];
+        if (sout) sout[slot] = __uint_as_float((uint32_t)(ent[e] >> 32));
+      }
+      if (eq) ++p2; else ++p1;
+    }
+    run1 += tot & 0xFFFFu;
+    run2 += tot >> 16;
+  }
+}
+
 template <int TPB, bool REGS, int EPT>
 void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const int64_t* q_pos, long max_cand,
             int k, uint32_t* hist, int32_t* idx_out, float* score_out, hipStream_t s) {
@@ -173,6 +337,13 @@ void launch_rows(long n_queries, int m, const float* scores, long ld_sc, const i
 }
 
 }  // namespace
+
+hipError_t launch_topk_lists(long n, int m, long max_cand, int k, const uint64_t* lists, long ld_list,
+                             const uint32_t* meta, int32_t* idx_out, float* score_out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  return launch("topk", topk_list_kernel, dim3((unsigned)n), dim3(kLTPB), 0, s, m, max_cand, k, lists, ld_list, meta,
+                idx_out, score_out);
+}
 
 hipError_t launch_hist_clear(uint32_t* hist, long n, hipStream_t s) {
   if (n == 0) return hipSuccess;

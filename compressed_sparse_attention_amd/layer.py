@@ -54,9 +54,15 @@ def pack_prefill_params(P: Dict[str, np.ndarray], dtype: str, device) -> Dict[st
 
 
 class PrefillBuffers:
-    """Intermediate and output buffers of one prefill shape (reused across calls)."""
+    """Intermediate and output buffers of one prefill shape (reused across calls).  selection = "dense"
+    (csa_index_topk: the causal score matrix, then the selector) or "stream" (csa_index_topk_stream: the
+    indexer keeps only the scores that can still be selected)."""
 
-    def __init__(self, n: int, m: int, k: int, nh: int, nhI: int, c: int, cI: int, dc: int, dtype, device):
+    def __init__(self, n: int, m: int, k: int, nh: int, nhI: int, c: int, cI: int, dc: int, dtype, device,
+                 selection: str = "dense"):
+        if selection not in ("dense", "stream"):
+            raise ValueError("selection must be 'dense' or 'stream'")
+        self.selection = selection
         width = 4 * c + 4 * cI + dc
         N = n // m
         self.Y_H = torch.empty(n, width, dtype=dtype, device=device)
@@ -68,19 +74,22 @@ class PrefillBuffers:
         self.idx = torch.empty(n, k, dtype=torch.int32, device=device)
         self.o = torch.empty(n, nh, c, dtype=dtype, device=device)
         self.lse = torch.empty(n, nh, dtype=torch.float32, device=device)
-        ws_i = api.csa_index_topk_workspace(n, N, nhI, k)
+        ws_i = (api.csa_index_topk_workspace(n, N, nhI, k) if selection == "dense"
+                else api.csa_index_topk_stream_workspace(n, N))
         ws_m = api.csa_sparse_mqa_workspace(n, nh, c, k)
         self.ws_index = torch.empty(max(ws_i, 1), dtype=torch.uint8, device=device)
         self.ws_mqa = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=device)
 
 
 def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int, nhI: int,
-            scale: Optional[float] = None, buf: Optional[PrefillBuffers] = None) -> PrefillBuffers:
-    """Eqs 1-11 for one sequence H [n, d]: every token is a query (causal)."""
+            scale: Optional[float] = None, buf: Optional[PrefillBuffers] = None,
+            selection: str = "dense") -> PrefillBuffers:
+    """Eqs 1-11 for one sequence H [n, d]: every token is a query (causal).  `selection` picks the eqs 8-9
+    path when buf is not given (see PrefillBuffers)."""
     n = H.shape[0]
     c, cI, dc = W["c"], W["cI"], W["dc"]
     if buf is None:
-        buf = PrefillBuffers(n, m, k, nh, nhI, c, cI, dc, H.dtype, H.device)
+        buf = PrefillBuffers(n, m, k, nh, nhI, c, cI, dc, H.dtype, H.device, selection=selection)
     Y = buf.Y_H
     api.csa_project(H, W["W_H_t"], Y)  # eqs 1, 2 (+ indexer copies), 5
     api.csa_project(H, W["W_w_t"], buf.wI)  # eq 7
@@ -91,8 +100,12 @@ def prefill(H: torch.Tensor, W: Dict[str, torch.Tensor], m: int, k: int, nh: int
     o = 4 * c
     api.csa_compress(Y[:, o:o + cI], Y[:, o + cI:o + 2 * cI], Y[:, o + 2 * cI:o + 3 * cI],
                      Y[:, o + 3 * cI:o + 4 * cI], W["B_aI"], W["B_bI"], m, buf.KIcomp)
-    api.csa_index_topk(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, n // m, buf.idx,
-                       workspace=buf.ws_index)  # eqs 8-9
+    if buf.selection == "stream":
+        api.csa_index_topk_stream(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, n // m, buf.idx,
+                                  workspace=buf.ws_index)  # eqs 8-9 without the score matrix
+    else:
+        api.csa_index_topk(buf.qI.view(n, nhI, cI), buf.wI, buf.KIcomp, m, k, n // m, buf.idx,
+                           workspace=buf.ws_index)  # eqs 8-9
     # the largest projection runs after the indexer, whose MFMA rate suffers
     # when it follows this GEMM directly
     api.csa_project(cQ, W["W_UQ_t"], buf.q)  # eq 10

@@ -294,6 +294,35 @@ csa_status csa_index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t
                           size_t ws_bytes, void* stream);
 
 /*
+ * csa_index_topk_stream -- eqs 8-9 for the queries of one sequence's prefill
+ * (query t at position t: the layout of csa_index_topk with q_seq, q_pos and
+ * kv_offset NULL), without materialising the causal score matrix (section
+ * "Lightning Indexer for Sparse Selection": only the top-k of each query's
+ * scores is ever used).  While the indexer walks a query's candidates in
+ * index order it keeps a histogram of its scores' keys and a running
+ * threshold bin b -- the highest bin with at least k of the scores seen so
+ * far at or above it -- and appends to the query's list, as (index, score)
+ * pairs, only the scores in bins >= b; b only rises, and the final top-k
+ * always lies at or above it, so nothing selectable is dropped.  The
+ * selection then runs on the lists.  The selected set is the same as
+ * csa_index_topk's; idx_out lists each row's selection in increasing index
+ * order (csa_index_topk's order within a row is unspecified), and score_out
+ * (nullable) gets the matching scores (-inf for -1 slots).
+ *
+ * The workspace (size from csa_index_topk_stream_workspace: lists of up to
+ * max_cand 8-byte entries per query plus 16 bytes of per-query state) needs
+ * no initialisation.  Arguments and limits otherwise as csa_index_topk, and:
+ * max_cand <= 65535; the tiled kernel's LDS must hold the histograms, so some
+ * (dtype, n_hI, cI) combinations return CSA_ERR_UNSUPPORTED (every shape with
+ * cI <= 128 is supported).
+ */
+csa_status csa_index_topk_stream_workspace(int64_t n_queries, int64_t max_cand, size_t* bytes);
+csa_status csa_index_topk_stream(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m, int32_t k,
+                                 const void* qI, const float* wI, const void* KIcomp, int64_t max_cand,
+                                 int32_t* idx_out, float* score_out, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * csa_sparse_mqa -- eq 11: shared key-value multi-query attention over the
  * selected compressed entries.  For query r of sequence seq (q_seq NULL: 0)
  * and head h, with the selected rows C_s = Ccomp[kv_offset[seq] + idx[r, j]]

@@ -134,6 +134,19 @@ int main(void) {
   EXPECT(csa_index_topk_varlen(CSA_BF16, 2, 100, 8, 64, 4, 16, P, PF, P, PL, PL, 30, PI, NULL, NULL, P, 8, NULL),
          CSA_ERR_WORKSPACE);
 
+  /* streaming prefill selection */
+  EXPECT(csa_index_topk_stream_workspace(-1, 100, &b), CSA_ERR_INVALID_ARG);
+  EXPECT(csa_index_topk_stream_workspace(big, 65536, &b), CSA_ERR_INVALID_ARG);
+  EXPECT(csa_index_topk_stream_workspace(big, 65535, &b), CSA_OK);
+  EXPECT(csa_index_topk_stream(CSA_BF16, 100, 8, 96, 4, 16, P, PF, P, 25, PI, NULL, P, 1 << 30, NULL),
+         CSA_ERR_INVALID_ARG);
+  EXPECT(csa_index_topk_stream(CSA_BF16, 100, 8, 64, 4, 16, P, PF, P, 70000, PI, NULL, P, 1 << 30, NULL),
+         CSA_ERR_INVALID_ARG);
+  EXPECT(csa_index_topk_stream(CSA_BF16, 100, 8, 64, 4, 16, P, PF, P, 25, PI, (float*)MIS, P, 1 << 30, NULL),
+         CSA_ERR_INVALID_ARG);
+  EXPECT(csa_index_topk_stream(CSA_BF16, 100, 8, 64, 4, 16, P, PF, P, 25, PI, NULL, P, 8, NULL), CSA_ERR_WORKSPACE);
+  EXPECT(csa_index_topk_stream(CSA_BF16, 0, 8, 64, 4, 16, NULL, NULL, NULL, 25, NULL, NULL, NULL, 0, NULL), CSA_OK);
+
   /* attention */
   EXPECT(csa_sparse_mqa_workspace(-1, 64, 512, 1024, &b), CSA_ERR_INVALID_ARG);
   EXPECT(csa_sparse_mqa_workspace(big, 256, 1024, 1 << 24, &b), CSA_OK); /* a large batch is not split */

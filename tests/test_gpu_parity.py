@@ -453,6 +453,82 @@ def test_index_topk_prefill(dtype, n, m, nhI, cI, k):
     check_topk(idx, rows, k)
 
 
+def _run_stream(qI, wI, K, m, k, dtype, max_cand):
+    n = qI.shape[0]
+    qd, Kd = to_device(qI, dtype, DEV), to_device(K, dtype, DEV)
+    wd = torch.from_numpy(np.ascontiguousarray(wI)).to(DEV)
+    idx = torch.full((n, k), 123456, dtype=torch.int32, device=DEV)
+    sc = torch.full((n, k), 7.0, dtype=torch.float32, device=DEV)
+    api.csa_index_topk_stream(qd, wd, Kd, m, k, max_cand, idx, score_out=sc)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _check_stream_rows(idx, sc, rows, k):
+    """Each row: a valid selection (the comparison rules), listed in increasing index order, -1 after it,
+    and score_out = the oracle's score of each listed index (fp32 rounding)."""
+    check_topk(idx, rows, k)
+    for t, row in enumerate(rows):
+        sel = idx[t][idx[t] >= 0]
+        assert np.all(np.diff(sel) > 0), f"row {t}: not in index order"
+        assert np.all(idx[t][len(sel):] == -1)
+        if sel.size:
+            ref = row[sel]
+            assert np.allclose(sc[t][:len(sel)], ref, rtol=1e-4, atol=1e-5 * np.abs(row).max()), f"row {t}: scores"
+        assert np.all(np.isneginf(sc[t][len(sel):]))
+
+
+@pytest.mark.parametrize("dtype,n,m,nhI,cI,k", [
+    ("f32", 512, 4, 4, 32, 16),      # the fp32 prefill workload's shapes
+    ("bf16", 1000, 4, 64, 128, 64),  # the 32768-token layer's widths on 1000 tokens
+    ("bf16", 333, 2, 16, 64, 8),
+    ("bf16", 4100, 1, 8, 32, 700),   # rows up to 4099 candidates: thresholds rise late
+    ("bf16", 9000, 1, 4, 64, 40),    # lists longer than one 8192-entry segment
+])
+def test_index_topk_stream(dtype, n, m, nhI, cI, k):
+    """Streaming selection (no causal score matrix) against the oracle's eq 8 scores: valid selections,
+    in index order, with their scores."""
+    rng = synth.rng_for(7 * n + nhI)
+    K = draw(rng, (n // m, cI), 1.0, dtype)
+    qI = draw(rng, (n, nhI, cI), 1.0 / math.sqrt(cI), dtype)
+    wI = rng.standard_normal((n, nhI), dtype=np.float32)
+    idx, sc = _run_stream(qI, wI, K, m, k, dtype, n // m)
+    K64 = f64(K, dtype)
+    rows = [O.index_scores_row(f64(qI[t], dtype), wI[t].astype(np.float64), K64, t // m) for t in range(n)]
+    _check_stream_rows(idx, sc, rows, k)
+
+
+@pytest.mark.parametrize("nhI,wset,k", [(1, (1.0,), 40), (8, (-1.0, 0.5, 2.0), 40), (64, (-2.0, 0.0, 1.0, 3.0), 40),
+                                        (1, (1.0,), 900)])
+def test_index_topk_stream_exact_ties(nhI, wset, k):
+    """Small-integer inputs make every fp32 score exact: the streaming selection must equal the oracle's
+    set exactly (lower-index tie-break, -0.0 == +0.0), also when most scores tie at the threshold (one head,
+    w = 1: half the scores are exactly 0)."""
+    rng = synth.rng_for(31 * nhI + k)
+    cI, m, n = 64, 4, 4000
+    K = synth.f32_to_bf16(rng.integers(-2, 3, size=(n // m, cI)).astype(np.float32))
+    qI = synth.f32_to_bf16(rng.integers(-1, 2, size=(n, nhI, cI)).astype(np.float32))
+    wI = rng.choice(np.array(wset, np.float32), size=(n, nhI))
+    idx, sc = _run_stream(qI, wI, K, m, k, "bf16", n // m)
+    K64 = f64(K, "bf16")
+    rows = [O.index_scores_row(f64(qI[t], "bf16"), wI[t].astype(np.float64), K64, t // m) for t in range(n)]
+    exact_sets_equal(idx, O.topk_rows(rows, k))
+    _check_stream_rows(idx, sc, rows, k)
+
+
+def test_index_topk_stream_same_sets_as_dense():
+    """The streaming and the materialised paths select the same sets on the same inputs (integer inputs:
+    exact scores, so no band-exempt differences are possible)."""
+    rng = synth.rng_for(4242)
+    n, m, nhI, cI, k = 3000, 4, 16, 64, 100
+    K = synth.f32_to_bf16(rng.integers(-3, 4, size=(n // m, cI)).astype(np.float32))
+    qI = synth.f32_to_bf16(rng.integers(-2, 3, size=(n, nhI, cI)).astype(np.float32))
+    wI = rng.choice(np.array((-1.0, 0.25, 1.0, 2.0), np.float32), size=(n, nhI))
+    idx_s, _ = _run_stream(qI, wI, K, m, k, "bf16", n // m)
+    idx_d, _ = _run_index_topk(qI, wI, K, m, k, None, None, "bf16", prefill_mode=True)
+    exact_sets_equal(idx_s, idx_d)
+
+
 # ---------------------------------------------------------------------------
 # sparse MQA (eq 11)
 # ---------------------------------------------------------------------------
