@@ -227,7 +227,8 @@ def bench_prefill(args, torch, api, synth, layer, selection="dense", HW=None):
     if ip:
         ach = idx_flops / (ip["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": "indexer_prefill", "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": _traffic("indexer_prefill") if selection == "dense" else None,
                 "algorithmic_flops_per_launch": idx_flops}
     out = {"workload": w.name, "selection": selection, "tokens": w.n, "ms": ms, "tokens_per_s": w.n / (ms * 1e-3),
            "kernels_ms_per_step": {n: round(s["total_ms"] / args.prefill_steps, 4) for n, s in kern.items()},
