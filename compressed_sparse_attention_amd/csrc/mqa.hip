@@ -588,12 +588,14 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
 // unit's start does not pay its two dependent memory round trips (slot ids,
 // then rows) with the CU otherwise idle: the next unit's slot ids are fetched
 // during the current unit's first chunk and staged after it, its query
-// fragments are fetched after the current unit's last S^T, and its first
-// rows are gathered during the current unit's last chunk.  Rows go straight
-// into LDS (global_load_lds issued from asm, one 1 KiB row per instruction),
-// one chunk ahead; the top of each chunk waits for them explicitly.  A unit
-// whose first rows could not be prefetched (the unit before had a single
-// chunk) gathers them when it starts.
+// fragments are fetched when the current unit finishes, and its first rows
+// are gathered during the current unit's last chunk.  Rows go straight into
+// LDS (global_load_lds issued from asm, one 1 KiB row per instruction), one
+// chunk ahead; the top of each chunk waits for them explicitly.  A unit whose
+// first rows could not be prefetched (the unit before had a single chunk)
+// gathers them when it starts.  Barriers inside the unit loop are LDS-only:
+// a plain barrier would also drain the row gathers and output stores in
+// flight.
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxStaged = 512;  // slot ids of a unit staged in LDS
 
@@ -679,18 +681,20 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
     }
     if (last_good < first_bad) d.nch = max(0, (last_good - d.sbeg + KS) / KS);
   };
-  // rows of chunk c of unit d into buffer b: wave w brings rows RPW w .. +RPW-1
+  // rows of chunk c of unit d into buffer b: wave w brings rows RPW w .. +RPW-1;
+  // the wave's row ids come from one LDS read (lane i holds row i's id)
   auto gather = [&](const G8Unit& d, int c, int b) {
+    const int sl0 = d.sbeg + c * KS + RPW * wave;
+    const int lid = s_ids[d.sb][min(sl0 + lane, d.send - 1) - d.sbeg];
+    const int myid = (lane < RPW && sl0 + lane < d.send) ? lid : -1;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-      const int row = RPW * wave + i;
-      const int sl = d.sbeg + c * KS + row;
-      const int id = __builtin_amdgcn_readfirstlane(sl < d.send ? s_ids[d.sb][sl - d.sbeg] : -1);
+      const int id = __builtin_amdgcn_readlane(myid, i);
       const bf16_t* src = id >= 0 ? d.Cb + (long)id * CD : q;  // -1: finite filler, weight 0
-      const uint32_t base = (uint32_t)(size_t)(lds_char*)&Cs[b][row * CPITCH];
+      const uint32_t base = (uint32_t)(size_t)(lds_char*)&Cs[b][(RPW * wave + i) * CPITCH];
       gather_row_lds(src + 8 * lane, __builtin_amdgcn_readfirstlane(base));
-      if (lane == 0) s_rows[b][row] = id;
     }
+    if (lane < RPW) s_rows[b][RPW * wave + lane] = myid;
   };
   Frag<bf16_t> qf[KSTEPS];
   auto load_q = [&](const G8Unit& d) {
@@ -749,15 +753,25 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       float x[2][4];
       float cm = -INFINITY;
       if (qlive) {
+        // key fragments are read two steps ahead of their MFMAs (the fences
+        // keep the compiler from sinking each read next to its use)
         f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const bf16_t* ka = &Cc[(32 * kh + c16) * CPITCH + 8 * g];
+        Frag<bf16_t> fa[3][2];
+        fa[0][0].load(ka);
+        fa[0][1].load(ka + 16 * CPITCH);
+        fa[1][0].load(ka + 32);
+        fa[1][1].load(ka + 16 * CPITCH + 32);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            Frag<bf16_t> ac;
-            ac.load(&Cc[(32 * kh + 16 * t + c16) * CPITCH + 32 * kk + 8 * g]);
-            mma(acc[t], ac, qf[kk]);
+          if (kk + 2 < KSTEPS) {
+            fa[(kk + 2) % 3][0].load(ka + 32 * (kk + 2));
+            fa[(kk + 2) % 3][1].load(ka + 16 * CPITCH + 32 * (kk + 2));
           }
+          issue_fence();
+          mma(acc[0], fa[kk % 3][0], qf[kk]);
+          mma(acc[1], fa[kk % 3][1], qf[kk]);
+          issue_fence();
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -769,10 +783,6 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
           }
         cm = wave_max_xor_16_32(cm);
         if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
-      }
-      if (ch == cu.nch - 1 && has_nu) {  // the last S^T of this unit: the next unit's query fragments
-        load_q(nu);
-        q_loaded = true;
       }
       // the next unit's slot ids are staged behind this unit's first chunk
       const bool staging = ch == 0 && has_nu;
@@ -823,31 +833,45 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
           }
         }
       }
+      {  // O^T: all P fragments of the chunk first, the transposed C reads two steps ahead
+        constexpr int NSTEP = (KS / 32) * DTPW;
+        Frag<bf16_t> bp[KS / 32][4];
 #pragma unroll
-      for (int kk = 0; kk < KS / 32; ++kk) {
-        Frag<bf16_t> bp[4];
+        for (int kk = 0; kk < KS / 32; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          if (nt < NT) bp[nt].load(&Ps[(16 * nt + c16) * PPITCH + 32 * kk + 8 * g]);
+          for (int nt = 0; nt < 4; ++nt) bp[kk][nt].load(&Ps[(16 * nt + c16) * PPITCH + 32 * kk + 8 * g]);
+        Frag<bf16_t> ac[3];
+        ac[0] = frag_ct<bf16_t>(Cc, CPITCH, 0, (wave * DTPW) * 16, lane);
+        ac[1] = frag_ct<bf16_t>(Cc, CPITCH, 32 * (1 / DTPW), (wave * DTPW + 1 % DTPW) * 16, lane);
 #pragma unroll
-        for (int dt = 0; dt < DTPW; ++dt) {
-          const Frag<bf16_t> ac = frag_ct<bf16_t>(Cc, CPITCH, 32 * kk, (wave * DTPW + dt) * 16, lane);
+        for (int st = 0; st < NSTEP; ++st) {
+          if (st + 2 < NSTEP)
+            ac[(st + 2) % 3] =
+                frag_ct<bf16_t>(Cc, CPITCH, 32 * ((st + 2) / DTPW), (wave * DTPW + (st + 2) % DTPW) * 16, lane);
+          issue_fence();
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt)
-            if (nt < NT) mma(acc_o[dt][nt], ac, bp[nt]);
+            if (nt < NT) mma(acc_o[st % DTPW][nt], ac[st % 3], bp[st / DTPW][nt]);
+          issue_fence();
         }
       }
       bufc ^= 1;
     }
 
-    // ---- finish the unit
+    // ---- finish the unit; the next unit's query fragments go in flight first
+    // (loading them during this unit's last chunk keeps two sets live and
+    // spills registers)
+    if (has_nu) {
+      load_q(nu);
+      q_loaded = true;
+    }
     if (nsplit == 1) {
       if (qlive && kh == 0 && g == 0) {
         s_l[16 * ht + c16] = l_run;
         if (lse && qhead < nh)
           lse[cu.r * nh + qhead] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
       }
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int head = cu.h0 + 16 * nt + c16;
@@ -890,7 +914,7 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       count_chunks(nu);
     }
     cu = nu;
-    __syncthreads();  // s_l, s_ext and the other s_ids buffer are free again
+    lds_barrier();  // s_l, s_ext and the other s_ids buffer are free again
     has_nu = u + stride < nunits;
     nu_staged = false;
     if (has_nu) nu = describe(u + stride, cu.sb ^ 1);
