@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
                                                       TO* __restrict__ Y, long ldy) {
   constexpr int VEC = 16 / sizeof(TI);      // elements per 16-byte load
   constexpr int BK = 128 / sizeof(TI);      // elements per 128-byte slab row
-  constexpr int PITCH = BK + VEC;           // padded LDS row (elements)
+  constexpr int PITCH = BK + 2 * VEC;       // padded LDS row: rows 32 bytes apart, conflict-free fragment reads
   constexpr int CHUNKS = BK / VEC;          // 16-byte chunks per slab row
   constexpr int ROWS_PER_PASS = 256 / CHUNKS;
   constexpr int PASSES = kBM / ROWS_PER_PASS;
@@ -271,8 +271,10 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
 //
 // Copy layout: wave w copies 16-row blocks 2w and 2w+1 of both operands per
 // stage; lane l lands at byte 16 l of its block, i.e. row l/4 and stored
-// chunk l%4, which holds the row's source chunk (l%4) ^ ((l/16)%4).  A
-// fragment read (16 rows, one chunk) then hits 16 distinct 4-bank groups.
+// chunk l%4, which holds the row's source chunk (l%4) ^ ((l/8)%4).  Rows r
+// and r+1 share the XOR term, and pairs of rows differ: measured on this
+// GPU, that reads a fragment (16 rows x 4 chunks of 16 bytes) at the full LDS
+// rate, where the term ((l/16)%4) took about 1.6 times as long.
 // The copies are asm (the compiler does not track them): each wave waits
 // for its own with an explicit vmcnt, then the workgroup meets at a barrier.
 // ---------------------------------------------------------------------------
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, c
 
   // copy sources: rows past M or N repeat the last row (their outputs are not written)
   const int rl = lane >> 2;
-  const int schunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int schunk = (lane & 3) ^ ((lane >> 3) & 3);
   const bf16_t* src[2][2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -347,8 +349,8 @@ __global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, c
     else wait_vm_n<0>();
   };
   // fragment rows: A wm*128 + 16 i + c16, B wn*64 + 16 j + c16; their chunk
-  // g is stored at g ^ ((row / 4) % 4) = g ^ (c16 / 4)
-  const int fchunk = (g ^ (c16 >> 2)) * 8;
+  // g is stored at g ^ ((row / 2) % 4) = g ^ ((c16 / 2) % 4)
+  const int fchunk = (g ^ ((c16 >> 1) & 3)) * 8;
   auto read_frags = [&](int kt, Frag<bf16_t>(&fa)[8], Frag<bf16_t>(&fb)[4]) {
     const bf16_t* As = smem + (kt % S) * STAGE;
     const bf16_t* Bs = As + 256 * kDmaK;

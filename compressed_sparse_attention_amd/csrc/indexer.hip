@@ -87,7 +87,7 @@ constexpr int kStreamWords = kStreamBins / 2;
 // streaming.
 template <typename T, int KK, int NHT, bool STREAM>
 constexpr size_t pf_lds_bytes() {
-  return 2 * (size_t)pf_tile<T, KK>() * (32 * KK + 16 / sizeof(T)) * sizeof(T) +
+  return 2 * (size_t)pf_tile<T, KK>() * (32 * KK + 32 / sizeof(T)) * sizeof(T) +
          (STREAM ? (size_t)pf_waves<T, KK, NHT, STREAM>() * kStreamWords * 4 : 0);
 }
 
@@ -114,7 +114,7 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT, STREAM>())) void indexer
   constexpr int kPfTile = pf_tile<T, KK>();
   constexpr int CI = 32 * KK;
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int PITCH = CI + VEC;  // padded LDS row (elements)
+  constexpr int PITCH = CI + 2 * VEC;  // padded LDS row: rows 32 bytes apart, conflict-free fragment reads
   constexpr int CHUNKS = CI / VEC;
   constexpr int TILE_VECS = kPfTile * CHUNKS;
   static_assert(!STREAM || (pf_fits<T, KK, NHT, STREAM>() && kPfTokPerWave == 1), "streaming layout");
@@ -171,7 +171,7 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT, STREAM>())) void indexer
       const int head = 16 * mt + c16;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        qa[tt][mt][kk].load_clamped(qI + (t * nhI + head) * CI + g * 8 * KK + 8 * kk, live && head < nhI, qI);
+        qa[tt][mt][kk].load_clamped(qI + (t * nhI + head) * CI + 32 * kk + 8 * g, live && head < nhI, qI);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int h = 16 * mt + 4 * g + rr;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT, STREAM>())) void indexer
       Frag<T> kb[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kb[kk].load(&Ks[cur][(grp * 16 + c16) * PITCH + g * 8 * KK + 8 * kk]);
+        kb[kk].load(&Ks[cur][(grp * 16 + c16) * PITCH + 32 * kk + 8 * g]);
 #pragma unroll
       for (int tt = 0; tt < kPfTokPerWave; ++tt) {
         float part = 0.f;

@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   constexpr int CD = 64 * DTW;  // head dim c
   constexpr int KS = group_chunk<T, DTW>();
   constexpr int VEC = 16 / sizeof(T);
-  constexpr int CPITCH = CD + VEC;
-  constexpr int PPITCH = KS + VEC;
+  constexpr int CPITCH = CD + 2 * VEC;  // rows staggered by 32 bytes: conflict-free 16-byte fragment reads
+  constexpr int PPITCH = KS + 2 * VEC;
   constexpr int KSTEPS = CD / 32;
   constexpr int VPF = sizeof(T) == 2 ? 4 : 8;          // VGPRs per fragment
   constexpr bool QREG = KSTEPS * VPF <= 64;             // keep the query fragments in registers
@@ -319,8 +319,8 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
                                                          float* __restrict__ part_ml) {
   constexpr int CD = 64 * DTW;
   constexpr int KS = kG8Chunk;
-  constexpr int CPITCH = CD + 8;
-  constexpr int PPITCH = KS + 8;
+  constexpr int CPITCH = CD + 16;  // rows staggered by 32 bytes: conflict-free 16-byte fragment reads
+  constexpr int PPITCH = KS + 16;
   constexpr int KSTEPS = CD / 32;
   constexpr int DTPW = CD / 16 / 8;  // output 16-dim tiles per wave
   constexpr int RPW = KS / 8;        // rows gathered per wave per chunk
@@ -616,8 +616,8 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
                                                          float* __restrict__ part_ml) {
   constexpr int CD = 512;
   constexpr int KS = kG8Chunk;
-  constexpr int CPITCH = CD + 8;
-  constexpr int PPITCH = KS + 8;
+  constexpr int CPITCH = CD + 16;  // rows staggered by 32 bytes: conflict-free 16-byte fragment reads
+  constexpr int PPITCH = KS + 16;
   constexpr int KSTEPS = CD / 32;
   constexpr int DTPW = CD / 16 / 8;
   constexpr int RPW = KS / 8;  // rows gathered per wave per chunk
@@ -943,8 +943,8 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
                                                        float* __restrict__ part_o,
                                                        float* __restrict__ part_ml) {
   constexpr int CD = 64 * DTW;
-  constexpr int CPITCH = CD + 8;
-  constexpr int PPITCH = kTileRows + 8;
+  constexpr int CPITCH = CD + 16;  // rows staggered by 32 bytes: conflict-free 16-byte fragment reads
+  constexpr int PPITCH = kTileRows + 16;
   constexpr int KSTEPS = CD / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Cs[kTileRows * CPITCH];
   __shared__ __attribute__((aligned(16))) bf16_t Ps[16 * PPITCH];
