@@ -595,7 +595,9 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
 // first rows could not be prefetched (the unit before had a single chunk)
 // gathers them when it starts.  Barriers inside the unit loop are LDS-only:
 // a plain barrier would also drain the row gathers and output stores in
-// flight.
+// flight.  The next chunk's rows are requested one row per two k-steps of
+// S^T: issued at once, a wave's eight direct-to-LDS loads stalled it for
+// about 1200 cycles per chunk while the address path took them in.
 // ---------------------------------------------------------------------------
 constexpr int kStreamMaxStaged = 512;  // slot ids of a unit staged in LDS
 
@@ -629,6 +631,7 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
   __shared__ float s_l[kHG];
   __shared__ int32_t s_ids[2][kStreamMaxStaged];
   __shared__ int s_ext[2][8];
+  __shared__ int s_flag[8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -742,20 +745,36 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       // the next chunk goes in flight into the other buffer (free: chunk
       // ch - 1 was read before the barrier); the next unit's slot ids are
       // requested once this unit has started
-      if (ch + 1 < cu.nch) {
-        gather(cu, ch + 1, cur ^ 1);
-      } else if (has_nu && nu_staged && nu.nch > 0) {
-        gather(nu, 0, cur ^ 1);
-        first_in_buf = true;
-      }
+      const bool g_cur = ch + 1 < cu.nch;
+      const bool g_any = g_cur || (has_nu && nu_staged && nu.nch > 0);
+      if (!g_cur && g_any) first_in_buf = true;
       if (ch == 0 && has_nu) fetch_ids(nu);
+      // row ids of the chunk to gather (lane i holds row i's), one LDS read
+      const int g_sb = g_cur ? cu.sb : nu.sb, g_sbeg = g_cur ? cu.sbeg : nu.sbeg;
+      const int g_send = g_cur ? cu.send : nu.send;
+      const int g_sl0 = (g_cur ? cu.sbeg + (ch + 1) * KS : nu.sbeg) + RPW * wave;
+      const bf16_t* gCb = g_cur ? cu.Cb : nu.Cb;
+      int gid = -1;
+      if (g_any) {
+        const int lid = s_ids[g_sb][min(g_sl0 + lane, g_send - 1) - g_sbeg];
+        gid = (lane < RPW && g_sl0 + lane < g_send) ? lid : -1;
+        if (lane < RPW) s_rows[cur ^ 1][RPW * wave + lane] = gid;
+      }
+      auto gissue = [&](int i) {
+        const int id = __builtin_amdgcn_readlane(gid, i);
+        const bf16_t* src = id >= 0 ? gCb + (long)id * CD : q;  // -1: finite filler, weight 0
+        const uint32_t base = (uint32_t)(size_t)(lds_char*)&Cs[cur ^ 1][(RPW * wave + i) * CPITCH];
+        gather_row_lds(src + 8 * lane, __builtin_amdgcn_readfirstlane(base));
+      };
       const bf16_t* Cc = Cs[cur];
       float x[2][4];
       float cm = -INFINITY;
-      if (qlive) {
-        // key fragments are read two steps ahead of their MFMAs (the fences
-        // keep the compiler from sinking each read next to its use)
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      // S^T (every wave, also over a head tile past nh: its results are
+      // discarded): key fragments are read two steps ahead of their MFMAs
+      // (the fences keep the compiler from sinking each read next to its
+      // use), and one row of the next chunk is gathered every two steps
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      {
         const bf16_t* ka = &Cc[(32 * kh + c16) * CPITCH + 8 * g];
         Frag<bf16_t> fa[3][2];
         fa[0][0].load(ka);
@@ -764,6 +783,7 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
         fa[1][1].load(ka + 16 * CPITCH + 32);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
+          if ((kk & 1) == 0 && g_any) gissue(kk >> 1);
           if (kk + 2 < KSTEPS) {
             fa[(kk + 2) % 3][0].load(ka + 32 * (kk + 2));
             fa[(kk + 2) % 3][1].load(ka + 16 * CPITCH + 32 * (kk + 2));
@@ -773,6 +793,8 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
           mma(acc[1], fa[kk % 3][1], qf[kk]);
           issue_fence();
         }
+      }
+      if (qlive) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -782,8 +804,37 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
             cm = fmaxf(cm, x[t][rr]);
           }
         cm = wave_max_xor_16_32(cm);
-        if (g == 0) s_red[0][kh][16 * ht + c16] = cm;
       }
+      // Numerators against the running reference maximum m_run.  Lazy
+      // rescaling: m_run moves only when a chunk's maximum exceeds it by more
+      // than 2^8 (so the exponentials stay below 256, exact in the fp32 sums
+      // and within bf16's range), decided per head from both key halves'
+      // maxima.  A wave that sees one of its heads exceed (or the unit's
+      // first chunk) raises a flag; only then do the waves exchange maxima
+      // and redo their numerators against the moved references, so most
+      // chunks need one barrier here instead of two.
+      const int hl = 16 * ht + c16;
+      auto numerators = [&](float mref) {
+        const bool none = (mref == -INFINITY);
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float p[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            p[rr] = none ? 0.f : exp2_fast(x[t][rr] - mref);
+            ps += p[rr];
+          }
+          *reinterpret_cast<uint2*>(&Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g]) =
+              make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+        }
+        ps = wave_sum_xor_16_32(ps);
+        if (g == 0) s_red[1][kh][hl] = ps;
+      };
+      const bool moves = qlive && (m_run == -INFINITY || cm > m_run + 8.f);
+      if (qlive) numerators(m_run);
+      const bool wave_moves = __ballot(moves) != 0;
+      if (lane == 0) s_flag[wave] = wave_moves;
       // the next unit's slot ids are staged behind this unit's first chunk
       const bool staging = ch == 0 && has_nu;
       if (staging) stage_ids(nu);
@@ -792,44 +843,33 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
         count_chunks(nu);
         nu_staged = true;
       }
+      bool any_moves = false;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) any_moves |= s_flag[w] != 0;
       float alpha = 1.f;
-      if (qlive) {
-        const int hl = 16 * ht + c16;
-        const float cmax = fmaxf(s_red[0][0][hl], s_red[0][1][hl]);
-        const float m_new = (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
-        const bool none = (m_new == -INFINITY);
-        alpha = none ? 1.f : exp2_fast(m_run - m_new);
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float p[4];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            p[rr] = none ? 0.f : exp2_fast(x[t][rr] - m_new);
-            ps += p[rr];
-          }
-          *reinterpret_cast<uint2*>(&Ps[hl * PPITCH + 32 * kh + 16 * t + 4 * g]) =
-              make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+      if (any_moves) {
+        if (qlive && g == 0) s_red[0][kh][hl] = cm;
+        lds_barrier();
+        if (qlive) {
+          const float cmax = fmaxf(s_red[0][0][hl], s_red[0][1][hl]);
+          const float m_new = (m_run == -INFINITY || cmax > m_run + 8.f) ? fmaxf(m_run, cmax) : m_run;
+          alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+          numerators(m_new);
+          if (g == 0 && kh == 0) s_alpha[hl] = alpha;
+          m_run = m_new;
         }
-        ps = wave_sum_xor_16_32(ps);
-        if (g == 0) {
-          s_red[1][kh][hl] = ps;
-          if (kh == 0) s_alpha[hl] = alpha;
-        }
-        m_run = m_new;
+        lds_barrier();
       }
-      lds_barrier();
-      if (qlive) {
-        const int hl = 16 * ht + c16;
-        l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
-      }
+      if (qlive) l_run = l_run * alpha + s_red[1][0][hl] + s_red[1][1][hl];
+      if (any_moves) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        if (nt < NT) {
-          const float a = s_alpha[16 * nt + c16];
-          if (__builtin_amdgcn_read_exec() & __ballot(a != 1.f)) {
+        for (int nt = 0; nt < 4; ++nt) {
+          if (nt < NT) {
+            const float a = s_alpha[16 * nt + c16];
+            if (__builtin_amdgcn_read_exec() & __ballot(a != 1.f)) {  // some head of this tile moved its maximum
 #pragma unroll
-            for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+              for (int dt = 0; dt < DTPW; ++dt) acc_o[dt][nt] *= a;
+            }
           }
         }
       }
