@@ -1130,11 +1130,18 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
     if (wave == 0 && g == 0 && lse)
       lse[r * nh + head] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   } else {
+    // the split's output normalised by its own sum, in bf16 (half the bytes
+    // of the raw fp32 accumulators; the merge weights it by l_run again)
     const long pb = u * nh + head;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    bf16_t* po = reinterpret_cast<bf16_t*>(part_o);
 #pragma unroll
-    for (int dt = 0; dt < DTW; ++dt)
-      *reinterpret_cast<float4*>(part_o + pb * CD + (wave * DTW + dt) * 16 + 4 * g) =
-          make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    for (int dt = 0; dt < DTW; ++dt) {
+      float v[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) v[rr] = acc_o[dt][rr] * inv;
+      store4<bf16_t>(po + pb * CD + (wave * DTW + dt) * 16 + 4 * g, v);
+    }
     if (wave == 0 && g == 0) {
       part_ml[pb * 2] = m_run;
       part_ml[pb * 2 + 1] = l_run;
@@ -1142,9 +1149,11 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
   }
 }
 
-template <typename T>
+// Partials PT: float = the splits' raw accumulators; bf16_t = each split's
+// output already divided by its own sum.
+template <typename T, typename PT>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, int c, int nsplit,
-                                                          const float* __restrict__ part_o,
+                                                          const PT* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           T* __restrict__ o, float* __restrict__ lse) {
   constexpr int U = 8;  // splits whose loads are in flight together
@@ -1168,7 +1177,13 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
     for (int u = 0; u < U; ++u) {
       const long b = b0 + (long)(j0 + u < nsplit ? j0 + u : 0) * nh;  // always in bounds
       ml[u] = *reinterpret_cast<const float2*>(part_ml + b * 2);
-      po[u] = *reinterpret_cast<const float4*>(part_o + b * c + d4);
+      if constexpr (sizeof(PT) == 4) {
+        po[u] = *reinterpret_cast<const float4*>(part_o + b * c + d4);
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(part_o + b * c + d4);
+        po[u] = make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u));
+      }
     }
     issue_fence();
     float mb = M;
@@ -1184,10 +1199,11 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
     for (int u = 0; u < U; ++u) {
       const float wgt = (j0 + u >= nsplit || ml[u].x == -INFINITY) ? 0.f : exp2_fast(ml[u].x - mb);
       L = fmaf(ml[u].y, wgt, L);
-      acc[0] = fmaf(wgt, po[u].x, acc[0]);
-      acc[1] = fmaf(wgt, po[u].y, acc[1]);
-      acc[2] = fmaf(wgt, po[u].z, acc[2]);
-      acc[3] = fmaf(wgt, po[u].w, acc[3]);
+      const float wo = sizeof(PT) == 4 ? wgt : wgt * ml[u].y;
+      acc[0] = fmaf(wo, po[u].x, acc[0]);
+      acc[1] = fmaf(wo, po[u].y, acc[1]);
+      acc[2] = fmaf(wo, po[u].z, acc[2]);
+      acc[3] = fmaf(wo, po[u].w, acc[3]);
     }
     M = mb;
   }
@@ -1285,8 +1301,12 @@ hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C
                lse, part_o, part_ml);
   if (e != hipSuccess || p.nsplit == 1) return e;
   const long threads = nq * nh * (64 * DTW / 4);
-  return launch("mqa_combine", mqa_combine_kernel<T>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                nq, nh, 64 * DTW, p.nsplit, (const float*)part_o, (const float*)part_ml, (T*)o, lse);
+  const dim3 cgrid((unsigned)((threads + 255) / 256));
+  if (p.tile)  // the tile kernel leaves normalised bf16 partials
+    return launch("mqa_combine", mqa_combine_kernel<T, bf16_t>, cgrid, dim3(256), 0, s, nq, nh, 64 * DTW, p.nsplit,
+                  (const bf16_t*)part_o, (const float*)part_ml, (T*)o, lse);
+  return launch("mqa_combine", mqa_combine_kernel<T, float>, cgrid, dim3(256), 0, s, nq, nh, 64 * DTW, p.nsplit,
+                (const float*)part_o, (const float*)part_ml, (T*)o, lse);
 }
 
 template <typename T>
