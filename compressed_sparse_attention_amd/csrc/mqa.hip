@@ -699,7 +699,21 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
     }
     if (lane < RPW) s_rows[b][RPW * wave + lane] = myid;
   };
+  // the unit's 64 query rows (one 1 KiB row per head) into buffer bf, eight per wave
+  auto stage_q = [&](const G8Unit& d, int bf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * wave + i;
+      const int head = min(d.h0 + row, nh - 1);  // heads past nh: finite filler, never stored
+      const uint32_t base = (uint32_t)(size_t)(lds_char*)&Cs[bf][row * CPITCH];
+      gather_row_lds(q + (d.r * nh + head) * CD + 8 * lane, __builtin_amdgcn_readfirstlane(base));
+    }
+  };
   Frag<bf16_t> qf[KSTEPS];
+  auto read_q = [&](int bf) {
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qf[kk].load(&Cs[bf][(16 * ht + c16) * CPITCH + 32 * kk + 8 * g]);
+  };
   auto load_q = [&](const G8Unit& d) {
     const int qhead = d.h0 + 16 * ht + c16;
 #pragma unroll
@@ -718,11 +732,12 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
   if (has_nu) nu = describe(u + stride, 1);
   load_q(cu);
   bool q_loaded = true;
+  bool q_lds = false;  // the current unit's query rows wait in the other row buffer
   int bufc = 0;
   bool first_in_buf = false;  // the current unit's chunk 0 is already in Cs[bufc] (or in flight to it)
 
   while (true) {
-    if (!q_loaded) load_q(cu);
+    if (!q_loaded && !q_lds) load_q(cu);
     q_loaded = false;
     if (cu.nch > 0 && !first_in_buf) gather(cu, 0, bufc);
     first_in_buf = false;
@@ -742,6 +757,11 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       // them) have landed; after the barrier, every wave's have
       wait_stores();
       lds_barrier();
+      if (q_lds) {  // (chunk 0) fragments from the staged rows, read before chunk 1's rows replace them
+        read_q(cur ^ 1);
+        lds_barrier();
+        q_lds = false;
+      }
       // the next chunk goes in flight into the other buffer (free: chunk
       // ch - 1 was read before the barrier); the next unit's slot ids are
       // requested once this unit has started
@@ -898,13 +918,11 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       bufc ^= 1;
     }
 
-    // ---- finish the unit; the next unit's query fragments go in flight first
-    // (loading them during this unit's last chunk keeps two sets live and
-    // spills registers)
-    if (has_nu) {
-      load_q(nu);
-      q_loaded = true;
-    }
+    // ---- finish the unit.  After the barrier every wave is done with this
+    // unit's last rows, and the next unit's query rows go into their buffer
+    // (one copy of each row, where fragment loads per wave fetched every
+    // head tile's rows twice).
+    q_lds = false;
     if (nsplit == 1) {
       if (qlive && kh == 0 && g == 0) {
         s_l[16 * ht + c16] = l_run;
@@ -912,6 +930,10 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
           lse[cu.r * nh + qhead] = (l_run > 0.f) ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
       }
       lds_barrier();
+      if (has_nu) {
+        stage_q(nu, bufc ^ 1);
+        q_lds = true;
+      }
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int head = cu.h0 + 16 * nt + c16;
@@ -928,6 +950,11 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
         }
       }
     } else {
+      lds_barrier();
+      if (has_nu) {
+        stage_q(nu, bufc ^ 1);
+        q_lds = true;
+      }
       const long pbase = (cu.r * nsplit + cu.j) * (long)nh;
       if (qlive && kh == 0 && g == 0 && qhead < nh) {
         part_ml[(pbase + qhead) * 2] = m_run;
@@ -954,7 +981,10 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
       count_chunks(nu);
     }
     cu = nu;
-    lds_barrier();  // s_l, s_ext and the other s_ids buffer are free again
+    // s_l, s_ext and the other s_ids buffer are next written after the next
+    // unit's first chunk barrier; a unit without chunks has none, and would
+    // write s_l while waves still read it for this unit's stores
+    if (cu.nch == 0) lds_barrier();
     has_nu = u + stride < nunits;
     nu_staged = false;
     if (has_nu) nu = describe(u + stride, cu.sb ^ 1);
