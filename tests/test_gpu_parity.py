@@ -551,6 +551,7 @@ def test_index_topk_stream_same_sets_as_dense():
     # long batch, c = 512, a partial head group (20 heads) and k not a multiple of the 64-slot chunk
     ("bf16", 600, 20, 512, 96, 120, 2.0, "scatter"),
     ("bf16", 530, 100, 512, 200, 250, 4.0, "ragged"),  # two head groups, the second partial
+    ("bf16", 520, 192, 512, 128, 200, 2.0, "ragged"),  # three head groups of one query in different workgroups
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
     rng = synth.rng_for(B * nh + k)
