@@ -102,8 +102,9 @@ bool use_lists(long n_queries, long max_cand) {
 //   counts [n_queries, P, 2]                 uint32   (use_lists)
 //   gt     [n_queries, P, min(kMChunk, k)]   uint64   (use_lists)
 //   eq     [n_queries, P, kMChunk]           uint64   (use_lists)
+//   b1g1   [n_queries, 2]                    uint32   (use_lists; the decode path that finishes rows in the MQA)
 struct IndexWs {
-  size_t scores = 0, hist = 0, arrive = 0, counts = 0, gt = 0, eq = 0, total = 0;
+  size_t scores = 0, hist = 0, arrive = 0, counts = 0, gt = 0, eq = 0, b1g1 = 0, total = 0;
 };
 IndexWs index_ws(long n_queries, long max_cand, int k) {
   using csa::ws_add;
@@ -126,6 +127,8 @@ IndexWs index_ws(long n_queries, long max_cand, int k) {
     at = ws_align(ws_add(at, ws_bytes(n_queries, P, gtc, sizeof(uint64_t))));
     w.eq = at;
     at = ws_align(ws_add(at, ws_bytes(n_queries, P, csa::kMChunk, sizeof(uint64_t))));
+    w.b1g1 = at;
+    at = ws_align(ws_add(at, ws_bytes(n_queries, 2 * sizeof(uint32_t))));
   }
   w.total = at;
   return w;
@@ -474,11 +477,17 @@ csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t
 
 namespace {
 // csa_index_topk; `clear` zeroes the histogram and arrival counters first
-// (csa_decode relies on the selectors leaving them zero instead).
+// (csa_decode relies on the selectors leaving them zero instead).  With
+// `classified` not null, rows on the multi-workgroup path are only
+// classified (TopkLists::b1g1) and *classified describes their lists, for
+// the attention to finish them; classified->b1g1 stays null when the batch
+// takes another path (the selection is then complete on return).
 csa_status index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t m, int32_t k,
                       const void* qI, const float* wI, const void* KIcomp, const int32_t* q_seq,
                       const int64_t* q_pos, const int64_t* kv_offset, int64_t max_cand, int32_t* idx_out,
-                      float* score_out, void* workspace, size_t ws_bytes, void* stream, bool clear) {
+                      float* score_out, void* workspace, size_t ws_bytes, void* stream, bool clear,
+                      csa::TopkLists* classified = nullptr) {
+  if (classified) *classified = csa::TopkLists{};
   CSA_REQUIRE(dtype_ok(dt), "csa_index_topk: unknown dtype");
   CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_index_topk: bad n_queries");
   CSA_REQUIRE(n_hI >= 1 && n_hI <= 64, "csa_index_topk: n_hI must be in [1, 64] (got %d)", n_hI);
@@ -524,13 +533,19 @@ csa_status index_topk(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
     lists.eq = (uint64_t*)(ws + w.eq);
     lists.P = topk_chunks(max_cand);
     lists.gtc = k < csa::kMChunk ? k : csa::kMChunk;
+    if (classified) {
+      lists.b1g1 = (uint32_t*)(ws + w.b1g1);
+      lists.hist = hist;
+    }
   }
   hipError_t e = csa::launch_indexer(dt, n_queries, n_hI, cI, m, qI, wI, KIcomp, q_seq, q_pos, kv_offset,
                                      max_cand, scores, ld, hist, k, s);
   if (e != hipSuccess) return hip_fail(e, "csa_index_topk indexer launch");
   e = csa::launch_topk(n_queries, m, scores, ld, q_pos, max_cand, k, hist, multi ? &lists : nullptr, idx_out,
                        score_out, s);
-  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_index_topk top-k launch");
+  if (e != hipSuccess) return hip_fail(e, "csa_index_topk top-k launch");
+  if (classified && lists.b1g1) *classified = lists;
+  return CSA_OK;
 }
 
 }  // namespace
@@ -608,10 +623,14 @@ csa_status csa_sparse_mqa_workspace(int64_t n_queries, int32_t n_h, int32_t c, i
   return CSA_OK;
 }
 
-csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
-                          float scale, const void* q, const void* Ccomp, const int32_t* q_seq,
-                          const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
-                          void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// csa_sparse_mqa; sel: see csa::TileSelect (csa_decode only)
+csa_status sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k, float scale,
+                      const void* q, const void* Ccomp, const int32_t* q_seq, const int64_t* kv_offset,
+                      const int32_t* idx, void* o, float* lse, void* workspace, size_t ws_bytes, void* stream,
+                      const csa::TileSelect* sel) {
   CSA_REQUIRE(dtype_ok(dt), "csa_sparse_mqa: unknown dtype");
   CSA_REQUIRE(n_queries >= 0 && n_queries <= 0x7FFFFFFF, "csa_sparse_mqa: bad n_queries");
   CSA_REQUIRE(n_h >= 1 && n_h <= 256, "csa_sparse_mqa: n_h must be in [1, 256] (got %d)", n_h);
@@ -630,8 +649,39 @@ csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t 
   csa_status st = check_device();
   if (st != CSA_OK) return st;
   hipError_t e = csa::launch_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx, o, lse,
-                                 workspace, (hipStream_t)stream);
+                                 workspace, (hipStream_t)stream, sel);
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_sparse_mqa launch");
+}
+
+// The two stages of csa_decode / csa_decode_noalloc on a workspace laid out
+// as [index_topk part | a | MQA part].  Where the attention can finish the
+// selection (csa::mqa_tile_selects, and the batch takes the top-k's
+// multi-workgroup path) the top-k launch only classifies, and the attention
+// resolves each row's threshold itself (csa::TileSelect).
+csa_status decode_stages(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c,
+                         int32_t m, int32_t k, float scale, const void* qI, const float* wI, const void* KIcomp,
+                         const void* q, const void* Ccomp, const int32_t* q_seq, const int64_t* q_pos,
+                         const int64_t* kv_offset, int64_t max_cand, int32_t* idx_out, float* score_out, void* o,
+                         float* lse, char* ws, size_t a, size_t ws_bytes, void* stream, bool clear) {
+  const bool fuse = csa::mqa_tile_selects(n_queries, n_h, c, k, dt == CSA_BF16);
+  csa::TopkLists lists{};
+  csa_status st = index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand,
+                             idx_out, score_out, ws, a, stream, clear, fuse ? &lists : nullptr);
+  if (st != CSA_OK) return st;
+  csa::TileSelect sel{m, q_pos, max_cand, lists, idx_out, score_out};
+  return sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
+                    ws ? ws + a : nullptr, ws_bytes - a, stream, lists.b1g1 ? &sel : nullptr);
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_sparse_mqa(csa_dtype dt, int64_t n_queries, int32_t n_h, int32_t c, int32_t k,
+                          float scale, const void* q, const void* Ccomp, const int32_t* q_seq,
+                          const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  return sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx, o, lse, workspace, ws_bytes,
+                    stream, nullptr);
 }
 
 csa_status csa_sparse_mqa_backward_workspace(int64_t n_queries, int32_t n_h, int32_t c, int32_t k, int64_t n_rows,
@@ -756,11 +806,8 @@ csa_status csa_decode(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI,
     return fail(CSA_ERR_WORKSPACE, "csa_decode: workspace needs %zu bytes (got %zu)", need, ws_bytes);
   csa_index_topk_workspace(n_queries, max_cand, n_hI, k, &a);
   a = align256(a);
-  st = index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand, idx_out,
-                  score_out, workspace, a, stream, false);
-  if (st != CSA_OK) return st;
-  return csa_sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
-                        workspace ? (char*)workspace + a : nullptr, ws_bytes - a, stream);
+  return decode_stages(dt, n_queries, n_hI, cI, n_h, c, m, k, scale, qI, wI, KIcomp, q, Ccomp, q_seq, q_pos,
+                       kv_offset, max_cand, idx_out, score_out, o, lse, (char*)workspace, a, ws_bytes, stream, false);
 }
 
 csa_status csa_decode_noalloc(csa_dtype dt, int64_t n_queries, int32_t n_hI, int32_t cI, int32_t n_h, int32_t c,
@@ -790,11 +837,8 @@ csa_status csa_decode_noalloc(csa_dtype dt, int64_t n_queries, int32_t n_hI, int
   // the scratch keeps whatever the last call left, laid out for that call's
   // sizes: the selection clears its histogram and counters first (a kernel,
   // not a memset)
-  st = index_topk(dt, n_queries, n_hI, cI, m, k, qI, wI, KIcomp, q_seq, q_pos, kv_offset, max_cand, idx_out,
-                  score_out, ws, a, stream, true);
-  if (st != CSA_OK) return st;
-  return csa_sparse_mqa(dt, n_queries, n_h, c, k, scale, q, Ccomp, q_seq, kv_offset, idx_out, o, lse,
-                        (char*)ws + a, b, stream);
+  return decode_stages(dt, n_queries, n_hI, cI, n_h, c, m, k, scale, qI, wI, KIcomp, q, Ccomp, q_seq, q_pos,
+                       kv_offset, max_cand, idx_out, score_out, o, lse, (char*)ws, a, a + b, stream, true);
 }
 
 csa_status csa_compress_varlen(csa_dtype dt, int64_t n_seqs, int32_t m, int32_t c, const void* Ca, const void* Cb,

@@ -150,6 +150,25 @@ struct TopkLists {
   uint64_t* eq;      // [n_queries, P, kMChunk]
   int P;             // chunks per row: ceil(max_cand / kMChunk)
   int gtc;           // min(kMChunk, k)
+  // Not null: the chunk workgroups only classify and publish their lists
+  // and each row's (b1, g1) here ([n_queries, 2]); the rows are finished by
+  // the decode attention (TileSelect), which also clears `hist`.  Rows with
+  // at most k candidates are still written out whole by the top-k launch.
+  uint32_t* b1g1 = nullptr;
+  uint32_t* hist = nullptr;  // the level-1 histograms the lists were classified with
+};
+
+// The decode attention finishing the selection itself (see TopkLists::b1g1):
+// every workgroup of the short-batch MQA kernel resolves its query's
+// threshold from the published lists, takes the slots of its own split and
+// writes them (workgroups of head tile 0) to idx_out / score_out.
+struct TileSelect {
+  int m;
+  const int64_t* q_pos;
+  long max_cand;
+  TopkLists lists;
+  int32_t* idx_out;
+  float* score_out;  // nullable
 };
 
 // Eq 9 selection per row of `scores`; `hist` (nullable) is the level-1
@@ -161,10 +180,14 @@ hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
 
 bool mqa_supported_c(int c);
 size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16);
+// sel (nullable; only where mqa_tile_selects): the attention finishes the
+// selection of rows whose top-k launch only classified them (TileSelect);
+// idx must then be sel->idx_out.
+bool mqa_tile_selects(long n_queries, int nh, int c, int k, bool bf16);
 hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float scale,
                       const void* q, const void* C, const int32_t* q_seq,
                       const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
-                      void* workspace, hipStream_t s);
+                      void* workspace, hipStream_t s, const TileSelect* sel = nullptr);
 
 // Backward of eq 11 (see csa_sparse_mqa_backward): bf16, c = 512.
 size_t mqa_backward_workspace_bytes(long n_queries, int nh, int k, long rows);

@@ -25,6 +25,7 @@
 // head, and the combine kernel merges the splits by log-sum-exp.
 #include "common.hpp"
 #include "internal.hpp"
+#include "select.hpp"
 
 #include <algorithm>
 
@@ -1002,7 +1003,16 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
 // ---------------------------------------------------------------------------
 constexpr int kTileRows = 128;
 
-template <int DTW>
+// SEL (c = 512, one 128-slot chunk per split): the selection of eq 9 is
+// finished here rather than by the top-k launch, which only classified each
+// row's chunks (TopkLists::b1g1).  Every workgroup resolves its query's
+// threshold from the published lists (the top-k's finishing phase, LDS taken
+// from the row-tile buffer before any row is gathered) but keeps only the
+// slots of its own split; the workgroups of head tile 0 also write those
+// slots to idx_out / score_out, and the one of split 0 clears the query's
+// level-1 histogram for the next call.  The query's heads are loaded first,
+// so their round trip overlaps the selection.
+template <int DTW, bool SEL>
 __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, int nht, int nsplit, int cps,
                                                        float scale_log2, const bf16_t* __restrict__ q,
                                                        const bf16_t* __restrict__ C,
@@ -1011,7 +1021,7 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
                                                        const int32_t* __restrict__ idx,
                                                        bf16_t* __restrict__ o, float* __restrict__ lse,
                                                        float* __restrict__ part_o,
-                                                       float* __restrict__ part_ml) {
+                                                       float* __restrict__ part_ml, TileSelect sel) {
   constexpr int CD = 64 * DTW;
   constexpr int CPITCH = CD + 16;  // rows staggered by 32 bytes: conflict-free 16-byte fragment reads
   constexpr int PPITCH = kTileRows + 16;
@@ -1021,6 +1031,7 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
   __shared__ int32_t s_rows[kTileRows];
   __shared__ float s_red[2][4][16];
   __shared__ __attribute__((aligned(16))) bf16_t s_q[16 * CPITCH];  // the tile's 16 query heads
+  __shared__ int32_t s_win[SEL ? kTileRows : 1];                      // SEL: this split's selection slots
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1039,9 +1050,25 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
   const long off = kv_off ? kv_off[seq] : 0;
 
   // the first chunk's row ids are loaded before the query fragments: the
-  // gather depends on them, the fragments are needed only after it
+  // gather depends on them, the fragments are needed only after it (SEL:
+  // every load the selection starts with -- the query's position, b1 and
+  // g1, the chunk counts and the first list entries -- goes out first, in
+  // one round trip)
   const int slot_first = (j * cps) * kTileRows + (kTileRows / 4) * wave + lane;
-  int raw_first = idx[r * k + (slot_first < k ? slot_first : k - 1)];
+  int raw_first = 0;
+  FinishPrefetch pf;
+  long sel_pos = 0;
+  uint32_t sel_b1 = 0, sel_g1 = 0;
+  if constexpr (SEL) {
+    const int P = sel.lists.P, gtc = sel.lists.gtc;
+    finish_prefetch<256, false>(pf, P, sel.lists.counts + r * P * 2, sel.lists.gt + r * P * (long)gtc, gtc,
+                                sel.lists.eq + r * P * (long)kMChunk, kMChunk);
+    sel_pos = sel.q_pos[r];
+    sel_b1 = sel.lists.b1g1[2 * r];
+    sel_g1 = sel.lists.b1g1[2 * r + 1];
+  } else {
+    raw_first = idx[r * k + (slot_first < k ? slot_first : k - 1)];
+  }
   // the tile's 16 query heads: each wave stages 4 of them in LDS (16-byte
   // pieces).  The pieces are loaded here but written to LDS only after the
   // first chunk's gather has been issued, so that their round trip overlaps
@@ -1055,6 +1082,38 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
     const int hl = 4 * wave + v / QCH, pc = (v % QCH) * 8;
     const int hh = 16 * ht + hl;
     qv[i] = load16_clamped(q + (r * nh + hh) * CD + pc, v < 4 * QCH && hh < nh, q);
+  }
+  if constexpr (SEL) {
+    static_assert(sizeof(FinishSmem<256>) <= sizeof(Cs), "the selection's LDS lives in the row-tile buffer");
+    const uint32_t s0 = (uint32_t)(j * kTileRows), s1 = (uint32_t)min(k, (j + 1) * kTileRows);
+    const long pos = sel_pos;
+    long ncl = pos > 0 ? pos / sel.m : 0;
+    ncl = ncl < sel.max_cand ? ncl : sel.max_cand;
+    if (tid < kTileRows) s_win[tid] = (ncl <= k && s0 + tid < (uint32_t)ncl) ? (int32_t)(s0 + tid) : -1;
+    __syncthreads();
+    if (ncl > k) {  // uniform: rows of at most k candidates keep all of them (the top-k launch wrote them out)
+      const int P = sel.lists.P, gtc = sel.lists.gtc;
+      const int Pr = (int)((ncl + kMChunk - 1) / kMChunk);
+      const uint32_t b1 = sel_b1, g1 = sel_g1;
+      FinishSmem<256>& fs = *reinterpret_cast<FinishSmem<256>*>(Cs);
+      int32_t* out = sel.idx_out + r * k;
+      float* sout = sel.score_out ? sel.score_out + r * k : nullptr;
+      finish_row<256, false>(fs, pf, P, Pr, k, b1, g1, sel.lists.counts + r * P * 2, sel.lists.gt + r * P * (long)gtc, gtc,
+                      sel.lists.eq + r * P * (long)kMChunk, kMChunk, s0, s1,
+                      [&](uint32_t slot, uint32_t i, float sc) {
+                        s_win[slot - s0] = (int32_t)i;
+                        if (ht == 0) {
+                          out[slot] = (int32_t)i;
+                          if (sout) sout[slot] = sc;
+                        }
+                      });
+      if (ht == 0 && j == 0) {  // every chunk workgroup of the top-k launch has read it
+        u32x4* h = reinterpret_cast<u32x4*>(sel.lists.hist + r * kL1Bins);
+        for (int b = tid; b < kL1Bins / 4; b += 256) h[b] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    __syncthreads();  // s_win complete; the row-tile buffer is free again
+    raw_first = s_win[lane < kTileRows / 4 ? (kTileRows / 4) * wave + lane : 0];
   }
   Frag<bf16_t> qf[KSTEPS];
 
@@ -1295,7 +1354,7 @@ Plan plan(long nq, int nh, int c, int k, bool bf16) {
 template <typename T, int DTW>
 hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C,
                const int32_t* q_seq, const int64_t* kv_off, const int32_t* idx, void* o,
-               float* lse, float* part_o, float* part_ml, hipStream_t s) {
+               float* lse, float* part_o, float* part_ml, const TileSelect* sel, hipStream_t s) {
   const Plan p = plan(nq, nh, 64 * DTW, k, sizeof(T) == 2);
   hipError_t e = hipSuccess;
   bool done = false;
@@ -1303,9 +1362,16 @@ hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C
     if (p.tile) {
       const long units = nq * p.nsplit;
       const unsigned blocks = (unsigned)(((units + 7) / 8) * 8 * p.nhg);
-      e = launch("mqa", mqa_tile_kernel<DTW>, dim3(blocks), dim3(256), 0, s, (int)nq, nh, k, p.nhg, p.nsplit,
-                 p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx, (bf16_t*)o,
-                 lse, part_o, part_ml);
+      if constexpr (DTW == 8) {
+        if (sel)
+          e = launch("mqa", mqa_tile_kernel<DTW, true>, dim3(blocks), dim3(256), 0, s, (int)nq, nh, k, p.nhg,
+                     p.nsplit, p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx,
+                     (bf16_t*)o, lse, part_o, part_ml, *sel);
+      }
+      if (!sel)
+        e = launch("mqa", mqa_tile_kernel<DTW, false>, dim3(blocks), dim3(256), 0, s, (int)nq, nh, k, p.nhg,
+                   p.nsplit, p.cps, scale * kLog2e, (const bf16_t*)q, (const bf16_t*)C, q_seq, kv_off, idx,
+                   (bf16_t*)o, lse, part_o, part_ml, TileSelect{});
       done = true;
     }
   }
@@ -1342,13 +1408,13 @@ hipError_t run(long nq, int nh, int k, float scale, const void* q, const void* C
 template <typename T>
 hipError_t pick(long nq, int nh, int c, int k, float scale, const void* q, const void* C,
                 const int32_t* q_seq, const int64_t* kv_off, const int32_t* idx, void* o, float* lse,
-                float* part_o, float* part_ml, hipStream_t s) {
+                float* part_o, float* part_ml, const TileSelect* sel, hipStream_t s) {
   switch (c / 64) {
-    case 1: return run<T, 1>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, s);
-    case 2: return run<T, 2>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, s);
-    case 4: return run<T, 4>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, s);
-    case 8: return run<T, 8>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, s);
-    case 16: return run<T, 16>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, s);
+    case 1: return run<T, 1>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, sel, s);
+    case 2: return run<T, 2>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, sel, s);
+    case 4: return run<T, 4>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, sel, s);
+    case 8: return run<T, 8>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, sel, s);
+    case 16: return run<T, 16>(nq, nh, k, scale, q, C, q_seq, kv_off, idx, o, lse, part_o, part_ml, sel, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1358,6 +1424,12 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 }  // namespace
 
 bool mqa_supported_c(int c) { return c == 64 || c == 128 || c == 256 || c == 512 || c == 1024; }
+
+bool mqa_tile_selects(long n_queries, int nh, int c, int k, bool bf16) {
+  if (n_queries <= 0 || c != 512) return false;
+  const Plan p = plan(n_queries, nh, c, k, bf16);
+  return p.tile && p.cps == 1;
+}
 
 size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
   if (n_queries <= 0) return 0;
@@ -1370,16 +1442,17 @@ size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
 hipError_t launch_mqa(csa_dtype dt, long n_queries, int nh, int c, int k, float scale,
                       const void* q, const void* C, const int32_t* q_seq,
                       const int64_t* kv_offset, const int32_t* idx, void* o, float* lse,
-                      void* workspace, hipStream_t s) {
+                      void* workspace, hipStream_t s, const TileSelect* sel) {
   if (n_queries == 0) return hipSuccess;
   const Plan p = plan(n_queries, nh, c, k, dt == CSA_BF16);
+  if (sel && !mqa_tile_selects(n_queries, nh, c, k, dt == CSA_BF16)) return hipErrorInvalidValue;
   float* part_o = (float*)workspace;
   float* part_ml =
       p.nsplit == 1 ? nullptr
                     : (float*)((char*)workspace + align256((size_t)n_queries * p.nsplit * nh * c * sizeof(float)));
   if (dt == CSA_F32)
-    return pick<float>(n_queries, nh, c, k, scale, q, C, q_seq, kv_offset, idx, o, lse, part_o, part_ml, s);
-  return pick<bf16_t>(n_queries, nh, c, k, scale, q, C, q_seq, kv_offset, idx, o, lse, part_o, part_ml, s);
+    return pick<float>(n_queries, nh, c, k, scale, q, C, q_seq, kv_offset, idx, o, lse, part_o, part_ml, sel, s);
+  return pick<bf16_t>(n_queries, nh, c, k, scale, q, C, q_seq, kv_offset, idx, o, lse, part_o, part_ml, sel, s);
 }
 
 }  // namespace csa

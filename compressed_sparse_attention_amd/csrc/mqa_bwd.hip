@@ -50,7 +50,7 @@ constexpr int kBwdSPitch = kBwdChunk + 8;  // row of dS for one head (32 keys)
 
 struct BwdLoop {
   bf16_t C[2][kBwdChunk * kBwdPitch];
-  float xch[4][2][8][64];  // partial S / dP exchange: [head tile][key tile][component][lane]
+  f32x4 xch[4][2][2][64];  // partial S / dP exchange: [head tile][key tile][S | dP][lane], 16 bytes per lane
   bf16_t W[kBwdChunk * kBwdWPitch];
   bf16_t dS[kBwdHeads * kBwdSPitch];
 };
@@ -269,25 +269,21 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
     }
     // the partner wave (same head tile, other half) finishes key tile 1 - half
     {
-      float* x = &sm.loop.xch[ht][1 - half][0][lane];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        x[rr * 64] = as[1 - half][rr];
-        x[(4 + rr) * 64] = ad[1 - half][rr];
-      }
+      sm.loop.xch[ht][1 - half][0][lane] = as[1 - half];
+      sm.loop.xch[ht][1 - half][1][lane] = ad[1 - half];
     }
     lds_barrier();
     // ---- B: P and dS for key tile `half`, heads of tile ht
     {
-      const float* x = &sm.loop.xch[ht][half][0][lane];
+      const f32x4 xs = sm.loop.xch[ht][half][0][lane], xd = sm.loop.xch[ht][half][1][lane];
       const int hl = 16 * ht + c16;
       const float l2 = s_lse2[hl], Dh = s_D[hl];
       float dsv[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int key = 16 * half + 4 * g + rr;
-        const float sv = as[half][rr] + x[rr * 64];
-        const float dp = ad[half][rr] + x[(4 + rr) * 64];
+        const float sv = as[half][rr] + xs[rr];
+        const float dp = ad[half][rr] + xd[rr];
         const float p = s_ids[sid][key] >= 0 ? exp2_fast(sv * scale_log2 - l2) : 0.f;
         dsv[rr] = p * (dp - Dh);
         sm.loop.W[key * kBwdWPitch + hl] = f2bf(p);

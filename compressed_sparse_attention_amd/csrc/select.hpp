@@ -476,65 +476,100 @@ __device__ __forceinline__ int chunk_of(const uint32_t* pre, int P, uint32_t e) 
 // each list in index order; an entry holds the key's index in the low 32
 // bits and the fp32 score bits (gt) or the score key (eq) above.
 // Copies the selected entries, chunk by chunk, to the first g1 slots; stages
-// the candidates in LDS, runs levels 2-4 on them and writes the remaining
-// k - g1 slots.  Every thread of the workgroup calls it.
+// the candidates in LDS, runs levels 2-4 on them and fills the remaining
+// k - g1 slots.  Only slots in [s0, s1) are handed out: put(slot, index,
+// score) once per such slot, by one thread (the whole row: [0, k)).  Every
+// thread of the workgroup calls it; `fs` is its LDS.  SAME_LAUNCH: the lists
+// were published by other workgroups of this launch and are read with
+// agent-scope loads; otherwise (a previous launch wrote them) plain cached
+// loads see them.
 template <int TPB>
-__device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32_t* __restrict__ counts,
-                           const uint64_t* __restrict__ gt, long gts, const uint64_t* __restrict__ eq, long eqs,
-                           int32_t* __restrict__ out, float* __restrict__ sout) {
-  __shared__ uint32_t s_ckey[kMSeg];
-  __shared__ uint32_t s_cidx[kMSeg];
-  __shared__ uint32_t s_h2[3][256];
-  __shared__ uint32_t s_pg[kRowChunksMax + 1], s_pe[kRowChunksMax + 1];
-  __shared__ uint32_t s_wave[TPB / 64];
-  __shared__ uint32_t s_res[2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+struct FinishSmem {
+  uint32_t ckey[kMSeg];
+  uint32_t cidx[kMSeg];
+  uint32_t h2[3][256];
+  uint32_t pg[kRowChunksMax + 1], pe[kRowChunksMax + 1];
+  uint32_t wave[TPB / 64];
+  uint32_t res[2];
+};
 
-  // A group of tpc threads serves each chunk.  The first batch of each
-  // thread's list entries is fetched before the counts are known (positions
-  // past a list's end read filler from inside it and are ignored), so the
-  // counts and the lists take one memory round trip, not two.
+// The first memory round trip of finish_row, which the caller issues as
+// early as it can: the counts of chunks c < Pl (wave 0, lane c) and the first
+// batch of each thread's list entries, threads laid out over Pl >= Pr chunks
+// (a group of tpc threads per chunk).  Entries past a list's end, and chunks
+// past the row's Pr, are filler from inside the lists and are ignored.
+struct FinishPrefetch {
+  uint64_t g[kMUnroll], e[kMUnroll];
+  uint32_t cg, ce;
+};
+
+__device__ __forceinline__ int finish_tpc(int TPB, int Pl) {
   int p2 = 1;
-  while (p2 < Pr) p2 <<= 1;
-  const int tpc = p2 >= TPB ? 1 : TPB / p2;
+  while (p2 < Pl) p2 <<= 1;
+  return p2 >= TPB ? 1 : TPB / p2;
+}
+
+template <int TPB, bool SAME_LAUNCH>
+__device__ __forceinline__ void finish_prefetch(FinishPrefetch& pf, int Pl, const uint32_t* __restrict__ counts,
+                                                const uint64_t* __restrict__ gt, long gts,
+                                                const uint64_t* __restrict__ eq, long eqs) {
+  auto ld = [](const auto* p) { return SAME_LAUNCH ? ld_agent(p) : *p; };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int tpc = finish_tpc(TPB, Pl);
   const int c_first = tid / tpc, sub = tid % tpc;
-  uint64_t spec_g[kMUnroll], spec_e[kMUnroll];
-  if (c_first < Pr) {
+  if (c_first < Pl) {
 #pragma unroll
     for (int u = 0; u < kMUnroll; ++u) {
       const long e = sub + u * tpc;
-      spec_g[u] = ld_agent(gt + c_first * gts + (e < gts ? e : gts - 1));
-      spec_e[u] = ld_agent(eq + c_first * eqs + (e < eqs ? e : eqs - 1));
+      pf.g[u] = ld(gt + c_first * gts + (e < gts ? e : gts - 1));
+      pf.e[u] = ld(eq + c_first * eqs + (e < eqs ? e : eqs - 1));
     }
   }
+  pf.cg = pf.ce = 0u;
+  if (tid < 64 && lane < Pl) {
+    pf.cg = ld(counts + 2 * lane);
+    pf.ce = ld(counts + 2 * lane + 1);
+  }
+}
+
+template <int TPB, bool SAME_LAUNCH, typename Put>
+__device__ void finish_row(FinishSmem<TPB>& fs, const FinishPrefetch& pf, int Pl, int Pr, int k, uint32_t b1,
+                           uint32_t g1, const uint32_t* __restrict__ counts, const uint64_t* __restrict__ gt,
+                           long gts, const uint64_t* __restrict__ eq, long eqs, uint32_t s0, uint32_t s1,
+                           Put&& put) {
+  static_assert(kRowChunksMax <= 64, "one wave scans the chunk counts");
+  uint32_t* s_ckey = fs.ckey;
+  uint32_t* s_cidx = fs.cidx;
+  uint32_t(*s_h2)[256] = fs.h2;
+  uint32_t* s_pg = fs.pg;
+  uint32_t* s_pe = fs.pe;
+  uint32_t* s_wave = fs.wave;
+  uint32_t* s_res = fs.res;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  auto ld = [](const auto* p) { return SAME_LAUNCH ? ld_agent(p) : *p; };
+
+  // A group of tpc threads serves each chunk (laid out over Pl chunks, as in
+  // finish_prefetch, whose batch is this thread's first).
+  const int tpc = finish_tpc(TPB, Pl);
+  const int c_first = tid / tpc, sub = tid % tpc;
   for (int b = tid; b < 3 * 256; b += TPB) (&s_h2[0][0])[b] = 0u;
-  if (wave == 0) {  // exclusive prefix of the per-chunk counts, 64 chunks per step
-    uint32_t run_g = 0, run_e = 0;
-    for (int base = 0; base < Pr; base += 64) {
-      const int c = base + lane;
-      const uint32_t cg = c < Pr ? ld_agent(counts + 2 * c) : 0u;
-      const uint32_t ce = c < Pr ? ld_agent(counts + 2 * c + 1) : 0u;
-      const uint32_t ig = wave_incl_scan(cg), ie = wave_incl_scan(ce);
-      s_pg[c] = run_g + ig - cg;  // c < Pr rounded up to 64 <= kRowChunksMax
-      s_pe[c] = run_e + ie - ce;
-      run_g += wave_last(ig);
-      run_e += wave_last(ie);
-    }
-    if (lane == 0) {
-      s_pg[Pr] = run_g;
-      s_pe[Pr] = run_e;
+  if (wave == 0) {  // exclusive prefix of the per-chunk counts (Pr <= 64)
+    const uint32_t cg = lane < Pr ? pf.cg : 0u, ce = lane < Pr ? pf.ce : 0u;
+    const uint32_t ig = wave_incl_scan(cg), ie = wave_incl_scan(ce);
+    s_pg[lane] = ig - cg;
+    s_pe[lane] = ie - ce;
+    if (lane == 63) {
+      s_pg[64] = ig;
+      s_pe[64] = ie;
     }
   }
-  __syncthreads();
+  __syncthreads();  // s_pg[Pr], s_pe[Pr]: the totals (counts past Pr are zero)
   const uint32_t n_cand = s_pe[Pr];
   const int nseg = (int)((n_cand + kMSeg - 1) / kMSeg);
 
-  auto put = [&](uint32_t slot, uint32_t i, uint32_t key) {
-    if (slot < (uint32_t)k) {
-      out[slot] = (int32_t)i;
-      if (sout) sout[slot] = key_score(key);
-    }
+  auto put_key = [&](uint32_t slot, uint32_t i, uint32_t key) {
+    if (slot >= s0 && slot < s1) put(slot, i, key_score(key));
   };
   // Both lists in one pass (chunk order = index order): selected entries go
   // straight to their slots; candidates go to LDS when they all fit.
@@ -546,28 +581,26 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
     const uint64_t* esrc = eq + c * eqs;
     for (uint32_t base = sub; base < nmax; base += tpc * kMUnroll) {
       uint64_t eg[kMUnroll], ee[kMUnroll];
-      if (c == c_first && base == (uint32_t)sub) {  // the batch fetched with the counts
+      if (c == c_first && base == (uint32_t)sub) {  // the batch of finish_prefetch
 #pragma unroll
         for (int u = 0; u < kMUnroll; ++u) {
-          eg[u] = spec_g[u];
-          ee[u] = spec_e[u];
+          eg[u] = pf.g[u];
+          ee[u] = pf.e[u];
         }
       } else {
 #pragma unroll
         for (int u = 0; u < kMUnroll; ++u) {
           const uint32_t e = base + u * tpc;
-          eg[u] = ld_agent(gsrc + (e < ng ? e : 0u));
-          ee[u] = ld_agent(esrc + (e < ne ? e : 0u));
+          eg[u] = ld(gsrc + (e < ng ? e : 0u));
+          ee[u] = ld(esrc + (e < ne ? e : 0u));
         }
         issue_fence();
       }
 #pragma unroll
       for (int u = 0; u < kMUnroll; ++u) {
         const uint32_t e = base + u * tpc;
-        if (e < ng && g0 + e < (uint32_t)k) {
-          out[g0 + e] = (int32_t)(uint32_t)eg[u];
-          if (sout) sout[g0 + e] = __uint_as_float((uint32_t)(eg[u] >> 32));
-        }
+        if (e < ng && g0 + e >= s0 && g0 + e < s1)
+          put(g0 + e, (uint32_t)eg[u], __uint_as_float((uint32_t)(eg[u] >> 32)));
         if (nseg == 1 && e < ne) {
           s_cidx[e0c + e] = (uint32_t)ee[u];
           s_ckey[e0c + e] = (uint32_t)(ee[u] >> 32);
@@ -585,7 +618,7 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
     for (uint32_t el_ = tid; el_ < cnt; el_ += TPB) {
       const uint32_t e = base + el_;
       const int c = chunk_of(s_pe, Pr, e);
-      const uint64_t ent = ld_agent(eq + c * eqs + (e - s_pe[c]));
+      const uint64_t ent = ld(eq + c * eqs + (e - s_pe[c]));
       s_cidx[el_] = (uint32_t)ent;
       s_ckey[el_] = (uint32_t)(ent >> 32);
     }
@@ -645,9 +678,9 @@ __device__ void finish_row(int Pr, int k, uint32_t b1, uint32_t g1, const uint32
     for (int e = 0; e < lim; ++e) {
       const uint32_t key = s_ckey[f + e];
       const uint32_t i = s_cidx[f + e];
-      if (key > T) put(g1 + p1++, i, key);
+      if (key > T) put_key(g1 + p1++, i, key);
       if (key == T) {
-        if (p2 < take_eq) put(g1 + gt2 + p2, i, key);
+        if (p2 < take_eq) put_key(g1 + gt2 + p2, i, key);
         ++p2;
       }
     }

@@ -78,10 +78,11 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
     int m, const float* __restrict__ scores, long ld, const int64_t* __restrict__ q_pos, long max_cand, int k,
     uint32_t* __restrict__ hist_g, uint32_t* __restrict__ arrive, uint32_t* __restrict__ counts,
     uint64_t* __restrict__ gt_list, uint64_t* __restrict__ eq_list, int P, int gtc, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out) {
+    float* __restrict__ score_out, uint32_t* __restrict__ b1g1) {
   __shared__ uint32_t s_wave[kMTPB / 64];
   __shared__ uint32_t s_res[2];
   __shared__ int s_last;
+  __shared__ FinishSmem<kMTPB> fs;
 
   const int tid = threadIdx.x;
   const long r = blockIdx.x / P;
@@ -147,6 +148,13 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
     st_agent(counts + (r * P + j) * 2, ng < (uint32_t)gtc ? ng : (uint32_t)gtc);
     st_agent(counts + (r * P + j) * 2 + 1, tot2 >> 16);
   }
+  if (b1g1) {  // classify only: the decode attention finishes the row
+    if (j == 0 && tid == 0) {
+      b1g1[2 * r] = b1;
+      b1g1[2 * r + 1] = g1;
+    }
+    return;
+  }
   // publish the lists, then count this chunk in; the last one finishes the row
   wait_stores();
   __syncthreads();
@@ -161,8 +169,14 @@ __global__ __launch_bounds__(kMTPB) void topk_multi_kernel(
     for (int b = tid; b < kL1Bins / 4; b += kMTPB) h[b] = u32x4{0u, 0u, 0u, 0u};
     if (tid == 0) arrive[r] = 0u;
   }
-  finish_row<kMTPB>(Pr, k, b1, g1, counts + r * P * 2, gt_list + r * P * (long)gtc, gtc,
-                    eq_list + r * P * (long)kMChunk, kMChunk, out, sout);
+  FinishPrefetch pf;
+  finish_prefetch<kMTPB, true>(pf, Pr, counts + r * P * 2, gt_list + r * P * (long)gtc, gtc,
+                               eq_list + r * P * (long)kMChunk, kMChunk);
+  finish_row<kMTPB, true>(fs, pf, Pr, Pr, k, b1, g1, counts + r * P * 2, gt_list + r * P * (long)gtc, gtc,
+                    eq_list + r * P * (long)kMChunk, kMChunk, 0u, (uint32_t)k, [&](uint32_t slot, uint32_t i, float sc) {
+                      out[slot] = (int32_t)i;
+                      if (sout) sout[slot] = sc;
+                    });
 }
 
 // ---------------------------------------------------------------------------
@@ -357,7 +371,7 @@ hipError_t launch_topk(long n_queries, int m, const float* scores, long ld_sc,
   if (hist && lists) {
     (void)csa::launch("topk", topk_multi_kernel, dim3((unsigned)(n_queries * lists->P)), dim3(kMTPB), 0, s, m,
                       scores, ld_sc, q_pos, max_cand, k, hist, lists->arrive, lists->counts, lists->gt, lists->eq,
-                      lists->P, lists->gtc, idx_out, score_out);
+                      lists->P, lists->gtc, idx_out, score_out, lists->b1g1);
     return hipGetLastError();
   }
   if (max_cand <= kShortTPB * kShortEPT)  // every row fits in registers

@@ -684,13 +684,21 @@ def test_sparse_mqa_backward_run_twice():
 # ---------------------------------------------------------------------------
 # csa_decode: eqs 8, 9 and 11 in one call with a persistent workspace
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("lens,nq_rep,nhI,cI,nh,c,k", [
+@pytest.mark.parametrize("lens,nq_rep,nhI,cI,nh,c,k,keys", [
     # per-chunk selector (long rows), a short row, an empty row
-    ([4 * 9000, 4 * 20000, 4 * 33000, 100, 0, 4 * 5000], 1, 8, 64, 16, 128, 512),
+    ([4 * 9000, 4 * 20000, 4 * 33000, 100, 0, 4 * 5000], 1, 8, 64, 16, 128, 512, "random"),
     # 520 long rows of one sequence: one workgroup per row from the sweep's histogram
-    ([4 * 9100], 520, 2, 32, 4, 64, 300),
+    ([4 * 9100], 520, 2, 32, 4, 64, 300, "random"),
+    # c = 512, short batch: the attention finishes the long rows' selection itself (each split its own
+    # slots); short and empty rows beside them
+    ([4 * 9000, 4 * 20000, 4 * 33000, 100, 0, 4 * 5000], 1, 8, 64, 16, 512, 512, "random"),
+    # the same with a ragged last split (k = 300) and a partly empty second head tile (20 heads)
+    ([4 * 9000, 4 * 12000, 4 * 70], 1, 4, 32, 20, 512, 300, "random"),
+    # every key one of two rows: each row's scores take two values, so thousands of keys tie at the
+    # threshold (more candidates than one LDS segment of the finishing phase holds)
+    ([4 * 12000, 4 * 30000], 1, 4, 64, 16, 512, 512, "two"),
 ])
-def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k):
+def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k, keys):
     """Three back-to-back csa_decode calls on one workspace (zeroed once), each with new queries, give
     exactly the results of csa_index_topk (fresh workspace) followed by csa_sparse_mqa: the calls leave
     the histogram and counters zero for the next one."""
@@ -711,7 +719,11 @@ def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k):
         rows = max(int(nblk.sum()), 1)
     B = len(pos)
     max_cand = int(pos.max() // m)
-    K = to_device(draw(rng, (rows, cI), 1.0, "bf16"), "bf16", DEV)
+    if keys == "two":
+        two = draw(rng, (2, cI), 1.0, "bf16")
+        K = to_device(two[np.arange(rows) % 2], "bf16", DEV)
+    else:
+        K = to_device(draw(rng, (rows, cI), 1.0, "bf16"), "bf16", DEV)
     C = to_device(draw(rng, (rows, c), 1.0, "bf16"), "bf16", DEV)
     q_pos = torch.tensor(pos, device=DEV)
     kv_off = torch.tensor(off, device=DEV)
