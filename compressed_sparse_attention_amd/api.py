@@ -48,6 +48,8 @@ _SIGS = {
                                     _i64, _vp]),
     "csa_compress_append": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _i64, _vp]),
+    "csa_compress_append_pair": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _vp, _vp, _i32, _vp, _i64, _vp, _vp, _vp,
+                                                _vp, _i64, _i32, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp]),
     "csa_compress_backward_workspace": (ctypes.c_int, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "csa_compress_backward": (ctypes.c_int, [ctypes.c_int, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp,
                                              _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -258,6 +260,31 @@ def csa_compress_append(new_rows, ring, Ba, Bb, m: int, t_new, kv_offset, Ccomp)
                                      _rowmajor(Ccomp, "Ccomp"), _stream(Ccomp.device)),
            "csa_compress_append")
     return Ccomp
+
+
+def csa_compress_append_pair(rows1, ring1, Ba1, Bb1, Ccomp1, rows2, ring2, Ba2, Bb2, Ccomp2, m: int, t_new,
+                             kv_offset):
+    """csa_compress_append on two caches of the same sequences (same t_new, kv_offset) in one launch."""
+    B = rows1.shape[0]
+    args = []
+    for x, (rows, ring, Ba, Bb, Ccomp) in enumerate(((rows1, ring1, Ba1, Bb1, Ccomp1), (rows2, ring2, Ba2, Bb2, Ccomp2))):
+        c = Ccomp.shape[1]
+        _contig(ring, "ring")
+        if rows.shape[0] != B or tuple(ring.shape) != (B, 2 * m, 4 * c) or ring.dtype != Ccomp1.dtype \
+                or rows.dtype != Ccomp1.dtype or Ccomp.dtype != Ccomp1.dtype:
+            raise CSAError(f"csa_compress_append_pair: cache {x + 1}: ring must be [B, 2m, 4c] of the cache dtype")
+        for t, nm in ((Ba, "Ba"), (Bb, "Bb")):
+            _contig(t, nm)
+            if tuple(t.shape) != (m, c) or t.dtype != Ccomp1.dtype:
+                raise CSAError(f"csa_compress_append_pair: cache {x + 1}: {nm} must be [m, c]")
+        args += [c, _ptr(rows), _rowmajor(rows, "new_rows"), _ptr(ring), _ptr(Ba), _ptr(Bb), _ptr(Ccomp),
+                 _rowmajor(Ccomp, "Ccomp")]
+    for t, nm in ((t_new, "t_new"), (kv_offset, "kv_offset")):
+        if t.dtype != torch.int64 or tuple(t.shape) != (B,):
+            raise CSAError(f"csa_compress_append_pair: {nm} must be int64 [B]")
+    _check(lib().csa_compress_append_pair(_dt(Ccomp1), B, m, _ptr(t_new), _ptr(kv_offset), *args,
+                                          _stream(Ccomp1.device)), "csa_compress_append_pair")
+    return Ccomp1, Ccomp2
 
 
 def csa_compress_backward_workspace(n: int, m: int, c: int) -> int:

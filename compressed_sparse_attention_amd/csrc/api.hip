@@ -463,6 +463,47 @@ csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, co
   return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_append launch");
 }
 
+csa_status csa_compress_append_pair(csa_dtype dt, int64_t B, int32_t m, const int64_t* t_new,
+                                    const int64_t* kv_offset, int32_t c1, const void* new_rows1, int64_t ld_new1,
+                                    void* ring1, const void* Ba1, const void* Bb1, void* Ccomp1, int64_t ld_out1,
+                                    int32_t c2, const void* new_rows2, int64_t ld_new2, void* ring2,
+                                    const void* Ba2, const void* Bb2, void* Ccomp2, int64_t ld_out2, void* stream) {
+  CSA_REQUIRE(dtype_ok(dt), "csa_compress_append_pair: unknown dtype");
+  CSA_REQUIRE(B >= 0 && B <= 0x3FFFFFFF, "csa_compress_append_pair: bad B");
+  CSA_REQUIRE(m >= 1 && m <= 64, "csa_compress_append_pair: m must be in [1, 64] (got %d)", m);
+  const int v = vec_elems(dt);
+  const int32_t cs[2] = {c1, c2};
+  const void* rows[2] = {new_rows1, new_rows2};
+  const void* rings[2] = {ring1, ring2};
+  const void* bas[2] = {Ba1, Ba2};
+  const void* bbs[2] = {Bb1, Bb2};
+  const void* outs[2] = {Ccomp1, Ccomp2};
+  const int64_t lds_new[2] = {ld_new1, ld_new2}, lds_out[2] = {ld_out1, ld_out2};
+  for (int x = 0; x < 2; ++x) {
+    CSA_REQUIRE(cs[x] > 0 && cs[x] % 4 == 0, "csa_compress_append_pair: c%d must be a positive multiple of 4 (got %d)",
+                x + 1, cs[x]);
+  }
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(t_new && kv_offset, "csa_compress_append_pair: null pointer");
+  for (int x = 0; x < 2; ++x) {
+    CSA_REQUIRE(rows[x] && rings[x] && bas[x] && bbs[x] && outs[x], "csa_compress_append_pair: null pointer (cache %d)",
+                x + 1);
+    CSA_REQUIRE(aligned16(rows[x]) && aligned16(rings[x]) && aligned16(bas[x]) && aligned16(bbs[x]) &&
+                    aligned16(outs[x]),
+                "csa_compress_append_pair: pointers must be 16-byte aligned (cache %d)", x + 1);
+    CSA_REQUIRE(lds_new[x] >= 4L * cs[x] && lds_out[x] >= cs[x],
+                "csa_compress_append_pair: leading dimension too small (cache %d)", x + 1);
+    CSA_REQUIRE(lds_new[x] % v == 0 && lds_out[x] % v == 0,
+                "csa_compress_append_pair: leading dimensions must keep rows 16-byte aligned (cache %d)", x + 1);
+  }
+  csa_status st = check_device();
+  if (st != CSA_OK) return st;
+  const csa::AppendCache a{c1, new_rows1, ld_new1, ring1, Ba1, Bb1, Ccomp1, ld_out1};
+  const csa::AppendCache b{c2, new_rows2, ld_new2, ring2, Ba2, Bb2, Ccomp2, ld_out2};
+  hipError_t e = csa::launch_compress_append_pair(dt, B, m, t_new, kv_offset, a, b, (hipStream_t)stream);
+  return e == hipSuccess ? CSA_OK : hip_fail(e, "csa_compress_append_pair launch");
+}
+
 csa_status csa_index_topk_workspace(int64_t n_queries, int64_t max_cand, int32_t n_hI, int32_t k,
                                     size_t* bytes) {
   CSA_REQUIRE(bytes, "csa_index_topk_workspace: null bytes");

@@ -139,14 +139,29 @@ __global__ __launch_bounds__(256) void compress_kernel(long nblk, int m, int c,
 // absent for i = 0) into row kv_offset[b] + i of the compressed cache; each
 // thread owns V channels of it.
 // ---------------------------------------------------------------------------
+template <typename T>
+struct AppendArgs {
+  int c;
+  const T* rows;
+  long ld_new;
+  T* ring;
+  const T* Ba;
+  const T* Bb;
+  T* out;
+  long ldo;
+};
+
 template <typename T, int V>
-__global__ __launch_bounds__(256) void compress_append_kernel(int m, int c, const T* __restrict__ rows, long ld_new,
-                                                              T* __restrict__ ring, const T* __restrict__ Ba,
-                                                              const T* __restrict__ Bb,
-                                                              const int64_t* __restrict__ t_new,
-                                                              const int64_t* __restrict__ kv_off,
-                                                              T* __restrict__ out, long ldo) {
-  const long b = blockIdx.x;
+__device__ __forceinline__ void append_one(int m, const AppendArgs<T>& p, long b, const int64_t* __restrict__ t_new,
+                                           const int64_t* __restrict__ kv_off) {
+  const int c = p.c;
+  const T* __restrict__ rows = p.rows;
+  const long ld_new = p.ld_new;
+  T* __restrict__ ring = p.ring;
+  const T* __restrict__ Ba = p.Ba;
+  const T* __restrict__ Bb = p.Bb;
+  T* __restrict__ out = p.out;
+  const long ldo = p.ldo;
   const long t = t_new[b];
   const int W4 = 4 * c;  // ring row: C^a | C^b | Z^a | Z^b
   T* rb = ring + b * (long)(2 * m) * W4;
@@ -194,6 +209,25 @@ __global__ __launch_bounds__(256) void compress_append_kernel(int m, int c, cons
     for (int q = 0; q < V; ++q) res[q] = acc[q] / den[q];
     Vec<T, V>::store(out + (kv_off[b] + i) * ldo + ch, res);
   }
+}
+
+template <typename T, int V>
+__global__ __launch_bounds__(256) void compress_append_kernel(int m, AppendArgs<T> p, const int64_t* __restrict__ t_new,
+                                                              const int64_t* __restrict__ kv_off) {
+  append_one<T, V>(m, p, blockIdx.x, t_new, kv_off);
+}
+
+// Two caches of the same sequences (the main and the indexer cache) in one
+// launch: workgroups below B append to the first, the others to the second.
+template <typename T, int V>
+__global__ __launch_bounds__(256) void compress_append_pair_kernel(int m, long B, AppendArgs<T> p1, AppendArgs<T> p2,
+                                                                   const int64_t* __restrict__ t_new,
+                                                                   const int64_t* __restrict__ kv_off) {
+  const long b = blockIdx.x;
+  if (b < B)
+    append_one<T, V>(m, p1, b, t_new, kv_off);
+  else
+    append_one<T, V>(m, p2, b - B, t_new, kv_off);
 }
 
 // ---------------------------------------------------------------------------
@@ -513,16 +547,39 @@ hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void
   if (B == 0) return hipSuccess;
   const dim3 grid((unsigned)B);
   if (dt == CSA_F32)
-    return launch("compress_append", compress_append_kernel<float, 4>, grid, dim3(256), 0, s, m, c,
-                  (const float*)rows, ld_new, (float*)ring, (const float*)Ba, (const float*)Bb, t_new, kv_off,
-                  (float*)out, ld_out);
+    return launch("compress_append", compress_append_kernel<float, 4>, grid, dim3(256), 0, s, m,
+                  AppendArgs<float>{c, (const float*)rows, ld_new, (float*)ring, (const float*)Ba, (const float*)Bb,
+                                    (float*)out, ld_out},
+                  t_new, kv_off);
+  const AppendArgs<bf16_t> p{c, (const bf16_t*)rows, ld_new, (bf16_t*)ring, (const bf16_t*)Ba, (const bf16_t*)Bb,
+                             (bf16_t*)out, ld_out};
   if (c % 8 == 0 && ld_new % 8 == 0 && ld_out % 8 == 0)
-    return launch("compress_append", compress_append_kernel<bf16_t, 8>, grid, dim3(256), 0, s, m, c,
-                  (const bf16_t*)rows, ld_new, (bf16_t*)ring, (const bf16_t*)Ba, (const bf16_t*)Bb, t_new, kv_off,
-                  (bf16_t*)out, ld_out);
-  return launch("compress_append", compress_append_kernel<bf16_t, 4>, grid, dim3(256), 0, s, m, c,
-                (const bf16_t*)rows, ld_new, (bf16_t*)ring, (const bf16_t*)Ba, (const bf16_t*)Bb, t_new, kv_off,
-                (bf16_t*)out, ld_out);
+    return launch("compress_append", compress_append_kernel<bf16_t, 8>, grid, dim3(256), 0, s, m, p, t_new, kv_off);
+  return launch("compress_append", compress_append_kernel<bf16_t, 4>, grid, dim3(256), 0, s, m, p, t_new, kv_off);
+}
+
+hipError_t launch_compress_append_pair(csa_dtype dt, long B, int m, const int64_t* t_new, const int64_t* kv_off,
+                                       const AppendCache& a, const AppendCache& b, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  const dim3 grid((unsigned)(2 * B));
+  if (dt == CSA_F32) {
+    const AppendArgs<float> p1{a.c, (const float*)a.rows, a.ld_new, (float*)a.ring, (const float*)a.Ba,
+                               (const float*)a.Bb, (float*)a.out, a.ld_out};
+    const AppendArgs<float> p2{b.c, (const float*)b.rows, b.ld_new, (float*)b.ring, (const float*)b.Ba,
+                               (const float*)b.Bb, (float*)b.out, b.ld_out};
+    return launch("compress_append", compress_append_pair_kernel<float, 4>, grid, dim3(256), 0, s, m, B, p1, p2,
+                  t_new, kv_off);
+  }
+  const AppendArgs<bf16_t> p1{a.c, (const bf16_t*)a.rows, a.ld_new, (bf16_t*)a.ring, (const bf16_t*)a.Ba,
+                              (const bf16_t*)a.Bb, (bf16_t*)a.out, a.ld_out};
+  const AppendArgs<bf16_t> p2{b.c, (const bf16_t*)b.rows, b.ld_new, (bf16_t*)b.ring, (const bf16_t*)b.Ba,
+                              (const bf16_t*)b.Bb, (bf16_t*)b.out, b.ld_out};
+  auto v8 = [](const AppendCache& x) { return x.c % 8 == 0 && x.ld_new % 8 == 0 && x.ld_out % 8 == 0; };
+  if (v8(a) && v8(b))
+    return launch("compress_append", compress_append_pair_kernel<bf16_t, 8>, grid, dim3(256), 0, s, m, B, p1, p2,
+                  t_new, kv_off);
+  return launch("compress_append", compress_append_pair_kernel<bf16_t, 4>, grid, dim3(256), 0, s, m, B, p1, p2,
+                t_new, kv_off);
 }
 
 }  // namespace csa

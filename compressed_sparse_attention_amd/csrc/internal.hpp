@@ -86,6 +86,20 @@ hipError_t launch_compress_backward_varlen(csa_dtype dt, long nseq, long nblk, i
                                            void* dZb, long ld_out, float* dBa, float* dBb, void* workspace,
                                            hipStream_t s);
 
+// One cache of csa_compress_append_pair.
+struct AppendCache {
+  int c;
+  const void* rows;
+  long ld_new;
+  void* ring;
+  const void* Ba;
+  const void* Bb;
+  void* out;
+  long ld_out;
+};
+hipError_t launch_compress_append_pair(csa_dtype dt, long B, int m, const int64_t* t_new, const int64_t* kv_off,
+                                       const AppendCache& a, const AppendCache& b, hipStream_t s);
+
 // Decode-time append (one new token per sequence); see csa_compress_append.
 hipError_t launch_compress_append(csa_dtype dt, long B, int m, int c, const void* rows, long ld_new, void* ring,
                                   const void* Ba, const void* Bb, const int64_t* t_new, const int64_t* kv_off,

@@ -363,10 +363,9 @@ def decode_step(H_new: torch.Tensor, W: Dict[str, torch.Tensor], state: DecodeSt
     api.csa_project_pair(H_new, W["W_H_t"], Y, W["W_w_t"], wI)  # eqs 1, 2 (+ indexer copies), 5; eq 7
     cQ = Y[:, 4 * c + 4 * cI:]
     api.csa_project_pair(cQ, W["W_UQ_t"], q, W["W_UQI_t"], qI)  # eq 10; eq 6
-    api.csa_compress_append(Y[:, :4 * c], state.ring, W["B_a"], W["B_b"], m, state.t, state.kv_offset,
-                            state.Ccomp)  # eqs 3-4
-    api.csa_compress_append(Y[:, 4 * c:4 * c + 4 * cI], state.ring_I, W["B_aI"], W["B_bI"], m, state.t,
-                            state.kv_offset, state.KIcomp)
+    api.csa_compress_append_pair(Y[:, :4 * c], state.ring, W["B_a"], W["B_b"], state.Ccomp,  # eqs 3-4, both caches
+                                 Y[:, 4 * c:4 * c + 4 * cI], state.ring_I, W["B_aI"], W["B_bI"], state.KIcomp,
+                                 m, state.t, state.kv_offset)
     # the block a token completes is not among its own candidates (s < floor(t/m))
     buf = decode(q.view(B, nh, c), qI.view(B, nhI, cI), wI, state.Ccomp, state.KIcomp, state.t, state.kv_offset,
                  m, k, state.capacity, scale=scale, buf=buf)

@@ -194,6 +194,21 @@ csa_status csa_compress_append(csa_dtype dt, int64_t B, int32_t m, int32_t c, co
                                int64_t ld_out, void* stream);
 
 /*
+ * csa_compress_append_pair -- csa_compress_append on two caches of the same
+ * B sequences in one launch (the same section and equations): the main
+ * cache (width c1) and the indexer's (width c2; "the same operation" on the
+ * indexer's projections), both advanced with the same t_new and kv_offset.
+ * Each cache's arguments mean what csa_compress_append's do; the limits are
+ * the same per cache (B <= 2^30).  Results equal two csa_compress_append
+ * calls.  The two caches must not overlap in memory.
+ */
+csa_status csa_compress_append_pair(csa_dtype dt, int64_t B, int32_t m, const int64_t* t_new,
+                                    const int64_t* kv_offset, int32_t c1, const void* new_rows1, int64_t ld_new1,
+                                    void* ring1, const void* Ba1, const void* Bb1, void* Ccomp1, int64_t ld_out1,
+                                    int32_t c2, const void* new_rows2, int64_t ld_new2, void* ring2,
+                                    const void* Ba2, const void* Bb2, void* Ccomp2, int64_t ld_out2, void* stream);
+
+/*
  * csa_compress_backward -- gradients of eqs 3-4 (section "Compressed Key-Value
  * Entries") for one sequence, given dCcomp = dL/dCcomp.  For block i and
  * channel j, with S_r the softmax weights of its 2m pairs (value v_r, logit

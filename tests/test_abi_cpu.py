@@ -101,6 +101,28 @@ def test_compress_append_rejects_bad_args(L):
     assert call(B=0, new=None, ring=None) == api.CSA_OK  # no sequences: nothing enqueued
 
 
+def test_compress_append_pair_rejects_bad_args(L):
+    p = ctypes.c_void_p(16)
+
+    def call(dt=1, B=2, m=4, t=p, off=p, c1=64, new1=p, ldn1=256, ring1=p, C1=p, ldo1=64, c2=32, new2=p, ldn2=128,
+             ring2=p, Ba2=p, C2=p, ldo2=32):
+        return L.csa_compress_append_pair(dt, B, m, t, off, c1, new1, ldn1, ring1, p, p, C1, ldo1, c2, new2, ldn2,
+                                          ring2, Ba2, p, C2, ldo2, None)
+    assert call(dt=7) == api.CSA_ERR_INVALID_ARG
+    assert call(m=0) == api.CSA_ERR_INVALID_ARG
+    assert call(c1=6) == api.CSA_ERR_INVALID_ARG
+    assert call(c2=0) == api.CSA_ERR_INVALID_ARG
+    assert call(t=None) == api.CSA_ERR_INVALID_ARG
+    assert call(ring2=None) == api.CSA_ERR_INVALID_ARG
+    assert "cache 2" in _err()
+    assert call(Ba2=None) == api.CSA_ERR_INVALID_ARG
+    assert call(ldn1=255) == api.CSA_ERR_INVALID_ARG
+    assert call(ldo2=31) == api.CSA_ERR_INVALID_ARG
+    assert call(new2=ctypes.c_void_p(18)) == api.CSA_ERR_INVALID_ARG
+    assert "aligned" in _err()
+    assert call(B=0, new1=None, ring2=None) == api.CSA_OK  # no sequences: nothing enqueued
+
+
 def test_decode_rejects_bad_args(L):
     p = ctypes.c_void_p(16)
 

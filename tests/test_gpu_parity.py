@@ -310,6 +310,42 @@ def test_compress_append(dtype, m, c, steps):
     assert torch.all(Cbig[:, c:] == 3.0)
 
 
+@pytest.mark.parametrize("dtype,m,c1,c2", [("bf16", 4, 512, 128), ("f32", 3, 64, 20), ("bf16", 1, 36, 64)])
+def test_compress_append_pair_equals_two_calls(dtype, m, c1, c2):
+    """csa_compress_append_pair on a main and an indexer cache of the same sequences gives, step after step,
+    exactly the caches and rings of two csa_compress_append calls (tokens that complete a block and tokens
+    that do not, sequences at different positions)."""
+    rng = synth.rng_for(m * 7 + c1 + c2)
+    pre = [0, 5, 2 * m + 3, 1]
+    B, steps = len(pre), 3 * m + 1
+    cap = max(pre) // m + steps // m + 2
+    off = torch.arange(B, dtype=torch.int64, device=DEV) * cap
+    t1 = torch.tensor(pre, dtype=torch.int64, device=DEV)
+    t2 = t1.clone()
+    caches = []
+    for c in (c1, c2):
+        Ba = to_device(draw(rng, (m, c), 0.5, dtype), dtype, DEV)
+        Bb = to_device(draw(rng, (m, c), 0.5, dtype), dtype, DEV)
+        ring = to_device(draw(rng, (B, 2 * m, 4 * c), 1.0, dtype), dtype, DEV)
+        cp = (c + 7) // 8 * 8  # cache rows padded to 16 bytes; the cache is a column slice
+        C = torch.full((B * cap, cp), 3.0, dtype=TD[dtype], device=DEV)[:, :c]
+        C2 = torch.full((B * cap, cp), 3.0, dtype=TD[dtype], device=DEV)[:, :c]
+        caches.append((c, Ba, Bb, ring, C, ring.clone(), C2))
+    wide = 4 * c1 + 4 * c2 + 8
+    for s in range(steps):
+        Y = to_device(draw(rng, (B, wide), 1.5, dtype), dtype, DEV)
+        (ca, Baa, Bba, ra, Ca, ra2, Ca2), (cb, Bab, Bbb, rb, Cb, rb2, Cb2) = caches
+        api.csa_compress_append_pair(Y[:, :4 * ca], ra, Baa, Bba, Ca, Y[:, 4 * ca:4 * ca + 4 * cb], rb, Bab, Bbb, Cb,
+                                     m, t1, off)
+        api.csa_compress_append(Y[:, :4 * ca], ra2, Baa, Bba, m, t2, off, Ca2)
+        api.csa_compress_append(Y[:, 4 * ca:4 * ca + 4 * cb], rb2, Bab, Bbb, m, t2, off, Cb2)
+        t1 += 1
+        t2 += 1
+        torch.cuda.synchronize()
+        for x, (c, _, _, r, C, r2, C2) in enumerate(caches):
+            assert torch.equal(r, r2) and torch.equal(C, C2), f"step {s}, cache {x + 1}"
+
+
 def _run_index_topk(qI, wI, K, m, k, lens, kv_offset, dtype, prefill_mode=False):
     B = qI.shape[0]
     idx = torch.full((B, k), 123456, dtype=torch.int32, device=DEV)
