@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * kBwdWaves) void compress_bwd_kernel(
     const int64_t* __restrict__ boff) {
   extern __shared__ float s_db[];  // [2m][64 V]: bias-gradient sums of this workgroup's blocks
   constexpr int G = kBwdRowGroup;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int W = 64 * V;
   const int ch = (blockIdx.x * 64 + lane) * V;
   const bool live = ch < c;

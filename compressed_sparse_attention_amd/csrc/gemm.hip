@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(int M, int N, int K, const
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int g = lane >> 4, c16 = lane & 15;
   const long m0 = (long)blockIdx.y * kBM;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
   const long n0 = (long)(r / gsize) * kG2N;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
   const int g = lane >> 4, c16 = lane & 15;
   const int lrow = tid >> 3;          // 0..63
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, c
   const long n0 = (long)(r / gsize) * kG2N;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
   const int g = lane >> 4, c16 = lane & 15;
   const int KT = K / kDmaK;  // even
@@ -481,7 +481,7 @@ __device__ __forceinline__ void smallm_tile(int M, int N, int K, const bf16_t* _
                                             const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y, long ldy,
                                             long n0, float (*s_part)[256]) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int nsup = (K + kSmSuper - 1) / kSmSuper;
   const int s0 = (wave * nsup) / 4, s1 = ((wave + 1) * nsup) / 4;  // this wave's super-steps

@@ -122,7 +122,7 @@ __global__ __launch_bounds__((64 * pf_waves<T, KK, NHT, STREAM>())) void indexer
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[STREAM ? kPfWaves * kStreamWords : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   // Token block of this workgroup: positions p0 .. p0+kPfTokens-1 of one
   // sequence of length len, whose rows start at row0 and keys at kbase.

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void mqa_kernel(int nh, int k, int nhg, int ns
   __shared__ float s_l[kHG];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const long bid = blockIdx.x;
   const int j = (int)(bid % nsplit);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(512) void mqa_group8_kernel(int nh, int k, int nhg,
   __shared__ int s_ext[2][8];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const long bid = blockIdx.x;
   const int j = (int)(bid % nsplit);
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(512) void mqa_stream_kernel(long nunits, int nh, in
   __shared__ int s_flag[8];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int ht = wave & 3, kh = wave >> 2;
   const long stride = gridDim.x;
@@ -1034,7 +1034,7 @@ __global__ __launch_bounds__(256) void mqa_tile_kernel(int nq, int nh, int k, in
   __shared__ int32_t s_win[SEL ? kTileRows : 1];                      // SEL: this split's selection slots
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int b = blockIdx.x;
   const int grp = b / (8 * nht);

@@ -79,10 +79,11 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
   __shared__ __attribute__((aligned(16))) BwdSmem sm;
   __shared__ __attribute__((aligned(16))) bf16_t s_dO[kBwdHeads * kBwdCD];
   __shared__ float s_D[kBwdHeads], s_lse2[kBwdHeads];
-  __shared__ int32_t s_ids[3][KC];  // slot ids of chunks ch - 1, ch, ch + 1 (by ch mod 3)
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[3][KC];  // slot ids of chunks ch - 1, ch, ch + 1 (by ch mod 3)
   __shared__ int s_ext[2][8];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: selects on it stay scalar
   const int g = lane >> 4, c16 = lane & 15;
   const long rl = blockIdx.x / nhg;  // query within this call's chunk of queries
   const int hg = (int)(blockIdx.x - rl * nhg);
@@ -269,8 +270,8 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
     }
     // the partner wave (same head tile, other half) finishes key tile 1 - half
     {
-      sm.loop.xch[ht][1 - half][0][lane] = as[1 - half];
-      sm.loop.xch[ht][1 - half][1][lane] = ad[1 - half];
+      sm.loop.xch[ht][1 - half][0][lane] = half ? as[0] : as[1];
+      sm.loop.xch[ht][1 - half][1][lane] = half ? ad[0] : ad[1];
     }
     lds_barrier();
     // ---- B: P and dS for key tile `half`, heads of tile ht
@@ -278,13 +279,14 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
       const f32x4 xs = sm.loop.xch[ht][half][0][lane], xd = sm.loop.xch[ht][half][1][lane];
       const int hl = 16 * ht + c16;
       const float l2 = s_lse2[hl], Dh = s_D[hl];
+      const int4 ids4 = *reinterpret_cast<const int4*>(&s_ids[sid][16 * half + 4 * g]);  // this lane's 4 keys
       float dsv[4];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int key = 16 * half + 4 * g + rr;
-        const float sv = as[half][rr] + xs[rr];
-        const float dp = ad[half][rr] + xd[rr];
-        const float p = s_ids[sid][key] >= 0 ? exp2_fast(sv * scale_log2 - l2) : 0.f;
+        const float sv = (half ? as[1][rr] : as[0][rr]) + xs[rr];
+        const float dp = (half ? ad[1][rr] : ad[0][rr]) + xd[rr];
+        const float p = (rr == 0 ? ids4.x : rr == 1 ? ids4.y : rr == 2 ? ids4.z : ids4.w) >= 0 ? exp2_fast(sv * scale_log2 - l2) : 0.f;
         dsv[rr] = p * (dp - Dh);
         sm.loop.W[key * kBwdWPitch + hl] = f2bf(p);
         sm.loop.W[key * kBwdWPitch + 64 + hl] = f2bf(scale * dsv[rr]);

@@ -32,7 +32,7 @@ __device__ __forceinline__ float key_score(uint32_t key) {
 // Exclusive scan over the workgroup; also returns the total.  Contains barriers.
 template <int TPB>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_wave, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) s_wave[wave] = x;
   __syncthreads();
@@ -203,7 +203,7 @@ __device__ __forceinline__ void select_row(SelectRowSmem<TPB, REGS>& sm, const f
   uint32_t* s_res = sm.res;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   if (nc <= k) {  // every candidate is kept
     for (int j = tid; j < k; j += TPB) {
@@ -546,7 +546,7 @@ __device__ void finish_row(FinishSmem<TPB>& fs, const FinishPrefetch& pf, int Pl
   uint32_t* s_wave = fs.wave;
   uint32_t* s_res = fs.res;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto ld = [](const auto* p) { return SAME_LAUNCH ? ld_agent(p) : *p; };
 
   // A group of tpc threads serves each chunk (laid out over Pl chunks, as in

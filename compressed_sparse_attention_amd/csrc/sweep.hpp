@@ -69,7 +69,7 @@ __device__ __forceinline__ long sweep_chunk(SweepSmem<T, KK, NHT>& sm, int r, lo
   float* s_w = sm.w;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
 
   // The query's heads and head weights are fetched first, by every wave,

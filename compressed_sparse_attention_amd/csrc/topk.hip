@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kLTPB) void topk_list_kernel(int m, long max_cand, 
   __shared__ uint32_t s_h[3][256];
   __shared__ uint32_t s_wave[kLTPB / 64];
   __shared__ uint32_t s_res[2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long r = blockIdx.x;
   long nc = r / m;
   nc = nc < max_cand ? nc : max_cand;
