@@ -95,63 +95,32 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
   const bf16_t* Cb = C + off * CD;
   const float scale_log2 = scale * kLog2e;
 
-  // ---- prologue: q and dO into registers (through LDS), D and lse per head
+  // ---- prologue: q and dO into registers (through LDS), D and lse per head.
+  // Every load of the query's state goes out first, together (the slot ids
+  // for the chunk count, q, dO and o): one memory round trip, not three.
   const int ht = wave & 3, half = wave >> 2;  // phase A: head tile, dims half
   Frag<bf16_t> qB[8], dB[8];                  // [16 heads of tile ht] x [256 dims of half], by 32-dim step
   Frag<bf16_t> xA[4][2];                      // [16 dims] x [32 heads] of q^T: the wave's dims tiles (dO^T: from LDS)
+  const int id0 = idx[r * k + (tid < k ? tid : 0)];
+  u32x4 vq[8], vd[8], vo[8];                  // piece tid + 512 i: head 8i + wave, dims 8 lane .. 8 lane + 7
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const bf16_t* src = pass == 0 ? q : dO;
-    float dsum[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {  // piece tid + 512 i: head 8i + wave, dims 8 lane .. 8 lane + 7
-      const int head = 8 * i + wave;
-      const bool live = h0 + head < nh;
-      const long base = ((long)r * nh + h0 + head) * CD + 8 * lane;
-      const u32x4 v = load16_clamped(src + base, live, src);
-      bf16_t* dst = pass == 0 ? &sm.X[head * P + 8 * lane] : &s_dO[swz512_at(head, 8 * lane)];
-      *reinterpret_cast<u32x4*>(dst) = live ? v : u32x4{0u, 0u, 0u, 0u};
-      dsum[i] = 0.f;
-      if (pass == 1) {
-        const u32x4 ov = load16_clamped(o + base, live, o);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dsum[i] = fmaf(__uint_as_float(v[j] << 16), __uint_as_float(ov[j] << 16), dsum[i]);
-          dsum[i] = fmaf(__uint_as_float(v[j] & 0xFFFF0000u), __uint_as_float(ov[j] & 0xFFFF0000u), dsum[i]);
-        }
-        dsum[i] = live ? dsum[i] : 0.f;
-      }
-    }
-    if (pass == 1) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = dsum[i];
-#pragma unroll
-        for (int sh = 1; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
-        if (lane == 0) s_D[8 * i + wave] = x;
-      }
-      if (tid < kBwdHeads)
-        s_lse2[tid] = h0 + tid < nh ? lse[(long)r * nh + h0 + tid] * kLog2e : INFINITY;  // dead heads: P = 0
-    }
-    __syncthreads();
-    if (pass == 0) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qB[kk].load(&sm.X[(16 * ht + c16) * P + 256 * half + 32 * kk + 8 * g]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) xA[dt][h2] = frag_ct<bf16_t>(sm.X, P, 32 * h2, 64 * wave + 16 * dt, lane);
-      __syncthreads();
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) dB[kk].load(&s_dO[swz512_at(16 * ht + c16, 256 * half + 32 * kk + 8 * g)]);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int head = 8 * i + wave;
+    const bool live = h0 + head < nh;
+    const long base = ((long)r * nh + h0 + head) * CD + 8 * lane;
+    vq[i] = load16_clamped(q + base, live, q);
+    vd[i] = load16_clamped(dO + base, live, dO);
+    vo[i] = load16_clamped(o + base, live, o);
   }
+  issue_fence();
 
   // Chunks to walk: when the valid slots form a prefix (the selector pads
   // with -1 at the end), chunks past it are skipped.
   int first_bad = 0x7FFFFFFF, last_good = -1;
-  for (int sl = tid; sl < k; sl += 512) {
+  if (tid < k) {
+    if (id0 < 0) first_bad = tid; else last_good = tid;
+  }
+  for (int sl = tid + 512; sl < k; sl += 512) {
     const int id = idx[r * k + sl];
     if (id < 0) first_bad = min(first_bad, sl); else last_good = max(last_good, sl);
   }
@@ -164,12 +133,46 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
     s_ext[0][wave] = first_bad;
     s_ext[1][wave] = last_good;
   }
+
+  float dsum[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int head = 8 * i + wave;
+    const bool live = h0 + head < nh;
+    *reinterpret_cast<u32x4*>(&sm.X[head * P + 8 * lane]) = live ? vq[i] : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&s_dO[swz512_at(head, 8 * lane)]) = live ? vd[i] : u32x4{0u, 0u, 0u, 0u};
+    dsum[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dsum[i] = fmaf(__uint_as_float(vd[i][j] << 16), __uint_as_float(vo[i][j] << 16), dsum[i]);
+      dsum[i] = fmaf(__uint_as_float(vd[i][j] & 0xFFFF0000u), __uint_as_float(vo[i][j] & 0xFFFF0000u), dsum[i]);
+    }
+    dsum[i] = live ? dsum[i] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x = dsum[i];
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) x += __shfl_xor(x, sh);
+    if (lane == 0) s_D[8 * i + wave] = x;
+  }
+  if (tid < kBwdHeads)
+    s_lse2[tid] = h0 + tid < nh ? lse[(long)r * nh + h0 + tid] * kLog2e : INFINITY;  // dead heads: P = 0
   __syncthreads();
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) qB[kk].load(&sm.X[(16 * ht + c16) * P + 256 * half + 32 * kk + 8 * g]);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) xA[dt][h2] = frag_ct<bf16_t>(sm.X, P, 32 * h2, 64 * wave + 16 * dt, lane);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) dB[kk].load(&s_dO[swz512_at(16 * ht + c16, 256 * half + 32 * kk + 8 * g)]);
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     first_bad = min(first_bad, s_ext[0][w]);
     last_good = max(last_good, s_ext[1][w]);
   }
+  __syncthreads();  // q's staging area is the loop's row buffer
   const int nch = last_good < first_bad ? (last_good + KC) / KC : (k + KC - 1) / KC;
 
   // Gather of chunk ch into buffer b: wave w brings slots 4w .. 4w+3, one
