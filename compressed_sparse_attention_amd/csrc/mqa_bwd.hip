@@ -250,7 +250,9 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
     wait_vm_all_but_one();
     lds_barrier();
     if (ch + 1 < nch) gather(ch + 1, ids_next);
-    if (ch > 0) shares(ch - 1);
+    // the two waves of a SIMD (w, w + 4) take the share products and phase
+    // A in opposite orders, so their LDS and MFMA use interleave
+    if (ch > 0 && half == 0) shares(ch - 1);
     if (ch + 1 < nch) ids_next = load_ids(ch + 2);
     const bf16_t* Cs = sm.loop.C[cur];
 
@@ -276,6 +278,7 @@ __global__ __launch_bounds__(512) void mqa_bwd_kernel(int nh, int k, int nhg, fl
       sm.loop.xch[ht][1 - half][0][lane] = half ? as[0] : as[1];
       sm.loop.xch[ht][1 - half][1][lane] = half ? ad[0] : ad[1];
     }
+    if (ch > 0 && half == 1) shares(ch - 1);
     lds_barrier();
     // ---- B: P and dS for key tile `half`, heads of tile ht
     {
