@@ -173,6 +173,7 @@ __global__ __launch_bounds__(512) void gemm256_kernel(int M, int N, int K, const
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
+  if (wave >= 4) __builtin_amdgcn_s_setprio(1);  // the later wave of each SIMD issues first
   const int g = lane >> 4, c16 = lane & 15;
   const int lrow = tid >> 3;          // 0..63
   const int lcol = (tid & 7) * 8;
@@ -318,6 +319,7 @@ __global__ __launch_bounds__(512) void gemm256_dma_kernel(int M, int N, int K, c
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves: 128 rows x 64 columns each
+  if (wave >= 4) __builtin_amdgcn_s_setprio(1);  // the later wave of each SIMD issues first
   const int g = lane >> 4, c16 = lane & 15;
   const int KT = K / kDmaK;  // even
 
