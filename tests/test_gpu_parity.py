@@ -733,6 +733,8 @@ def test_sparse_mqa_backward_run_twice():
     # every key one of two rows: each row's scores take two values, so thousands of keys tie at the
     # threshold (more candidates than one LDS segment of the finishing phase holds)
     ([4 * 12000, 4 * 30000], 1, 4, 64, 16, 512, 512, "two"),
+    # the longest rows the per-chunk selector takes (64 chunks of 2048 candidates), beside shorter ones
+    ([4 * 131000, 4 * 70000, 4 * 9000], 1, 4, 64, 16, 512, 512, "random"),
 ])
 def test_decode_call_equals_two_calls(lens, nq_rep, nhI, cI, nh, c, k, keys):
     """Three back-to-back csa_decode calls on one workspace (zeroed once), each with new queries, give
