@@ -45,6 +45,11 @@ def f64(x, dtype):
     ("bf16", "bf16", 520, 296, 192),
     ("bf16", "f32", 260, 260, 1024),
     ("bf16", "bf16", 777, 1032, 1536),
+    # the copy-pipelined kernel: four 32-deep stages (one more than its ring holds), twelve with ragged
+    # edges, thirty-two on one whole tile
+    ("bf16", "bf16", 300, 264, 128),
+    ("bf16", "bf16", 513, 520, 384),
+    ("bf16", "bf16", 256, 256, 1024),
     ("bf16", "bf16", 8, 4096, 4096),  # few-row (decode token) kernel
     ("bf16", "f32", 3, 64, 200),
     ("bf16", "bf16", 16, 1000, 1536),
