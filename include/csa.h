@@ -29,8 +29,11 @@
  *   A failed launch returns CSA_ERR_HIP.  Faults inside kernels surface, as
  *   usual in HIP, at the caller's next synchronisation.  No C++ exception
  *   crosses this interface.
- * - The library is thread-safe: its only global state is a per-device
- *   property cache filled once and the thread-local error text.  Calls that
+ * - The library is thread-safe.  Its global state: a per-device property
+ *   cache filled once, the thread-local error text, the timing records of
+ *   csa_timing_enable (guarded by a lock), and the static scratch array of
+ *   csa_decode_noalloc with its per-device address (looked up once, under a
+ *   lock; calls that use the array race as described there).  Calls that
  *   share a workspace or output buffer on the same device race unless they
  *   are ordered on one stream.
  * - Inputs must be finite (no NaN/Inf); behaviour on non-finite input is
