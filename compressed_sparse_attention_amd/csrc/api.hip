@@ -86,8 +86,12 @@ std::map<std::string, Family> g_families;
 
 long scores_ld(long max_cand) { return (max_cand + 3) & ~3L; }
 
-// Long rows get the top-k's first radix level from the indexer sweep.
-bool use_hist(long max_cand) { return max_cand > 8192; }
+// Rows of more than 1024 candidates get the top-k's first radix level from
+// the indexer sweep.  The one-workgroup-per-row selector costs 12-15 us per
+// row however short the row; on the sweep's histogram the multi-workgroup
+// selector took 32 rows of 2048 candidates from 15.0 to 4.5 us (classifying
+// only) and 64 rows of up to 8192 from 18.9 to 9.4 us.
+bool use_hist(long max_cand) { return max_cand > 1024; }
 // ... and, for few rows, a selector that spreads each row over workgroups.
 int topk_chunks(long max_cand) { return (int)((max_cand + csa::kMChunk - 1) / csa::kMChunk); }
 bool use_lists(long n_queries, long max_cand) {

@@ -23,6 +23,8 @@
 // itself.  Short batches (decode) split the slots across workgroups to fill
 // the GPU; each split then writes its unnormalised output and (max, sum) per
 // head, and the combine kernel merges the splits by log-sum-exp.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "select.hpp"
@@ -1302,16 +1304,19 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(long nrows, int nh, in
   if (d4 == 0 && lse) lse[rh] = (M == -INFINITY) ? -INFINITY : (M + log2f(L)) * 0.6931471805599453f;
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; threads
+// that race on the first query store the same value).
 int compute_units() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int q = 0;
+    n = hipDeviceGetAttribute(&q, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && q > 0 ? q : 256;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 struct Plan {
@@ -1425,10 +1430,17 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 bool mqa_supported_c(int c) { return c == 64 || c == 128 || c == 256 || c == 512 || c == 1024; }
 
+// The attention finishes the selection when every split is one 128-row chunk
+// and the whole grid runs in one round (the kernel's LDS allows one workgroup
+// per CU): in a second round the finishing phase would be paid again, which
+// measured slower than the top-k launch finishing the rows (32 queries x 4
+// splits x 4 head tiles: attention 15.4 -> 23.4 us for 10.5 us less top-k).
 bool mqa_tile_selects(long n_queries, int nh, int c, int k, bool bf16) {
   if (n_queries <= 0 || c != 512) return false;
   const Plan p = plan(n_queries, nh, c, k, bf16);
-  return p.tile && p.cps == 1;
+  if (!p.tile || p.cps != 1) return false;
+  const long blocks = ((n_queries * p.nsplit + 7) / 8) * 8 * p.nhg;  // as launched
+  return blocks <= compute_units();
 }
 
 size_t mqa_workspace_bytes(long n_queries, int nh, int c, int k, bool bf16) {
