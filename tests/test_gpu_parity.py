@@ -593,6 +593,10 @@ def test_index_topk_stream_same_sets_as_dense():
     ("bf16", 600, 20, 512, 96, 120, 2.0, "scatter"),
     ("bf16", 530, 100, 512, 200, 250, 4.0, "ragged"),  # two head groups, the second partial
     ("bf16", 520, 192, 512, 128, 200, 2.0, "ragged"),  # three head groups of one query in different workgroups
+    # short batches of many queries (16-head tiles over several rounds), partial head tiles, c = 512, 256, 128
+    ("bf16", 200, 20, 512, 300, 400, 2.0, "scatter"),
+    ("bf16", 40, 40, 256, 400, 500, 4.0, "ragged"),
+    ("bf16", 100, 64, 128, 300, 350, 1.0, "prefix"),
 ])
 def test_sparse_mqa(dtype, B, nh, c, k, nblk, qmult, layout):
     rng = synth.rng_for(B * nh + k)
