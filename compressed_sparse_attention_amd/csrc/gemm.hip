@@ -572,6 +572,108 @@ __global__ __launch_bounds__(256) void gemm_smallm_pair_kernel(int M, int K, con
 }
 
 // ---------------------------------------------------------------------------
+// Few rows with a short K (M <= 16, K <= kWideMaxK): the products of the
+// decode-time query side (eqs 6 and 10, K = d_c).  A 256-thread workgroup owns
+// 64 output columns; each wave owns 16 of them over ALL of K, so no partial
+// sums cross waves.  The few rows of X (all of K) are staged once in LDS, and
+// each wave streams its 16 weight rows through a rolling window of
+// kWideDepth 128-deep super-steps: a slot is refilled as soon as its MFMAs
+// are issued, so a wave computes while its later weights stream in (the
+// pattern of the decode indexer sweep).  The k-slots are permuted as in
+// smallm_tile (load kk of lane group g takes k = 32 kk + 8 g .. +7 of the
+// super-step, on both operands).
+// ---------------------------------------------------------------------------
+constexpr int kWideN = 64;        // output columns per workgroup
+constexpr int kWideMaxK = 1920;  // keeps the X stage within 64 KiB of LDS
+constexpr int kWideDepth = 4;     // super-steps in flight per wave
+
+// LDS bytes of one workgroup: 16 rows of X over K rounded up to a super-step,
+// rows staggered by 32 bytes (conflict-free 16-byte fragment reads).
+inline uint32_t wide_lds_bytes(long K) {
+  const long kp = (K + kSmSuper - 1) / kSmSuper * kSmSuper;
+  return (uint32_t)(16 * (kp + 16) * sizeof(bf16_t));
+}
+
+template <typename TO>
+__device__ __forceinline__ void smallm_wide_tile(int M, int N, int K, const bf16_t* __restrict__ X, long ldx,
+                                                 const bf16_t* __restrict__ W, long ldw, TO* __restrict__ Y,
+                                                 long ldy, long n0, bf16_t* __restrict__ s_x) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nsup = (K + kSmSuper - 1) / kSmSuper;
+  const int XP = nsup * kSmSuper + 16;  // LDS pitch of an X row
+  const long col = n0 + 16 * wave + c16;
+  const bf16_t* Wr = W + (col < N ? col : 0) * ldw + 8 * g;  // columns past N read row 0: not written
+
+  Frag<bf16_t> wb[kWideDepth][4];
+  // pieces past K read the start of the lane's own row (X is zero there)
+  auto issue = [&](int ss, int slot) {
+    if (ss >= nsup) return;  // uniform
+    const long k = (long)ss * kSmSuper;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) wb[slot][kk].load_clamped(Wr + k + 32 * kk, k + 32 * kk + 8 * g < K, Wr);
+  };
+#pragma unroll
+  for (int d = 0; d < kWideDepth; ++d) issue(d, d);
+  issue_fence();
+
+  // X rows 0..15 over k < nsup * 128 into LDS; rows past M and pieces past K
+  // are zero (K % 8 == 0: a piece is all in or all out)
+  const int pieces = nsup * (kSmSuper / 8);
+  for (int p = tid; p < 16 * pieces; p += 256) {
+    const int row = p / pieces, kc = (p - row * pieces) * 8;
+    const bool ok = row < M && kc < K;
+    u32x4 v = load16_clamped(X + (long)row * ldx + kc, ok, X);
+    if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(&s_x[row * XP + kc]) = v;
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16_t* xr = s_x + c16 * XP + 8 * g;
+  for (int ss = 0; ss < nsup; ss += kWideDepth) {
+#pragma unroll
+    for (int d = 0; d < kWideDepth; ++d) {
+      if (ss + d < nsup) {  // uniform
+        Frag<bf16_t> xf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) xf[kk].load(xr + (ss + d) * kSmSuper + 32 * kk);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) mma(acc, xf[kk], wb[d][kk]);
+      }
+      issue(ss + d + kWideDepth, d);
+      issue_fence();
+    }
+  }
+  // acc[r] = Y[4 g + r][col]
+  if (col < N) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < M) Y[row * ldy + col] = from_f32<TO>(acc[r]);
+    }
+  }
+}
+
+// Two such products of the same X in one launch (workgroups below nb1 take
+// Y1 = X W1, the rest Y2 = X W2).
+template <typename TO1, typename TO2>
+__global__ __launch_bounds__(256) void gemm_smallm_wide_pair_kernel(int M, int K, const bf16_t* __restrict__ X,
+                                                                    long ldx, int nb1, int N1,
+                                                                    const bf16_t* __restrict__ W1, long ldw1,
+                                                                    TO1* __restrict__ Y1, long ldy1, int N2,
+                                                                    const bf16_t* __restrict__ W2, long ldw2,
+                                                                    TO2* __restrict__ Y2, long ldy2) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t s_x_dyn[];
+  const int b = (int)blockIdx.x;
+  if (b < nb1)
+    smallm_wide_tile<TO1>(M, N1, K, X, ldx, W1, ldw1, Y1, ldy1, (long)b * kWideN, s_x_dyn);
+  else
+    smallm_wide_tile<TO2>(M, N2, K, X, ldx, W2, ldw2, Y2, ldy2, (long)(b - nb1) * kWideN, s_x_dyn);
+}
+
+// ---------------------------------------------------------------------------
 // dst[c][r] = src[r][c] for r < R, c < C, and dst[c][r] = 0 for R <= r < Rp
 // (the padded tail of each destination row).  64 x 64 tiles through LDS with
 // 16-byte loads and stores; requires C, Rp, the leading dimensions and both
@@ -664,6 +766,12 @@ namespace {
 template <typename TO1, typename TO2>
 hipError_t launch_pair_typed(long M, long K, const void* X, long ldx, long N1, const void* W1, long ldw1, void* Y1,
                              long ldy1, long N2, const void* W2, long ldw2, void* Y2, long ldy2, hipStream_t s) {
+  if (K <= kWideMaxK && N1 + N2 >= 256L * kWideN) {  // enough 64-column workgroups to fill the chip
+    const int nw1 = (int)((N1 + kWideN - 1) / kWideN), nw2 = (int)((N2 + kWideN - 1) / kWideN);
+    return launch("gemm_smallm", gemm_smallm_wide_pair_kernel<TO1, TO2>, dim3((unsigned)(nw1 + nw2)), dim3(256),
+                  wide_lds_bytes(K), s, (int)M, (int)K, (const bf16_t*)X, ldx, nw1, (int)N1, (const bf16_t*)W1,
+                  ldw1, (TO1*)Y1, ldy1, (int)N2, (const bf16_t*)W2, ldw2, (TO2*)Y2, ldy2);
+  }
   const int nb1 = (int)((N1 + kSmN - 1) / kSmN), nb2 = (int)((N2 + kSmN - 1) / kSmN);
   const dim3 grid((unsigned)(nb1 + nb2));
   // super-step depth as for one product of this K

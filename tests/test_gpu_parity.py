@@ -71,6 +71,11 @@ def test_project(din, dout, M, N, K):
     ("bf16", "bf16", "f32", 8, 4096, 64, 4096),    # one launch: a stacked H-side weight with the w^I head weights
     ("bf16", "bf16", "bf16", 8, 1000, 264, 1536),  # one launch, ragged column blocks in both products
     ("bf16", "f32", "bf16", 3, 40, 24, 200),       # one launch, K tail
+    # 64-column workgroups over all of K (the decode query side: eq 10 and eq 6 weights, d_c = 1536)
+    ("bf16", "bf16", "bf16", 8, 32768, 8192, 1536),
+    # the same kernel with ragged column blocks in both products, a K tail inside a super-step, 5 rows
+    ("bf16", "bf16", "f32", 5, 12344, 4104, 1000),
+    ("bf16", "bf16", "bf16", 16, 16000, 400, 1920),  # 16 rows, the largest K it takes
     ("bf16", "bf16", "f32", 40, 296, 64, 200),     # more than 16 rows: two launches
     ("f32", "f32", "f32", 5, 48, 16, 24),
 ])
