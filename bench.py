@@ -619,6 +619,18 @@ def calib_copy(torch):
     print(json.dumps({"calib_copy_bytes_each_way": 4 * n, "launches": 3}))
 
 
+# the legs, by the name --only takes
+_LEGS = {
+    "decode": lambda a, t, api, sy, la: bench_decode(a, t, api, sy, la),
+    "prefill": lambda a, t, api, sy, la: bench_prefill(a, t, api, sy, la, "dense"),
+    "selection_long": lambda a, t, api, sy, la: bench_selection_long(a, t, api, sy, la),
+    "decode_step": lambda a, t, api, sy, la: bench_decode_step(a, t, api, sy, la),
+    "prefill_varlen": lambda a, t, api, sy, la: bench_prefill_varlen(a, t, api, sy, la),
+    "prefill_backward": lambda a, t, api, sy, la: bench_prefill_backward(a, t, api, sy, la),
+    "other_configs": lambda a, t, api, sy, la: bench_other_configs(a, t, api, sy, la),
+}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -635,6 +647,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--only", choices=sorted(_LEGS), default=None,
+                    help="run one leg on its own and print its record (for per-leg profiler traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the CSA path here is single-GPU "
@@ -647,6 +661,15 @@ def main():
         return
     from compressed_sparse_attention_amd import api, layer, synth
     api.lib()
+    if args.only:
+        rec = _LEGS[args.only](args, torch, api, synth, layer)
+        if args.only == "decode":
+            rec = {k: rec[k] for k in ("ms", "ms_eager", "ms_warm", "roofline", "step_bytes")} | {
+                "kernels_us": {n: round(s_["avg_us"], 3) for n, s_ in rec["kernels"].items()}}
+        elif args.only == "prefill":
+            rec = rec[0]
+        print(json.dumps({"only": args.only, "record": rec}, default=str), flush=True)
+        return
 
     dec = bench_decode(args, torch, api, synth, layer)
     pre = pre_stream = sel_long = None
