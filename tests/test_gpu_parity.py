@@ -76,6 +76,9 @@ def test_project(din, dout, M, N, K):
     # the same kernel with ragged column blocks in both products, a K tail inside a super-step, 5 rows
     ("bf16", "bf16", "f32", 5, 12344, 4104, 1000),
     ("bf16", "bf16", "bf16", 16, 16000, 400, 1920),  # 16 rows, the largest K it takes
+    # the waves splitting K over d-long rows: 3 rows, a K tail inside a super-step, ragged column blocks
+    ("bf16", "bf16", "f32", 3, 296, 40, 2200),
+    ("bf16", "bf16", "bf16", 8, 520, 16, 4096),
     ("bf16", "bf16", "f32", 40, 296, 64, 200),     # more than 16 rows: two launches
     ("f32", "f32", "f32", 5, 48, 16, 24),
 ])
