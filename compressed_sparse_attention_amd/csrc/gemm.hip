@@ -656,6 +656,14 @@ __device__ __forceinline__ void smallm_wide_tile(int M, int N, int K, const bf16
   }
 }
 
+template <typename TO>
+__global__ __launch_bounds__(256) void gemm_smallm_wide_kernel(int M, int N, int K, const bf16_t* __restrict__ X,
+                                                               long ldx, const bf16_t* __restrict__ W, long ldw,
+                                                               TO* __restrict__ Y, long ldy) {
+  extern __shared__ __attribute__((aligned(16))) bf16_t s_x_dyn[];
+  smallm_wide_tile<TO>(M, N, K, X, ldx, W, ldw, Y, ldy, (long)blockIdx.x * kWideN, s_x_dyn);
+}
+
 // Two such products of the same X in one launch (workgroups below nb1 take
 // Y1 = X W1, the rest Y2 = X W2).
 template <typename TO1, typename TO2>
@@ -708,6 +716,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(long R, long C, long Rp,
 
 hipError_t launch_gemm(csa_dtype in_dt, csa_dtype out_dt, long M, long N, long K, const void* X,
                        long ldx, const void* W, long ldw, void* Y, long ldy, hipStream_t s) {
+  if (in_dt == CSA_BF16 && M <= 16 && K <= kWideMaxK && N >= 256L * kWideN) {  // enough 64-column workgroups
+    const dim3 gw((unsigned)((N + kWideN - 1) / kWideN));
+    if (out_dt == CSA_BF16)
+      return launch("gemm_smallm", gemm_smallm_wide_kernel<bf16_t>, gw, dim3(256), wide_lds_bytes(K), s, (int)M,
+                    (int)N, (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (bf16_t*)Y, ldy);
+    return launch("gemm_smallm", gemm_smallm_wide_kernel<float>, gw, dim3(256), wide_lds_bytes(K), s, (int)M, (int)N,
+                  (int)K, (const bf16_t*)X, ldx, (const bf16_t*)W, ldw, (float*)Y, ldy);
+  }
   if (in_dt == CSA_BF16 && M <= 16) {
     // all of a wave's super-steps in flight when K is short (measured: up to
     // 8% faster at K = 1536), two otherwise

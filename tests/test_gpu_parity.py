@@ -54,6 +54,9 @@ def f64(x, dtype):
     ("bf16", "f32", 3, 64, 200),
     ("bf16", "bf16", 16, 1000, 1536),
     ("bf16", "bf16", 1, 40, 8),
+    # few rows, short K, many columns: 64-column workgroups over all of K (a ragged last block, a K tail)
+    ("bf16", "bf16", 8, 32768, 1536),
+    ("bf16", "f32", 5, 16392, 1000),
 ])
 def test_project(din, dout, M, N, K):
     rng = synth.rng_for(M * 7 + N)
