@@ -4,10 +4,12 @@
 // row-vector projections of this form.  Both operands are K-contiguous, so
 // each 16x16x32 MFMA operand is one 16-byte LDS read per lane.
 //
-// Four kernels: gemm_smallm (below) for bf16 with M <= 16, gemm256 and its
-// copy-pipelined form gemm256_dma (K a multiple of 64) (below) for bf16
-// operands with M, N >= 256, and the general gemm_nt (fp32 too, any
-// shape): 128x128 output tile per 256-thread
+// Kernels: gemm_smallm and its wide form (below) for bf16 with M <= 16 (the
+// wide form, 64 columns per workgroup over all of K with X staged in LDS, for
+// a short K and many columns), gemm256 and its copy-pipelined form
+// gemm256_dma (K a multiple of 64) (below) for bf16 operands with
+// M, N >= 256, and the general gemm_nt (fp32 too, any shape): 128x128 output
+// tile per 256-thread
 // workgroup (4 waves in 2x2, each 64x64 = 4x4 MFMA tiles), K staged through
 // LDS in 128-byte slabs, double buffered: the next slab is fetched into
 // registers while the current one feeds the MFMAs.  LDS rows are padded by
