@@ -50,8 +50,9 @@ def _kernel_stats(api, names):
     return out
 
 
-def _traffic(kernel: str):
-    """HBM bytes per launch from committed counter runs, while the kernel's sources are unchanged."""
+def _traffic(kernel: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (or the record's `key`) from committed counter runs, while the kernel's sources are
+    unchanged."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -65,7 +66,7 @@ def _traffic(kernel: str):
             h.update(f.read())
     if rec.get("sources_sha256") != h.hexdigest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get(key)
 
 
 def per_step_stats(torch, run_one, n_pool, steps):
@@ -569,7 +570,8 @@ def bench_decode_step(args, torch, api, synth, layer):
         t_step = g["total_ms"] / args.steps * 1e-3
         ach = gemm_bytes / t_step / 1e9
         roof = {"kernel": "gemm_smallm", "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": _traffic("gemm_smallm_decode_step", "hbm_bytes_per_step"),
                 "algorithmic_bytes_per_step": gemm_bytes, "launches_per_step": g["launches"] // args.steps}
     step_bytes = gemm_bytes + 2 * B * N * cI + B * (2 * wd.k * c + 2 * wd.nh * c + 4 * wd.k)
     return {"workload": "decode_step_b8_ctx128k_d4096_bf16", "batch": B, "context": L, "d": d, "dc": dc,
