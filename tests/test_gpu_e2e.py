@@ -333,3 +333,40 @@ def test_prefill_varlen_packed_sequences(dtype):
         _check_o_over_gpu_selection(idx_all[sl], ref["q"], ref["Ccomp"], o_all[sl], 1 / math.sqrt(w.c))
         t0 += L
         b0 += nb
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("selection", ["dense", "stream"])
+def test_prefill_run_twice_bitwise(selection):
+    """The forward path has no order-dependent accumulation (no atomics into outputs, fixed reduction
+    orders), so two prefills of the same 4096 tokens at the long-prefill widths (d = 4096, c = 512, 64 + 64
+    heads, k = 512), each into fresh buffers, give bit-identical compressed caches, projections, selections,
+    outputs and lse; and so do two packed prefills of ragged sequences."""
+    w = synth.WORKLOADS[3]
+    P = synth.make_prefill(w, seed=91, n=4096)
+    W = pack_prefill_params(P, w.dtype, DEV)
+    H = to_device(P["H"], w.dtype, DEV)
+    runs = []
+    for _ in range(2):
+        buf = prefill(H, W, w.m, w.k, w.nh, w.nhI, selection=selection)
+        torch.cuda.synchronize()
+        runs.append([buf.Ccomp.clone(), buf.KIcomp.clone(), buf.qI.clone(), buf.wI.clone(), buf.q.clone(),
+                     buf.idx.clone(), buf.o.clone(), buf.lse.clone()])
+        del buf
+    names = ("Ccomp", "KIcomp", "qI", "wI", "q", "idx", "o", "lse")
+    for a, b, nm in zip(runs[0], runs[1], names):
+        assert torch.equal(_bits(a), _bits(b)), f"{selection}: {nm} differs between runs"
+    assert int((runs[0][5] >= 0).sum()) > 0
+    if selection == "dense":
+        lengths = [1500, 7, 0, 2589]
+        outs = []
+        for _ in range(2):
+            vb = prefill_varlen(H, lengths, W, w.m, w.k, w.nh, w.nhI)
+            torch.cuda.synchronize()
+            outs.append([vb.Ccomp.clone(), vb.KIcomp.clone(), vb.idx.clone(), vb.o.clone(), vb.lse.clone()])
+            del vb
+        for a, b, nm in zip(outs[0], outs[1], ("Ccomp", "KIcomp", "idx", "o", "lse")):
+            assert torch.equal(_bits(a), _bits(b)), f"packed: {nm} differs between runs"
